@@ -1,0 +1,110 @@
+/*
+ * kda.h — C ABI of the MI355X (gfx950) KDA chunked forward library (libkda.so).
+ *
+ * KDA (Kimi Delta Attention) is a gated delta-rule linear attention with a
+ * per-channel decay gate.  Per sequence and head it carries a K x V fp32 state
+ * S and, token by token, computes
+ *     q^ = q / sqrt(|q|^2 + 1e-6),  k^ = k / sqrt(|k|^2 + 1e-6)
+ *     beta  = sigmoid(raw_beta)
+ *     g_c   = lower_bound * sigmoid(exp(A_log[h]) * (raw_gate_c + dt_bias[h, c]))
+ *     S     = (I - beta k^ k^T) Diag(exp(g)) S + beta k^ v^T
+ *     o     = scale * S^T q^
+ * The library evaluates this with 64-token chunks (partial tail chunks
+ * allowed) on one GPU.
+ *
+ * Sources.  The argument list and roles follow the 14-argument
+ * torch.ops._flashkda_C.fwd call and get_workspace_size(T, H, N) in the vLLM
+ * PR report "[Kimi-K3] Bump FlashKDA to fix unstable inverse" (section
+ * "关键源码片段", the near-collinear-keys test).  The in-kernel L2 norm, beta
+ * sigmoid and gate come from the chunk_kda flags on the instagit page "What
+ * CUDA Version Is Required to Use FlashKDA?" (section "Usage Examples").  The
+ * pages never print the gate formula; the one above is this library's stated
+ * reading, as is eps = 1e-6 and reading the output from the updated state.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous,
+ *     in the layouts given below.  The library never allocates, frees or
+ *     synchronises; kda_fwd is asynchronous on `stream`.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Argument checks happen on the host before any device work; a rejected
+ *     call returns its status and touches no memory.
+ *   - There is no fallback path: unsupported shapes are rejected.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_SUCCESS = 0,
+  KDA_ERR_INVALID = 1,     /* NULL required pointer, bad sizes, inconsistent B/N */
+  KDA_ERR_UNSUPPORTED = 2, /* K != 128, V != 128, or lower_bound outside [-5, 0] */
+  KDA_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than kda_workspace_size() */
+  KDA_ERR_LAUNCH = 4       /* a kernel launch failed (hipGetLastError after launch) */
+} kda_status_t;
+
+/*
+ * Bytes of device workspace kda_fwd needs for T_total packed tokens, H heads
+ * and N sequences (the page's get_workspace_size(T, H, 1) for one sequence).
+ * The caller allocates it (any alignment >= 256 bytes) and passes it to
+ * kda_fwd.  Its contents are scratch: undefined before and after a call.
+ * Returns 0 if any argument is < 1 (T_total may be 0).
+ */
+size_t kda_workspace_size(int64_t T_total, int64_t H, int64_t N);
+
+/*
+ * 1 if kda_fwd supports head dims K, V with this lower_bound, else 0 (the
+ * page's is_flashkda_supported(128, bf16, lower_bound) probe).  Supported:
+ * K == V == 128 and -5 <= lower_bound <= 0.  The -5 limit keeps every
+ * 16-token decay ratio inside fp32/bf16 range (exp(16 * 5) < FLT_MAX).
+ */
+int kda_is_supported(int64_t K, int64_t V, float lower_bound);
+
+/*
+ * KDA chunked forward.
+ *
+ *   q, k        bf16 [B, T, H, K]   (q == k is allowed: the pages pass one
+ *                                    tensor twice)
+ *   v           bf16 [B, T, H, V]
+ *   raw_gate    bf16 [B, T, H, K]   (pre-activation gate)
+ *   raw_beta    bf16 [B, T, H]      (pre-sigmoid write strength)
+ *   scale       output scale (e.g. K^-0.5)
+ *   out         bf16 [B, T, H, V]   written; must not overlap any input
+ *   workspace   device scratch of workspace_bytes >= kda_workspace_size(B*T, H, N)
+ *   A_log       fp32 [H]
+ *   dt_bias     fp32 [H, K]
+ *   lower_bound log-decay floor, in [-5, 0]
+ *   initial_state fp32 [N, H, K, V] (S[k][v] at offset k*V + v), or NULL for zeros
+ *   final_state   fp32 [N, H, K, V] written, or NULL to skip; may equal
+ *                 initial_state (in-place update)
+ *   cu_seqlens  int32 [N + 1] device array of packed sequence offsets, or NULL.
+ *               With cu_seqlens, B must be 1 and T is the packed token count;
+ *               cu_seqlens[0] == 0, non-decreasing, cu_seqlens[N] == T is the
+ *               caller's contract (not checked: that would need a device sync).
+ *               Zero-length sequences are allowed (final = initial).
+ *               Without cu_seqlens there are N == B sequences of length T.
+ *   B, T, H, K, V, N sizes as above (T >= 0; B, H, N >= 1)
+ *   stream      hipStream_t as void*
+ *
+ * Returns KDA_SUCCESS after enqueueing the work, or an error status.
+ */
+kda_status_t kda_fwd(const void* q, const void* k, const void* v, const void* raw_gate,
+                     const void* raw_beta, float scale, void* out, void* workspace,
+                     size_t workspace_bytes, const float* A_log, const float* dt_bias,
+                     float lower_bound, const float* initial_state, float* final_state,
+                     const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t K,
+                     int64_t V, int64_t N, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* kda_status_string(kda_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI library (CPU only: no kernel is launched).
+
+Every rejected call returns its status before any HIP call, so these run on a
+machine without a GPU.  Pointers passed here are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunked_gated_delta_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails a host check
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(kda.exported_symbols)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(kda.library_path)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_library_exports_are_c_abi():
+    # extern "C": unmangled names in the dynamic symbol table
+    import subprocess
+    syms = subprocess.run(["nm", "-D", "--defined-only", kda.library_path], capture_output=True,
+                          text=True, check=True).stdout
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", syms, re.M), name
+
+
+def test_workspace_size():
+    assert kda.kda_workspace_size(200, 2, 1) > 0
+    assert kda.kda_workspace_size(32768, 96, 1) >= 256
+    assert kda.kda_workspace_size(65536, 32, 16) >= kda.kda_workspace_size(65536, 32, 1)
+    assert kda.kda_workspace_size(0, 2, 1) > 0          # an empty batch is legal
+    assert kda.kda_workspace_size(10, 0, 1) == 0
+    assert kda.kda_workspace_size(10, 2, 0) == 0
+    # room for a processing order of all N sequences
+    assert kda.kda_workspace_size(10 ** 6, 1, 10 ** 5) >= 4 * 10 ** 5
+
+
+def test_is_supported():
+    assert kda.kda_is_supported(128, 128, -5.0)
+    assert kda.kda_is_supported(128, 128, 0.0)
+    assert kda.kda_is_supported(128, 128, -2.5)
+    assert not kda.kda_is_supported(64, 128, -5.0)
+    assert not kda.kda_is_supported(128, 256, -5.0)
+    assert not kda.kda_is_supported(128, 128, -5.5)
+    assert not kda.kda_is_supported(128, 128, 0.5)
+
+
+def call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, scale=0.088, out=FAKE, ws=FAKE,
+             ws_bytes=1 << 20, A_log=FAKE, dt=FAKE, lb=-5.0, init=None, fin=None, cu=None,
+             B=1, T=200, H=2, K=128, V=128, N=1, stream=None)
+    a.update(over)
+    return kda.raw_call(a["q"], a["k"], a["v"], a["g"], a["b"], ctypes.c_float(a["scale"]),
+                        a["out"], a["ws"], ctypes.c_size_t(a["ws_bytes"]), a["A_log"], a["dt"],
+                        ctypes.c_float(a["lb"]), a["init"], a["fin"], a["cu"], a["B"], a["T"],
+                        a["H"], a["K"], a["V"], a["N"], a["stream"])
+
+
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "g", "b", "out", "A_log", "dt"])
+def test_null_required_pointer_is_invalid(field):
+    assert call(**{field: None}) == INVALID
+
+
+@pytest.mark.parametrize("over", [dict(B=0), dict(T=-1), dict(H=0), dict(N=0), dict(N=2),
+                                  dict(B=2, N=2, cu=FAKE), dict(scale=float("nan"))])
+def test_bad_sizes_are_invalid(over):
+    assert call(**over) == INVALID
+
+
+@pytest.mark.parametrize("over", [dict(K=64), dict(V=64), dict(K=256, V=256), dict(lb=-6.0),
+                                  dict(lb=1.0)])
+def test_unsupported_shapes(over):
+    assert call(**over) == UNSUPPORTED
+
+
+def test_workspace_checks():
+    need = kda.kda_workspace_size(200, 2, 1)
+    assert call(ws=None) == WORKSPACE
+    assert call(ws_bytes=need - 1) == WORKSPACE
+    assert call(ws_bytes=0) == WORKSPACE
+
+
+def test_status_strings():
+    lib = ctypes.CDLL(kda.library_path)
+    lib.kda_status_string.restype = ctypes.c_char_p
+    for code, name in kda.STATUS.items():
+        assert lib.kda_status_string(code).decode() == name
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
+    v = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        kda.kda_fwd(x, x, v, x, torch.zeros(1, 4, 1, dtype=torch.bfloat16), 1.0, v.clone(),
+                    torch.zeros(512, dtype=torch.uint8), torch.zeros(1), torch.zeros(1, 128), -5.0)
