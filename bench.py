@@ -1,0 +1,189 @@
+"""Benchmark of the KDA chunked forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one kda_fwd call (every kernel of the forward pass) over the
+throughput headline workload: B=1, T=32768, H=96, K=V=128, bf16 q/k/v/raw_gate
+and raw_beta ~N(0,1), A_log ~U(0, ln 16), dt_bias ~N(0, 0.1), lower_bound -5,
+scale K^-0.5, a zero fp32 initial state, final state written.  Inputs are
+synthetic (seeded, tests/workloads.py) and resident in HBM before timing
+starts.  Prints one JSON line.
+
+Roofline: the forward kernel is HBM-bound.  Its algorithmic traffic is
+1282 bytes per head-token (q, k, v, raw_gate: 4 x 128 x 2 B; raw_beta 2 B;
+out 128 x 2 B) plus 2 x 64 KiB of fp32 state I/O per (sequence, head); the
+achieved rate is that byte count divided by the kernel's average duration,
+measured with HIP events recorded on the launch stream around every timed
+launch.  ``traffic`` is the measured HBM bytes per launch from rocprofv3
+FETCH_SIZE / WRITE_SIZE counters (profiles/), reported only while the kernel
+source is unchanged since the counters were taken.
+
+cpu_baseline: the fp64 CPU oracle (test infrastructure) timed on the host's
+cores over a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path[:0] = [ROOT, os.path.join(ROOT, "tests")]
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+BF16_DENSE_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
+BYTES_PER_HEAD_TOKEN = 4 * 128 * 2 + 2 + 128 * 2
+STATE_BYTES = 128 * 128 * 4
+KERNEL_SRC = os.path.join(ROOT, "chunked_gated_delta_amd", "csrc", "kda_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_fwd_c3_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if doc.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return doc.get("hbm_bytes_per_launch")
+
+
+def algorithmic_flops_per_head_token(C=64, K=128, V=128):
+    # triangular-aware count of the chunk algebra (A_kk, A_qk, T, W, U, D, O, S update)
+    return (C - 1) * K + (C + 1) * K + C * C / 3 + (C + 1) * K + (C + 1) * V + 3 * 2 * K * V \
+        + (C + 1) * V
+
+
+def cpu_baseline(x, heads):
+    """Time the oracle on `heads` of the workload (all tokens)."""
+    from oracle import oracle_fwd, oracle_threads
+
+    t0 = time.perf_counter()
+    oracle_fwd(x.q, x.k, x.v, x.raw_gate, x.raw_beta, x.scale, x.A_log, x.dt_bias,
+               x.lower_bound, x.initial_state, x.cu_seqlens, heads=heads, want_final=True)
+    dt = time.perf_counter() - t0
+    ht = x.B * x.T * len(heads)
+    return {"value": ht / dt, "unit": "head-tokens/s", "cores": oracle_threads(), "kind": "oracle",
+            "sample": f"fp64 token recurrence over heads 0..{len(heads) - 1} of {x.H}, all "
+                      f"{x.T} tokens ({ht} head-tokens, {dt:.1f} s)"}
+
+
+def copy_calibration(gib: float = 2.0):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--T", type=int, default=32768)
+    ap.add_argument("--H", type=int, default=96)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=96)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (the KDA forward shards heads and "
+              "sequences with no exchange; multi-GPU runs are out of scope)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+
+    import chunked_gated_delta_amd as kda
+    import workloads
+
+    x = workloads.c3_headline(T=args.T, H=args.H)
+    x.initial_state = torch.zeros(1, x.H, x.K, x.V, dtype=torch.float32)
+    dev = torch.device("cuda:0")
+    d = lambda t: None if t is None else t.to(dev)  # noqa: E731
+    q, k, v, g, b = d(x.q), d(x.k), d(x.v), d(x.raw_gate), d(x.raw_beta)
+    al, dt, init = d(x.A_log), d(x.dt_bias), d(x.initial_state)
+    cu = torch.tensor([0, x.T], dtype=torch.int32, device=dev)
+    out = torch.empty_like(v)
+    fin = torch.empty_like(init)
+    ws = torch.empty(kda.kda_workspace_size(x.T, x.H, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def step():
+        kda.kda_fwd(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, init, fin, cu,
+                    stream=sh)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_kern_s = sum(kern_ms) / len(kern_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    head_tokens = x.B * x.T * x.H
+    value = head_tokens / (wall / args.steps)
+
+    alg_bytes = head_tokens * BYTES_PER_HEAD_TOKEN + 2 * x.N * x.H * STATE_BYTES
+    achieved = alg_bytes / avg_kern_s / 1e9
+    flops = head_tokens * algorithmic_flops_per_head_token()
+    line = {
+        "metric": "KDA fwd head-tokens/s at H=96 T=32K bf16; % of MFMA/HBM roofline",
+        "value": value,
+        "unit": "head-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"kda_fwd B=1 T={x.T} H={x.H} K=V=128 chunk=64 lower_bound=-5 "
+                               "zero initial state, final state written",
+                   "B": 1, "T": x.T, "H": x.H, "K": 128, "V": 128},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "kernel": "kda_fwd_kernel", "avg_kernel_ms": avg_kern_s * 1e3,
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "mfma": {"achieved_tflops": flops / avg_kern_s / 1e12, "peak_tflops": BF16_DENSE_TFLOPS,
+                 "frac": flops / avg_kern_s / 1e12 / BF16_DENSE_TFLOPS,
+                 "algorithmic_flops_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        heads = list(range(min(args.cpu_heads, x.H)))
+        line["cpu_baseline"] = cpu_baseline(x, heads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -121,7 +121,24 @@ struct Params {
   int n_items;           // N * H
   float scale;
   float lb2;             // lower_bound * log2(e)
+#ifdef KDA_PHASE_TIMERS
+  unsigned long long* timers;  // [grid][16] per-phase cycle totals seen by wave 0
+#endif
 };
+
+// Optional per-phase cycle counters (compiled out unless KDA_PHASE_TIMERS is
+// defined): thread 0 accumulates s_memtime deltas between phase marks.
+#ifdef KDA_PHASE_TIMERS
+#define KDA_TIMER_DECL unsigned long long tacc_[12] = {0}; unsigned long long tlast_ = 0;
+#define KDA_TIMER_MARK(i) do { if (tid == 0) { const unsigned long long t_ = __builtin_readcyclecounter(); \
+    if ((i) > 0) tacc_[(i) - 1] += t_ - tlast_; tlast_ = t_; } } while (0)
+#define KDA_TIMER_STORE() do { if (tid == 0 && p.timers) for (int i_ = 0; i_ < 12; ++i_) \
+    p.timers[blockIdx.x * 16 + i_] = tacc_[i_]; } while (0)
+#else
+#define KDA_TIMER_DECL
+#define KDA_TIMER_MARK(i) do { } while (0)
+#define KDA_TIMER_STORE() do { } while (0)
+#endif
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
@@ -229,8 +246,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
       }
   }
 
+  KDA_TIMER_DECL
   for (int64_t c0 = bos; c0 < eos; c0 += CH) {
     const int L = (int)((eos - c0) < CH ? (eos - c0) : CH);
+    KDA_TIMER_MARK(0);
 
     // =========================== 1. prep ===================================
     const int ti = 16 * w + tl;  // chunk-local token of this lane
@@ -293,6 +312,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
     }
     if (gq == 0) sB[ti] = beta;
     __syncthreads();
+    KDA_TIMER_MARK(1);
     if (tid < KD) {
       float acc = 0.f;
       sP[tid] = 0.f;
@@ -304,6 +324,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
       sGL[tid] = fexp2(acc);
     }
     __syncthreads();
+    KDA_TIMER_MARK(2);
 
     // operands of this lane's token (32 channels)
     bf16x8 kLFh[4], kLFl[4], kEh[4], kEl[4], qLF[4];
@@ -352,6 +373,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
       }
     }
     __syncthreads();
+    KDA_TIMER_MARK(3);
 
     // ======================= 2. A_kk and A_qk ==============================
     // wave w owns row-block w; lane holds C[16w + 4gq + ii][16b + tl]
@@ -412,6 +434,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
       }
     }
     __syncthreads();
+    KDA_TIMER_MARK(4);
 
     // ======================= 3. T = (I + A_kk)^-1 ==========================
     // 3a: diagonal 16x16 blocks by forward substitution (wave 0: lane = block,
@@ -434,6 +457,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
       for (int i = 0; i < 16; ++i) sA[(16 * bb + i) * AP + 16 * bb + cc] = x[i];
     }
     __syncthreads();
+    KDA_TIMER_MARK(5);
     // 3b: off-diagonal blocks, row-block by row-block:
     //     T_{b,b'} = -T_bb * sum_{m=b'}^{b-1} A_{b,m} T_{m,b'}
     for (int b = 1; b < 4; ++b) {
@@ -463,6 +487,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
       }
       __syncthreads();
     }
+    KDA_TIMER_MARK(6);
     // 3c: Tb = T diag(b) (lower triangle, zeros above) in fp16 and bf16 hi/lo
     for (int idx = tid; idx < CH * CH; idx += NTHREADS) {
       const int i = idx >> 6;
@@ -476,6 +501,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
       sTbbl[i * TBP + j] = (__bf16)(t - (float)tb);
     }
     __syncthreads();
+    KDA_TIMER_MARK(7);
 
     // ======================= 4. W and U ====================================
     f32x4 U[4];
@@ -529,6 +555,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
             sW[(16 * m + 4 * gq + ii) * KP + 32 * w + 16 * n + tl] = (_Float16)(-Wacc[m][n][ii]);
     }
     __syncthreads();
+    KDA_TIMER_MARK(8);
 
     // ======================= 5. state recurrence ===========================
     {
@@ -606,7 +633,9 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
       }
     }
     __syncthreads();
+    KDA_TIMER_MARK(9);
   }
+  KDA_TIMER_STORE();
 
   if (p.fin) {
     float* dst = p.fin + ((int64_t)seq * H + h) * KD * VD;
@@ -713,6 +742,10 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const void* ra
   prm.n_items = (int)(N * H);
   prm.scale = scale;
   prm.lb2 = lower_bound * LOG2E;
+#ifdef KDA_PHASE_TIMERS
+  // timer build only: the caller's workspace is extended past the order array
+  prm.timers = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + need);
+#endif
   // 8 XCDs x NV slices per group of 8 items
   const int64_t groups = (prm.n_items + 7) / 8;
   const unsigned grid = (unsigned)(groups * 8 * NV);
