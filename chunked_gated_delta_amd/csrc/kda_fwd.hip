@@ -87,20 +87,30 @@ static_assert(OFF_KRF_LO + 48 * KP * 2 <= R1_END, "R1");
 // region R2: A_kk / T (fp32) aliased with -W (f16 token-row)
 constexpr int OFF_A = R1_END;                               // f32 [64][AP]
 constexpr int OFF_W = R1_END;                               // f16 [64][KP]
-constexpr int R2_END = OFF_A + CH * AP * 4;                 // 17408
+constexpr int R2_END = OFF_A + CH * AP * 4;
 static_assert(CH * KP * 2 <= CH * AP * 4, "R2");
-constexpr int OFF_KG_HI = R2_END;                           // f16 [128][TP]
-constexpr int OFF_KG_LO = OFF_KG_HI + KD * TP * 2;
-constexpr int OFF_KT_HI = OFF_KG_LO + KD * TP * 2;
+constexpr int OFF_KG = R2_END;                              // f16 [128][TP]
+constexpr int OFF_KT_HI = OFF_KG + KD * TP * 2;             // f16 [128][TP]
 constexpr int OFF_KT_LO = OFF_KT_HI + KD * TP * 2;
 constexpr int OFF_QG = OFF_KT_LO + KD * TP * 2;             // f16 [64][KP]
 constexpr int OFF_AQK = OFF_QG + CH * KP * 2;               // f16 [64][TBP]
-constexpr int OFF_P = OFF_AQK + CH * TBP * 2;               // f32 [5][128]
-constexpr int OFF_TOT = OFF_P + 5 * KD * 4;                 // f32 [4][128]
-constexpr int OFF_ROW = OFF_TOT + 4 * KD * 4;               // f32 [64] beta
-constexpr int OFF_GL = OFF_ROW + CH * 4;                    // f32 [128]
+constexpr int OFF_P = OFF_AQK + CH * TBP * 2;               // f32 [5][128] sub-chunk prefixes
+constexpr int OFF_TOT = OFF_P + 5 * KD * 4;                 // f32 [4][128] sub-chunk totals
+constexpr int NFAC = 15;
+constexpr int OFF_FAC = OFF_TOT + 4 * KD * 4;               // f32 [NFAC][128] decay factors
+constexpr int OFF_NB = OFF_FAC + NFAC * KD * 4;             // f32 [128] gate offsets
+constexpr int OFF_ROW = OFF_NB + KD * 4;                    // f32 [64] beta
+constexpr int OFF_GL = OFF_ROW + CH * 4;                    // f32 [128] exp(G_L)
 constexpr int LDS_BYTES = OFF_GL + KD * 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+
+// decay-factor table rows (per channel c, log2 units, P_w = prefix before sub-chunk w):
+//   FAC_ET + w : exp2(P_{w+1} - P_w)   (whole sub-chunk w)
+//   FAC_EP + w : exp2(P_w)             (chunk start -> sub-chunk w start)
+//   FAC_EL + w : exp2(P_4 - P_w)       (sub-chunk w start -> chunk end)
+//   FAC_F20, FAC_F30, FAC_F31 : exp2(P_w - P_{b+1}) for the off-diagonal A
+//   blocks (w, b) with b < w - 1
+constexpr int FAC_ET = 0, FAC_EP = 4, FAC_EL = 8, FAC_F20 = 12, FAC_F30 = 13, FAC_F31 = 14;
 
 struct Params {
   const uint16_t* q;
@@ -127,7 +137,7 @@ struct Params {
 };
 
 // Optional per-phase cycle counters (compiled out unless KDA_PHASE_TIMERS is
-// defined): thread 0 accumulates s_memtime deltas between phase marks.
+// defined): thread 0 accumulates cycle-counter deltas between phase marks.
 #ifdef KDA_PHASE_TIMERS
 #define KDA_TIMER_DECL unsigned long long tacc_[12] = {0}; unsigned long long tlast_ = 0;
 #define KDA_TIMER_MARK(i) do { if (tid == 0) { const unsigned long long t_ = __builtin_readcyclecounter(); \
@@ -173,6 +183,22 @@ __device__ __forceinline__ f16x8 lds_f16x8_split(const _Float16* row, int o) {
   return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+__device__ __forceinline__ void lds_f32x8(const float* src, float (&d)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(src);
+  const float4 b = *reinterpret_cast<const float4*>(src + 4);
+  d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
+  d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4 v, float (&d)[8]) {
+  const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    d[2 * u] = __uint_as_float(a[u] << 16);
+    d[2 * u + 1] = __uint_as_float(a[u] & 0xffff0000u);
+  }
+}
+
 __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   __bf16* sKRFh = reinterpret_cast<__bf16*>(smem + OFF_KRF_HI);
@@ -183,14 +209,15 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
   __bf16* sTbbl = reinterpret_cast<__bf16*>(smem + OFF_TBB_LO);
   float* sA = reinterpret_cast<float*>(smem + OFF_A);
   _Float16* sW = reinterpret_cast<_Float16*>(smem + OFF_W);
-  _Float16* sKGh = reinterpret_cast<_Float16*>(smem + OFF_KG_HI);
-  _Float16* sKGl = reinterpret_cast<_Float16*>(smem + OFF_KG_LO);
+  _Float16* sKG = reinterpret_cast<_Float16*>(smem + OFF_KG);
   _Float16* sKth = reinterpret_cast<_Float16*>(smem + OFF_KT_HI);
   _Float16* sKtl = reinterpret_cast<_Float16*>(smem + OFF_KT_LO);
   _Float16* sQG = reinterpret_cast<_Float16*>(smem + OFF_QG);
   _Float16* sAqk = reinterpret_cast<_Float16*>(smem + OFF_AQK);
   float* sP = reinterpret_cast<float*>(smem + OFF_P);
   float* sTot = reinterpret_cast<float*>(smem + OFF_TOT);
+  float* sFac = reinterpret_cast<float*>(smem + OFF_FAC);
+  float* sNB = reinterpret_cast<float*>(smem + OFF_NB);
   float* sB = reinterpret_cast<float*>(smem + OFF_ROW);
   float* sGL = reinterpret_cast<float*>(smem + OFF_GL);
 
@@ -223,14 +250,9 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
   const int gq = lane >> 4;
   const int H = p.H;
 
-  // per-lane gate constants for channels c = 32kb + 8gq + e
-  const float gm = __expf(p.A_log[h]);
-  const float na = -gm * LOG2E;
-  float nb[4][8];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) nb[kb][e] = na * p.dt_bias[h * KD + 32 * kb + 8 * gq + e];
+  // gate: sigmoid(x) = 1 / (1 + 2^(raw * na + nb_c)) with na = -exp(A_log) log2(e)
+  const float na = -__expf(p.A_log[h]) * LOG2E;
+  if (tid < KD) sNB[tid] = na * p.dt_bias[h * KD + tid];
 
   // ---- state slice S[c][vs + 16w + tl], c = 16mt + 4gq + ii
   f32x4 S[8];
@@ -246,46 +268,68 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
       }
   }
 
+  // prefetched bf16 inputs of the next chunk: lane (token 16w + tl, channels
+  // 32kb + 8gq + e)
+  uint4 pq[4], pk[4], pg[4];
+  uint16_t pb = 0;
+  auto load_chunk = [&](int64_t cstart) {
+    const int ti = 16 * w + tl;
+    const bool valid = cstart + ti < eos;
+    const int64_t trow = (cstart + ti) * H + h;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      pq[kb] = make_uint4(0, 0, 0, 0);
+      pk[kb] = pq[kb];
+      pg[kb] = pq[kb];
+      if (valid) {
+        const int64_t off = trow * KD + 32 * kb + 8 * gq;
+        pq[kb] = *reinterpret_cast<const uint4*>(p.q + off);
+        pk[kb] = *reinterpret_cast<const uint4*>(p.k + off);
+        pg[kb] = *reinterpret_cast<const uint4*>(p.g + off);
+      }
+    }
+    pb = valid ? p.beta[trow] : (uint16_t)0;
+  };
+  if (bos < eos) load_chunk(bos);
+  __syncthreads();  // sNB
+
   KDA_TIMER_DECL
   for (int64_t c0 = bos; c0 < eos; c0 += CH) {
     const int L = (int)((eos - c0) < CH ? (eos - c0) : CH);
     KDA_TIMER_MARK(0);
 
+    // V operand for phase 4, issued now so its latency hides behind prep:
+    // lane (col vcol, k-group gq) holds tokens 32ks + 8gq + e of column vs + vcol
+    bf16x8 vop[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tj = 32 * ks + 8 * gq + e;
+        uint16_t bits = 0;
+        if (tj < L) bits = p.v[((c0 + tj) * H + h) * VD + vs + vcol];
+        vop[ks][e] = __builtin_bit_cast(__bf16, bits);
+      }
+
     // =========================== 1. prep ===================================
     const int ti = 16 * w + tl;  // chunk-local token of this lane
     const bool valid = ti < L;
-    const int64_t trow = (c0 + ti) * H + h;  // (token, head) row index
-    float qf[4][8], kf[4][8], gl[4][8];
+    // q and k stay packed (bf16) in pq/pk and are unpacked where used
+    float gl[4][8];
     float ssq = 0.f, ssk = 0.f;
-    float braw = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      uint4 qv = make_uint4(0, 0, 0, 0), kv = qv, gv = qv;
-      if (valid) {
-        const int64_t off = trow * KD + 32 * kb + 8 * gq;
-        qv = *reinterpret_cast<const uint4*>(p.q + off);
-        kv = *reinterpret_cast<const uint4*>(p.k + off);
-        gv = *reinterpret_cast<const uint4*>(p.g + off);
-      }
-      const uint32_t qa[4] = {qv.x, qv.y, qv.z, qv.w};
-      const uint32_t ka[4] = {kv.x, kv.y, kv.z, kv.w};
-      const uint32_t ga[4] = {gv.x, gv.y, gv.z, gv.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        qf[kb][2 * u] = __uint_as_float(qa[u] << 16);
-        qf[kb][2 * u + 1] = __uint_as_float(qa[u] & 0xffff0000u);
-        kf[kb][2 * u] = __uint_as_float(ka[u] << 16);
-        kf[kb][2 * u + 1] = __uint_as_float(ka[u] & 0xffff0000u);
-        gl[kb][2 * u] = __uint_as_float(ga[u] << 16);
-        gl[kb][2 * u + 1] = __uint_as_float(ga[u] & 0xffff0000u);
-      }
+      float qf[8], kf[8];
+      unpack_bf16x8(pq[kb], qf);
+      unpack_bf16x8(pk[kb], kf);
+      unpack_bf16x8(pg[kb], gl[kb]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        ssq += qf[kb][e] * qf[kb][e];
-        ssk += kf[kb][e] * kf[kb][e];
+        ssq += qf[e] * qf[e];
+        ssk += kf[e] * kf[e];
       }
     }
-    if (valid) braw = bf16_bits_to_f32(p.beta[trow]);
+    const float braw = bf16_bits_to_f32(pb);
     ssq += __shfl_xor(ssq, 16);
     ssq += __shfl_xor(ssq, 32);
     ssk += __shfl_xor(ssk, 16);
@@ -294,34 +338,46 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
     const float rk = __builtin_amdgcn_rsqf(ssk + L2_EPS);
     const float beta = valid ? __builtin_amdgcn_rcpf(1.0f + fexp2(-braw * LOG2E)) : 0.0f;
 
-    // gate in log2 units: g2 = lb*log2e * sigmoid(exp(A_log) (raw + dt)), then
-    // the inclusive scan over the 16 tokens of this sub-chunk
+    // gate in log2 units, then the inclusive scan over the sub-chunk's 16 tokens
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+      float nb[8];
+      lds_f32x8(sNB + 32 * kb + 8 * gq, nb);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float g2 = p.lb2 * __builtin_amdgcn_rcpf(1.0f + fexp2(gl[kb][e] * na + nb[kb][e]));
+        float g2 = p.lb2 * __builtin_amdgcn_rcpf(1.0f + fexp2(gl[kb][e] * na + nb[e]));
         g2 = valid ? g2 : 0.0f;
         gl[kb][e] = row_scan16(g2);
       }
+    }
     if (tl == 15) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sTot[w * KD + 32 * kb + 8 * gq + e] = gl[kb][e];
+      for (int kb = 0; kb < 4; ++kb) {
+        float4* dst = reinterpret_cast<float4*>(sTot + w * KD + 32 * kb + 8 * gq);
+        dst[0] = make_float4(gl[kb][0], gl[kb][1], gl[kb][2], gl[kb][3]);
+        dst[1] = make_float4(gl[kb][4], gl[kb][5], gl[kb][6], gl[kb][7]);
+      }
     }
     if (gq == 0) sB[ti] = beta;
     __syncthreads();
     KDA_TIMER_MARK(1);
     if (tid < KD) {
-      float acc = 0.f;
-      sP[tid] = 0.f;
+      float P[5];
+      P[0] = 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) P[b + 1] = P[b] + sTot[b * KD + tid];
+#pragma unroll
+      for (int b = 0; b < 5; ++b) sP[b * KD + tid] = P[b];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        acc += sTot[b * KD + tid];
-        sP[(b + 1) * KD + tid] = acc;
+        sFac[(FAC_ET + b) * KD + tid] = fexp2(P[b + 1] - P[b]);
+        sFac[(FAC_EP + b) * KD + tid] = fexp2(P[b]);
+        sFac[(FAC_EL + b) * KD + tid] = fexp2(P[4] - P[b]);
       }
-      sGL[tid] = fexp2(acc);
+      sFac[FAC_F20 * KD + tid] = fexp2(P[2] - P[1]);
+      sFac[FAC_F30 * KD + tid] = fexp2(P[3] - P[1]);
+      sFac[FAC_F31 * KD + tid] = fexp2(P[3] - P[2]);
+      sGL[tid] = fexp2(P[4]);
     }
     __syncthreads();
     KDA_TIMER_MARK(2);
@@ -330,18 +386,23 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
     bf16x8 kLFh[4], kLFl[4], kEh[4], kEl[4], qLF[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
+      float ET[8], EP[8], EL[8];
+      lds_f32x8(sFac + (FAC_ET + w) * KD + 32 * kb + 8 * gq, ET);
+      lds_f32x8(sFac + (FAC_EP + w) * KD + 32 * kb + 8 * gq, EP);
+      lds_f32x8(sFac + (FAC_EL + w) * KD + 32 * kb + 8 * gq, EL);
       bf16x8 krh, krl;
+      f16x8 qg;
+      float qf[8], kf[8];
+      unpack_bf16x8(pq[kb], qf);
+      unpack_bf16x8(pk[kb], kf);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int c = 32 * kb + 8 * gq + e;
-        const float Pw = sP[w * KD + c];
-        const float Pw1 = sP[(w + 1) * KD + c];
-        const float P4 = sP[4 * KD + c];
         const float Gl = gl[kb][e];
-        const float LF = fexp2(Gl);
-        const float E = fexp2(-Gl);
-        const float kn = kf[kb][e] * rk;
-        const float qn = qf[kb][e] * rq;
+        const float LF = fexp2(Gl);   // exp(G_t - P_w) <= 1
+        const float E = fexp2(-Gl);   // exp(P_w - G_t) in [1, 2^116]
+        const float kn = kf[e] * rk;
+        const float qn = qf[e] * rq;
         const float a = kn * LF;
         const __bf16 ah = (__bf16)a;
         kLFh[kb][e] = ah;
@@ -350,23 +411,20 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
         const __bf16 bh = (__bf16)b;
         kEh[kb][e] = bh;
         kEl[kb][e] = (__bf16)(b - (float)bh);
-        qLF[kb][e] = (__bf16)(qn * LF);
-        const float rf = b * fexp2(Pw1 - Pw);  // k^ exp(P_{w+1} - G_t) <= |k^|
+        const float ql = qn * LF;
+        qLF[kb][e] = (__bf16)ql;
+        const float rf = b * ET[e];  // k^ exp(P_{w+1} - G_t) <= |k^|
         const __bf16 rh = (__bf16)rf;
         krh[e] = rh;
         krl[e] = (__bf16)(rf - (float)rh);
-        const float gam = LF * fexp2(Pw);          // exp(G_t)
-        const float gl_over = E * fexp2(P4 - Pw);  // exp(G_L - G_t)
-        const float kg = kn * gam;
-        const _Float16 kgh = (_Float16)kg;
-        sKGh[c * TP + ti] = kgh;
-        sKGl[c * TP + ti] = (_Float16)(kg - (float)kgh);
-        const float kt = kn * gl_over;
+        sKG[c * TP + ti] = (_Float16)(a * EP[e]);       // k^ exp(G_t)
+        const float kt = b * EL[e];                      // k^ exp(G_L - G_t)
         const _Float16 kth = (_Float16)kt;
         sKth[c * TP + ti] = kth;
         sKtl[c * TP + ti] = (_Float16)(kt - (float)kth);
-        sQG[ti * KP + c] = (_Float16)(qn * gam);
+        qg[e] = (_Float16)(ql * EP[e]);                 // q^ exp(G_t)
       }
+      *reinterpret_cast<f16x8*>(sQG + ti * KP + 32 * kb + 8 * gq) = qg;
       if (w < 3) {
         *reinterpret_cast<bf16x8*>(sKRFh + ti * KP + 32 * kb + 8 * gq) = krh;
         *reinterpret_cast<bf16x8*>(sKRFl + ti * KP + 32 * kb + 8 * gq) = krl;
@@ -392,22 +450,23 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
           }
         } else {
           const int jrow = 16 * b + tl;
+          const int frow = (b == w - 1) ? -1 : (w == 2 ? FAC_F20 : (b == 0 ? FAC_F30 : FAC_F31));
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
             const bf16x8 rh = *reinterpret_cast<const bf16x8*>(sKRFh + jrow * KP + 32 * kb + 8 * gq);
             const bf16x8 rl = *reinterpret_cast<const bf16x8*>(sKRFl + jrow * KP + 32 * kb + 8 * gq);
             bf16x8 lh = kLFh[kb], ll = kLFl[kb], lq = qLF[kb];
-            if (b < w - 1) {
+            if (frow >= 0) {
               // left factor exp(G_i - P_{b+1}) = LF * exp(P_w - P_{b+1})
+              float f[8];
+              lds_f32x8(sFac + frow * KD + 32 * kb + 8 * gq, f);
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
-                const int c = 32 * kb + 8 * gq + e;
-                const float f = fexp2(sP[w * KD + c] - sP[(b + 1) * KD + c]);
-                const float a = ((float)kLFh[kb][e] + (float)kLFl[kb][e]) * f;
+                const float a = ((float)kLFh[kb][e] + (float)kLFl[kb][e]) * f[e];
                 const __bf16 ah = (__bf16)a;
                 lh[e] = ah;
                 ll[e] = (__bf16)(a - (float)ah);
-                lq[e] = (__bf16)((float)qLF[kb][e] * f);
+                lq[e] = (__bf16)((float)qLF[kb][e] * f[e]);
               }
             }
             akk = mfma_bf16(lh, rh, akk);
@@ -432,33 +491,30 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) sAqk[(i0 + ii) * TBP + 16 * b + tl] = (_Float16)0.0f;
       }
+      // diagonal block inverse T_ww = (I + A_ww)^-1 by forward substitution,
+      // lane cc < 16 owns column cc.  This wave wrote A_ww itself just above
+      // (LDS operations of one wave complete in order), so no barrier is needed.
+      if (lane < 16) {
+        const int cc = lane;
+        const float* Ab = sA + (16 * w) * AP + 16 * w;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float s = (i == cc) ? 1.0f : 0.0f;
+#pragma unroll
+          for (int m = 0; m < i; ++m) s -= Ab[i * AP + m] * x[m];
+          x[i] = (i < cc) ? 0.0f : s;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sA[(16 * w + i) * AP + 16 * w + cc] = x[i];
+      }
     }
     __syncthreads();
     KDA_TIMER_MARK(4);
+    KDA_TIMER_MARK(5);
 
     // ======================= 3. T = (I + A_kk)^-1 ==========================
-    // 3a: diagonal 16x16 blocks by forward substitution (wave 0: lane = block,
-    // column), written in place.
-    if (w == 0) {
-      const int bb = lane >> 4;
-      const int cc = lane & 15;
-      const float* Ab = sA + (16 * bb) * AP + 16 * bb;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = (i == cc) ? 1.0f : 0.0f;
-#pragma unroll
-        for (int m = 0; m < i; ++m) s -= Ab[i * AP + m] * x[m];
-        x[i] = (i < cc) ? 0.0f : s;
-      }
-      // every lane of this wave has read its block above before any lane
-      // writes (one instruction stream); only this wave touches these blocks
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sA[(16 * bb + i) * AP + 16 * bb + cc] = x[i];
-    }
-    __syncthreads();
-    KDA_TIMER_MARK(5);
-    // 3b: off-diagonal blocks, row-block by row-block:
+    // off-diagonal blocks, row-block by row-block:
     //     T_{b,b'} = -T_bb * sum_{m=b'}^{b-1} A_{b,m} T_{m,b'}
     for (int b = 1; b < 4; ++b) {
       f32x4 res = {0.f, 0.f, 0.f, 0.f};
@@ -488,17 +544,31 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
       __syncthreads();
     }
     KDA_TIMER_MARK(6);
-    // 3c: Tb = T diag(b) (lower triangle, zeros above) in fp16 and bf16 hi/lo
-    for (int idx = tid; idx < CH * CH; idx += NTHREADS) {
-      const int i = idx >> 6;
-      const int j = idx & 63;
-      const float t = (j < i) ? sA[i * AP + j] * sB[j] : ((j == i) ? sB[j] : 0.0f);
-      const _Float16 th = (_Float16)t;
-      sTb16h[i * TBP + j] = th;
-      sTb16l[i * TBP + j] = (_Float16)(t - (float)th);
-      const __bf16 tb = (__bf16)t;
-      sTbbh[i * TBP + j] = tb;
-      sTbbl[i * TBP + j] = (__bf16)(t - (float)tb);
+    // Tb = T diag(b) (lower triangle, zeros above) in fp16 and bf16 hi/lo;
+    // thread handles 8 consecutive columns of one row
+    for (int it = tid; it < CH * 8; it += NTHREADS) {
+      const int i = it >> 3;
+      const int j0 = (it & 7) * 8;
+      float t8[8], b8[8];
+      lds_f32x8(sA + i * AP + j0, t8);
+      lds_f32x8(sB + j0, b8);
+      f16x8 h16, l16;
+      bf16x8 hb, lb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = j0 + e;
+        const float t = (j < i) ? t8[e] * b8[e] : ((j == i) ? b8[e] : 0.0f);
+        const _Float16 th = (_Float16)t;
+        h16[e] = th;
+        l16[e] = (_Float16)(t - (float)th);
+        const __bf16 tb = (__bf16)t;
+        hb[e] = tb;
+        lb[e] = (__bf16)(t - (float)tb);
+      }
+      *reinterpret_cast<f16x8*>(sTb16h + i * TBP + j0) = h16;
+      *reinterpret_cast<f16x8*>(sTb16l + i * TBP + j0) = l16;
+      *reinterpret_cast<bf16x8*>(sTbbh + i * TBP + j0) = hb;
+      *reinterpret_cast<bf16x8*>(sTbbl + i * TBP + j0) = lb;
     }
     __syncthreads();
     KDA_TIMER_MARK(7);
@@ -506,18 +576,6 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
     // ======================= 4. W and U ====================================
     f32x4 U[4];
     {
-      // V operand straight from global: lane (col vcol, k-group gq) holds
-      // tokens 32ks + 8gq + e of column vs + vcol
-      bf16x8 vop[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tj = 32 * ks + 8 * gq + e;
-          uint16_t bits = 0;
-          if (tj < L) bits = p.v[((c0 + tj) * H + h) * VD + vs + vcol];
-          vop[ks][e] = __builtin_bit_cast(__bf16, bits);
-        }
       f32x4 Wacc[4][2];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -535,17 +593,15 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
 #pragma unroll
           for (int n = 0; n < 2; ++n) {
             const int ch = 32 * w + 16 * n + tl;
-            const f16x8 kgh = *reinterpret_cast<const f16x8*>(sKGh + ch * TP + 32 * ks + 8 * gq);
-            const f16x8 kgl = *reinterpret_cast<const f16x8*>(sKGl + ch * TP + 32 * ks + 8 * gq);
-            Wacc[m][n] = mfma_f16(th, kgh, Wacc[m][n]);
-            Wacc[m][n] = mfma_f16(th, kgl, Wacc[m][n]);
-            Wacc[m][n] = mfma_f16(tlo, kgh, Wacc[m][n]);
+            const f16x8 kg = *reinterpret_cast<const f16x8*>(sKG + ch * TP + 32 * ks + 8 * gq);
+            Wacc[m][n] = mfma_f16(th, kg, Wacc[m][n]);
+            Wacc[m][n] = mfma_f16(tlo, kg, Wacc[m][n]);
           }
           U[m] = mfma_bf16(tbh, vop[ks], U[m]);
           U[m] = mfma_bf16(tbl, vop[ks], U[m]);
         }
       }
-      // -W overwrites the fp32 T array; phase 3c's trailing barrier ordered it
+      // -W overwrites the fp32 T array; the barrier above ordered the reads
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -558,6 +614,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
     KDA_TIMER_MARK(8);
 
     // ======================= 5. state recurrence ===========================
+    // prefetch the next chunk's q/k/gate/beta; consumed at the top of the loop
+    if (c0 + CH < eos) load_chunk(c0 + CH);
     {
       f16x8 Sb[4];
 #pragma unroll
@@ -618,8 +676,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_fwd_kernel(Params p) {
       // S = Diag(G_L) S + Kt^T D
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) S[mt][ii] *= sGL[16 * mt + 4 * gq + ii];
+        const float4 gl4 = *reinterpret_cast<const float4*>(sGL + 16 * mt + 4 * gq);
+        S[mt][0] *= gl4.x;
+        S[mt][1] *= gl4.y;
+        S[mt][2] *= gl4.z;
+        S[mt][3] *= gl4.w;
         const _Float16* khrow = sKth + (16 * mt + tl) * TP;
         const _Float16* klrow = sKtl + (16 * mt + tl) * TP;
 #pragma unroll
