@@ -36,13 +36,17 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 BF16_DENSE_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
 BYTES_PER_HEAD_TOKEN = 4 * 128 * 2 + 2 + 128 * 2
 STATE_BYTES = 128 * 128 * 4
-KERNEL_SRC = os.path.join(ROOT, "chunked_gated_delta_amd", "csrc", "kda_fwd.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "chunked_gated_delta_amd", "csrc", f)
+               for f in ("kda_common.h", "kda_intra.hip", "kda_inter.hip", "kda_api.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_fwd_c3_traffic.json")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():
@@ -173,7 +177,8 @@ def main():
                    "B": 1, "T": x.T, "H": x.H, "K": 128, "V": 128},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "kda_fwd_kernel", "avg_kernel_ms": avg_kern_s * 1e3,
+                     "kernel": "kda_fwd (intra-chunk + inter-chunk kernels, one forward)",
+                     "avg_kernel_ms": avg_kern_s * 1e3,
                      "algorithmic_bytes_per_launch": alg_bytes},
         "mfma": {"achieved_tflops": flops / avg_kern_s / 1e12, "peak_tflops": BF16_DENSE_TFLOPS,
                  "frac": flops / avg_kern_s / 1e12 / BF16_DENSE_TFLOPS,

@@ -1,0 +1,187 @@
+// C ABI of the gfx950 KDA forward (include/kda.h): argument checks, workspace
+// layout, varlen scheduling and the launch sequence
+//     [varlen only] chunk offsets + longest-first order  ->  intra  ->  inter
+// all asynchronous on the caller's stream.  The argument list follows the
+// 14-argument torch.ops._flashkda_C.fwd call and get_workspace_size(T, H, N)
+// of the vLLM PR report ("关键源码片段"), with sizes and the stream appended.
+
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/kda.h"
+#include "kda_common.h"
+
+namespace kda {
+namespace {
+
+constexpr int kMaxSortN = 16384;
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct Layout {
+  size_t choff, order, rec, total;
+};
+
+Layout workspace_layout(int64_t T_total, int64_t H, int64_t N) {
+  Layout l;
+  l.choff = 256;
+  l.order = l.choff + align256((size_t)(N + 1) * sizeof(int32_t));
+  l.rec = l.order + align256((size_t)N * sizeof(int32_t));
+  const size_t max_chunks = (size_t)(T_total / CH) + (size_t)N;
+  l.total = l.rec + max_chunks * (size_t)H * REC_BYTES;
+  return l;
+}
+
+// choff[n] = sum_{m<n} ceil(len_m / 64), choff[N] = total chunks (one block).
+__global__ void __launch_bounds__(1024) kda_chunk_offsets_kernel(const int32_t* __restrict__ cu, int N,
+                                                                 int32_t* __restrict__ choff) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < N; base += 1024) {
+    const int i = base + tid;
+    const int c = (i < N) ? (cu[i + 1] - cu[i] + CH - 1) / CH : 0;
+    int x = c;  // inclusive scan within the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    int before = carry;
+    for (int u = 0; u < wv; ++u) before += wsum[u];
+    if (i < N) choff[i] = before + x - c;
+    __syncthreads();
+    if (tid == 1023) carry = before + x;
+    __syncthreads();
+  }
+  if (tid == 0) choff[N] = carry;
+}
+
+// Longest-first processing order of the sequences: rank of sequence i = number
+// of sequences that are longer, or equally long with a smaller index.
+__global__ void kda_order_kernel(const int32_t* __restrict__ cu, int N, int32_t* __restrict__ order) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N) return;
+  const int li = cu[i + 1] - cu[i];
+  int rank = 0;
+  for (int j = 0; j < N; ++j) {
+    const int lj = cu[j + 1] - cu[j];
+    rank += (lj > li) || (lj == li && j < i);
+  }
+  order[rank] = i;
+}
+
+// The launch's own return code (not hipGetLastError, which also reports
+// errors left behind by earlier, unrelated runtime calls).  KDA_DEBUG=1 in the
+// environment prints the HIP error behind KDA_ERR_LAUNCH.
+kda_status_t launch_status(hipError_t err, const char* what) {
+  if (err == hipSuccess) return KDA_SUCCESS;
+  if (getenv("KDA_DEBUG")) fprintf(stderr, "kda: %s launch failed: %s\n", what, hipGetErrorString(err));
+  return KDA_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace kda
+
+using namespace kda;
+
+extern "C" {
+
+size_t kda_workspace_size(int64_t T_total, int64_t H, int64_t N) {
+  if (T_total < 0 || H < 1 || N < 1) return 0;
+  return workspace_layout(T_total, H, N).total;
+}
+
+int kda_is_supported(int64_t K, int64_t V, float lower_bound) {
+  return K == KD && V == VD && lower_bound >= -5.0f && lower_bound <= 0.0f;
+}
+
+const char* kda_status_string(kda_status_t s) {
+  switch (s) {
+    case KDA_SUCCESS: return "KDA_SUCCESS";
+    case KDA_ERR_INVALID: return "KDA_ERR_INVALID";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+kda_status_t kda_fwd(const void* q, const void* k, const void* v, const void* raw_gate,
+                     const void* raw_beta, float scale, void* out, void* workspace,
+                     size_t workspace_bytes, const float* A_log, const float* dt_bias,
+                     float lower_bound, const float* initial_state, float* final_state,
+                     const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t K,
+                     int64_t V, int64_t N, void* stream) {
+  if (!q || !k || !v || !raw_gate || !raw_beta || !out || !A_log || !dt_bias) return KDA_ERR_INVALID;
+  if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID;
+  if (cu_seqlens ? (B != 1) : (N != B)) return KDA_ERR_INVALID;
+  if (!(scale == scale)) return KDA_ERR_INVALID;
+  if (!kda_is_supported(K, V, lower_bound)) return KDA_ERR_UNSUPPORTED;
+  if (B * T * H > ((int64_t)1 << 40) || N * H > ((int64_t)1 << 28) || N > ((int64_t)1 << 30))
+    return KDA_ERR_INVALID;
+  const int64_t T_total = B * T;
+  const Layout lay = workspace_layout(T_total, H, N);
+  if (!workspace || workspace_bytes < lay.total) return KDA_ERR_WORKSPACE;
+  const int64_t max_chunks = cu_seqlens ? T_total / CH + N : B * ((T + CH - 1) / CH);
+  if (max_chunks * H > ((int64_t)1 << 31) - 1) return KDA_ERR_INVALID;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* choff = reinterpret_cast<int32_t*>(ws + lay.choff);
+  int32_t* order = nullptr;
+  int n32 = (int)N;
+  if (cu_seqlens) {
+    void* cargs[] = {(void*)&cu_seqlens, (void*)&n32, (void*)&choff};
+    if (launch_status(hipLaunchKernel(reinterpret_cast<const void*>(&kda_chunk_offsets_kernel), dim3(1),
+                                      dim3(1024), cargs, 0, st),
+                      "chunk offsets") != KDA_SUCCESS)
+      return KDA_ERR_LAUNCH;
+    if (N > 1 && N <= kMaxSortN) {
+      order = reinterpret_cast<int32_t*>(ws + lay.order);
+      void* oargs[] = {(void*)&cu_seqlens, (void*)&n32, (void*)&order};
+      if (launch_status(hipLaunchKernel(reinterpret_cast<const void*>(&kda_order_kernel),
+                                        dim3((unsigned)((N + 255) / 256)), dim3(256), oargs, 0, st),
+                        "order") != KDA_SUCCESS)
+        return KDA_ERR_LAUNCH;
+    }
+  }
+  ChunkMap map;
+  map.cu = cu_seqlens;
+  map.choff = cu_seqlens ? choff : nullptr;
+  map.T = T;
+  map.N = (int)N;
+
+  IntraArgs ia;
+  ia.q = static_cast<const uint16_t*>(q);
+  ia.k = static_cast<const uint16_t*>(k);
+  ia.g = static_cast<const uint16_t*>(raw_gate);
+  ia.beta = static_cast<const uint16_t*>(raw_beta);
+  ia.A_log = A_log;
+  ia.dt_bias = dt_bias;
+  ia.rec = ws + lay.rec;
+  ia.map = map;
+  ia.H = (int)H;
+  ia.lb2 = lower_bound * LOG2E;
+  if (launch_status(launch_intra(ia, max_chunks, st), "intra") != KDA_SUCCESS) return KDA_ERR_LAUNCH;
+
+  InterArgs xa;
+  xa.v = static_cast<const uint16_t*>(v);
+  xa.out = static_cast<uint16_t*>(out);
+  xa.init = initial_state;
+  xa.fin = final_state;
+  xa.rec = ws + lay.rec;
+  xa.order = order;
+  xa.map = map;
+  xa.H = (int)H;
+  xa.scale = scale;
+  return launch_status(launch_inter(xa, st), "inter");
+}
+
+}  // extern "C"

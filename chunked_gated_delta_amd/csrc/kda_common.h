@@ -1,0 +1,138 @@
+// Shared definitions of the gfx950 KDA forward kernels (intra-chunk kernel,
+// inter-chunk kernel, host API).  Internal header: not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int KD = 128;   // head dim K
+constexpr int VD = 128;   // head dim V
+constexpr int CH = 64;    // chunk length
+constexpr int SUB = 16;   // sub-chunk length (decay reference granularity)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float L2_EPS = 1e-6f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Per (chunk, head) record written by the intra-chunk kernel and read by the
+// inter-chunk kernel.  Every array is laid out so that one MFMA operand
+// fragment of the reader is one 16-byte load per lane.
+//   NW   : -W = -T diag(beta) (K^ * exp(G))      f16  [64 tok][128 ch]
+//   QG   : Q^ * exp(G)                           f16  [64 tok][128 ch]
+//   KTH/L: (K^ * exp(G_L - G))^T  hi / lo        f16  [128 ch][64 tok]
+//   AQK  : A_qk (zero above the diagonal)        f16  [64 tok][64 tok]
+//   TBH/L: T diag(beta) (zero above diagonal)    bf16 [64 tok][64 tok] hi / lo
+//   GL   : exp(G_L) per channel                  f32  [128]
+// ---------------------------------------------------------------------------
+constexpr size_t REC_NW = 0;
+constexpr size_t REC_QG = REC_NW + CH * KD * 2;
+constexpr size_t REC_KTH = REC_QG + CH * KD * 2;
+constexpr size_t REC_KTL = REC_KTH + KD * CH * 2;
+constexpr size_t REC_AQK = REC_KTL + KD * CH * 2;
+constexpr size_t REC_TBH = REC_AQK + CH * CH * 2;
+constexpr size_t REC_TBL = REC_TBH + CH * CH * 2;
+constexpr size_t REC_GL = REC_TBL + CH * CH * 2;
+constexpr size_t REC_BYTES = REC_GL + KD * 4;  // 90624
+static_assert(REC_BYTES % 256 == 0, "record alignment");
+
+// Chunk bookkeeping shared by both kernels.  Without cu_seqlens there are N
+// sequences of length T and sequence n owns chunks [n*ceil(T/64), ...).  With
+// cu_seqlens the chunk offsets come from a device prefix sum (choff[N+1]).
+struct ChunkMap {
+  const int32_t* cu;     // nullptr: N sequences of length T
+  const int32_t* choff;  // [N+1] exclusive prefix of per-sequence chunk counts (varlen)
+  int64_t T;
+  int N;
+};
+
+__device__ __forceinline__ void seq_bounds(const ChunkMap& m, int n, int64_t& bos, int64_t& eos) {
+  if (m.cu) {
+    bos = m.cu[n];
+    eos = m.cu[n + 1];
+  } else {
+    bos = (int64_t)n * m.T;
+    eos = bos + m.T;
+  }
+}
+
+__device__ __forceinline__ int64_t first_chunk(const ChunkMap& m, int n) {
+  return m.cu ? (int64_t)m.choff[n] : (int64_t)n * ((m.T + CH - 1) / CH);
+}
+
+__device__ __forceinline__ int64_t total_chunks(const ChunkMap& m) {
+  return m.cu ? (int64_t)m.choff[m.N] : (int64_t)m.N * ((m.T + CH - 1) / CH);
+}
+
+// sequence owning global chunk g (g < total_chunks)
+__device__ __forceinline__ int chunk_owner(const ChunkMap& m, int64_t g) {
+  if (!m.cu) return (int)(g / ((m.T + CH - 1) / CH));
+  int lo = 0, hi = m.N - 1;  // largest n with choff[n] <= g and g < choff[n+1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (m.choff[mid] <= g) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4 v, float (&d)[8]) {
+  const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    d[2 * u] = __uint_as_float(a[u] << 16);
+    d[2 * u + 1] = __uint_as_float(a[u] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ void lds_f32x8(const float* src, float (&d)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(src);
+  const float4 b = *reinterpret_cast<const float4*>(src + 4);
+  d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
+  d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
+}
+
+// Host-side launchers (defined next to their kernels).
+struct IntraArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* g;
+  const uint16_t* beta;
+  const float* A_log;
+  const float* dt_bias;
+  char* rec;        // records [max_chunks][H]
+  ChunkMap map;
+  int H;
+  float lb2;        // lower_bound * log2(e)
+};
+struct InterArgs {
+  const uint16_t* v;
+  uint16_t* out;
+  const float* init;
+  float* fin;
+  const char* rec;
+  const int32_t* order;  // nullptr: identity order of sequences
+  ChunkMap map;
+  int H;
+  float scale;
+};
+hipError_t launch_intra(const IntraArgs& a, int64_t max_chunks, hipStream_t st);
+hipError_t launch_inter(const InterArgs& a, hipStream_t st);
+
+}  // namespace kda

@@ -1,0 +1,287 @@
+// Inter-chunk kernel of the gfx950 KDA forward: the sequential recurrence over
+// chunks.  For every chunk, with the per-chunk record of the intra-chunk
+// kernel (W, Q exp(G), (K exp(G_L - G))^T, A_qk, T diag(b), exp(G_L)):
+//     U = T diag(b) V                       (bf16 hi/lo x exact bf16 V, 2 passes)
+//     D = U - W S                           (fp16 W, fp16 copy of S)
+//     O = scale [ (Q exp(G)) S + A_qk D ]   -> bf16 output
+//     S = Diag(exp(G_L)) S + (K exp(G_L - G))^T D   (fp16 hi/lo x fp16 hi/lo, 3 passes)
+// The state S is fp32 and stays in MFMA accumulator registers for the whole
+// sequence; its fp16 copy, the chunk's V tile and D live in LDS in
+// column-major form so that every B operand is one 16-byte LDS read.
+//
+// One workgroup (4 waves) per (sequence, head, V-half).  Wave w computes the
+// token rows 16w..16w+15 of U, D and O (its A operands are 16-byte global
+// loads from the record) and the state rows (channels) 32w..32w+31.
+
+#include "kda_common.h"
+
+namespace kda {
+namespace {
+
+constexpr int NTHREADS = 256;
+constexpr int NV = 2;            // V slices per (sequence, head)
+constexpr int VT = VD / NV;      // 64 state columns per workgroup
+constexpr int TP = CH + 8;       // token pitch of [v][token] arrays (halves)
+constexpr int SP = KD + 8;       // channel pitch of the [v][channel] state copy
+
+constexpr int OFF_VT = 0;                          // bf16 [VT][TP]   V^T
+constexpr int OFF_ST = OFF_VT + VT * TP * 2;       // f16  [VT][SP]   S^T
+constexpr int OFF_DTH = OFF_ST + VT * SP * 2;      // f16  [VT][TP]   D^T hi
+constexpr int OFF_DTL = OFF_DTH + VT * TP * 2;     // f16  [VT][TP]   D^T lo
+constexpr int LDS_BYTES = OFF_DTL + VT * TP * 2;
+
+// the record operands one wave needs per chunk
+struct Ops {
+  f16x8 nw[4];        // -W rows 16w+tl, channels 32kb + 8gq..
+  f16x8 qg[4];        // Q exp(G) rows
+  f16x8 aqk[2];       // A_qk rows, tokens 32ks + 8gq..
+  bf16x8 tbh[2], tbl[2];
+  f16x8 kth[2][2], ktl[2][2];  // [mt][ks]: channel 32w + 16mt + tl, tokens 32ks + 8gq..
+  float4 gl[2];       // exp(G_L) of channels 32w + 16mt + 4gq + 0..3
+};
+
+__device__ __forceinline__ void load_ops(Ops& o, const char* rec, int w, int tl, int gq) {
+  const _Float16* nw = reinterpret_cast<const _Float16*>(rec + REC_NW);
+  const _Float16* qg = reinterpret_cast<const _Float16*>(rec + REC_QG);
+  const _Float16* aq = reinterpret_cast<const _Float16*>(rec + REC_AQK);
+  const __bf16* th = reinterpret_cast<const __bf16*>(rec + REC_TBH);
+  const __bf16* tlw = reinterpret_cast<const __bf16*>(rec + REC_TBL);
+  const _Float16* kh = reinterpret_cast<const _Float16*>(rec + REC_KTH);
+  const _Float16* kl = reinterpret_cast<const _Float16*>(rec + REC_KTL);
+  const float* gl = reinterpret_cast<const float*>(rec + REC_GL);
+  const int row = 16 * w + tl;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    o.nw[kb] = *reinterpret_cast<const f16x8*>(nw + row * KD + 32 * kb + 8 * gq);
+    o.qg[kb] = *reinterpret_cast<const f16x8*>(qg + row * KD + 32 * kb + 8 * gq);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    o.aqk[ks] = *reinterpret_cast<const f16x8*>(aq + row * CH + 32 * ks + 8 * gq);
+    o.tbh[ks] = *reinterpret_cast<const bf16x8*>(th + row * CH + 32 * ks + 8 * gq);
+    o.tbl[ks] = *reinterpret_cast<const bf16x8*>(tlw + row * CH + 32 * ks + 8 * gq);
+  }
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int c = 32 * w + 16 * mt + tl;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      o.kth[mt][ks] = *reinterpret_cast<const f16x8*>(kh + c * CH + 32 * ks + 8 * gq);
+      o.ktl[mt][ks] = *reinterpret_cast<const f16x8*>(kl + c * CH + 32 * ks + 8 * gq);
+    }
+    o.gl[mt] = *reinterpret_cast<const float4*>(gl + 32 * w + 16 * mt + 4 * gq);
+  }
+}
+
+// V tile of a chunk: thread -> (token tid/4, columns 16*(tid%4) .. +15)
+__device__ __forceinline__ void load_v(uint4 (&vv)[2], const uint16_t* v, int64_t c0, int L, int H,
+                                       int h, int vs, int tid) {
+  const int t = tid >> 2;
+  const int cg = tid & 3;
+  vv[0] = make_uint4(0, 0, 0, 0);
+  vv[1] = vv[0];
+  if (t < L) {
+    const uint4* src = reinterpret_cast<const uint4*>(v + ((c0 + t) * H + h) * VD + vs + 16 * cg);
+    vv[0] = src[0];
+    vv[1] = src[1];
+  }
+}
+
+__device__ __forceinline__ void store_vt(__bf16* sVt, const uint4 (&vv)[2], int tid) {
+  const int t = tid >> 2;
+  const int cg = tid & 3;
+  const uint32_t wds[8] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w, vv[1].x, vv[1].y, vv[1].z, vv[1].w};
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int col = 16 * cg + 2 * u;
+    sVt[col * TP + t] = __builtin_bit_cast(__bf16, (uint16_t)(wds[u] & 0xffffu));
+    sVt[(col + 1) * TP + t] = __builtin_bit_cast(__bf16, (uint16_t)(wds[u] >> 16));
+  }
+}
+
+__global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  __bf16* sVt = reinterpret_cast<__bf16*>(smem + OFF_VT);
+  _Float16* sSt = reinterpret_cast<_Float16*>(smem + OFF_ST);
+  _Float16* sDth = reinterpret_cast<_Float16*>(smem + OFF_DTH);
+  _Float16* sDtl = reinterpret_cast<_Float16*>(smem + OFF_DTL);
+
+  // XCD-aware mapping: ids are dispatched round-robin over the 8 XCDs, so the
+  // two V-halves of one (sequence, head) get ids with equal residue mod 8 and
+  // read the chunk records through the same L2.
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int r = bid >> 3;
+  const int item = 8 * (r / NV) + xcd;
+  const int slice = r % NV;
+  const int H = a.H;
+  if (item >= a.map.N * H) return;
+  const int pos = item / H;
+  const int h = item - pos * H;
+  const int seq = a.order ? a.order[pos] : pos;
+  int64_t bos, eos;
+  seq_bounds(a.map, seq, bos, eos);
+  const int64_t gfirst = first_chunk(a.map, seq);
+  const int vs = slice * VT;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int tl = lane & 15;
+  const int gq = lane >> 4;
+  const int ksmax = (w >= 2) ? 2 : 1;  // token rows 16w.. only see tokens <= 16w + 15
+
+  // state rows (channels) 32w + 16mt + 4gq + ii, columns vs + 16n + tl
+  f32x4 S[2][4];
+  {
+    const float* src = a.init ? a.init + ((int64_t)seq * H + h) * KD * VD : nullptr;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nn = 0; nn < 4; ++nn)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int c = 32 * w + 16 * mt + 4 * gq + ii;
+          S[mt][nn][ii] = src ? src[c * VD + vs + 16 * nn + tl] : 0.0f;
+        }
+  }
+  auto store_st = [&]() {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nn = 0; nn < 4; ++nn) {
+        const f16x4 hv = {(_Float16)S[mt][nn][0], (_Float16)S[mt][nn][1], (_Float16)S[mt][nn][2],
+                          (_Float16)S[mt][nn][3]};
+        *reinterpret_cast<f16x4*>(sSt + (16 * nn + tl) * SP + 32 * w + 16 * mt + 4 * gq) = hv;
+      }
+  };
+  store_st();
+
+  Ops cur, nxt;
+  uint4 vnext[2];
+  int64_t c0 = bos;
+  int64_t gch = gfirst;
+  if (c0 < eos) {
+    load_ops(cur, a.rec + ((size_t)gch * H + h) * REC_BYTES, w, tl, gq);
+    uint4 v0[2];
+    load_v(v0, a.v, c0, (int)((eos - c0) < CH ? (eos - c0) : CH), H, h, vs, tid);
+    store_vt(sVt, v0, tid);
+  }
+  __syncthreads();
+
+  for (; c0 < eos; c0 += CH, ++gch) {
+    const int L = (int)((eos - c0) < CH ? (eos - c0) : CH);
+    const bool more = c0 + CH < eos;
+    // prefetch the next chunk's record operands and V tile
+    if (more) {
+      load_ops(nxt, a.rec + ((size_t)(gch + 1) * H + h) * REC_BYTES, w, tl, gq);
+      const int64_t c1 = c0 + CH;
+      load_v(vnext, a.v, c1, (int)((eos - c1) < CH ? (eos - c1) : CH), H, h, vs, tid);
+    }
+
+    // ---- U, D = U - W S, O = QG S (token rows 16w.., all 64 columns)
+    f32x4 D[4], O[4];
+#pragma unroll
+    for (int nn = 0; nn < 4; ++nn) {
+      const int col = 16 * nn + tl;
+      f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (ks < ksmax) {
+          const bf16x8 vb = *reinterpret_cast<const bf16x8*>(sVt + col * TP + 32 * ks + 8 * gq);
+          u = mfma_bf16(cur.tbh[ks], vb, u);
+          u = mfma_bf16(cur.tbl[ks], vb, u);
+        }
+      }
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const f16x8 sb = *reinterpret_cast<const f16x8*>(sSt + col * SP + 32 * kb + 8 * gq);
+        u = mfma_f16(cur.nw[kb], sb, u);
+        o = mfma_f16(cur.qg[kb], sb, o);
+      }
+      D[nn] = u;
+      O[nn] = o;
+      // D^T hi/lo: lane holds tokens 16w + 4gq + 0..3 of column col
+      f16x4 dh, dl;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const _Float16 hv = (_Float16)u[ii];
+        dh[ii] = hv;
+        dl[ii] = (_Float16)(u[ii] - (float)hv);
+      }
+      *reinterpret_cast<f16x4*>(sDth + col * TP + 16 * w + 4 * gq) = dh;
+      *reinterpret_cast<f16x4*>(sDtl + col * TP + 16 * w + 4 * gq) = dl;
+    }
+    __syncthreads();
+
+    // ---- O += A_qk D, store; S = Diag(exp(G_L)) S + Kt^T D
+#pragma unroll
+    for (int nn = 0; nn < 4; ++nn) {
+      const int col = 16 * nn + tl;
+      f16x8 dh[2], dl[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        dh[ks] = *reinterpret_cast<const f16x8*>(sDth + col * TP + 32 * ks + 8 * gq);
+        dl[ks] = *reinterpret_cast<const f16x8*>(sDtl + col * TP + 32 * ks + 8 * gq);
+      }
+      f32x4 o = O[nn];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        if (ks < ksmax) o = mfma_f16(cur.aqk[ks], dh[ks], o);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int tt = 16 * w + 4 * gq + ii;
+        if (tt < L) {
+          const __bf16 ob = (__bf16)(o[ii] * a.scale);
+          a.out[((c0 + tt) * H + h) * VD + vs + col] = __builtin_bit_cast(uint16_t, ob);
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x4 s = S[mt][nn];
+        s[0] *= cur.gl[mt].x;
+        s[1] *= cur.gl[mt].y;
+        s[2] *= cur.gl[mt].z;
+        s[3] *= cur.gl[mt].w;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          s = mfma_f16(cur.kth[mt][ks], dh[ks], s);
+          s = mfma_f16(cur.kth[mt][ks], dl[ks], s);
+          s = mfma_f16(cur.ktl[mt][ks], dh[ks], s);
+        }
+        S[mt][nn] = s;
+      }
+    }
+    store_st();
+    if (more) {
+      store_vt(sVt, vnext, tid);  // U of this chunk read sVt before the barrier above
+      cur = nxt;
+    }
+    __syncthreads();
+  }
+
+  if (a.fin) {
+    float* dst = a.fin + ((int64_t)seq * H + h) * KD * VD;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nn = 0; nn < 4; ++nn)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          dst[(32 * w + 16 * mt + 4 * gq + ii) * VD + vs + 16 * nn + tl] = S[mt][nn][ii];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_inter(const InterArgs& args, hipStream_t st) {
+  const int64_t items = (int64_t)args.map.N * args.H;
+  const int64_t grid = (items + 7) / 8 * 8 * NV;
+  InterArgs a = args;
+  void* kargs[] = {(void*)&a};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_inter_kernel), dim3((unsigned)grid),
+                         dim3(NTHREADS), kargs, 0, st);
+}
+
+}  // namespace kda
