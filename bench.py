@@ -12,9 +12,9 @@ starts.  Prints one JSON line.
 Roofline: the forward kernel is HBM-bound.  Its algorithmic traffic is
 1282 bytes per head-token (q, k, v, raw_gate: 4 x 128 x 2 B; raw_beta 2 B;
 out 128 x 2 B) plus 2 x 64 KiB of fp32 state I/O per (sequence, head); the
-achieved rate is that byte count divided by the kernel's average duration,
-measured with HIP events recorded on the launch stream around every timed
-launch.  ``traffic`` is the measured HBM bytes per launch from rocprofv3
+achieved rate is that byte count divided by the average device time of one
+forward (its intra-chunk and inter-chunk kernels back to back), measured with
+HIP events recorded on the launch stream around every timed launch.  ``traffic`` is the measured HBM bytes per launch from rocprofv3
 FETCH_SIZE / WRITE_SIZE counters (profiles/), reported only while the kernel
 source is unchanged since the counters were taken.
 

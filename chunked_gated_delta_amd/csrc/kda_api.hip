@@ -169,6 +169,12 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const void* ra
   ia.map = map;
   ia.H = (int)H;
   ia.lb2 = lower_bound * LOG2E;
+  ia.timers = nullptr;
+#ifdef KDA_PHASE_TIMERS
+  // timer builds only: the caller extends the workspace by 16 counters per
+  // workgroup of each kernel, intra first
+  ia.timers = reinterpret_cast<unsigned long long*>(ws + lay.total);
+#endif
   if (launch_status(launch_intra(ia, max_chunks, st), "intra") != KDA_SUCCESS) return KDA_ERR_LAUNCH;
 
   InterArgs xa;
@@ -181,6 +187,10 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const void* ra
   xa.map = map;
   xa.H = (int)H;
   xa.scale = scale;
+  xa.timers = nullptr;
+#ifdef KDA_PHASE_TIMERS
+  xa.timers = reinterpret_cast<unsigned long long*>(ws + lay.total) + (size_t)max_chunks * H * 16;
+#endif
   return launch_status(launch_inter(xa, st), "inter");
 }
 

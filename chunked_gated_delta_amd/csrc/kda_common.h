@@ -21,8 +21,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // Per (chunk, head) record written by the intra-chunk kernel and read by the
-// inter-chunk kernel.  Every array is laid out so that one MFMA operand
-// fragment of the reader is one 16-byte load per lane.
+// inter-chunk kernel.  Arrays are stored in the reader's MFMA fragment order:
+// fragment f of an operand is 64 lanes x 16 bytes, contiguous, so every load
+// instruction of the reader moves one aligned 1 KB block.
 //   NW   : -W = -T diag(beta) (K^ * exp(G))      f16  [64 tok][128 ch]
 //   QG   : Q^ * exp(G)                           f16  [64 tok][128 ch]
 //   KTH/L: (K^ * exp(G_L - G))^T  hi / lo        f16  [128 ch][64 tok]
@@ -40,6 +41,22 @@ constexpr size_t REC_TBL = REC_TBH + CH * CH * 2;
 constexpr size_t REC_GL = REC_TBL + CH * CH * 2;
 constexpr size_t REC_BYTES = REC_GL + KD * 4;  // 90624
 static_assert(REC_BYTES % 256 == 0, "record alignment");
+
+// Element index (in 16-bit units) of the fragment-ordered record arrays.  The
+// reader's lane l = 16 gq + tl of wave w loads 8 consecutive k elements:
+//   [64 tok][128 ch] (NW, QG): row 16w + tl, channels 32kb + 8gq + 0..7, fragment 4w + kb
+//   [64 tok][64 tok] (AQK, TB): row 16w + tl, tokens 32ks + 8gq + 0..7, fragment 2w + ks
+//   [128 ch][64 tok] (KT):      channel 32w + 16mt + tl, tokens 32ks + 8gq + 0..7,
+//                               fragment 4w + 2mt + ks
+__host__ __device__ constexpr int frag_tc(int i, int c) {  // [64][128]
+  return ((((i >> 4) * 4 + (c >> 5)) * 64 + ((c >> 3) & 3) * 16 + (i & 15)) << 3) + (c & 7);
+}
+__host__ __device__ constexpr int frag_tt(int i, int j) {  // [64][64]
+  return ((((i >> 4) * 2 + (j >> 5)) * 64 + ((j >> 3) & 3) * 16 + (i & 15)) << 3) + (j & 7);
+}
+__host__ __device__ constexpr int frag_ct(int c, int t) {  // [128][64]
+  return ((((c >> 4) * 2 + (t >> 5)) * 64 + ((t >> 3) & 3) * 16 + (c & 15)) << 3) + (t & 7);
+}
 
 // Chunk bookkeeping shared by both kernels.  Without cu_seqlens there are N
 // sequences of length T and sequence n owns chunks [n*ceil(T/64), ...).  With
@@ -108,6 +125,21 @@ __device__ __forceinline__ void lds_f32x8(const float* src, float (&d)[8]) {
   d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
 }
 
+// Optional per-phase cycle counters, compiled out unless KDA_PHASE_TIMERS is
+// defined: thread 0 of each workgroup accumulates cycle-counter deltas between
+// phase marks and stores them to timers[blockIdx.x * 16 + i].
+#ifdef KDA_PHASE_TIMERS
+#define KDA_TIMER_DECL unsigned long long tacc_[15] = {0}; unsigned long long tlast_ = 0;
+#define KDA_TIMER_MARK(i) do { if (threadIdx.x == 0) { const unsigned long long t_ = __builtin_readcyclecounter(); \
+    if ((i) > 0) tacc_[(i) - 1] += t_ - tlast_; tlast_ = t_; } } while (0)
+#define KDA_TIMER_STORE(ptr) do { if (threadIdx.x == 0 && (ptr)) for (int i_ = 0; i_ < 15; ++i_) \
+    (ptr)[(size_t)blockIdx.x * 16 + i_] = tacc_[i_]; } while (0)
+#else
+#define KDA_TIMER_DECL
+#define KDA_TIMER_MARK(i) do { } while (0)
+#define KDA_TIMER_STORE(ptr) do { } while (0)
+#endif
+
 // Host-side launchers (defined next to their kernels).
 struct IntraArgs {
   const uint16_t* q;
@@ -120,6 +152,7 @@ struct IntraArgs {
   ChunkMap map;
   int H;
   float lb2;        // lower_bound * log2(e)
+  unsigned long long* timers;  // phase timers (KDA_PHASE_TIMERS builds only), else nullptr
 };
 struct InterArgs {
   const uint16_t* v;
@@ -131,6 +164,7 @@ struct InterArgs {
   ChunkMap map;
   int H;
   float scale;
+  unsigned long long* timers;  // phase timers (KDA_PHASE_TIMERS builds only), else nullptr
 };
 hipError_t launch_intra(const IntraArgs& a, int64_t max_chunks, hipStream_t st);
 hipError_t launch_inter(const InterArgs& a, hipStream_t st);

@@ -28,7 +28,9 @@ constexpr int OFF_VT = 0;                          // bf16 [VT][TP]   V^T
 constexpr int OFF_ST = OFF_VT + VT * TP * 2;       // f16  [VT][SP]   S^T
 constexpr int OFF_DTH = OFF_ST + VT * SP * 2;      // f16  [VT][TP]   D^T hi
 constexpr int OFF_DTL = OFF_DTH + VT * TP * 2;     // f16  [VT][TP]   D^T lo
-constexpr int LDS_BYTES = OFF_DTL + VT * TP * 2;
+constexpr int OP = VT + 8;                         // token-row pitch of the output tile
+constexpr int OFF_O = OFF_DTL + VT * TP * 2;       // bf16 [CH][OP]   output staging
+constexpr int LDS_BYTES = OFF_O + CH * OP * 2;
 
 // the record operands one wave needs per chunk
 struct Ops {
@@ -40,62 +42,65 @@ struct Ops {
   float4 gl[2];       // exp(G_L) of channels 32w + 16mt + 4gq + 0..3
 };
 
-__device__ __forceinline__ void load_ops(Ops& o, const char* rec, int w, int tl, int gq) {
-  const _Float16* nw = reinterpret_cast<const _Float16*>(rec + REC_NW);
-  const _Float16* qg = reinterpret_cast<const _Float16*>(rec + REC_QG);
-  const _Float16* aq = reinterpret_cast<const _Float16*>(rec + REC_AQK);
-  const __bf16* th = reinterpret_cast<const __bf16*>(rec + REC_TBH);
-  const __bf16* tlw = reinterpret_cast<const __bf16*>(rec + REC_TBL);
-  const _Float16* kh = reinterpret_cast<const _Float16*>(rec + REC_KTH);
-  const _Float16* kl = reinterpret_cast<const _Float16*>(rec + REC_KTL);
+__device__ __forceinline__ void load_ops(Ops& o, const char* rec, int w, int lane, int gq, int ksmax) {
+  // every load below is one contiguous 1 KB fragment (64 lanes x 16 bytes)
+  const f16x8* nw = reinterpret_cast<const f16x8*>(rec + REC_NW) + lane;
+  const f16x8* qg = reinterpret_cast<const f16x8*>(rec + REC_QG) + lane;
+  const f16x8* aq = reinterpret_cast<const f16x8*>(rec + REC_AQK) + lane;
+  const bf16x8* th = reinterpret_cast<const bf16x8*>(rec + REC_TBH) + lane;
+  const bf16x8* tlw = reinterpret_cast<const bf16x8*>(rec + REC_TBL) + lane;
+  const f16x8* kh = reinterpret_cast<const f16x8*>(rec + REC_KTH) + lane;
+  const f16x8* kl = reinterpret_cast<const f16x8*>(rec + REC_KTL) + lane;
   const float* gl = reinterpret_cast<const float*>(rec + REC_GL);
-  const int row = 16 * w + tl;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    o.nw[kb] = *reinterpret_cast<const f16x8*>(nw + row * KD + 32 * kb + 8 * gq);
-    o.qg[kb] = *reinterpret_cast<const f16x8*>(qg + row * KD + 32 * kb + 8 * gq);
+    o.nw[kb] = nw[(4 * w + kb) * 64];
+    o.qg[kb] = qg[(4 * w + kb) * 64];
   }
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    o.aqk[ks] = *reinterpret_cast<const f16x8*>(aq + row * CH + 32 * ks + 8 * gq);
-    o.tbh[ks] = *reinterpret_cast<const bf16x8*>(th + row * CH + 32 * ks + 8 * gq);
-    o.tbl[ks] = *reinterpret_cast<const bf16x8*>(tlw + row * CH + 32 * ks + 8 * gq);
+    // rows 16w.. of the lower-triangular A_qk and T only see tokens < 16w + 16:
+    // waves 0 and 1 re-read their first k-step instead of the zero upper half
+    const int kk = ks < ksmax ? ks : 0;
+    o.aqk[ks] = aq[(2 * w + kk) * 64];
+    o.tbh[ks] = th[(2 * w + kk) * 64];
+    o.tbl[ks] = tlw[(2 * w + kk) * 64];
   }
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    const int c = 32 * w + 16 * mt + tl;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      o.kth[mt][ks] = *reinterpret_cast<const f16x8*>(kh + c * CH + 32 * ks + 8 * gq);
-      o.ktl[mt][ks] = *reinterpret_cast<const f16x8*>(kl + c * CH + 32 * ks + 8 * gq);
+      o.kth[mt][ks] = kh[(4 * w + 2 * mt + ks) * 64];
+      o.ktl[mt][ks] = kl[(4 * w + 2 * mt + ks) * 64];
     }
     o.gl[mt] = *reinterpret_cast<const float4*>(gl + 32 * w + 16 * mt + 4 * gq);
   }
 }
 
-// V tile of a chunk: thread -> (token tid/4, columns 16*(tid%4) .. +15)
+// V tile of a chunk: thread -> (token tid/4, columns 16*(tid%4) .. +15).  Rows
+// past the chunk end are loaded from the clamped last row and zeroed only when
+// written to LDS, so issuing the prefetch never waits for its data.
 __device__ __forceinline__ void load_v(uint4 (&vv)[2], const uint16_t* v, int64_t c0, int L, int H,
                                        int h, int vs, int tid) {
   const int t = tid >> 2;
   const int cg = tid & 3;
-  vv[0] = make_uint4(0, 0, 0, 0);
-  vv[1] = vv[0];
-  if (t < L) {
-    const uint4* src = reinterpret_cast<const uint4*>(v + ((c0 + t) * H + h) * VD + vs + 16 * cg);
-    vv[0] = src[0];
-    vv[1] = src[1];
-  }
+  const int tc = t < L ? t : L - 1;  // L >= 1: the clamped row is inside the sequence
+  const uint4* src = reinterpret_cast<const uint4*>(v + ((c0 + tc) * H + h) * VD + vs + 16 * cg);
+  vv[0] = src[0];
+  vv[1] = src[1];
 }
 
-__device__ __forceinline__ void store_vt(__bf16* sVt, const uint4 (&vv)[2], int tid) {
+__device__ __forceinline__ void store_vt(__bf16* sVt, const uint4 (&vv)[2], int tid, int L) {
   const int t = tid >> 2;
   const int cg = tid & 3;
+  const bool keep = t < L;
   const uint32_t wds[8] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w, vv[1].x, vv[1].y, vv[1].z, vv[1].w};
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int col = 16 * cg + 2 * u;
-    sVt[col * TP + t] = __builtin_bit_cast(__bf16, (uint16_t)(wds[u] & 0xffffu));
-    sVt[(col + 1) * TP + t] = __builtin_bit_cast(__bf16, (uint16_t)(wds[u] >> 16));
+    const uint32_t wv = keep ? wds[u] : 0u;
+    sVt[col * TP + t] = __builtin_bit_cast(__bf16, (uint16_t)(wv & 0xffffu));
+    sVt[(col + 1) * TP + t] = __builtin_bit_cast(__bf16, (uint16_t)(wv >> 16));
   }
 }
 
@@ -156,31 +161,42 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
       }
   };
   store_st();
-
-  Ops cur, nxt;
-  uint4 vnext[2];
-  int64_t c0 = bos;
-  int64_t gch = gfirst;
-  if (c0 < eos) {
-    load_ops(cur, a.rec + ((size_t)gch * H + h) * REC_BYTES, w, tl, gq);
-    uint4 v0[2];
-    load_v(v0, a.v, c0, (int)((eos - c0) < CH ? (eos - c0) : CH), H, h, vs, tid);
-    store_vt(sVt, v0, tid);
+  __bf16* sO = reinterpret_cast<__bf16*>(smem + OFF_O);
+  // Record operands and V tiles are prefetched two chunks ahead: three sets
+  // rotate through the 3x unrolled loop below (chunk c uses set c % 3).
+  Ops opsA, opsB, opsC;
+  uint4 vA[2], vB[2], vC[2];
+  auto chunk_len = [&](int64_t c) { return (int)((eos - c) < CH ? (eos - c) : CH); };
+  if (bos < eos) {
+    const bool two = bos + CH < eos;
+    load_ops(opsA, a.rec + ((size_t)gfirst * H + h) * REC_BYTES, w, lane, gq, ksmax);
+    load_v(vA, a.v, bos, chunk_len(bos), H, h, vs, tid);
+    load_ops(opsB, a.rec + ((size_t)(two ? gfirst + 1 : gfirst) * H + h) * REC_BYTES, w, lane, gq, ksmax);
+    load_v(vB, a.v, two ? bos + CH : bos, two ? chunk_len(bos + CH) : chunk_len(bos), H, h, vs, tid);
+    store_vt(sVt, vA, tid, chunk_len(bos));
   }
   __syncthreads();
 
-  for (; c0 < eos; c0 += CH, ++gch) {
-    const int L = (int)((eos - c0) < CH ? (eos - c0) : CH);
-    const bool more = c0 + CH < eos;
-    // prefetch the next chunk's record operands and V tile
-    if (more) {
-      load_ops(nxt, a.rec + ((size_t)(gch + 1) * H + h) * REC_BYTES, w, tl, gq);
-      const int64_t c1 = c0 + CH;
-      load_v(vnext, a.v, c1, (int)((eos - c1) < CH ? (eos - c1) : CH), H, h, vs, tid);
+  KDA_TIMER_DECL
+  // one chunk step: `cur` holds this chunk's record operands; `v1` the V tile
+  // of chunk c+1 (written to LDS at the end of this step); chunk c+2's operands
+  // and V tile are issued into `pre` / `v2`
+  auto step = [&](Ops& cur, Ops& pre, uint4 (&v1)[2], uint4 (&v2)[2], int64_t c0, int64_t gch) {
+    KDA_TIMER_MARK(0);
+    const int L = chunk_len(c0);
+    const int64_t c1 = c0 + CH, c2 = c0 + 2 * CH;
+    // Issued unconditionally (past the end of the sequence the current chunk
+    // is re-read and ignored) so that every path has the same number of
+    // outstanding loads and the wait counts stay two chunks deep.
+    {
+      const bool in = c2 < eos;
+      load_ops(pre, a.rec + ((size_t)(in ? gch + 2 : gch) * H + h) * REC_BYTES, w, lane, gq, ksmax);
+      load_v(v2, a.v, in ? c2 : c0, in ? chunk_len(c2) : L, H, h, vs, tid);
     }
+    KDA_TIMER_MARK(1);
 
     // ---- U, D = U - W S, O = QG S (token rows 16w.., all 64 columns)
-    f32x4 D[4], O[4];
+    f32x4 O[4];
 #pragma unroll
     for (int nn = 0; nn < 4; ++nn) {
       const int col = 16 * nn + tl;
@@ -200,7 +216,6 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
         u = mfma_f16(cur.nw[kb], sb, u);
         o = mfma_f16(cur.qg[kb], sb, o);
       }
-      D[nn] = u;
       O[nn] = o;
       // D^T hi/lo: lane holds tokens 16w + 4gq + 0..3 of column col
       f16x4 dh, dl;
@@ -213,9 +228,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
       *reinterpret_cast<f16x4*>(sDth + col * TP + 16 * w + 4 * gq) = dh;
       *reinterpret_cast<f16x4*>(sDtl + col * TP + 16 * w + 4 * gq) = dl;
     }
+    KDA_TIMER_MARK(2);
     __syncthreads();
+    KDA_TIMER_MARK(3);
 
-    // ---- O += A_qk D, store; S = Diag(exp(G_L)) S + Kt^T D
+    // ---- O += A_qk D; S = Diag(exp(G_L)) S + Kt^T D
 #pragma unroll
     for (int nn = 0; nn < 4; ++nn) {
       const int col = 16 * nn + tl;
@@ -229,14 +246,9 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
         if (ks < ksmax) o = mfma_f16(cur.aqk[ks], dh[ks], o);
+      // output tile rows 16w + 4gq + ii, column col (staged for 16-byte stores)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int tt = 16 * w + 4 * gq + ii;
-        if (tt < L) {
-          const __bf16 ob = (__bf16)(o[ii] * a.scale);
-          a.out[((c0 + tt) * H + h) * VD + vs + col] = __builtin_bit_cast(uint16_t, ob);
-        }
-      }
+      for (int ii = 0; ii < 4; ++ii) sO[(16 * w + 4 * gq + ii) * OP + col] = (__bf16)(o[ii] * a.scale);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         f32x4 s = S[mt][nn];
@@ -253,13 +265,39 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
         S[mt][nn] = s;
       }
     }
-    store_st();
-    if (more) {
-      store_vt(sVt, vnext, tid);  // U of this chunk read sVt before the barrier above
-      cur = nxt;
+    // this wave's 16 output rows: lane -> row 16w + lane/4, 16 columns per lane
+    {
+      const int orow = 16 * w + (lane >> 2);
+      const int ocol = 16 * (lane & 3);
+      if (orow < L) {
+        const uint4* srcp = reinterpret_cast<const uint4*>(sO + orow * OP + ocol);
+        uint4* dstp = reinterpret_cast<uint4*>(a.out + ((c0 + orow) * H + h) * VD + vs + ocol);
+        dstp[0] = srcp[0];
+        dstp[1] = srcp[1];
+      }
     }
+    KDA_TIMER_MARK(4);
+    store_st();
+    if (c1 < eos) store_vt(sVt, v1, tid, chunk_len(c1));  // U of this chunk read sVt before the barrier above
+    KDA_TIMER_MARK(5);
     __syncthreads();
+    KDA_TIMER_MARK(6);
+  };
+
+  for (int64_t c0 = bos, gch = gfirst; c0 < eos;) {
+    step(opsA, opsC, vB, vC, c0, gch);
+    c0 += CH;
+    ++gch;
+    if (c0 >= eos) break;
+    step(opsB, opsA, vC, vA, c0, gch);
+    c0 += CH;
+    ++gch;
+    if (c0 >= eos) break;
+    step(opsC, opsB, vA, vB, c0, gch);
+    c0 += CH;
+    ++gch;
   }
+  KDA_TIMER_STORE(a.timers);
 
   if (a.fin) {
     float* dst = a.fin + ((int64_t)seq * H + h) * KD * VD;

@@ -114,6 +114,8 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
   const int lane = tid & 63;
   const int tl = lane & 15;
   const int gq = lane >> 4;
+  KDA_TIMER_DECL
+  KDA_TIMER_MARK(0);
 
   // gate: sigmoid(x) = 1 / (1 + 2^(raw * na + nb_c)), na = -exp(A_log) log2(e)
   const float na = -__expf(a.A_log[h]) * LOG2E;
@@ -138,6 +140,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
   }
   const float braw = valid ? __uint_as_float((uint32_t)a.beta[trow] << 16) : 0.0f;
   __syncthreads();  // sNB
+  KDA_TIMER_MARK(1);
 
   // ============================ prep ======================================
   float gl[4][8];
@@ -184,6 +187,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
   }
   if (gq == 0) sB[ti] = beta;
   __syncthreads();
+  KDA_TIMER_MARK(2);
   if (tid < KD) {
     float P[5];
     P[0] = 0.f;
@@ -203,6 +207,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
     gGL[tid] = fexp2(P[4]);
   }
   __syncthreads();
+  KDA_TIMER_MARK(3);
 
   // ============================ operands ==================================
   bf16x8 kLFh[4], kLFl[4], kEh[4], kEl[4], qLF[4];
@@ -241,17 +246,18 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
       sKG[c * TP + ti] = (_Float16)(x * EP[e]);   // k^ exp(G_t)
       const float kt = y * EL[e];                  // k^ exp(G_L - G_t)
       const _Float16 kth = (_Float16)kt;
-      gKTH[c * CH + ti] = kth;
-      gKTL[c * CH + ti] = (_Float16)(kt - (float)kth);
+      gKTH[frag_ct(c, ti)] = kth;
+      gKTL[frag_ct(c, ti)] = (_Float16)(kt - (float)kth);
       qg[e] = (_Float16)(ql * EP[e]);              // q^ exp(G_t)
     }
-    *reinterpret_cast<f16x8*>(gQG + ti * KD + 32 * kb + 8 * gq) = qg;
+    *reinterpret_cast<f16x8*>(gQG + frag_tc(ti, 32 * kb + 8 * gq)) = qg;
     if (w < 3) {
       *reinterpret_cast<bf16x8*>(sKRFh + ti * KP + 32 * kb + 8 * gq) = krh;
       *reinterpret_cast<bf16x8*>(sKRFl + ti * KP + 32 * kb + 8 * gq) = krl;
     }
   }
   __syncthreads();
+  KDA_TIMER_MARK(4);
 
   // ======================= A_kk and A_qk ==================================
   // wave w owns row-block w; lane holds C[16w + 4gq + ii][16b + tl]
@@ -301,12 +307,12 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
       for (int ii = 0; ii < 4; ++ii) {
         const int i = i0 + ii;
         sA[i * AP + j] = (j < i) ? akk[ii] * sB[i] : 0.0f;
-        gAQK[i * CH + j] = (_Float16)((j <= i) ? aqk[ii] : 0.0f);
+        gAQK[frag_tt(i, j)] = (_Float16)((j <= i) ? aqk[ii] : 0.0f);
       }
     }
     for (int b = w + 1; b < 4; ++b) {
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) gAQK[(i0 + ii) * CH + 16 * b + tl] = (_Float16)0.0f;
+      for (int ii = 0; ii < 4; ++ii) gAQK[frag_tt(i0 + ii, 16 * b + tl)] = (_Float16)0.0f;
     }
     // T_ww = (I + A_ww)^-1 by forward substitution, lane cc < 16 owns column
     // cc.  This wave wrote A_ww just above and LDS operations of one wave
@@ -327,6 +333,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
     }
   }
   __syncthreads();
+  KDA_TIMER_MARK(5);
 
   // ============= off-diagonal blocks of T, row-block by row-block ==========
   //     T_{b,b'} = -T_bb * sum_{m=b'}^{b-1} A_{b,m} T_{m,b'}   (fp32 MFMA)
@@ -358,6 +365,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
     __syncthreads();
   }
 
+  KDA_TIMER_MARK(6);
   // ======= T diag(b): fp16 hi/lo into LDS (for W), bf16 hi/lo to the record
   for (int it = tid; it < CH * 8; it += NTHREADS) {
     const int i = it >> 3;
@@ -380,10 +388,11 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
     }
     *reinterpret_cast<f16x8*>(sTbh + i * TBP + j0) = h16;
     *reinterpret_cast<f16x8*>(sTbl + i * TBP + j0) = l16;
-    *reinterpret_cast<bf16x8*>(gTBH + i * CH + j0) = hb;
-    *reinterpret_cast<bf16x8*>(gTBL + i * CH + j0) = lb;
+    *reinterpret_cast<bf16x8*>(gTBH + frag_tt(i, j0)) = hb;
+    *reinterpret_cast<bf16x8*>(gTBL + frag_tt(i, j0)) = lb;
   }
   __syncthreads();
+  KDA_TIMER_MARK(7);
 
   // ======================= -W = -(T diag(b)) (K^ exp(G)) ===================
   // wave w: channels 32w..32w+31 (2 column tiles), all 64 rows
@@ -408,8 +417,10 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
     for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
-        gNW[(16 * m + 4 * gq + ii) * KD + 32 * w + 16 * nn + tl] = (_Float16)(-acc[nn][ii]);
+        gNW[frag_tc(16 * m + 4 * gq + ii, 32 * w + 16 * nn + tl)] = (_Float16)(-acc[nn][ii]);
   }
+  KDA_TIMER_MARK(8);
+  KDA_TIMER_STORE(a.timers);
 }
 
 }  // namespace
