@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -94,6 +95,52 @@ def copy_calibration(gib: float = 2.0):
     print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 3}))
 
 
+def write_traffic(fwd_fetch, fwd_write, copy_fetch, copy_write, copy_bytes=2 << 30):
+    """Turn four rocprofv3 --pmc counter CSVs (FETCH_SIZE / WRITE_SIZE, KiB per
+    dispatch) of this benchmark and of --copy-calibration into the traffic file.
+
+    Each counter is scaled by what it reads for the plain copy of known size;
+    the forward's figure is the average over its dispatches of each kernel."""
+    import collections
+    import csv
+
+    def per_kernel(path, counter):
+        acc = collections.defaultdict(float)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                acc[(int(r["Dispatch_Id"]), r["Kernel_Name"])] += float(r["Counter_Value"])
+        by = collections.defaultdict(list)
+        for (_, name), kib in acc.items():
+            by[name].append(kib)
+        return by
+
+    def factor(path, counter):
+        runs = [k for name, ks in per_kernel(path, counter).items() if "copyBuffer" in name for k in ks]
+        kib = max(runs)  # the 2 GiB copies (small runtime copies read far less)
+        return copy_bytes / (kib * 1024.0)
+
+    ff, wf = factor(copy_fetch, "FETCH_SIZE"), factor(copy_write, "WRITE_SIZE")
+    kernels = {}
+    for path, counter, fac, key in ((fwd_fetch, "FETCH_SIZE", ff, "read_bytes"),
+                                    (fwd_write, "WRITE_SIZE", wf, "write_bytes")):
+        for name, ks in per_kernel(path, counter).items():
+            if not name.startswith("kda::"):
+                continue
+            short = re.search(r"(kda_\w+_kernel)", name).group(1)
+            kernels.setdefault(short, {})[key] = sum(ks) / len(ks) * 1024.0 * fac
+    total = sum(v.get("read_bytes", 0.0) + v.get("write_bytes", 0.0) for v in kernels.values())
+    doc = {"workload": "kda_fwd B=1 T=32768 H=96 K=V=128 (bench.py defaults)",
+           "kernel_source_sha256": kernel_source_hash(),
+           "hbm_bytes_per_launch": total,
+           "kernels": kernels,
+           "calibration": {"copy_bytes": copy_bytes, "fetch_size_factor": ff,
+                           "write_size_factor": wf}}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(doc, f, indent=1)
+        f.write("\n")
+    print(json.dumps(doc))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,7 +151,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=96)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FWD_FETCH", "FWD_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 counter_collection.csv files -> profiles/kda_fwd_c3_traffic.json")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
