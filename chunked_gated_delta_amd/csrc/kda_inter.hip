@@ -42,39 +42,57 @@ struct Ops {
   float4 gl[2];       // exp(G_L) of channels 32w + 16mt + 4gq + 0..3
 };
 
+// One group of a chunk's record operands (P = 0..4).  The groups are issued
+// at different points of the previous step so that the vector-memory path
+// drains them while that step's MFMAs run, instead of stalling one block of
+// issue.  Every load is one contiguous 1 KB fragment (64 lanes x 16 bytes).
+template <int P>
 __device__ __forceinline__ void load_ops(Ops& o, const char* rec, int w, int lane, int gq, int ksmax) {
-  // every load below is one contiguous 1 KB fragment (64 lanes x 16 bytes)
-  const f16x8* nw = reinterpret_cast<const f16x8*>(rec + REC_NW) + lane;
-  const f16x8* qg = reinterpret_cast<const f16x8*>(rec + REC_QG) + lane;
-  const f16x8* aq = reinterpret_cast<const f16x8*>(rec + REC_AQK) + lane;
-  const bf16x8* th = reinterpret_cast<const bf16x8*>(rec + REC_TBH) + lane;
-  const bf16x8* tlw = reinterpret_cast<const bf16x8*>(rec + REC_TBL) + lane;
-  const f16x8* kh = reinterpret_cast<const f16x8*>(rec + REC_KTH) + lane;
-  const f16x8* kl = reinterpret_cast<const f16x8*>(rec + REC_KTL) + lane;
-  const float* gl = reinterpret_cast<const float*>(rec + REC_GL);
+  if constexpr (P == 0) {
+    const f16x8* nw = reinterpret_cast<const f16x8*>(rec + REC_NW) + lane;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    o.nw[kb] = nw[(4 * w + kb) * 64];
-    o.qg[kb] = qg[(4 * w + kb) * 64];
-  }
+    for (int kb = 0; kb < 4; ++kb) o.nw[kb] = nw[(4 * w + kb) * 64];
+  } else if constexpr (P == 1) {
+    const f16x8* qg = reinterpret_cast<const f16x8*>(rec + REC_QG) + lane;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    // rows 16w.. of the lower-triangular A_qk and T only see tokens < 16w + 16:
-    // waves 0 and 1 re-read their first k-step instead of the zero upper half
-    const int kk = ks < ksmax ? ks : 0;
-    o.aqk[ks] = aq[(2 * w + kk) * 64];
-    o.tbh[ks] = th[(2 * w + kk) * 64];
-    o.tbl[ks] = tlw[(2 * w + kk) * 64];
-  }
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+    for (int kb = 0; kb < 4; ++kb) o.qg[kb] = qg[(4 * w + kb) * 64];
+  } else if constexpr (P == 2) {
+    const f16x8* aq = reinterpret_cast<const f16x8*>(rec + REC_AQK) + lane;
+    const bf16x8* th = reinterpret_cast<const bf16x8*>(rec + REC_TBH) + lane;
+    const bf16x8* tlw = reinterpret_cast<const bf16x8*>(rec + REC_TBL) + lane;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      o.kth[mt][ks] = kh[(4 * w + 2 * mt + ks) * 64];
-      o.ktl[mt][ks] = kl[(4 * w + 2 * mt + ks) * 64];
+      // rows 16w.. of the lower-triangular A_qk and T only see tokens < 16w + 16:
+      // waves 0 and 1 re-read their first k-step instead of the zero upper half
+      const int kk = ks < ksmax ? ks : 0;
+      o.aqk[ks] = aq[(2 * w + kk) * 64];
+      o.tbh[ks] = th[(2 * w + kk) * 64];
+      o.tbl[ks] = tlw[(2 * w + kk) * 64];
     }
-    o.gl[mt] = *reinterpret_cast<const float4*>(gl + 32 * w + 16 * mt + 4 * gq);
+  } else if constexpr (P == 3) {
+    const f16x8* kh = reinterpret_cast<const f16x8*>(rec + REC_KTH) + lane;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) o.kth[mt][ks] = kh[(4 * w + 2 * mt + ks) * 64];
+  } else {
+    const f16x8* kl = reinterpret_cast<const f16x8*>(rec + REC_KTL) + lane;
+    const float* gl = reinterpret_cast<const float*>(rec + REC_GL);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) o.ktl[mt][ks] = kl[(4 * w + 2 * mt + ks) * 64];
+      o.gl[mt] = *reinterpret_cast<const float4*>(gl + 32 * w + 16 * mt + 4 * gq);
+    }
   }
+}
+
+__device__ __forceinline__ void load_ops_all(Ops& o, const char* rec, int w, int lane, int gq, int ksmax) {
+  load_ops<0>(o, rec, w, lane, gq, ksmax);
+  load_ops<1>(o, rec, w, lane, gq, ksmax);
+  load_ops<2>(o, rec, w, lane, gq, ksmax);
+  load_ops<3>(o, rec, w, lane, gq, ksmax);
+  load_ops<4>(o, rec, w, lane, gq, ksmax);
 }
 
 // V tile of a chunk: thread -> (token tid/4, columns 16*(tid%4) .. +15).  Rows
@@ -162,37 +180,50 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
   };
   store_st();
   __bf16* sO = reinterpret_cast<__bf16*>(smem + OFF_O);
-  // Record operands and V tiles are prefetched two chunks ahead: three sets
-  // rotate through the 3x unrolled loop below (chunk c uses set c % 3).
-  Ops opsA, opsB, opsC;
-  uint4 vA[2], vB[2], vC[2];
+  // Record operands are prefetched one chunk ahead into two register sets
+  // that alternate through the 2x unrolled loop below; the loads of chunk c+1
+  // are spread over chunk c's step.
+  // With an odd number of chunks the first step is peeled off, so that the
+  // loop always runs whole pairs: a conditional exit between the two steps
+  // would merge a path with set B's loads still in flight into the loop head
+  // and force shallow waits there.
+  Ops opsA, opsB;
   auto chunk_len = [&](int64_t c) { return (int)((eos - c) < CH ? (eos - c) : CH); };
+  const bool odd = ((eos - bos + CH - 1) / CH) & 1;
   if (bos < eos) {
-    const bool two = bos + CH < eos;
-    load_ops(opsA, a.rec + ((size_t)gfirst * H + h) * REC_BYTES, w, lane, gq, ksmax);
-    load_v(vA, a.v, bos, chunk_len(bos), H, h, vs, tid);
-    load_ops(opsB, a.rec + ((size_t)(two ? gfirst + 1 : gfirst) * H + h) * REC_BYTES, w, lane, gq, ksmax);
-    load_v(vB, a.v, two ? bos + CH : bos, two ? chunk_len(bos + CH) : chunk_len(bos), H, h, vs, tid);
-    store_vt(sVt, vA, tid, chunk_len(bos));
+    uint4 v0[2];
+    load_v(v0, a.v, bos, chunk_len(bos), H, h, vs, tid);
+    const char* r0 = a.rec + ((size_t)gfirst * H + h) * REC_BYTES;
+    if (odd)
+      load_ops_all(opsA, r0, w, lane, gq, ksmax);
+    else
+      load_ops_all(opsB, r0, w, lane, gq, ksmax);
+    store_vt(sVt, v0, tid, chunk_len(bos));
   }
   __syncthreads();
 
   KDA_TIMER_DECL
-  // one chunk step: `cur` holds this chunk's record operands; `v1` the V tile
-  // of chunk c+1 (written to LDS at the end of this step); chunk c+2's operands
-  // and V tile are issued into `pre` / `v2`
-  auto step = [&](Ops& cur, Ops& pre, uint4 (&v1)[2], uint4 (&v2)[2], int64_t c0, int64_t gch) {
+  // one chunk step: `cur` holds this chunk's record operands; chunk c+1's
+  // operands are issued into `pre` and its V tile is written to LDS at the end
+  auto step = [&](Ops& cur, Ops& pre, int64_t c0, int64_t gch) {
     KDA_TIMER_MARK(0);
     const int L = chunk_len(c0);
-    const int64_t c1 = c0 + CH, c2 = c0 + 2 * CH;
-    // Issued unconditionally (past the end of the sequence the current chunk
-    // is re-read and ignored) so that every path has the same number of
-    // outstanding loads and the wait counts stay two chunks deep.
-    {
-      const bool in = c2 < eos;
-      load_ops(pre, a.rec + ((size_t)(in ? gch + 2 : gch) * H + h) * REC_BYTES, w, lane, gq, ksmax);
-      load_v(v2, a.v, in ? c2 : c0, in ? chunk_len(c2) : L, H, h, vs, tid);
-    }
+    const int64_t c1 = c0 + CH;
+    // Chunk c+1's loads are issued unconditionally (past the end of the
+    // sequence the current chunk is re-read and ignored) so that every path
+    // has the same number of outstanding loads.
+    const bool in1 = c1 < eos;
+    const char* prec = a.rec + ((size_t)(in1 ? gch + 1 : gch) * H + h) * REC_BYTES;
+    // issue point of a load group, pinned between compute blocks
+#define KDA_ISSUE(stmt)                   \
+  do {                                    \
+    __builtin_amdgcn_sched_barrier(0);    \
+    stmt;                                 \
+    __builtin_amdgcn_sched_barrier(0);    \
+  } while (0)
+    uint4 vn[2];
+    KDA_ISSUE(load_v(vn, a.v, in1 ? c1 : c0, in1 ? chunk_len(c1) : L, H, h, vs, tid));
+    KDA_ISSUE(load_ops<0>(pre, prec, w, lane, gq, ksmax));
     KDA_TIMER_MARK(1);
 
     // ---- U, D = U - W S, O = QG S (token rows 16w.., all 64 columns)
@@ -203,11 +234,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
       f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        if (ks < ksmax) {
-          const bf16x8 vb = *reinterpret_cast<const bf16x8*>(sVt + col * TP + 32 * ks + 8 * gq);
-          u = mfma_bf16(cur.tbh[ks], vb, u);
-          u = mfma_bf16(cur.tbl[ks], vb, u);
-        }
+        // Uniform control flow: every loaded operand register is consumed on
+        // every path, so no load is still outstanding when its register is
+        // reloaded (waves 0 and 1 multiply by zero for their upper k-step).
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(sVt + col * TP + 32 * ks + 8 * gq);
+        u = mfma_bf16(ks < ksmax ? cur.tbh[ks] : bf16x8{}, vb, u);
+        u = mfma_bf16(ks < ksmax ? cur.tbl[ks] : bf16x8{}, vb, u);
       }
       f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -227,6 +259,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
       }
       *reinterpret_cast<f16x4*>(sDth + col * TP + 16 * w + 4 * gq) = dh;
       *reinterpret_cast<f16x4*>(sDtl + col * TP + 16 * w + 4 * gq) = dl;
+      if (nn == 0) KDA_ISSUE(load_ops<1>(pre, prec, w, lane, gq, ksmax));
+      if (nn == 1) KDA_ISSUE(load_ops<2>(pre, prec, w, lane, gq, ksmax));
     }
     KDA_TIMER_MARK(2);
     __syncthreads();
@@ -244,8 +278,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
       }
       f32x4 o = O[nn];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        if (ks < ksmax) o = mfma_f16(cur.aqk[ks], dh[ks], o);
+      for (int ks = 0; ks < 2; ++ks) o = mfma_f16(ks < ksmax ? cur.aqk[ks] : f16x8{}, dh[ks], o);
       // output tile rows 16w + 4gq + ii, column col (staged for 16-byte stores)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) sO[(16 * w + 4 * gq + ii) * OP + col] = (__bf16)(o[ii] * a.scale);
@@ -264,7 +297,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
         }
         S[mt][nn] = s;
       }
+      if (nn == 0) KDA_ISSUE(load_ops<3>(pre, prec, w, lane, gq, ksmax));
+      if (nn == 1) KDA_ISSUE(load_ops<4>(pre, prec, w, lane, gq, ksmax));
     }
+#undef KDA_ISSUE
     // this wave's 16 output rows: lane -> row 16w + lane/4, 16 columns per lane
     {
       const int orow = 16 * w + (lane >> 2);
@@ -278,24 +314,23 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     }
     KDA_TIMER_MARK(4);
     store_st();
-    if (c1 < eos) store_vt(sVt, v1, tid, chunk_len(c1));  // U of this chunk read sVt before the barrier above
+    // U of this chunk read sVt before the barrier above; past the end of the
+    // sequence this rewrites the current tile, which nothing reads
+    store_vt(sVt, vn, tid, in1 ? chunk_len(c1) : L);
     KDA_TIMER_MARK(5);
     __syncthreads();
     KDA_TIMER_MARK(6);
   };
 
-  for (int64_t c0 = bos, gch = gfirst; c0 < eos;) {
-    step(opsA, opsC, vB, vC, c0, gch);
+  int64_t c0 = bos, gch = gfirst;
+  if (odd) {
+    step(opsA, opsB, c0, gch);
     c0 += CH;
     ++gch;
-    if (c0 >= eos) break;
-    step(opsB, opsA, vC, vA, c0, gch);
-    c0 += CH;
-    ++gch;
-    if (c0 >= eos) break;
-    step(opsC, opsB, vA, vB, c0, gch);
-    c0 += CH;
-    ++gch;
+  }
+  for (; c0 < eos; c0 += 2 * CH, gch += 2) {
+    step(opsB, opsA, c0, gch);
+    step(opsA, opsB, c0 + CH, gch + 1);
   }
   KDA_TIMER_STORE(a.timers);
 
