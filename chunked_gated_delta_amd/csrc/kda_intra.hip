@@ -119,26 +119,25 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
 
   // gate: sigmoid(x) = 1 / (1 + 2^(raw * na + nb_c)), na = -exp(A_log) log2(e)
   const float na = -__expf(a.A_log[h]) * LOG2E;
-  if (tid < KD) sNB[tid] = na * a.dt_bias[h * KD + tid];
+  // dt_bias first, then every input load of the chunk, all unconditional: rows
+  // past the chunk end read the last valid row and are zeroed through their
+  // norms, gate and beta below, so no load waits behind a branch.
+  const float dtb = a.dt_bias[h * KD + (tid & (KD - 1))];
 
   // ---- inputs of this lane's token: channels 32kb + 8gq + e
   const int ti = 16 * w + tl;
   const bool valid = ti < L;
-  const int64_t trow = (c0 + ti) * H + h;
+  const int64_t trow = (c0 + (valid ? ti : L - 1)) * H + h;
   uint4 pq[4], pk[4], pg[4];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    pq[kb] = make_uint4(0, 0, 0, 0);
-    pk[kb] = pq[kb];
-    pg[kb] = pq[kb];
-    if (valid) {
-      const int64_t off = trow * KD + 32 * kb + 8 * gq;
-      pq[kb] = *reinterpret_cast<const uint4*>(a.q + off);
-      pk[kb] = *reinterpret_cast<const uint4*>(a.k + off);
-      pg[kb] = *reinterpret_cast<const uint4*>(a.g + off);
-    }
+    const int64_t off = trow * KD + 32 * kb + 8 * gq;
+    pq[kb] = *reinterpret_cast<const uint4*>(a.q + off);
+    pk[kb] = *reinterpret_cast<const uint4*>(a.k + off);
+    pg[kb] = *reinterpret_cast<const uint4*>(a.g + off);
   }
-  const float braw = valid ? __uint_as_float((uint32_t)a.beta[trow] << 16) : 0.0f;
+  const uint16_t braw16 = a.beta[trow];
+  if (tid < KD) sNB[tid] = na * dtb;
   __syncthreads();  // sNB
   KDA_TIMER_MARK(1);
 
@@ -161,8 +160,9 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
   ssq += __shfl_xor(ssq, 32);
   ssk += __shfl_xor(ssk, 16);
   ssk += __shfl_xor(ssk, 32);
-  const float rq = __builtin_amdgcn_rsqf(ssq + L2_EPS);
-  const float rk = __builtin_amdgcn_rsqf(ssk + L2_EPS);
+  const float rq = valid ? __builtin_amdgcn_rsqf(ssq + L2_EPS) : 0.0f;
+  const float rk = valid ? __builtin_amdgcn_rsqf(ssk + L2_EPS) : 0.0f;
+  const float braw = __uint_as_float((uint32_t)braw16 << 16);
   const float beta = valid ? __builtin_amdgcn_rcpf(1.0f + fexp2(-braw * LOG2E)) : 0.0f;
 
   // log-decay in log2 units, inclusive scan over the sub-chunk's 16 tokens
@@ -211,6 +211,14 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
 
   // ============================ operands ==================================
   bf16x8 kLFh[4], kLFl[4], kEh[4], kEl[4], qLF[4];
+  // identity B operands: idt[s] selects channels 16s..16s+15 of a 32-channel
+  // k-block, so that an A fragment [16 tokens][32 channels] comes out of the
+  // MFMA transposed (lane: 4 consecutive tokens of one channel)
+  f16x8 idt[2];
+#pragma unroll
+  for (int sv = 0; sv < 2; ++sv)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) idt[sv][e] = (_Float16)((8 * gq + e == 16 * sv + tl) ? 1.0f : 0.0f);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     float ET[8], EP[8], EL[8], qf[8], kf[8];
@@ -220,7 +228,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
     unpack_bf16x8(pq[kb], qf);
     unpack_bf16x8(pk[kb], kf);
     bf16x8 krh, krl;
-    f16x8 qg;
+    f16x8 qg, kth8, ktl8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int c = 32 * kb + 8 * gq + e;
@@ -246,11 +254,23 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
       sKG[c * TP + ti] = (_Float16)(x * EP[e]);   // k^ exp(G_t)
       const float kt = y * EL[e];                  // k^ exp(G_L - G_t)
       const _Float16 kth = (_Float16)kt;
-      gKTH[frag_ct(c, ti)] = kth;
-      gKTL[frag_ct(c, ti)] = (_Float16)(kt - (float)kth);
+      kth8[e] = kth;
+      ktl8[e] = (_Float16)(kt - (float)kth);
       qg[e] = (_Float16)(ql * EP[e]);              // q^ exp(G_t)
     }
     *reinterpret_cast<f16x8*>(gQG + frag_tc(ti, 32 * kb + 8 * gq)) = qg;
+    // (K^ exp(G_L - G))^T hi/lo: f16 x 1 products summed in fp32 are exact
+#pragma unroll
+    for (int sv = 0; sv < 2; ++sv) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 th = mfma_f16(kth8, idt[sv], zero);
+      const f32x4 tlo = mfma_f16(ktl8, idt[sv], zero);
+      const int cc = 32 * kb + 16 * sv + tl;  // lane: channel cc, tokens 16w + 4gq + 0..3
+      const f16x4 h4 = {(_Float16)th[0], (_Float16)th[1], (_Float16)th[2], (_Float16)th[3]};
+      const f16x4 l4 = {(_Float16)tlo[0], (_Float16)tlo[1], (_Float16)tlo[2], (_Float16)tlo[3]};
+      *reinterpret_cast<f16x4*>(gKTH + frag_ct(cc, 16 * w + 4 * gq)) = h4;
+      *reinterpret_cast<f16x4*>(gKTL + frag_ct(cc, 16 * w + 4 * gq)) = l4;
+    }
     if (w < 3) {
       *reinterpret_cast<bf16x8*>(sKRFh + ti * KP + 32 * kb + 8 * gq) = krh;
       *reinterpret_cast<bf16x8*>(sKRFl + ti * KP + 32 * kb + 8 * gq) = krl;
@@ -272,7 +292,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
           akk = mfma_bf16(kLFh[kb], kEh[kb], akk);
           akk = mfma_bf16(kLFh[kb], kEl[kb], akk);
           akk = mfma_bf16(kLFl[kb], kEh[kb], akk);
-          aqk = mfma_bf16(qLF[kb], kEh[kb], aqk);
+          aqk = mfma_bf16(kEh[kb], qLF[kb], aqk);  // transposed tile
         }
       } else {
         const int jrow = 16 * b + tl;
@@ -298,7 +318,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
           akk = mfma_bf16(lh, rh, akk);
           akk = mfma_bf16(lh, rl, akk);
           akk = mfma_bf16(ll, rh, akk);
-          aqk = mfma_bf16(lq, rh, aqk);
+          aqk = mfma_bf16(rh, lq, aqk);  // transposed tile
         }
       }
       // operands are L2-normalised: only beta_i scales the rows of A_kk
@@ -307,12 +327,16 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
       for (int ii = 0; ii < 4; ++ii) {
         const int i = i0 + ii;
         sA[i * AP + j] = (j < i) ? akk[ii] * sB[i] : 0.0f;
-        gAQK[frag_tt(i, j)] = (_Float16)((j <= i) ? aqk[ii] : 0.0f);
       }
+      // A_qk came out transposed: lane holds row 16w + tl, columns 16b + 4gq + 0..3
+      f16x4 q4;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) q4[ii] = (_Float16)((16 * b + 4 * gq + ii <= ti) ? aqk[ii] : 0.0f);
+      *reinterpret_cast<f16x4*>(gAQK + frag_tt(ti, 16 * b + 4 * gq)) = q4;
     }
     for (int b = w + 1; b < 4; ++b) {
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) gAQK[frag_tt(i0 + ii, 16 * b + tl)] = (_Float16)0.0f;
+      const f16x4 z4 = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
+      *reinterpret_cast<f16x4*>(gAQK + frag_tt(ti, 16 * b + 4 * gq)) = z4;
     }
     // T_ww = (I + A_ww)^-1 by forward substitution, lane cc < 16 owns column
     // cc.  This wave wrote A_ww just above and LDS operations of one wave
@@ -395,7 +419,8 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
   KDA_TIMER_MARK(7);
 
   // ======================= -W = -(T diag(b)) (K^ exp(G)) ===================
-  // wave w: channels 32w..32w+31 (2 column tiles), all 64 rows
+  // wave w: channels 32w..32w+31 (2 column tiles), all 64 rows; the tiles are
+  // computed transposed so that each lane stores 4 consecutive channels
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -409,15 +434,17 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
       for (int nn = 0; nn < 2; ++nn) {
         const int ch = 32 * w + 16 * nn + tl;
         const f16x8 kg = *reinterpret_cast<const f16x8*>(sKG + ch * TP + 32 * ks + 8 * gq);
-        acc[nn] = mfma_f16(th, kg, acc[nn]);
-        acc[nn] = mfma_f16(tlo, kg, acc[nn]);
+        acc[nn] = mfma_f16(kg, th, acc[nn]);   // transposed tile
+        acc[nn] = mfma_f16(kg, tlo, acc[nn]);
       }
     }
+    // lane: row 16m + tl, channels 32w + 16nn + 4gq + 0..3
 #pragma unroll
-    for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        gNW[frag_tc(16 * m + 4 * gq + ii, 32 * w + 16 * nn + tl)] = (_Float16)(-acc[nn][ii]);
+    for (int nn = 0; nn < 2; ++nn) {
+      const f16x4 w4 = {(_Float16)(-acc[nn][0]), (_Float16)(-acc[nn][1]), (_Float16)(-acc[nn][2]),
+                        (_Float16)(-acc[nn][3])};
+      *reinterpret_cast<f16x4*>(gNW + frag_tc(16 * m + tl, 32 * w + 16 * nn + 4 * gq)) = w4;
+    }
   }
   KDA_TIMER_MARK(8);
   KDA_TIMER_STORE(a.timers);
