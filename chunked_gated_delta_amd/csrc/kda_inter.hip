@@ -108,17 +108,39 @@ __device__ __forceinline__ void load_v(uint4 (&vv)[2], const uint16_t* v, int64_
   vv[1] = src[1];
 }
 
+// Token slot of V^T: token t of column c sits at t ^ vt_swz(c).  The XOR
+// moves whole 8-token (16-byte) groups, so a B-operand read of 8 consecutive
+// tokens stays one 16-byte read, while the packed 2-token writes below spread
+// over all banks instead of hitting 8 column groups in the same ones.
+__device__ __forceinline__ int vt_swz(int c) { return 8 * ((c >> 3) & 7); }
+
+// Write the V tile transposed (column-major, 2 tokens per dword).  Lanes of
+// neighbouring tokens t, t^1 (lanes 4 apart) trade half their columns, so
+// each lane writes 8 packed dwords: the even token's lane columns
+// 16cg + 0..7, the odd token's lane columns 16cg + 8..15.
 __device__ __forceinline__ void store_vt(__bf16* sVt, const uint4 (&vv)[2], int tid, int L) {
   const int t = tid >> 2;
   const int cg = tid & 3;
   const bool keep = t < L;
+  const bool odd = t & 1;
   const uint32_t wds[8] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w, vv[1].x, vv[1].y, vv[1].z, vv[1].w};
+  uint32_t mine[4], recv[4];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int col = 16 * cg + 2 * u;
-    const uint32_t wv = keep ? wds[u] : 0u;
-    sVt[col * TP + t] = __builtin_bit_cast(__bf16, (uint16_t)(wv & 0xffffu));
-    sVt[(col + 1) * TP + t] = __builtin_bit_cast(__bf16, (uint16_t)(wv >> 16));
+  for (int j = 0; j < 4; ++j) {
+    mine[j] = keep ? (odd ? wds[4 + j] : wds[j]) : 0u;
+    const uint32_t send = keep ? (odd ? wds[j] : wds[4 + j]) : 0u;
+    recv[j] = (uint32_t)__shfl_xor((int)send, 4);
+  }
+  const int tp = t & ~1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = 16 * cg + (odd ? 8 : 0) + 2 * j;
+    const uint32_t lo = odd ? recv[j] : mine[j];  // token tp
+    const uint32_t hi = odd ? mine[j] : recv[j];  // token tp + 1
+    const uint32_t d0 = (lo & 0xffffu) | (hi << 16);           // column c
+    const uint32_t d1 = (lo >> 16) | (hi & 0xffff0000u);       // column c + 1
+    *reinterpret_cast<uint32_t*>(sVt + c * TP + (tp ^ vt_swz(c))) = d0;
+    *reinterpret_cast<uint32_t*>(sVt + (c + 1) * TP + (tp ^ vt_swz(c + 1))) = d1;
   }
 }
 
@@ -226,7 +248,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     KDA_ISSUE(load_ops<0>(pre, prec, w, lane, gq, ksmax));
     KDA_TIMER_MARK(1);
 
-    // ---- U, D = U - W S, O = QG S (token rows 16w.., all 64 columns)
+    // ---- U, D = U - W S, O = QG S (token rows 16w.., all 64 columns); the
+    // two products share each read of the state copy
     f32x4 O[4];
 #pragma unroll
     for (int nn = 0; nn < 4; ++nn) {
@@ -237,7 +260,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
         // Uniform control flow: every loaded operand register is consumed on
         // every path, so no load is still outstanding when its register is
         // reloaded (waves 0 and 1 multiply by zero for their upper k-step).
-        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(sVt + col * TP + 32 * ks + 8 * gq);
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(sVt + col * TP + ((32 * ks + 8 * gq) ^ vt_swz(col)));
         u = mfma_bf16(ks < ksmax ? cur.tbh[ks] : bf16x8{}, vb, u);
         u = mfma_bf16(ks < ksmax ? cur.tbl[ks] : bf16x8{}, vb, u);
       }

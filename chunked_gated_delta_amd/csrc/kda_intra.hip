@@ -76,7 +76,13 @@ __device__ __forceinline__ float row_scan16(float x) {
   return x;
 }
 
-__global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
+// The chunk table, A_log and the record base are also passed as separate
+// __restrict__ arguments: with no possible aliasing by the record stores, the
+// wave-uniform loads from them can go through the scalar unit and never wait
+// behind the vector memory queue.
+__global__ void __launch_bounds__(NTHREADS, 2)
+    kda_intra_kernel(IntraArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ choff,
+                     const float* __restrict__ A_log, char* __restrict__ recs) {
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   __bf16* sKRFh = reinterpret_cast<__bf16*>(smem + OFF_KRF_HI);
   __bf16* sKRFl = reinterpret_cast<__bf16*>(smem + OFF_KRF_LO);
@@ -91,15 +97,73 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
   float* sB = reinterpret_cast<float*>(smem + OFF_B);
 
   const int H = a.H;
-  const int h = (int)(blockIdx.x % (unsigned)H);
-  const int64_t g = blockIdx.x / (unsigned)H;
-  if (g >= total_chunks(a.map)) return;
-  const int n = chunk_owner(a.map, g);
-  int64_t bos, eos;
-  seq_bounds(a.map, n, bos, eos);
-  const int64_t c0 = bos + (g - first_chunk(a.map, n)) * CH;
-  const int L = (int)((eos - c0) < CH ? (eos - c0) : CH);
-  char* rec = a.rec + ((size_t)g * H + h) * REC_BYTES;
+
+  // Work items are (chunk, head) pairs, item = chunk * H + head, taken in
+  // grid-stride order.  The next item's inputs are loaded while the current
+  // one is in its MFMA phases, so their latency is hidden.
+  // (the host checks that chunks x heads fits in an int)
+  ChunkMap map = a.map;
+  map.cu = cu;
+  map.choff = choff;
+  const int items = (int)(total_chunks(map) * H);
+  int item = blockIdx.x;
+  if (item >= items) return;
+
+  // inputs of one item for this lane's token: channels 32kb + 8gq + e.  All
+  // loads are unconditional: rows past the chunk end read the last valid row
+  // and are zeroed through their norms, gate and beta, so no load waits
+  // behind a branch.
+  uint4 pq[4], pk[4], pg[4];
+  uint16_t braw16;
+  float dtb, alog;
+  auto locate = [&](int it, int& hh, int64_t& gg, int64_t& cc0, int& LL) {
+    it = __builtin_amdgcn_readfirstlane(it);  // wave-uniform: scalar math and loads
+    hh = it % H;
+    gg = it / H;
+    const int nn = chunk_owner(map, gg);
+    int64_t bos, eos;
+    seq_bounds(map, nn, bos, eos);
+    cc0 = bos + (gg - first_chunk(map, nn)) * CH;
+    LL = (int)((eos - cc0) < CH ? (eos - cc0) : CH);
+  };
+  auto issue = [&](int hh, int64_t cc0, int LL) {
+    // lane offsets from an opaque thread id: nothing lane-derived stays live
+    // across the item loop
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    const int tok = 16 * (t >> 6) + (t & 15);
+    const int grp = (t >> 4) & 3;
+    const int64_t trow = (cc0 + (tok < LL ? tok : LL - 1)) * H + hh;
+    braw16 = a.beta[trow];
+    alog = A_log[hh];
+    dtb = a.dt_bias[hh * KD + (t & (KD - 1))];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int64_t off = trow * KD + 32 * kb + 8 * grp;
+      pq[kb] = *reinterpret_cast<const uint4*>(a.q + off);
+      pk[kb] = *reinterpret_cast<const uint4*>(a.k + off);
+      pg[kb] = *reinterpret_cast<const uint4*>(a.g + off);
+    }
+  };
+  int h, L;
+  int64_t g, c0;
+  locate(item, h, g, c0, L);
+  issue(h, c0, L);
+  KDA_TIMER_DECL
+
+  for (;;) {
+  // Lane-derived indices are re-derived from an opaque copy of the thread id
+  // every item, so the compiler recomputes the (cheap) per-lane addresses in
+  // the body instead of hoisting dozens of them out of the loop into spills.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int tl = lane & 15;
+  const int gq = lane >> 4;
+  const int ti = 16 * w + tl;  // this lane's token within the chunk
+  KDA_TIMER_MARK(0);
+  char* rec = recs + ((size_t)g * H + h) * REC_BYTES;
   _Float16* gNW = reinterpret_cast<_Float16*>(rec + REC_NW);
   _Float16* gQG = reinterpret_cast<_Float16*>(rec + REC_QG);
   _Float16* gKTH = reinterpret_cast<_Float16*>(rec + REC_KTH);
@@ -108,35 +172,10 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
   __bf16* gTBH = reinterpret_cast<__bf16*>(rec + REC_TBH);
   __bf16* gTBL = reinterpret_cast<__bf16*>(rec + REC_TBL);
   float* gGL = reinterpret_cast<float*>(rec + REC_GL);
-
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int lane = tid & 63;
-  const int tl = lane & 15;
-  const int gq = lane >> 4;
-  KDA_TIMER_DECL
-  KDA_TIMER_MARK(0);
+  const bool valid = ti < L;
 
   // gate: sigmoid(x) = 1 / (1 + 2^(raw * na + nb_c)), na = -exp(A_log) log2(e)
-  const float na = -__expf(a.A_log[h]) * LOG2E;
-  // dt_bias first, then every input load of the chunk, all unconditional: rows
-  // past the chunk end read the last valid row and are zeroed through their
-  // norms, gate and beta below, so no load waits behind a branch.
-  const float dtb = a.dt_bias[h * KD + (tid & (KD - 1))];
-
-  // ---- inputs of this lane's token: channels 32kb + 8gq + e
-  const int ti = 16 * w + tl;
-  const bool valid = ti < L;
-  const int64_t trow = (c0 + (valid ? ti : L - 1)) * H + h;
-  uint4 pq[4], pk[4], pg[4];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const int64_t off = trow * KD + 32 * kb + 8 * gq;
-    pq[kb] = *reinterpret_cast<const uint4*>(a.q + off);
-    pk[kb] = *reinterpret_cast<const uint4*>(a.k + off);
-    pg[kb] = *reinterpret_cast<const uint4*>(a.g + off);
-  }
-  const uint16_t braw16 = a.beta[trow];
+  const float na = -__expf(alog) * LOG2E;
   if (tid < KD) sNB[tid] = na * dtb;
   __syncthreads();  // sNB
   KDA_TIMER_MARK(1);
@@ -356,6 +395,18 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
       for (int i = 0; i < 16; ++i) sA[(16 * w + i) * AP + 16 * w + cc] = x[i];
     }
   }
+  // The A operands of this item are dead: start the next item's loads (the
+  // last item re-reads its own, so every path has the same loads in flight).
+  const int next = item + (int)gridDim.x;
+  const bool more = next < items;
+  int h2, L2;
+  int64_t g2, c02;
+  if (more)
+    locate(next, h2, g2, c02, L2);
+  else {
+    h2 = h; g2 = g; c02 = c0; L2 = L;
+  }
+  issue(h2, c02, L2);
   __syncthreads();
   KDA_TIMER_MARK(5);
 
@@ -447,16 +498,31 @@ __global__ void __launch_bounds__(NTHREADS, 2) kda_intra_kernel(IntraArgs a) {
     }
   }
   KDA_TIMER_MARK(8);
+  if (!more) break;
+  item = next;
+  h = h2; g = g2; c0 = c02; L = L2;
+  __syncthreads();  // LDS of this item is read above until the W phase
+  }
   KDA_TIMER_STORE(a.timers);
 }
 
 }  // namespace
 
 hipError_t launch_intra(const IntraArgs& args, int64_t max_chunks, hipStream_t st) {
-  const int64_t grid = max_chunks * args.H;
+  // persistent grid: two resident workgroups per CU (LDS and register budget)
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t items = max_chunks * args.H;
+  const int64_t grid = items < 2 * (int64_t)cus ? items : 2 * (int64_t)cus;
   if (grid <= 0) return hipSuccess;
   IntraArgs a = args;
-  void* kargs[] = {(void*)&a};
+  const int32_t* cu = a.map.cu;
+  const int32_t* choff = a.map.choff;
+  const float* alog = a.A_log;
+  char* recs = a.rec;
+  void* kargs[] = {(void*)&a, (void*)&cu, (void*)&choff, (void*)&alog, (void*)&recs};
   return hipLaunchKernel(reinterpret_cast<const void*>(&kda_intra_kernel), dim3((unsigned)grid),
                          dim3(NTHREADS), kargs, 0, st);
 }
