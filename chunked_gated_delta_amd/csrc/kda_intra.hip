@@ -30,7 +30,8 @@
 // an fp64 reference for identical (collinear) keys, where the chunk sums
 // telescope and 16-bit rounding of A, T or W alone would exceed it.
 //
-// One workgroup (4 waves) per (chunk, head); wave w owns sub-chunk w.
+// Persistent workgroups (4 waves) loop over (chunk, head) items; in each item
+// every wave owns one 16-token sub-chunk, in a role that rotates per item.
 
 #include "kda_common.h"
 
@@ -98,14 +99,15 @@ __global__ void __launch_bounds__(NTHREADS, 2)
 
   const int H = a.H;
 
-  // Work items are (chunk, head) pairs, item = chunk * H + head, taken in
-  // grid-stride order.  The next item's inputs are loaded while the current
-  // one is in its MFMA phases, so their latency is hidden.
-  // (the host checks that chunks x heads fits in an int)
+  // Work items are (chunk, head) pairs, item = (last chunk - chunk) * H + head,
+  // taken in grid-stride order.  The next item's inputs are loaded while the
+  // current one is in its MFMA phases, so their latency is hidden.  (The host
+  // checks that chunks x heads fits in an int.)
   ChunkMap map = a.map;
   map.cu = cu;
   map.choff = choff;
-  const int items = (int)(total_chunks(map) * H);
+  const int64_t nchunk = total_chunks(map);
+  const int items = (int)(nchunk * H);
   int item = blockIdx.x;
   if (item >= items) return;
 
@@ -118,37 +120,60 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   float dtb, alog;
   auto locate = [&](int it, int& hh, int64_t& gg, int64_t& cc0, int& LL) {
     it = __builtin_amdgcn_readfirstlane(it);  // wave-uniform: scalar math and loads
+    // chunks are produced last to first: the consumer starts at chunk 0, whose
+    // records are then the most recently written (likeliest still in cache)
     hh = it % H;
-    gg = it / H;
-    const int nn = chunk_owner(map, gg);
+    gg = nchunk - 1 - it / H;
+    int nn;
+    if (map.cu) {
+      nn = chunk_owner(map, gg);
+    } else {
+      // 32-bit division by an opaque divisor: recomputed per item rather
+      // than a reciprocal hoisted out of the item loop
+      int nch = (int)((map.T + CH - 1) / CH);
+      asm volatile("" : "+s"(nch));
+      nn = (int)gg / nch;
+    }
     int64_t bos, eos;
     seq_bounds(map, nn, bos, eos);
     cc0 = bos + (gg - first_chunk(map, nn)) * CH;
     LL = (int)((eos - cc0) < CH ? (eos - cc0) : CH);
   };
-  auto issue = [&](int hh, int64_t cc0, int LL) {
-    // lane offsets from an opaque thread id: nothing lane-derived stays live
-    // across the item loop
+  // Loads of one item in two parts (P = 0: q and k; P = 1: raw gate, beta,
+  // dt_bias, A_log), so that the next item's prefetch is spread over two
+  // phases.  Lane offsets come from an opaque thread id: nothing lane-derived
+  // stays live across the item loop.  A_log is read with an index the
+  // compiler cannot prove uniform, so it is a vector load (a scalar load would
+  // share its wait counter with every LDS access in between).
+  auto issue = [&](int part, int it, int hh, int64_t cc0, int LL) {
     int t = threadIdx.x;
     asm volatile("" : "+v"(t));
-    const int tok = 16 * (t >> 6) + (t & 15);
+    const int tok = 16 * (((t >> 6) + it) & 3) + (t & 15);  // sub-chunk role of item `it`
     const int grp = (t >> 4) & 3;
     const int64_t trow = (cc0 + (tok < LL ? tok : LL - 1)) * H + hh;
-    braw16 = a.beta[trow];
-    alog = A_log[hh];
-    dtb = a.dt_bias[hh * KD + (t & (KD - 1))];
+    if (part == 0) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int64_t off = trow * KD + 32 * kb + 8 * grp;
-      pq[kb] = *reinterpret_cast<const uint4*>(a.q + off);
-      pk[kb] = *reinterpret_cast<const uint4*>(a.k + off);
-      pg[kb] = *reinterpret_cast<const uint4*>(a.g + off);
+      for (int kb = 0; kb < 4; ++kb) {
+        const int64_t off = trow * KD + 32 * kb + 8 * grp;
+        pq[kb] = *reinterpret_cast<const uint4*>(a.q + off);
+        pk[kb] = *reinterpret_cast<const uint4*>(a.k + off);
+      }
+    } else {
+      braw16 = a.beta[trow];
+      alog = A_log[hh + (t >> 31)];
+      dtb = a.dt_bias[hh * KD + (t & (KD - 1))];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int64_t off = trow * KD + 32 * kb + 8 * grp;
+        pg[kb] = *reinterpret_cast<const uint4*>(a.g + off);
+      }
     }
   };
   int h, L;
   int64_t g, c0;
   locate(item, h, g, c0, L);
-  issue(h, c0, L);
+  issue(1, item, h, c0, L);
+  issue(0, item, h, c0, L);
   KDA_TIMER_DECL
 
   for (;;) {
@@ -157,7 +182,11 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   // the body instead of hoisting dozens of them out of the loop into spills.
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
-  const int w = tid >> 6;
+  // Sub-chunk role of this wave for this item.  The roles rotate from item
+  // to item: the A blocks of sub-chunk w cost w + 1 block products and the
+  // off-diagonal T blocks 3 - w, so a fixed role would load the SIMDs
+  // unevenly.
+  const int w = ((tid >> 6) + item) & 3;
   const int lane = tid & 63;
   const int tl = lane & 15;
   const int gq = lane >> 4;
@@ -173,6 +202,16 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   __bf16* gTBL = reinterpret_cast<__bf16*>(rec + REC_TBL);
   float* gGL = reinterpret_cast<float*>(rec + REC_GL);
   const bool valid = ti < L;
+  // the next item's place (scalar table lookups, overlapped with this item)
+  const int next = item + (int)gridDim.x;
+  const bool more = next < items;
+  int h2, L2;
+  int64_t g2, c02;
+  if (more)
+    locate(next, h2, g2, c02, L2);
+  else {
+    h2 = h; g2 = g; c02 = c0; L2 = L;
+  }
 
   // gate: sigmoid(x) = 1 / (1 + 2^(raw * na + nb_c)), na = -exp(A_log) log2(e)
   const float na = -__expf(alog) * LOG2E;
@@ -195,10 +234,14 @@ __global__ void __launch_bounds__(NTHREADS, 2)
       ssk += kf[e] * kf[e];
     }
   }
-  ssq += __shfl_xor(ssq, 16);
-  ssq += __shfl_xor(ssq, 32);
-  ssk += __shfl_xor(ssk, 16);
-  ssk += __shfl_xor(ssk, 32);
+  // sums over the 4 lanes (gq) that share the token: lane ^ 16, lane ^ 32
+  auto xor_lane = [&](float v, int m) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __float_as_int(v)));
+  };
+  ssq += xor_lane(ssq, 16);
+  ssq += xor_lane(ssq, 32);
+  ssk += xor_lane(ssk, 16);
+  ssk += xor_lane(ssk, 32);
   const float rq = valid ? __builtin_amdgcn_rsqf(ssq + L2_EPS) : 0.0f;
   const float rk = valid ? __builtin_amdgcn_rsqf(ssk + L2_EPS) : 0.0f;
   const float braw = __uint_as_float((uint32_t)braw16 << 16);
@@ -322,6 +365,7 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   // wave w owns row-block w; lane holds C[16w + 4gq + ii][16b + tl]
   {
     const int i0 = 16 * w + 4 * gq;
+#pragma unroll 1
     for (int b = 0; b <= w; ++b) {
       f32x4 akk = {0.f, 0.f, 0.f, 0.f};
       f32x4 aqk = {0.f, 0.f, 0.f, 0.f};
@@ -373,7 +417,9 @@ __global__ void __launch_bounds__(NTHREADS, 2)
       for (int ii = 0; ii < 4; ++ii) q4[ii] = (_Float16)((16 * b + 4 * gq + ii <= ti) ? aqk[ii] : 0.0f);
       *reinterpret_cast<f16x4*>(gAQK + frag_tt(ti, 16 * b + 4 * gq)) = q4;
     }
-    for (int b = w + 1; b < 4; ++b) {
+    // zero blocks above the diagonal; rows 0..31 skip tokens 32..63, a whole
+    // record fragment that the reader never loads
+    for (int b = w + 1; b < (w < 2 ? 2 : 4); ++b) {
       const f16x4 z4 = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
       *reinterpret_cast<f16x4*>(gAQK + frag_tt(ti, 16 * b + 4 * gq)) = z4;
     }
@@ -397,16 +443,7 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   }
   // The A operands of this item are dead: start the next item's loads (the
   // last item re-reads its own, so every path has the same loads in flight).
-  const int next = item + (int)gridDim.x;
-  const bool more = next < items;
-  int h2, L2;
-  int64_t g2, c02;
-  if (more)
-    locate(next, h2, g2, c02, L2);
-  else {
-    h2 = h; g2 = g; c02 = c0; L2 = L;
-  }
-  issue(h2, c02, L2);
+  issue(0, more ? next : item, h2, c02, L2);
   __syncthreads();
   KDA_TIMER_MARK(5);
 
@@ -441,10 +478,12 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   }
 
   KDA_TIMER_MARK(6);
+  issue(1, more ? next : item, h2, c02, L2);
   // ======= T diag(b): fp16 hi/lo into LDS (for W), bf16 hi/lo to the record
   for (int it = tid; it < CH * 8; it += NTHREADS) {
     const int i = it >> 3;
     const int j0 = (it & 7) * 8;
+    if (i < 32 && j0 >= 32) continue;  // all-zero fragment, read by no one
     float t8[8], b8[8];
     lds_f32x8(sA + i * AP + j0, t8);
     lds_f32x8(sB + j0, b8);
@@ -502,6 +541,7 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   item = next;
   h = h2; g = g2; c0 = c02; L = L2;
   __syncthreads();  // LDS of this item is read above until the W phase
+  KDA_TIMER_MARK(9);
   }
   KDA_TIMER_STORE(a.timers);
 }
