@@ -2,7 +2,8 @@
 
 Argument marshalling only: every step of the forward pass runs in the HIP
 kernels behind the C ABI of include/kda.h.  The names mirror that header:
-``kda_fwd``, ``kda_workspace_size``, ``kda_is_supported``.  PyTorch provides
+``kda_fwd``, ``kda_workspace_size``, ``kda_is_supported``, ``kda_shard_affine``,
+``kda_shard_scan``.  PyTorch provides
 device memory and the current stream; there is no CPU or PyTorch fallback, and
 importing this module fails if the library has not been built.
 """
@@ -18,23 +19,24 @@ import os
 # in the process, and whichever initialises second sees no device.
 import torch  # noqa: F401
 
-__all__ = ["kda_fwd", "kda_workspace_size", "kda_is_supported", "KdaError", "STATUS",
-           "library_path", "exported_symbols"]
+__all__ = ["kda_fwd", "kda_workspace_size", "kda_is_supported", "kda_shard_affine",
+           "kda_shard_scan", "KdaError", "STATUS", "library_path", "exported_symbols"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkda.so")
 
 STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERR_INVALID", 2: "KDA_ERR_UNSUPPORTED",
           3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_LAUNCH"}
-exported_symbols = ("kda_fwd", "kda_workspace_size", "kda_is_supported", "kda_status_string")
+exported_symbols = ("kda_fwd", "kda_workspace_size", "kda_is_supported", "kda_status_string",
+                    "kda_shard_affine", "kda_shard_scan")
 
 
 class KdaError(RuntimeError):
     """A non-zero kda_status_t returned by the library."""
 
-    def __init__(self, status: int):
+    def __init__(self, status: int, what: str = "kda_fwd"):
         self.status = status
-        super().__init__(f"kda_fwd failed: {STATUS.get(status, status)}")
+        super().__init__(f"{what} failed: {STATUS.get(status, status)}")
 
 
 if not os.path.exists(library_path):
@@ -53,6 +55,11 @@ _lib.kda_status_string.restype = ctypes.c_char_p
 _lib.kda_fwd.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P, _P,
                          ctypes.c_float, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]
 _lib.kda_fwd.restype = ctypes.c_int
+_lib.kda_shard_affine.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, ctypes.c_float,
+                                  _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]
+_lib.kda_shard_affine.restype = ctypes.c_int
+_lib.kda_shard_scan.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
+_lib.kda_shard_scan.restype = ctypes.c_int
 
 
 def kda_workspace_size(T: int, H: int, N: int) -> int:
@@ -68,6 +75,41 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _check_inputs(q, k, v, raw_gate, raw_beta, out, A_log, dt_bias, cu_seqlens):
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("raw_gate", raw_gate), ("raw_beta", raw_beta),
+                    ("out", out)):
+        if t is not None and (t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda):
+            raise ValueError(f"{name} must be a contiguous bf16 device tensor")
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous fp32 device tensor")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
+        raise ValueError("cu_seqlens must be an int32 device tensor")
+    if tuple(k.shape) != (B, T, H, K) or tuple(raw_gate.shape) != (B, T, H, K) or \
+            tuple(v.shape) != (B, T, H, V) or (out is not None and tuple(out.shape) != (B, T, H, V)) or \
+            tuple(raw_beta.shape) != (B, T, H):
+        raise ValueError("inconsistent q/k/v/raw_gate/raw_beta/out shapes")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    return B, T, H, K, V, N
+
+
+def _check_f32(name, t, shape):
+    if t is None:
+        return
+    if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous fp32 device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}")
+
+
+def _stream(stream, dev):
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    return ctypes.c_void_p(int(stream))
+
+
 def kda_fwd(q, k, v, raw_gate, raw_beta, scale, out, workspace, A_log, dt_bias, lower_bound,
             initial_state=None, final_state=None, cu_seqlens=None, stream=None):
     """Enqueue one KDA forward on ``stream`` (default: torch's current stream).
@@ -78,35 +120,48 @@ def kda_fwd(q, k, v, raw_gate, raw_beta, scale, out, workspace, A_log, dt_bias, 
     dt_bias fp32 [H,K]; initial_state / final_state fp32 [N,H,K,V] or None;
     cu_seqlens int32 [N+1] or None.  Raises KdaError on a non-zero status.
     """
-    B, T, H, K = q.shape
-    V = v.shape[-1]
-    for name, t in (("q", q), ("k", k), ("v", v), ("raw_gate", raw_gate), ("raw_beta", raw_beta),
-                    ("out", out)):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous bf16 device tensor")
-    for name, t in (("A_log", A_log), ("dt_bias", dt_bias), ("initial_state", initial_state),
-                    ("final_state", final_state)):
-        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda):
-            raise ValueError(f"{name} must be a contiguous fp32 device tensor")
-    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
-        raise ValueError("cu_seqlens must be an int32 device tensor")
-    if tuple(k.shape) != (B, T, H, K) or tuple(raw_gate.shape) != (B, T, H, K) or \
-            tuple(v.shape) != (B, T, H, V) or tuple(out.shape) != (B, T, H, V) or \
-            tuple(raw_beta.shape) != (B, T, H):
-        raise ValueError("inconsistent q/k/v/raw_gate/raw_beta/out shapes")
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
-    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
-        if t is not None and tuple(t.shape) != (N, H, K, V):
-            raise ValueError(f"{name} must have shape [N, H, K, V] = {(N, H, K, V)}")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+    if out is None:
+        raise ValueError("out is required")
+    B, T, H, K, V, N = _check_inputs(q, k, v, raw_gate, raw_beta, out, A_log, dt_bias, cu_seqlens)
+    _check_f32("initial_state", initial_state, (N, H, K, V))
+    _check_f32("final_state", final_state, (N, H, K, V))
     rc = _lib.kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(raw_beta), float(scale),
                       _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                       _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
-                      _ptr(final_state), _ptr(cu_seqlens), B, T, H, K, V, N,
-                      ctypes.c_void_p(int(stream)))
+                      _ptr(final_state), _ptr(cu_seqlens), B, T, H, K, V, N, _stream(stream, q.device))
     if rc != 0:
         raise KdaError(rc)
+
+
+def kda_shard_affine(q, k, v, raw_gate, raw_beta, workspace, A_log, dt_bias, lower_bound, P, R,
+                     cu_seqlens=None, stream=None):
+    """Enqueue the per-shard affine maps: every sequence n of the call (a shard)
+    takes an entering state S to P[n] S + R[n].  P fp32 [N,H,K,K], R fp32 [N,H,K,V]."""
+    B, T, H, K, V, N = _check_inputs(q, k, v, raw_gate, raw_beta, None, A_log, dt_bias, cu_seqlens)
+    _check_f32("P", P, (N, H, K, K))
+    _check_f32("R", R, (N, H, K, V))
+    rc = _lib.kda_shard_affine(_ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(raw_beta), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _ptr(A_log), _ptr(dt_bias),
+                               float(lower_bound), _ptr(P), _ptr(R), _ptr(cu_seqlens), B, T, H, K, V, N,
+                               _stream(stream, q.device))
+    if rc != 0:
+        raise KdaError(rc, "kda_shard_affine")
+
+
+def kda_shard_scan(P, R, starts, initial_state=None, final_state=None, stream=None):
+    """Enqueue the fold over consecutive shards: starts[0] = initial_state (or 0),
+    starts[r+1] = P[r] starts[r] + R[r]; final_state gets the state after the last shard."""
+    n, H, K, _ = P.shape
+    V = R.shape[-1]
+    _check_f32("P", P, (n, H, K, K))
+    _check_f32("R", R, (n, H, K, V))
+    _check_f32("starts", starts, (n, H, K, V))
+    _check_f32("initial_state", initial_state, (H, K, V))
+    _check_f32("final_state", final_state, (H, K, V))
+    rc = _lib.kda_shard_scan(_ptr(P), _ptr(R), _ptr(initial_state), _ptr(starts), _ptr(final_state),
+                             n, H, K, V, _stream(stream, P.device))
+    if rc != 0:
+        raise KdaError(rc, "kda_shard_scan")
 
 
 def raw_call(*args):

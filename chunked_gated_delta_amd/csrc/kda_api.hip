@@ -113,29 +113,43 @@ const char* kda_status_string(kda_status_t s) {
   return "KDA_ERR_UNKNOWN";
 }
 
-kda_status_t kda_fwd(const void* q, const void* k, const void* v, const void* raw_gate,
-                     const void* raw_beta, float scale, void* out, void* workspace,
-                     size_t workspace_bytes, const float* A_log, const float* dt_bias,
-                     float lower_bound, const float* initial_state, float* final_state,
-                     const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t K,
-                     int64_t V, int64_t N, void* stream) {
-  if (!q || !k || !v || !raw_gate || !raw_beta || !out || !A_log || !dt_bias) return KDA_ERR_INVALID;
+}  // extern "C"
+
+namespace kda {
+namespace {
+
+// What the intra-chunk pass of one call leaves for the inter-chunk passes.
+struct Prepared {
+  ChunkMap map;
+  int32_t* order;
+  char* rec;
+  char* ws;
+  Layout lay;
+  int64_t max_chunks;
+};
+
+// Argument checks shared by every entry point that runs the chunked forward,
+// then the varlen bookkeeping and the intra-chunk kernel on `st`.
+kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const void* raw_beta,
+                     void* workspace, size_t workspace_bytes, const float* A_log,
+                     const float* dt_bias, float lower_bound, const int32_t* cu_seqlens, int64_t B,
+                     int64_t T, int64_t H, int64_t K, int64_t V, int64_t N, hipStream_t st,
+                     Prepared& pr) {
+  if (!q || !k || !raw_gate || !raw_beta || !A_log || !dt_bias) return KDA_ERR_INVALID;
   if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID;
   if (cu_seqlens ? (B != 1) : (N != B)) return KDA_ERR_INVALID;
-  if (!(scale == scale)) return KDA_ERR_INVALID;
   if (!kda_is_supported(K, V, lower_bound)) return KDA_ERR_UNSUPPORTED;
   if (B * T * H > ((int64_t)1 << 40) || N * H > ((int64_t)1 << 28) || N > ((int64_t)1 << 30))
     return KDA_ERR_INVALID;
   const int64_t T_total = B * T;
-  const Layout lay = workspace_layout(T_total, H, N);
-  if (!workspace || workspace_bytes < lay.total) return KDA_ERR_WORKSPACE;
-  const int64_t max_chunks = cu_seqlens ? T_total / CH + N : B * ((T + CH - 1) / CH);
-  if (max_chunks * H > ((int64_t)1 << 31) - 1) return KDA_ERR_INVALID;
+  pr.lay = workspace_layout(T_total, H, N);
+  if (!workspace || workspace_bytes < pr.lay.total) return KDA_ERR_WORKSPACE;
+  pr.max_chunks = cu_seqlens ? T_total / CH + N : B * ((T + CH - 1) / CH);
+  if (pr.max_chunks * H > ((int64_t)1 << 31) - 1) return KDA_ERR_INVALID;
 
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  int32_t* choff = reinterpret_cast<int32_t*>(ws + lay.choff);
-  int32_t* order = nullptr;
+  pr.ws = static_cast<char*>(workspace);
+  int32_t* choff = reinterpret_cast<int32_t*>(pr.ws + pr.lay.choff);
+  pr.order = nullptr;
   int n32 = (int)N;
   if (cu_seqlens) {
     void* cargs[] = {(void*)&cu_seqlens, (void*)&n32, (void*)&choff};
@@ -144,19 +158,19 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const void* ra
                       "chunk offsets") != KDA_SUCCESS)
       return KDA_ERR_LAUNCH;
     if (N > 1 && N <= kMaxSortN) {
-      order = reinterpret_cast<int32_t*>(ws + lay.order);
-      void* oargs[] = {(void*)&cu_seqlens, (void*)&n32, (void*)&order};
+      pr.order = reinterpret_cast<int32_t*>(pr.ws + pr.lay.order);
+      void* oargs[] = {(void*)&cu_seqlens, (void*)&n32, (void*)&pr.order};
       if (launch_status(hipLaunchKernel(reinterpret_cast<const void*>(&kda_order_kernel),
                                         dim3((unsigned)((N + 255) / 256)), dim3(256), oargs, 0, st),
                         "order") != KDA_SUCCESS)
         return KDA_ERR_LAUNCH;
     }
   }
-  ChunkMap map;
-  map.cu = cu_seqlens;
-  map.choff = cu_seqlens ? choff : nullptr;
-  map.T = T;
-  map.N = (int)N;
+  pr.map.cu = cu_seqlens;
+  pr.map.choff = cu_seqlens ? choff : nullptr;
+  pr.map.T = T;
+  pr.map.N = (int)N;
+  pr.rec = pr.ws + pr.lay.rec;
 
   IntraArgs ia;
   ia.q = static_cast<const uint16_t*>(q);
@@ -165,33 +179,97 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const void* ra
   ia.beta = static_cast<const uint16_t*>(raw_beta);
   ia.A_log = A_log;
   ia.dt_bias = dt_bias;
-  ia.rec = ws + lay.rec;
-  ia.map = map;
+  ia.rec = pr.rec;
+  ia.map = pr.map;
   ia.H = (int)H;
   ia.lb2 = lower_bound * LOG2E;
   ia.timers = nullptr;
 #ifdef KDA_PHASE_TIMERS
   // timer builds only: the caller extends the workspace by 16 counters per
   // workgroup of each kernel, intra first
-  ia.timers = reinterpret_cast<unsigned long long*>(ws + lay.total);
+  ia.timers = reinterpret_cast<unsigned long long*>(pr.ws + pr.lay.total);
 #endif
-  if (launch_status(launch_intra(ia, max_chunks, st), "intra") != KDA_SUCCESS) return KDA_ERR_LAUNCH;
+  return launch_status(launch_intra(ia, pr.max_chunks, st), "intra");
+}
 
+InterArgs inter_args(const Prepared& pr, int64_t H) {
   InterArgs xa;
+  xa.v = nullptr;
+  xa.out = nullptr;
+  xa.init = nullptr;
+  xa.fin = nullptr;
+  xa.init_identity = 0;
+  xa.rec = pr.rec;
+  xa.order = pr.order;
+  xa.map = pr.map;
+  xa.H = (int)H;
+  xa.scale = 1.0f;
+  xa.timers = nullptr;
+#ifdef KDA_PHASE_TIMERS
+  xa.timers = reinterpret_cast<unsigned long long*>(pr.ws + pr.lay.total) + (size_t)pr.max_chunks * H * 16;
+#endif
+  return xa;
+}
+
+}  // namespace
+}  // namespace kda
+
+extern "C" {
+
+kda_status_t kda_fwd(const void* q, const void* k, const void* v, const void* raw_gate,
+                     const void* raw_beta, float scale, void* out, void* workspace,
+                     size_t workspace_bytes, const float* A_log, const float* dt_bias,
+                     float lower_bound, const float* initial_state, float* final_state,
+                     const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t K,
+                     int64_t V, int64_t N, void* stream) {
+  if (!v || !out) return KDA_ERR_INVALID;
+  if (!(scale == scale)) return KDA_ERR_INVALID;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Prepared pr;
+  const kda_status_t s = prepare(q, k, raw_gate, raw_beta, workspace, workspace_bytes, A_log, dt_bias,
+                                 lower_bound, cu_seqlens, B, T, H, K, V, N, st, pr);
+  if (s != KDA_SUCCESS) return s;
+  InterArgs xa = inter_args(pr, H);
   xa.v = static_cast<const uint16_t*>(v);
   xa.out = static_cast<uint16_t*>(out);
   xa.init = initial_state;
   xa.fin = final_state;
-  xa.rec = ws + lay.rec;
-  xa.order = order;
-  xa.map = map;
-  xa.H = (int)H;
   xa.scale = scale;
-  xa.timers = nullptr;
-#ifdef KDA_PHASE_TIMERS
-  xa.timers = reinterpret_cast<unsigned long long*>(ws + lay.total) + (size_t)max_chunks * H * 16;
-#endif
   return launch_status(launch_inter(xa, st), "inter");
+}
+
+kda_status_t kda_shard_affine(const void* q, const void* k, const void* v, const void* raw_gate,
+                              const void* raw_beta, void* workspace, size_t workspace_bytes,
+                              const float* A_log, const float* dt_bias, float lower_bound, float* P,
+                              float* R, const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H,
+                              int64_t K, int64_t V, int64_t N, void* stream) {
+  if (!v || !P || !R) return KDA_ERR_INVALID;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Prepared pr;
+  const kda_status_t s = prepare(q, k, raw_gate, raw_beta, workspace, workspace_bytes, A_log, dt_bias,
+                                 lower_bound, cu_seqlens, B, T, H, K, V, N, st, pr);
+  if (s != KDA_SUCCESS) return s;
+  // R: the shard's own contribution, its final state from a zero start
+  InterArgs xr = inter_args(pr, H);
+  xr.v = static_cast<const uint16_t*>(v);
+  xr.fin = R;
+  if (launch_status(launch_inter(xr, st), "inter (R)") != KDA_SUCCESS) return KDA_ERR_LAUNCH;
+  // P: the homogeneous map, the final state of V = 0 from S0 = I (K == V)
+  InterArgs xp = inter_args(pr, H);
+  xp.fin = P;
+  xp.init_identity = 1;
+  return launch_status(launch_inter(xp, st), "inter (P)");
+}
+
+kda_status_t kda_shard_scan(const float* P, const float* R, const float* initial_state, float* starts,
+                            float* final_state, int64_t n_shards, int64_t H, int64_t K, int64_t V,
+                            void* stream) {
+  if (!P || !R || !starts) return KDA_ERR_INVALID;
+  if (n_shards < 1 || H < 1 || n_shards * H > ((int64_t)1 << 28)) return KDA_ERR_INVALID;
+  if (K != KD || V != VD) return KDA_ERR_UNSUPPORTED;
+  return launch_status(launch_shard_scan(P, R, initial_state, starts, final_state, (int)n_shards, (int)H,
+                                         reinterpret_cast<hipStream_t>(stream)),
+                       "shard scan");
 }
 
 }  // extern "C"

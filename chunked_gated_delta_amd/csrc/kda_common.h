@@ -155,10 +155,11 @@ struct IntraArgs {
   unsigned long long* timers;  // phase timers (KDA_PHASE_TIMERS builds only), else nullptr
 };
 struct InterArgs {
-  const uint16_t* v;
-  uint16_t* out;
-  const float* init;
+  const uint16_t* v;     // nullptr: V = 0 (homogeneous recurrence)
+  uint16_t* out;         // nullptr: no outputs, final state only
+  const float* init;     // nullptr: zero state, or the identity if init_identity
   float* fin;
+  int init_identity;     // with init == nullptr: start every (sequence, head) from I (needs K == V)
   const char* rec;
   const int32_t* order;  // nullptr: identity order of sequences
   ChunkMap map;
@@ -168,5 +169,7 @@ struct InterArgs {
 };
 hipError_t launch_intra(const IntraArgs& a, int64_t max_chunks, hipStream_t st);
 hipError_t launch_inter(const InterArgs& a, hipStream_t st);
+hipError_t launch_shard_scan(const float* P, const float* R, const float* init, float* starts, float* fin,
+                             int n_shards, int H, hipStream_t st);
 
 }  // namespace kda

@@ -46,16 +46,18 @@ struct Ops {
 // at different points of the previous step so that the vector-memory path
 // drains them while that step's MFMAs run, instead of stalling one block of
 // issue.  Every load is one contiguous 1 KB fragment (64 lanes x 16 bytes).
-template <int P>
+template <int P, bool HAS_V = true, bool WRITE_OUT = true>
 __device__ __forceinline__ void load_ops(Ops& o, const char* rec, int w, int lane, int gq, int ksmax) {
   if constexpr (P == 0) {
     const f16x8* nw = reinterpret_cast<const f16x8*>(rec + REC_NW) + lane;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) o.nw[kb] = nw[(4 * w + kb) * 64];
   } else if constexpr (P == 1) {
-    const f16x8* qg = reinterpret_cast<const f16x8*>(rec + REC_QG) + lane;
+    if constexpr (WRITE_OUT) {
+      const f16x8* qg = reinterpret_cast<const f16x8*>(rec + REC_QG) + lane;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) o.qg[kb] = qg[(4 * w + kb) * 64];
+      for (int kb = 0; kb < 4; ++kb) o.qg[kb] = qg[(4 * w + kb) * 64];
+    }
   } else if constexpr (P == 2) {
     const f16x8* aq = reinterpret_cast<const f16x8*>(rec + REC_AQK) + lane;
     const bf16x8* th = reinterpret_cast<const bf16x8*>(rec + REC_TBH) + lane;
@@ -65,9 +67,11 @@ __device__ __forceinline__ void load_ops(Ops& o, const char* rec, int w, int lan
       // rows 16w.. of the lower-triangular A_qk and T only see tokens < 16w + 16:
       // waves 0 and 1 re-read their first k-step instead of the zero upper half
       const int kk = ks < ksmax ? ks : 0;
-      o.aqk[ks] = aq[(2 * w + kk) * 64];
-      o.tbh[ks] = th[(2 * w + kk) * 64];
-      o.tbl[ks] = tlw[(2 * w + kk) * 64];
+      if constexpr (WRITE_OUT) o.aqk[ks] = aq[(2 * w + kk) * 64];
+      if constexpr (HAS_V) {
+        o.tbh[ks] = th[(2 * w + kk) * 64];
+        o.tbl[ks] = tlw[(2 * w + kk) * 64];
+      }
     }
   } else if constexpr (P == 3) {
     const f16x8* kh = reinterpret_cast<const f16x8*>(rec + REC_KTH) + lane;
@@ -87,12 +91,13 @@ __device__ __forceinline__ void load_ops(Ops& o, const char* rec, int w, int lan
   }
 }
 
+template <bool HAS_V, bool WRITE_OUT>
 __device__ __forceinline__ void load_ops_all(Ops& o, const char* rec, int w, int lane, int gq, int ksmax) {
-  load_ops<0>(o, rec, w, lane, gq, ksmax);
-  load_ops<1>(o, rec, w, lane, gq, ksmax);
-  load_ops<2>(o, rec, w, lane, gq, ksmax);
-  load_ops<3>(o, rec, w, lane, gq, ksmax);
-  load_ops<4>(o, rec, w, lane, gq, ksmax);
+  load_ops<0, HAS_V, WRITE_OUT>(o, rec, w, lane, gq, ksmax);
+  load_ops<1, HAS_V, WRITE_OUT>(o, rec, w, lane, gq, ksmax);
+  load_ops<2, HAS_V, WRITE_OUT>(o, rec, w, lane, gq, ksmax);
+  load_ops<3, HAS_V, WRITE_OUT>(o, rec, w, lane, gq, ksmax);
+  load_ops<4, HAS_V, WRITE_OUT>(o, rec, w, lane, gq, ksmax);
 }
 
 // V tile of a chunk: thread -> (token tid/4, columns 16*(tid%4) .. +15).  Rows
@@ -144,6 +149,10 @@ __device__ __forceinline__ void store_vt(__bf16* sVt, const uint4 (&vv)[2], int 
   }
 }
 
+// HAS_V = false runs the recurrence with V = 0 (the homogeneous part of the
+// chunk map, used for the per-shard affine map); WRITE_OUT = false computes
+// only the final state.
+template <bool HAS_V, bool WRITE_OUT>
 __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   __bf16* sVt = reinterpret_cast<__bf16*>(smem + OFF_VT);
@@ -187,7 +196,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int c = 32 * w + 16 * mt + 4 * gq + ii;
-          S[mt][nn][ii] = src ? src[c * VD + vs + 16 * nn + tl] : 0.0f;
+          const int col = vs + 16 * nn + tl;
+          S[mt][nn][ii] = src ? src[c * VD + col] : ((a.init_identity && c == col) ? 1.0f : 0.0f);
         }
   }
   auto store_st = [&]() {
@@ -214,13 +224,13 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
   const bool odd = ((eos - bos + CH - 1) / CH) & 1;
   if (bos < eos) {
     uint4 v0[2];
-    load_v(v0, a.v, bos, chunk_len(bos), H, h, vs, tid);
+    if constexpr (HAS_V) load_v(v0, a.v, bos, chunk_len(bos), H, h, vs, tid);
     const char* r0 = a.rec + ((size_t)gfirst * H + h) * REC_BYTES;
     if (odd)
-      load_ops_all(opsA, r0, w, lane, gq, ksmax);
+      load_ops_all<HAS_V, WRITE_OUT>(opsA, r0, w, lane, gq, ksmax);
     else
-      load_ops_all(opsB, r0, w, lane, gq, ksmax);
-    store_vt(sVt, v0, tid, chunk_len(bos));
+      load_ops_all<HAS_V, WRITE_OUT>(opsB, r0, w, lane, gq, ksmax);
+    if constexpr (HAS_V) store_vt(sVt, v0, tid, chunk_len(bos));
   }
   __syncthreads();
 
@@ -244,8 +254,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     __builtin_amdgcn_sched_barrier(0);    \
   } while (0)
     uint4 vn[2];
-    KDA_ISSUE(load_v(vn, a.v, in1 ? c1 : c0, in1 ? chunk_len(c1) : L, H, h, vs, tid));
-    KDA_ISSUE(load_ops<0>(pre, prec, w, lane, gq, ksmax));
+    if constexpr (HAS_V) KDA_ISSUE(load_v(vn, a.v, in1 ? c1 : c0, in1 ? chunk_len(c1) : L, H, h, vs, tid));
+    KDA_ISSUE((load_ops<0, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
     KDA_TIMER_MARK(1);
 
     // ---- U, D = U - W S, O = QG S (token rows 16w.., all 64 columns); the
@@ -255,21 +265,23 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     for (int nn = 0; nn < 4; ++nn) {
       const int col = 16 * nn + tl;
       f32x4 u = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (HAS_V) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        // Uniform control flow: every loaded operand register is consumed on
-        // every path, so no load is still outstanding when its register is
-        // reloaded (waves 0 and 1 multiply by zero for their upper k-step).
-        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(sVt + col * TP + ((32 * ks + 8 * gq) ^ vt_swz(col)));
-        u = mfma_bf16(ks < ksmax ? cur.tbh[ks] : bf16x8{}, vb, u);
-        u = mfma_bf16(ks < ksmax ? cur.tbl[ks] : bf16x8{}, vb, u);
+        for (int ks = 0; ks < 2; ++ks) {
+          // Uniform control flow: every loaded operand register is consumed on
+          // every path, so no load is still outstanding when its register is
+          // reloaded (waves 0 and 1 multiply by zero for their upper k-step).
+          const bf16x8 vb = *reinterpret_cast<const bf16x8*>(sVt + col * TP + ((32 * ks + 8 * gq) ^ vt_swz(col)));
+          u = mfma_bf16(ks < ksmax ? cur.tbh[ks] : bf16x8{}, vb, u);
+          u = mfma_bf16(ks < ksmax ? cur.tbl[ks] : bf16x8{}, vb, u);
+        }
       }
       f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const f16x8 sb = *reinterpret_cast<const f16x8*>(sSt + col * SP + 32 * kb + 8 * gq);
         u = mfma_f16(cur.nw[kb], sb, u);
-        o = mfma_f16(cur.qg[kb], sb, o);
+        if constexpr (WRITE_OUT) o = mfma_f16(cur.qg[kb], sb, o);
       }
       O[nn] = o;
       // D^T hi/lo: lane holds tokens 16w + 4gq + 0..3 of column col
@@ -282,8 +294,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
       }
       *reinterpret_cast<f16x4*>(sDth + col * TP + 16 * w + 4 * gq) = dh;
       *reinterpret_cast<f16x4*>(sDtl + col * TP + 16 * w + 4 * gq) = dl;
-      if (nn == 0) KDA_ISSUE(load_ops<1>(pre, prec, w, lane, gq, ksmax));
-      if (nn == 1) KDA_ISSUE(load_ops<2>(pre, prec, w, lane, gq, ksmax));
+      if (nn == 0) KDA_ISSUE((load_ops<1, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
+      if (nn == 1) KDA_ISSUE((load_ops<2, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
     }
     KDA_TIMER_MARK(2);
     __syncthreads();
@@ -299,12 +311,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
         dh[ks] = *reinterpret_cast<const f16x8*>(sDth + col * TP + 32 * ks + 8 * gq);
         dl[ks] = *reinterpret_cast<const f16x8*>(sDtl + col * TP + 32 * ks + 8 * gq);
       }
-      f32x4 o = O[nn];
+      if constexpr (WRITE_OUT) {
+        f32x4 o = O[nn];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) o = mfma_f16(ks < ksmax ? cur.aqk[ks] : f16x8{}, dh[ks], o);
-      // output tile rows 16w + 4gq + ii, column col (staged for 16-byte stores)
+        for (int ks = 0; ks < 2; ++ks) o = mfma_f16(ks < ksmax ? cur.aqk[ks] : f16x8{}, dh[ks], o);
+        // output tile rows 16w + 4gq + ii, column col (staged for 16-byte stores)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) sO[(16 * w + 4 * gq + ii) * OP + col] = (__bf16)(o[ii] * a.scale);
+        for (int ii = 0; ii < 4; ++ii) sO[(16 * w + 4 * gq + ii) * OP + col] = (__bf16)(o[ii] * a.scale);
+      }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         f32x4 s = S[mt][nn];
@@ -320,12 +334,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
         }
         S[mt][nn] = s;
       }
-      if (nn == 0) KDA_ISSUE(load_ops<3>(pre, prec, w, lane, gq, ksmax));
-      if (nn == 1) KDA_ISSUE(load_ops<4>(pre, prec, w, lane, gq, ksmax));
+      if (nn == 0) KDA_ISSUE((load_ops<3, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
+      if (nn == 1) KDA_ISSUE((load_ops<4, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
     }
 #undef KDA_ISSUE
     // this wave's 16 output rows: lane -> row 16w + lane/4, 16 columns per lane
-    {
+    if constexpr (WRITE_OUT) {
       const int orow = 16 * w + (lane >> 2);
       const int ocol = 16 * (lane & 3);
       if (orow < L) {
@@ -339,7 +353,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     store_st();
     // U of this chunk read sVt before the barrier above; past the end of the
     // sequence this rewrites the current tile, which nothing reads
-    store_vt(sVt, vn, tid, in1 ? chunk_len(c1) : L);
+    if constexpr (HAS_V) store_vt(sVt, vn, tid, in1 ? chunk_len(c1) : L);
     KDA_TIMER_MARK(5);
     __syncthreads();
     KDA_TIMER_MARK(6);
@@ -376,8 +390,14 @@ hipError_t launch_inter(const InterArgs& args, hipStream_t st) {
   const int64_t grid = (items + 7) / 8 * 8 * NV;
   InterArgs a = args;
   void* kargs[] = {(void*)&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_inter_kernel), dim3((unsigned)grid),
-                         dim3(NTHREADS), kargs, 0, st);
+  const void* fn;
+  if (a.v)
+    fn = a.out ? reinterpret_cast<const void*>(&kda_inter_kernel<true, true>)
+               : reinterpret_cast<const void*>(&kda_inter_kernel<true, false>);
+  else
+    fn = a.out ? reinterpret_cast<const void*>(&kda_inter_kernel<false, true>)
+               : reinterpret_cast<const void*>(&kda_inter_kernel<false, false>);
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(NTHREADS), kargs, 0, st);
 }
 
 }  // namespace kda

@@ -100,6 +100,53 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const void* ra
                      const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t K,
                      int64_t V, int64_t N, void* stream);
 
+/*
+ * Per-shard affine map, for splitting one long sequence over several devices
+ * (context parallelism: the torchtitan PR page names KDA context parallelism,
+ * KCP, in its "Summary" section, without giving an algorithm).  The gated
+ * delta rule is affine in the state, so each sequence of the call (a shard)
+ * maps the state it is entered with, S, to
+ *     S_end = P S + R,
+ * where P (K x K) is the product of the per-token maps (I - b k k^T) Diag(a)
+ * over the shard and R is the shard's final state from a zero start.
+ *
+ *   q, k, v, raw_gate, raw_beta, workspace, A_log, dt_bias, lower_bound,
+ *   cu_seqlens, B, T, H, K, V, N   exactly as for kda_fwd (no scale or out:
+ *                                  no outputs are produced)
+ *   P   fp32 [N, H, K, K] written: P[n][h][i][j] multiplies S[j][:] into row i
+ *   R   fp32 [N, H, K, V] written
+ *
+ * Needs K == V (P is computed as the final state of the V = 0 recurrence from
+ * S = I).  Shards then combine with kda_shard_scan, and kda_fwd with the
+ * scanned entering states as initial_state produces the shards' outputs.
+ * Same errors as kda_fwd; P and R must not overlap the inputs.
+ */
+kda_status_t kda_shard_affine(const void* q, const void* k, const void* v, const void* raw_gate,
+                              const void* raw_beta, void* workspace, size_t workspace_bytes,
+                              const float* A_log, const float* dt_bias, float lower_bound, float* P,
+                              float* R, const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H,
+                              int64_t K, int64_t V, int64_t N, void* stream);
+
+/*
+ * Fold the affine maps of n_shards consecutive shards of one sequence:
+ *     starts[0] = initial_state (or zeros),
+ *     starts[r + 1] = P[r] starts[r] + R[r],
+ * in fp32, and final_state = P[n-1] starts[n-1] + R[n-1].
+ *
+ *   P       fp32 [n_shards, H, K, K]   from kda_shard_affine
+ *   R       fp32 [n_shards, H, K, V]   from kda_shard_affine
+ *   initial_state fp32 [H, K, V] or NULL for zeros
+ *   starts  fp32 [n_shards, H, K, V] written (the entering state of every shard,
+ *           ready to pass as kda_fwd's initial_state for the shard batch)
+ *   final_state fp32 [H, K, V] written, or NULL to skip
+ *
+ * Supported: K == V == 128.  Returns KDA_ERR_INVALID for NULL P, R or starts
+ * or n_shards, H < 1; outputs must not overlap the inputs.
+ */
+kda_status_t kda_shard_scan(const float* P, const float* R, const float* initial_state, float* starts,
+                            float* final_state, int64_t n_shards, int64_t H, int64_t K, int64_t V,
+                            void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* kda_status_string(kda_status_t status);
 

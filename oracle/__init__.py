@@ -7,7 +7,9 @@ library (no kernels, headers, helpers, tables or pre/post-processing).
 
 Contents
   recurrence.py  the oracle proper: fp64 token-by-token recurrence (plain C,
-                 OpenMP over (sequence, head)), loaded through ctypes.
+                 OpenMP over (sequence, head)), loaded through ctypes; the
+                 per-shard affine map (P, R) of a sequence split into shards,
+                 and the fold of consecutive shards' maps.
   chunked.py     a second, independent fp64 CPU form that processes 64-token
                  (or 16/32) chunks with the WY/UT chunk algebra; used only to
                  check the recurrence.
@@ -16,11 +18,12 @@ Contents
   build.py       compiles kda_oracle.c with gcc.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
-against closed forms, brute force, invariants and special cases, with one
+and ``tests/test_oracle_kcp_pins.py`` against closed forms, brute force,
+invariants and special cases, with one
 exception stated in the design notes: the gate formula itself (log alpha =
 lower_bound * sigmoid(exp(A_log) * (raw_gate + dt_bias))) is a reading, since
 the pages never print it, so agreement with FlashKDA's own gate is
 "parity unpinned".
 """
 
-from .recurrence import oracle_fwd, oracle_threads, metrics  # noqa: F401
+from .recurrence import oracle_fwd, oracle_threads, metrics, oracle_shard_affine, oracle_shard_fold  # noqa: F401

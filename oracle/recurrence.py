@@ -109,3 +109,43 @@ def metrics(x: np.ndarray, ref: np.ndarray) -> dict:
         "max_abs": float(np.abs(d).max()) if finite and d.size else (0.0 if finite else float("inf")),
         "finite": finite,
     }
+
+
+def oracle_shard_affine(q, k, v, raw_gate, raw_beta, A_log, dt_bias, lower_bound, cu_seqlens=None,
+                        heads=None, threads: int = 0):
+    """Affine map of every sequence (shard) of the call, in fp64.
+
+    Each token applies S -> (I - b k^ k^T) Diag(exp(g)) S + b k^ v^T, so a whole
+    shard maps its entering state S to P S + R with
+        R = the shard's final state from S = 0,
+        P = the shard's final state with v = 0 from S = I   (needs K == V).
+    This is the split that context parallelism over one sequence needs (the
+    torchtitan PR page names KDA context parallelism without giving its form).
+    Returns (P fp64 [N, nh, K, K], R fp64 [N, nh, K, V]).
+    """
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if K != V:
+        raise ValueError("the affine map is computed as a state, which needs K == V")
+    _, R = oracle_fwd(q, k, v, raw_gate, raw_beta, 1.0, A_log, dt_bias, lower_bound, None,
+                      cu_seqlens, heads, threads)
+    N = B if cu_seqlens is None else (len(cu_seqlens) - 1)
+    eye = np.broadcast_to(np.eye(K, dtype=np.float32), (N, H, K, K)).copy()
+    _, P = oracle_fwd(q, k, torch.zeros_like(v), raw_gate, raw_beta, 1.0, A_log, dt_bias,
+                      lower_bound, eye, cu_seqlens, heads, threads)
+    return P, R
+
+
+def oracle_shard_fold(P, R, initial_state=None):
+    """Fold consecutive shards' maps in fp64: starts[0] = S0 (or 0),
+    starts[r+1] = P[r] starts[r] + R[r].  P [n, H, K, K], R [n, H, K, V],
+    initial_state [H, K, V] or None.  Returns (starts [n, H, K, V], final [H, K, V])."""
+    P = np.asarray(P, dtype=np.float64)
+    R = np.asarray(R, dtype=np.float64)
+    n, H, K, V = R.shape
+    S = np.zeros((H, K, V)) if initial_state is None else np.asarray(initial_state, dtype=np.float64).copy()
+    starts = np.empty((n, H, K, V))
+    for r in range(n):
+        starts[r] = S
+        S = np.matmul(P[r], S) + R[r]
+    return starts, S

@@ -116,3 +116,41 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         kda.kda_fwd(x, x, v, x, torch.zeros(1, 4, 1, dtype=torch.bfloat16), 1.0, v.clone(),
                     torch.zeros(512, dtype=torch.uint8), torch.zeros(1), torch.zeros(1, 128), -5.0)
+
+
+def shard_affine_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, ws=FAKE, ws_bytes=1 << 40, A_log=FAKE, dt=FAKE,
+             lb=-5.0, P=FAKE, R=FAKE, cu=None, B=1, T=64, H=2, K=128, V=128, N=1)
+    a.update(over)
+    return kda._lib.kda_shard_affine(a["q"], a["k"], a["v"], a["g"], a["b"], a["ws"], a["ws_bytes"],
+                                     a["A_log"], a["dt"], ctypes.c_float(a["lb"]), a["P"], a["R"], a["cu"],
+                                     a["B"], a["T"], a["H"], a["K"], a["V"], a["N"], None)
+
+
+def shard_scan_call(**over):
+    a = dict(P=FAKE, R=FAKE, init=None, starts=FAKE, fin=None, n=2, H=2, K=128, V=128)
+    a.update(over)
+    return kda._lib.kda_shard_scan(a["P"], a["R"], a["init"], a["starts"], a["fin"], a["n"], a["H"],
+                                   a["K"], a["V"], None)
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "g", "b", "A_log", "dt", "P", "R"])
+def test_shard_affine_null_pointer_is_invalid(field):
+    assert shard_affine_call(**{field: None}) == INVALID
+
+
+def test_shard_affine_checks():
+    assert shard_affine_call(K=64, V=64) == UNSUPPORTED
+    assert shard_affine_call(lb=-6.0) == UNSUPPORTED
+    assert shard_affine_call(B=2, N=1) == INVALID
+    assert shard_affine_call(ws_bytes=16) == WORKSPACE
+    assert shard_affine_call(ws=None) == WORKSPACE
+
+
+def test_shard_scan_checks():
+    for field in ("P", "R", "starts"):
+        assert shard_scan_call(**{field: None}) == INVALID
+    assert shard_scan_call(n=0) == INVALID
+    assert shard_scan_call(H=0) == INVALID
+    assert shard_scan_call(K=64) == UNSUPPORTED
+    assert shard_scan_call(V=96) == UNSUPPORTED
