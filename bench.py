@@ -38,7 +38,7 @@ BF16_DENSE_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
 BYTES_PER_HEAD_TOKEN = 4 * 128 * 2 + 2 + 128 * 2
 STATE_BYTES = 128 * 128 * 4
 KERNEL_SRCS = [os.path.join(ROOT, "chunked_gated_delta_amd", "csrc", f)
-               for f in ("kda_common.h", "kda_intra.hip", "kda_inter.hip", "kda_api.hip", "kda_kcp.hip")]
+               for f in ("kda_common.h", "kda_intra.hip", "kda_inter.hip", "kda_api.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_fwd_c3_traffic.json")
 
 
@@ -141,6 +141,96 @@ def write_traffic(fwd_fetch, fwd_write, copy_fetch, copy_write, copy_bytes=2 << 
     print(json.dumps(doc))
 
 
+def timed(fn, steps, warmup, stream):
+    """Average device time (ms) of fn() over `steps` launches, HIP events on `stream`."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / steps
+
+
+def bench_kcp(args):
+    """Split-sequence path on the headline workload: the sequence is cut into
+    `args.kcp_shards` equal shards (one varlen batch); time the per-shard
+    affine maps, the shard scan and the forward over the shards from the
+    scanned entering states."""
+    import torch
+
+    import chunked_gated_delta_amd as kda
+    import workloads
+
+    x = workloads.c3_headline(T=args.T, H=args.H)
+    n = args.kcp_shards
+    dev = torch.device("cuda:0")
+    d = lambda t: t.to(dev)  # noqa: E731
+    q, k, v, g, b, al, dt = (d(t) for t in (x.q, x.k, x.v, x.raw_gate, x.raw_beta, x.A_log, x.dt_bias))
+    cut = torch.tensor([i * x.T // n for i in range(n + 1)], dtype=torch.int32, device=dev)
+    ws = torch.empty(kda.kda_workspace_size(x.T, x.H, n), dtype=torch.uint8, device=dev)
+    P = torch.empty(n, x.H, 128, 128, device=dev)
+    R = torch.empty_like(P)
+    starts = torch.empty_like(P)
+    fin = torch.empty_like(P)
+    out = torch.empty_like(v)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    t_aff = timed(lambda: kda.kda_shard_affine(q, k, v, g, b, ws, al, dt, x.lower_bound, P, R, cut, stream=sh),
+                  args.steps, args.warmup, stream)
+    t_scan = timed(lambda: kda.kda_shard_scan(P, R, starts, stream=sh), args.steps, args.warmup, stream)
+    t_fwd = timed(lambda: kda.kda_fwd(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, starts, fin, cut,
+                                      stream=sh), args.steps, args.warmup, stream)
+    ht = x.T * x.H
+    total = t_aff + t_scan + t_fwd
+    print(json.dumps({
+        "metric": "KDA split-sequence (per-shard affine map + scan + forward) head-tokens/s",
+        "value": ht / (total / 1e3), "unit": "head-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"kda_shard_affine + kda_shard_scan + kda_fwd, B=1 T={x.T} H={x.H} "
+                               f"K=V=128 cut into {n} equal shards", "shards": n},
+        "ms": {"shard_affine": t_aff, "shard_scan": t_scan, "forward_from_starts": t_fwd, "total": total},
+    }), flush=True)
+
+
+def bench_decode(args):
+    """Token-by-token decode step: B = args.decode sequences, T = 1, H = args.H,
+    fp32 states updated in place.  HBM-bound on the state: per (sequence, head)
+    the algorithmic bytes are the 2 x 64 KiB state read and write plus the
+    token's q, k, v, raw_gate, out (5 x 256 B) and raw_beta (2 B)."""
+    import torch
+
+    import chunked_gated_delta_amd as kda
+    import workloads
+
+    x = workloads.random_inputs("decode-bench", 5, args.decode, 1, args.H, init_std=0.1)
+    dev = torch.device("cuda:0")
+    d = lambda t: t.to(dev)  # noqa: E731
+    q, k, v, g, b, al, dt, st = (d(t) for t in (x.q, x.k, x.v, x.raw_gate, x.raw_beta, x.A_log, x.dt_bias,
+                                                x.initial_state))
+    out = torch.empty_like(v)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    ms = timed(lambda: kda.kda_decode(q, k, v, g, b, x.scale, out, al, dt, x.lower_bound, st, st, stream=sh),
+               args.steps, args.warmup, stream)
+    pairs = x.B * x.H
+    alg = pairs * (2 * STATE_BYTES + 5 * 128 * 2 + 2)
+    gbs = alg / (ms / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "KDA decode step (T=1) sequence-heads/s", "value": pairs / (ms / 1e3),
+        "unit": "sequence-heads/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "dtype": "fp32 state, bf16 io", "data": "synthetic",
+        "config": {"workload": f"kda_decode B={x.B} T=1 H={x.H} K=V=128, in-place fp32 state"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +241,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=96)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--decode", type=int, default=0,
+                    help="time the decode step for this many sequences (T=1) instead")
+    ap.add_argument("--kcp-shards", type=int, default=0,
+                    help="time the split-sequence path with this many shards instead")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FWD_FETCH", "FWD_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="rocprofv3 counter_collection.csv files -> profiles/kda_fwd_c3_traffic.json")
     args = ap.parse_args()
@@ -165,6 +259,12 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.kcp_shards:
+        bench_kcp(args)
+        return
+    if args.decode:
+        bench_decode(args)
         return
 
     import torch

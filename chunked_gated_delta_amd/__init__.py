@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the forward pass runs in the HIP
 kernels behind the C ABI of include/kda.h.  The names mirror that header:
 ``kda_fwd``, ``kda_workspace_size``, ``kda_is_supported``, ``kda_shard_affine``,
-``kda_shard_scan``.  PyTorch provides
+``kda_shard_scan``, ``kda_decode``.  PyTorch provides
 device memory and the current stream; there is no CPU or PyTorch fallback, and
 importing this module fails if the library has not been built.
 """
@@ -20,7 +20,7 @@ import os
 import torch  # noqa: F401
 
 __all__ = ["kda_fwd", "kda_workspace_size", "kda_is_supported", "kda_shard_affine",
-           "kda_shard_scan", "KdaError", "STATUS", "library_path", "exported_symbols"]
+           "kda_shard_scan", "kda_decode", "KdaError", "STATUS", "library_path", "exported_symbols"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkda.so")
@@ -28,7 +28,7 @@ library_path = os.path.join(_HERE, "libkda.so")
 STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERR_INVALID", 2: "KDA_ERR_UNSUPPORTED",
           3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_LAUNCH"}
 exported_symbols = ("kda_fwd", "kda_workspace_size", "kda_is_supported", "kda_status_string",
-                    "kda_shard_affine", "kda_shard_scan")
+                    "kda_shard_affine", "kda_shard_scan", "kda_decode")
 
 
 class KdaError(RuntimeError):
@@ -60,6 +60,9 @@ _lib.kda_shard_affine.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _
 _lib.kda_shard_affine.restype = ctypes.c_int
 _lib.kda_shard_scan.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
 _lib.kda_shard_scan.restype = ctypes.c_int
+_lib.kda_decode.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_float, _P, _P,
+                            _I64, _I64, _I64, _I64, _I64, _P]
+_lib.kda_decode.restype = ctypes.c_int
 
 
 def kda_workspace_size(T: int, H: int, N: int) -> int:
@@ -162,6 +165,23 @@ def kda_shard_scan(P, R, starts, initial_state=None, final_state=None, stream=No
                              n, H, K, V, _stream(stream, P.device))
     if rc != 0:
         raise KdaError(rc, "kda_shard_scan")
+
+
+def kda_decode(q, k, v, raw_gate, raw_beta, scale, out, A_log, dt_bias, lower_bound,
+               initial_state=None, final_state=None, stream=None):
+    """Enqueue the token-by-token step over B sequences of T tokens (layouts as for
+    kda_fwd, states fp32 [B,H,K,V]; final_state may be initial_state for an in-place
+    update).  Raises KdaError on a non-zero status."""
+    if out is None:
+        raise ValueError("out is required")
+    B, T, H, K, V, _ = _check_inputs(q, k, v, raw_gate, raw_beta, out, A_log, dt_bias, None)
+    _check_f32("initial_state", initial_state, (B, H, K, V))
+    _check_f32("final_state", final_state, (B, H, K, V))
+    rc = _lib.kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(raw_beta), float(scale), _ptr(out),
+                         _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
+                         _ptr(final_state), B, T, H, K, V, _stream(stream, q.device))
+    if rc != 0:
+        raise KdaError(rc, "kda_decode")
 
 
 def raw_call(*args):

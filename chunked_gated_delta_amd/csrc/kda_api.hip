@@ -135,8 +135,10 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
                      const float* dt_bias, float lower_bound, const int32_t* cu_seqlens, int64_t B,
                      int64_t T, int64_t H, int64_t K, int64_t V, int64_t N, hipStream_t st,
                      Prepared& pr) {
-  if (!q || !k || !raw_gate || !raw_beta || !A_log || !dt_bias) return KDA_ERR_INVALID;
   if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID;
+  // token arrays may be NULL only when there are no tokens (empty tensors)
+  if (B * T > 0 && (!q || !k || !raw_gate || !raw_beta)) return KDA_ERR_INVALID;
+  if (!A_log || !dt_bias) return KDA_ERR_INVALID;
   if (cu_seqlens ? (B != 1) : (N != B)) return KDA_ERR_INVALID;
   if (!kda_is_supported(K, V, lower_bound)) return KDA_ERR_UNSUPPORTED;
   if (B * T * H > ((int64_t)1 << 40) || N * H > ((int64_t)1 << 28) || N > ((int64_t)1 << 30))
@@ -222,7 +224,7 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const void* ra
                      float lower_bound, const float* initial_state, float* final_state,
                      const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t K,
                      int64_t V, int64_t N, void* stream) {
-  if (!v || !out) return KDA_ERR_INVALID;
+  if (B * T > 0 && (!v || !out)) return KDA_ERR_INVALID;
   if (!(scale == scale)) return KDA_ERR_INVALID;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   Prepared pr;
@@ -243,7 +245,7 @@ kda_status_t kda_shard_affine(const void* q, const void* k, const void* v, const
                               const float* A_log, const float* dt_bias, float lower_bound, float* P,
                               float* R, const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H,
                               int64_t K, int64_t V, int64_t N, void* stream) {
-  if (!v || !P || !R) return KDA_ERR_INVALID;
+  if ((B * T > 0 && !v) || !P || !R) return KDA_ERR_INVALID;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   Prepared pr;
   const kda_status_t s = prepare(q, k, raw_gate, raw_beta, workspace, workspace_bytes, A_log, dt_bias,

@@ -23,7 +23,8 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous,
- *     in the layouts given below.  The library never allocates, frees or
+ *     in the layouts given below.  Per-token arrays (q, k, v, raw_gate,
+ *     raw_beta, out) may be NULL when the call has no tokens (B * T == 0).  The library never allocates, frees or
  *     synchronises; kda_fwd is asynchronous on `stream`.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *   - Argument checks happen on the host before any device work; a rejected
@@ -146,6 +147,32 @@ kda_status_t kda_shard_affine(const void* q, const void* k, const void* v, const
 kda_status_t kda_shard_scan(const float* P, const float* R, const float* initial_state, float* starts,
                             float* final_state, int64_t n_shards, int64_t H, int64_t K, int64_t V,
                             void* stream);
+
+/*
+ * Token-by-token step for decoding and short continuations: B sequences of T
+ * tokens each (T small, typically 1), applying the same per-token gated delta
+ * rule as kda_fwd directly in fp32 (the serving decode path named in the vLLM
+ * PR report's risk section).  The state is read once, kept on chip across the
+ * T tokens and written once, so the cost is the state's 2 x 64 KiB of HBM
+ * traffic per sequence and head; no workspace is needed.
+ *
+ *   q, k, raw_gate  bf16 [B, T, H, K];  v, out bf16 [B, T, H, V];  raw_beta bf16 [B, T, H]
+ *   scale, A_log fp32 [H], dt_bias fp32 [H, K], lower_bound   as for kda_fwd
+ *   initial_state fp32 [B, H, K, V] or NULL for zeros
+ *   final_state   fp32 [B, H, K, V] written, or NULL; may equal initial_state
+ *                 (the usual in-place decode update)
+ *   B, H >= 1, T >= 0; K == V == 128, lower_bound in [-5, 0]
+ *
+ * Returns KDA_SUCCESS after enqueueing, KDA_ERR_INVALID / KDA_ERR_UNSUPPORTED
+ * from the host checks, or KDA_ERR_LAUNCH.  For long prompts use kda_fwd,
+ * whose chunked form is far faster per token; both give the same results up
+ * to rounding.
+ */
+kda_status_t kda_decode(const void* q, const void* k, const void* v, const void* raw_gate,
+                        const void* raw_beta, float scale, void* out, const float* A_log,
+                        const float* dt_bias, float lower_bound, const float* initial_state,
+                        float* final_state, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                        void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* kda_status_string(kda_status_t status);

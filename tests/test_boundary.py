@@ -154,3 +154,26 @@ def test_shard_scan_checks():
     assert shard_scan_call(H=0) == INVALID
     assert shard_scan_call(K=64) == UNSUPPORTED
     assert shard_scan_call(V=96) == UNSUPPORTED
+
+
+def decode_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, scale=0.088, out=FAKE, A_log=FAKE, dt=FAKE, lb=-5.0,
+             init=None, fin=None, B=2, T=1, H=2, K=128, V=128)
+    a.update(over)
+    return kda._lib.kda_decode(a["q"], a["k"], a["v"], a["g"], a["b"], ctypes.c_float(a["scale"]), a["out"],
+                               a["A_log"], a["dt"], ctypes.c_float(a["lb"]), a["init"], a["fin"], a["B"],
+                               a["T"], a["H"], a["K"], a["V"], None)
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "g", "b", "out", "A_log", "dt"])
+def test_decode_null_pointer_is_invalid(field):
+    assert decode_call(**{field: None}) == INVALID
+
+
+def test_decode_checks():
+    assert decode_call(B=0) == INVALID
+    assert decode_call(H=0) == INVALID
+    assert decode_call(T=-1) == INVALID
+    assert decode_call(scale=float("nan")) == INVALID
+    assert decode_call(K=64, V=64) == UNSUPPORTED
+    assert decode_call(lb=0.5) == UNSUPPORTED

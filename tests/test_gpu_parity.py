@@ -239,3 +239,17 @@ def test_runs_on_a_side_stream():
     o, f = run_gpu(x, stream=s.cuda_stream)
     ro, rf = oracle(x)
     check(o, f, ro, rf, "side stream")
+
+
+def test_zero_tokens_copies_the_state():
+    """B sequences of T = 0 tokens (empty, NULL-pointer tensors): final = initial."""
+    import chunked_gated_delta_amd as kda
+    dev = "cuda:0"
+    x = W.random_inputs("empty", 71, 2, 0, 3, init_std=0.3)
+    fin = torch.full((2, 3, 128, 128), float("nan"), device=dev)
+    out = torch.empty(2, 0, 3, 128, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(kda.kda_workspace_size(0, 3, 2), 1), dtype=torch.uint8, device=dev)
+    kda.kda_fwd(*(t.to(dev) for t in (x.q, x.k, x.v, x.raw_gate, x.raw_beta)), x.scale, out, ws,
+                x.A_log.to(dev), x.dt_bias.to(dev), x.lower_bound, x.initial_state.to(dev), fin)
+    torch.cuda.synchronize()
+    assert torch.equal(fin.cpu(), x.initial_state)
