@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the forward pass runs in the HIP
 kernels behind the C ABI of include/kda.h.  The names mirror that header:
 ``kda_fwd``, ``kda_workspace_size``, ``kda_is_supported``, ``kda_shard_affine``,
-``kda_shard_scan``, ``kda_decode``.  PyTorch provides
+``kda_shard_scan``, ``kda_decode``, ``kda_fwd_ex`` (with the ``FLAG_*`` variant bits).  PyTorch provides
 device memory and the current stream; there is no CPU or PyTorch fallback, and
 importing this module fails if the library has not been built.
 """
@@ -19,8 +19,9 @@ import os
 # in the process, and whichever initialises second sees no device.
 import torch  # noqa: F401
 
-__all__ = ["kda_fwd", "kda_workspace_size", "kda_is_supported", "kda_shard_affine",
-           "kda_shard_scan", "kda_decode", "KdaError", "STATUS", "library_path", "exported_symbols"]
+__all__ = ["kda_fwd", "kda_fwd_ex", "kda_workspace_size", "kda_is_supported", "kda_shard_affine",
+           "kda_shard_scan", "kda_decode", "KdaError", "STATUS", "library_path", "exported_symbols",
+           "FLAG_GATE_GIVEN", "FLAG_BETA_GIVEN", "FLAG_NO_QK_NORM", "FLAG_STATE_VK"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkda.so")
@@ -28,7 +29,9 @@ library_path = os.path.join(_HERE, "libkda.so")
 STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERR_INVALID", 2: "KDA_ERR_UNSUPPORTED",
           3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_LAUNCH"}
 exported_symbols = ("kda_fwd", "kda_workspace_size", "kda_is_supported", "kda_status_string",
-                    "kda_shard_affine", "kda_shard_scan", "kda_decode")
+                    "kda_shard_affine", "kda_shard_scan", "kda_decode", "kda_fwd_ex")
+# kda_fwd_ex variant bits (KDA_FLAG_* in include/kda.h)
+FLAG_GATE_GIVEN, FLAG_BETA_GIVEN, FLAG_NO_QK_NORM, FLAG_STATE_VK = 1, 2, 4, 8
 
 
 class KdaError(RuntimeError):
@@ -55,6 +58,9 @@ _lib.kda_status_string.restype = ctypes.c_char_p
 _lib.kda_fwd.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P, _P,
                          ctypes.c_float, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]
 _lib.kda_fwd.restype = ctypes.c_int
+_lib.kda_fwd_ex.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P, _P,
+                            ctypes.c_float, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.c_uint, _P]
+_lib.kda_fwd_ex.restype = ctypes.c_int
 _lib.kda_shard_affine.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, ctypes.c_float,
                                   _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]
 _lib.kda_shard_affine.restype = ctypes.c_int
@@ -86,7 +92,7 @@ def _check_inputs(q, k, v, raw_gate, raw_beta, out, A_log, dt_bias, cu_seqlens):
         if t is not None and (t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda):
             raise ValueError(f"{name} must be a contiguous bf16 device tensor")
     for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
-        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda):
             raise ValueError(f"{name} must be a contiguous fp32 device tensor")
     if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
         raise ValueError("cu_seqlens must be an int32 device tensor")
@@ -134,6 +140,27 @@ def kda_fwd(q, k, v, raw_gate, raw_beta, scale, out, workspace, A_log, dt_bias, 
                       _ptr(final_state), _ptr(cu_seqlens), B, T, H, K, V, N, _stream(stream, q.device))
     if rc != 0:
         raise KdaError(rc)
+
+
+def kda_fwd_ex(q, k, v, raw_gate, raw_beta, scale, out, workspace, A_log, dt_bias, lower_bound,
+               initial_state=None, final_state=None, cu_seqlens=None, flags=0, stream=None):
+    """kda_fwd with variant flags (an OR of the FLAG_* bits).  With FLAG_GATE_GIVEN,
+    A_log and dt_bias may be None; with FLAG_STATE_VK the states are [N,H,V,K]."""
+    if out is None:
+        raise ValueError("out is required")
+    if not flags & FLAG_GATE_GIVEN and (A_log is None or dt_bias is None):
+        raise ValueError("A_log and dt_bias are required unless FLAG_GATE_GIVEN")
+    B, T, H, K, V, N = _check_inputs(q, k, v, raw_gate, raw_beta, out, A_log, dt_bias, cu_seqlens)
+    st_shape = (N, H, V, K) if flags & FLAG_STATE_VK else (N, H, K, V)
+    _check_f32("initial_state", initial_state, st_shape)
+    _check_f32("final_state", final_state, st_shape)
+    rc = _lib.kda_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(raw_beta), float(scale),
+                         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                         _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
+                         _ptr(final_state), _ptr(cu_seqlens), B, T, H, K, V, N, int(flags),
+                         _stream(stream, q.device))
+    if rc != 0:
+        raise KdaError(rc, "kda_fwd_ex")
 
 
 def kda_shard_affine(q, k, v, raw_gate, raw_beta, workspace, A_log, dt_bias, lower_bound, P, R,

@@ -134,11 +134,14 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
                      void* workspace, size_t workspace_bytes, const float* A_log,
                      const float* dt_bias, float lower_bound, const int32_t* cu_seqlens, int64_t B,
                      int64_t T, int64_t H, int64_t K, int64_t V, int64_t N, hipStream_t st,
-                     Prepared& pr) {
+                     Prepared& pr, unsigned flags = 0) {
   if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID;
+  if (flags & ~(unsigned)(FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM | FLAG_STATE_VK))
+    return KDA_ERR_INVALID;
   // token arrays may be NULL only when there are no tokens (empty tensors)
   if (B * T > 0 && (!q || !k || !raw_gate || !raw_beta)) return KDA_ERR_INVALID;
-  if (!A_log || !dt_bias) return KDA_ERR_INVALID;
+  const bool gate_given = flags & FLAG_GATE_GIVEN;
+  if (!gate_given && (!A_log || !dt_bias)) return KDA_ERR_INVALID;
   if (cu_seqlens ? (B != 1) : (N != B)) return KDA_ERR_INVALID;
   if (!kda_is_supported(K, V, lower_bound)) return KDA_ERR_UNSUPPORTED;
   if (B * T * H > ((int64_t)1 << 40) || N * H > ((int64_t)1 << 28) || N > ((int64_t)1 << 30))
@@ -179,8 +182,12 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
   ia.k = static_cast<const uint16_t*>(k);
   ia.g = static_cast<const uint16_t*>(raw_gate);
   ia.beta = static_cast<const uint16_t*>(raw_beta);
-  ia.A_log = A_log;
-  ia.dt_bias = dt_bias;
+  // With the gate given, A_log and dt_bias are unused but the prefetch still
+  // reads them unconditionally (fixed wait depths): point absent ones at the
+  // record area, which is large enough and whose values are then ignored.
+  ia.A_log = A_log ? A_log : reinterpret_cast<const float*>(pr.rec);
+  ia.dt_bias = dt_bias ? dt_bias : reinterpret_cast<const float*>(pr.rec);
+  ia.flags = (int)(flags & (FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM));
   ia.rec = pr.rec;
   ia.map = pr.map;
   ia.H = (int)H;
@@ -201,6 +208,7 @@ InterArgs inter_args(const Prepared& pr, int64_t H) {
   xa.init = nullptr;
   xa.fin = nullptr;
   xa.init_identity = 0;
+  xa.state_vk = 0;
   xa.rec = pr.rec;
   xa.order = pr.order;
   xa.map = pr.map;
@@ -218,18 +226,18 @@ InterArgs inter_args(const Prepared& pr, int64_t H) {
 
 extern "C" {
 
-kda_status_t kda_fwd(const void* q, const void* k, const void* v, const void* raw_gate,
-                     const void* raw_beta, float scale, void* out, void* workspace,
-                     size_t workspace_bytes, const float* A_log, const float* dt_bias,
-                     float lower_bound, const float* initial_state, float* final_state,
-                     const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t K,
-                     int64_t V, int64_t N, void* stream) {
+kda_status_t kda_fwd_ex(const void* q, const void* k, const void* v, const void* raw_gate,
+                        const void* raw_beta, float scale, void* out, void* workspace,
+                        size_t workspace_bytes, const float* A_log, const float* dt_bias,
+                        float lower_bound, const float* initial_state, float* final_state,
+                        const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t K,
+                        int64_t V, int64_t N, unsigned flags, void* stream) {
   if (B * T > 0 && (!v || !out)) return KDA_ERR_INVALID;
   if (!(scale == scale)) return KDA_ERR_INVALID;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   Prepared pr;
   const kda_status_t s = prepare(q, k, raw_gate, raw_beta, workspace, workspace_bytes, A_log, dt_bias,
-                                 lower_bound, cu_seqlens, B, T, H, K, V, N, st, pr);
+                                 lower_bound, cu_seqlens, B, T, H, K, V, N, st, pr, flags);
   if (s != KDA_SUCCESS) return s;
   InterArgs xa = inter_args(pr, H);
   xa.v = static_cast<const uint16_t*>(v);
@@ -237,7 +245,18 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const void* ra
   xa.init = initial_state;
   xa.fin = final_state;
   xa.scale = scale;
+  xa.state_vk = (flags & FLAG_STATE_VK) ? 1 : 0;
   return launch_status(launch_inter(xa, st), "inter");
+}
+
+kda_status_t kda_fwd(const void* q, const void* k, const void* v, const void* raw_gate,
+                     const void* raw_beta, float scale, void* out, void* workspace,
+                     size_t workspace_bytes, const float* A_log, const float* dt_bias,
+                     float lower_bound, const float* initial_state, float* final_state,
+                     const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t K,
+                     int64_t V, int64_t N, void* stream) {
+  return kda_fwd_ex(q, k, v, raw_gate, raw_beta, scale, out, workspace, workspace_bytes, A_log, dt_bias,
+                    lower_bound, initial_state, final_state, cu_seqlens, B, T, H, K, V, N, 0u, stream);
 }
 
 kda_status_t kda_shard_affine(const void* q, const void* k, const void* v, const void* raw_gate,

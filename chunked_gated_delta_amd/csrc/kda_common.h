@@ -140,6 +140,12 @@ __device__ __forceinline__ void lds_f32x8(const float* src, float (&d)[8]) {
 #define KDA_TIMER_STORE(ptr) do { } while (0)
 #endif
 
+// Variant bits (same values as the KDA_FLAG_* constants of the C ABI).
+constexpr int FLAG_GATE_GIVEN = 1;   // raw_gate holds the natural-log decay g
+constexpr int FLAG_BETA_GIVEN = 2;   // raw_beta holds beta
+constexpr int FLAG_NO_QK_NORM = 4;   // q, k used without L2 normalisation
+constexpr int FLAG_STATE_VK = 8;     // states stored transposed, [N, H, V, K]
+
 // Host-side launchers (defined next to their kernels).
 struct IntraArgs {
   const uint16_t* q;
@@ -152,6 +158,7 @@ struct IntraArgs {
   ChunkMap map;
   int H;
   float lb2;        // lower_bound * log2(e)
+  int flags;        // FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM
   unsigned long long* timers;  // phase timers (KDA_PHASE_TIMERS builds only), else nullptr
 };
 struct InterArgs {
@@ -160,6 +167,7 @@ struct InterArgs {
   const float* init;     // nullptr: zero state, or the identity if init_identity
   float* fin;
   int init_identity;     // with init == nullptr: start every (sequence, head) from I (needs K == V)
+  int state_vk;          // states stored transposed: S[c][j] at j * K + c
   const char* rec;
   const int32_t* order;  // nullptr: identity order of sequences
   ChunkMap map;

@@ -197,7 +197,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
         for (int ii = 0; ii < 4; ++ii) {
           const int c = 32 * w + 16 * mt + 4 * gq + ii;
           const int col = vs + 16 * nn + tl;
-          S[mt][nn][ii] = src ? src[c * VD + col] : ((a.init_identity && c == col) ? 1.0f : 0.0f);
+          S[mt][nn][ii] = src ? src[a.state_vk ? col * KD + c : c * VD + col]
+                              : ((a.init_identity && c == col) ? 1.0f : 0.0f);
         }
   }
   auto store_st = [&]() {
@@ -378,8 +379,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
 #pragma unroll
       for (int nn = 0; nn < 4; ++nn)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          dst[(32 * w + 16 * mt + 4 * gq + ii) * VD + vs + 16 * nn + tl] = S[mt][nn][ii];
+        for (int ii = 0; ii < 4; ++ii) {
+          const int c = 32 * w + 16 * mt + 4 * gq + ii;
+          const int col = vs + 16 * nn + tl;
+          dst[a.state_vk ? col * KD + c : c * VD + col] = S[mt][nn][ii];
+        }
   }
 }
 

@@ -242,10 +242,13 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   ssq += xor_lane(ssq, 32);
   ssk += xor_lane(ssk, 16);
   ssk += xor_lane(ssk, 32);
-  const float rq = valid ? __builtin_amdgcn_rsqf(ssq + L2_EPS) : 0.0f;
-  const float rk = valid ? __builtin_amdgcn_rsqf(ssk + L2_EPS) : 0.0f;
+  const bool qk_norm = !(a.flags & FLAG_NO_QK_NORM);
+  const float rq = valid ? (qk_norm ? __builtin_amdgcn_rsqf(ssq + L2_EPS) : 1.0f) : 0.0f;
+  const float rk = valid ? (qk_norm ? __builtin_amdgcn_rsqf(ssk + L2_EPS) : 1.0f) : 0.0f;
   const float braw = __uint_as_float((uint32_t)braw16 << 16);
-  const float beta = valid ? __builtin_amdgcn_rcpf(1.0f + fexp2(-braw * LOG2E)) : 0.0f;
+  const float beta =
+      valid ? ((a.flags & FLAG_BETA_GIVEN) ? braw : __builtin_amdgcn_rcpf(1.0f + fexp2(-braw * LOG2E))) : 0.0f;
+  const bool gate_given = a.flags & FLAG_GATE_GIVEN;
 
   // log-decay in log2 units, inclusive scan over the sub-chunk's 16 tokens
 #pragma unroll
@@ -254,7 +257,10 @@ __global__ void __launch_bounds__(NTHREADS, 2)
     lds_f32x8(sNB + 32 * kb + 8 * gq, nb);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float g2 = a.lb2 * __builtin_amdgcn_rcpf(1.0f + fexp2(gl[kb][e] * na + nb[e]));
+      // log2 decay: lb2 * sigmoid(exp(A_log)(raw + dt)), or the given natural-log
+      // decay clamped to [lower_bound, 0]
+      float g2 = gate_given ? fminf(fmaxf(gl[kb][e] * LOG2E, a.lb2), 0.0f)
+                            : a.lb2 * __builtin_amdgcn_rcpf(1.0f + fexp2(gl[kb][e] * na + nb[e]));
       g2 = valid ? g2 : 0.0f;
       gl[kb][e] = row_scan16(g2);
     }

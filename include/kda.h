@@ -174,6 +174,38 @@ kda_status_t kda_decode(const void* q, const void* k, const void* v, const void*
                         float* final_state, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                         void* stream);
 
+/*
+ * Variants of kda_fwd (kda_fwd_ex `flags`), the in-kernel switches of the
+ * chunk_kda call on the instagit FlashKDA page ("Usage Examples"):
+ *   KDA_FLAG_GATE_GIVEN  (use_gate_in_kernel off) raw_gate already holds the
+ *       natural-log decay g, bf16; values are clamped to [lower_bound, 0]
+ *       (lower_bound keeps its [-5, 0] range and role as the decay floor).
+ *       A_log and dt_bias are unused and may be NULL.
+ *   KDA_FLAG_BETA_GIVEN  (use_beta_sigmoid_in_kernel off) raw_beta already
+ *       holds beta; keep it in [0, 1] for the documented accuracy.
+ *   KDA_FLAG_NO_QK_NORM  (use_qk_l2norm_in_kernel off) q and k are used as
+ *       given; the caller keeps |k|, |q| <= 1 (the rule is only stable for
+ *       beta |k|^2 <= 2, and the kernel's fp16 operands assume unit scale).
+ *   KDA_FLAG_STATE_VK    (transpose_state_layout) initial_state and
+ *       final_state are stored transposed, [N, H, V, K]: S[k][v] at v*K + k.
+ */
+#define KDA_FLAG_GATE_GIVEN 1u
+#define KDA_FLAG_BETA_GIVEN 2u
+#define KDA_FLAG_NO_QK_NORM 4u
+#define KDA_FLAG_STATE_VK 8u
+
+/*
+ * kda_fwd with variant flags (any OR of the KDA_FLAG_* bits; other bits give
+ * KDA_ERR_INVALID).  Every other argument is as for kda_fwd, and
+ * kda_fwd(...) == kda_fwd_ex(..., 0, stream).
+ */
+kda_status_t kda_fwd_ex(const void* q, const void* k, const void* v, const void* raw_gate,
+                        const void* raw_beta, float scale, void* out, void* workspace,
+                        size_t workspace_bytes, const float* A_log, const float* dt_bias,
+                        float lower_bound, const float* initial_state, float* final_state,
+                        const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t K,
+                        int64_t V, int64_t N, unsigned flags, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* kda_status_string(kda_status_t status);
 

@@ -39,8 +39,12 @@ def _matmul(A, B):
 
 
 def brute_fwd(q, k, v, raw_gate, raw_beta, scale, A_log, dt_bias, lower_bound,
-              initial_state=None, head: int = 0, digits: int = 40):
-    """One sequence (B=1), one head.  Returns (out [T][V], final [K][V]) as Decimals."""
+              initial_state=None, head: int = 0, digits: int = 40, gate_given=False,
+              beta_given=False, no_qk_norm=False):
+    """One sequence (B=1), one head.  Returns (out [T][V], final [K][V]) as Decimals.
+
+    gate_given: raw_gate is the log-decay g itself (clamped to [lower_bound, 0]);
+    beta_given: raw_beta is beta itself; no_qk_norm: q, k are used unnormalised."""
     getcontext().prec = digits
     _, T, H, K = q.shape
     V = v.shape[-1]
@@ -54,15 +58,23 @@ def brute_fwd(q, k, v, raw_gate, raw_beta, scale, A_log, dt_bias, lower_bound,
 
     def norm(row):
         xs = [_dec(x) for x in row.tolist()]
+        if no_qk_norm:
+            return xs
         r = Decimal(1) / (sum((x * x for x in xs), Decimal(0)) + EPS).sqrt()
         return [x * r for x in xs]
 
+    def clamp_gate(x):
+        return lb if x < lb else (Decimal(0) if x > 0 else x)
+
     qn = [norm(qf[t]) for t in range(T)]
     kn = [norm(kf[t]) for t in range(T)]
-    beta = [_sig(_dec(bf[t])) for t in range(T)]
+    beta = [_dec(bf[t]) if beta_given else _sig(_dec(bf[t])) for t in range(T)]
     gm = al.exp()
-    alpha = [[(lb * _sig(gm * (_dec(gf[t, c]) + dt[c]))).exp() for c in range(K)]
-             for t in range(T)]
+    if gate_given:
+        alpha = [[clamp_gate(_dec(gf[t, c])).exp() for c in range(K)] for t in range(T)]
+    else:
+        alpha = [[(lb * _sig(gm * (_dec(gf[t, c]) + dt[c]))).exp() for c in range(K)]
+                 for t in range(T)]
     # transition matrices M_s = (I - beta k k^T) Diag(alpha)
     Ms = []
     for s in range(T):

@@ -28,6 +28,14 @@
  * o_t = scale S_t^T q_t.  eps = 1e-6 is also a reading (the pages are silent).
  *
  * Inputs arrive as raw bf16 bit patterns (uint16) and are widened exactly.
+ *
+ * Variants (the chunk_kda flags on the same page, each switching one in-kernel
+ * step off), selected by the bits of `flags`:
+ *   ORACLE_GATE_GIVEN  raw_gate already holds g (natural-log decay; values are
+ *                      clamped to [lower_bound, 0]); A_log, dt_bias unused
+ *   ORACLE_BETA_GIVEN  raw_beta already holds beta (no sigmoid)
+ *   ORACLE_NO_QK_NORM  q^ = q, k^ = k (no L2 normalisation)
+ *   ORACLE_STATE_VK    initial/final states stored transposed, [N, H, V, K]
  */
 #include <math.h>
 #include <stdint.h>
@@ -38,6 +46,10 @@
 #endif
 
 #define ORACLE_L2_EPS 1e-6
+#define ORACLE_GATE_GIVEN 1
+#define ORACLE_BETA_GIVEN 2
+#define ORACLE_NO_QK_NORM 4
+#define ORACLE_STATE_VK 8
 
 static double widen_bf16(uint16_t bits) {
   uint32_t u = ((uint32_t)bits) << 16;
@@ -48,14 +60,15 @@ static double widen_bf16(uint16_t bits) {
 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
-/* out[c] = x[c] / sqrt(sum_c x[c]^2 + eps) */
-static void l2_normalise(const uint16_t* x, int64_t n, double* out) {
+/* out[c] = x[c] / sqrt(sum_c x[c]^2 + eps), or x[c] unchanged if !normalise */
+static void l2_normalise(const uint16_t* x, int64_t n, double* out, int normalise) {
   double ss = 0.0;
   for (int64_t c = 0; c < n; ++c) {
     double xc = widen_bf16(x[c]);
     out[c] = xc;
     ss += xc * xc;
   }
+  if (!normalise) return;
   double r = 1.0 / sqrt(ss + ORACLE_L2_EPS);
   for (int64_t c = 0; c < n; ++c) out[c] *= r;
 }
@@ -73,14 +86,15 @@ int kda_oracle_threads(void) {
  * A_log fp32 [H]; dt_bias fp32 [H, K]; initial_state fp32 [N, H, K, V] or NULL (zeros)
  * cu_seqlens int32 [N+1] (host); heads: the n_heads head indices to evaluate.
  * out: fp64 [T_total, n_heads, V]; final_state: fp64 [N, n_heads, K, V] (may be NULL).
- * n_threads <= 0 keeps the OpenMP default.  Returns 0, or -1 on bad sizes.
+ * n_threads <= 0 keeps the OpenMP default; flags: ORACLE_* bits above.
+ * Returns 0, or -1 on bad sizes.
  */
 int kda_oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                    const uint16_t* raw_gate, const uint16_t* raw_beta, double scale,
                    const float* A_log, const float* dt_bias, double lower_bound,
                    const float* initial_state, const int32_t* cu_seqlens, int64_t N,
                    int64_t T_total, int64_t H, int64_t K, int64_t V, const int32_t* heads,
-                   int64_t n_heads, double* out, double* final_state, int n_threads) {
+                   int64_t n_heads, double* out, double* final_state, int n_threads, int flags) {
   if (N < 1 || H < 1 || K < 1 || V < 1 || n_heads < 1) return -1;
   if (cu_seqlens[0] != 0 || cu_seqlens[N] != T_total) return -1;
   for (int64_t n = 0; n < N; ++n)
@@ -105,18 +119,29 @@ int kda_oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 #pragma omp for schedule(dynamic, 1)
     for (int64_t job = 0; job < jobs; ++job) {
       int64_t n = job / n_heads, hi = job % n_heads, h = heads[hi];
-      /* initial state */
-      for (int64_t i = 0; i < K * V; ++i)
-        S[i] = initial_state ? (double)initial_state[(n * H + h) * K * V + i] : 0.0;
-      double gate_mul = exp((double)A_log[h]);
+      /* initial state: S[c][j] at c*V + j, or at j*K + c in the transposed layout */
+      const int vk = (flags & ORACLE_STATE_VK) != 0;
+      for (int64_t c = 0; c < K; ++c)
+        for (int64_t j = 0; j < V; ++j)
+          S[c * V + j] = initial_state
+                             ? (double)initial_state[(n * H + h) * K * V + (vk ? j * K + c : c * V + j)]
+                             : 0.0;
+      double gate_mul = (flags & ORACLE_GATE_GIVEN) ? 0.0 : exp((double)A_log[h]);
       for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
         int64_t th = t * H + h;
-        l2_normalise(q + th * K, K, qh);
-        l2_normalise(k + th * K, K, kh);
-        double beta = sigmoid(widen_bf16(raw_beta[th]));
+        int normalise = (flags & ORACLE_NO_QK_NORM) == 0;
+        l2_normalise(q + th * K, K, qh, normalise);
+        l2_normalise(k + th * K, K, kh, normalise);
+        double rb = widen_bf16(raw_beta[th]);
+        double beta = (flags & ORACLE_BETA_GIVEN) ? rb : sigmoid(rb);
         for (int64_t c = 0; c < K; ++c) {
-          double x = gate_mul * (widen_bf16(raw_gate[th * K + c]) + (double)dt_bias[h * K + c]);
-          alpha[c] = exp(lower_bound * sigmoid(x));
+          double rg = widen_bf16(raw_gate[th * K + c]);
+          double g;
+          if (flags & ORACLE_GATE_GIVEN)
+            g = rg < lower_bound ? lower_bound : (rg > 0.0 ? 0.0 : rg);
+          else
+            g = lower_bound * sigmoid(gate_mul * (rg + (double)dt_bias[h * K + c]));
+          alpha[c] = exp(g);
         }
         /* decay: S <- Diag(alpha) S */
         for (int64_t c = 0; c < K; ++c)
@@ -136,7 +161,9 @@ int kda_oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
         for (int64_t j = 0; j < V; ++j) out[(t * n_heads + hi) * V + j] = scale * acc[j];
       }
       if (final_state)
-        for (int64_t i = 0; i < K * V; ++i) final_state[(n * n_heads + hi) * K * V + i] = S[i];
+        for (int64_t c = 0; c < K; ++c)
+          for (int64_t j = 0; j < V; ++j)
+            final_state[(n * n_heads + hi) * K * V + (vk ? j * K + c : c * V + j)] = S[c * V + j];
     }
     free(S); free(qh); free(kh); free(alpha); free(delta); free(acc);
   }

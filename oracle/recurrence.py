@@ -34,7 +34,8 @@ def _lib():
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         lib.kda_oracle_fwd.argtypes = [P, P, P, P, P, ctypes.c_double, P, P, ctypes.c_double,
-                                       P, P, I64, I64, I64, I64, I64, P, I64, P, P, ctypes.c_int]
+                                       P, P, I64, I64, I64, I64, I64, P, I64, P, P, ctypes.c_int,
+                                       ctypes.c_int]
         lib.kda_oracle_fwd.restype = ctypes.c_int
         lib.kda_oracle_threads.restype = ctypes.c_int
         _LIB = lib
@@ -57,10 +58,18 @@ def _f32(t) -> np.ndarray:
     return np.ascontiguousarray(t, dtype=np.float32)
 
 
+# variant bits (the chunk_kda in-kernel switches on the instagit FlashKDA page)
+GATE_GIVEN, BETA_GIVEN, NO_QK_NORM, STATE_VK = 1, 2, 4, 8
+
+
 def oracle_fwd(q, k, v, raw_gate, raw_beta, scale, A_log, dt_bias, lower_bound,
                initial_state=None, cu_seqlens=None, heads=None, threads: int = 0,
-               want_final: bool = True):
+               want_final: bool = True, flags: int = 0):
     """Run the fp64 recurrence.
+
+    flags: GATE_GIVEN (raw_gate holds the log-decay g, clamped to
+    [lower_bound, 0]), BETA_GIVEN (raw_beta holds beta), NO_QK_NORM (no L2
+    norm of q, k), STATE_VK (states stored transposed, [N, H, V, K]).
 
     q, k, raw_gate: bf16 [B, T, H, K]; v: bf16 [B, T, H, V]; raw_beta: bf16 [B, T, H];
     A_log fp32 [H]; dt_bias fp32 [H, K]; initial_state fp32 [N, H, K, V] or None;
@@ -90,7 +99,8 @@ def oracle_fwd(q, k, v, raw_gate, raw_beta, scale, A_log, dt_bias, lower_bound,
     ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
     rc = _lib().kda_oracle_fwd(ptr(qb), ptr(kb), ptr(vb), ptr(gb), ptr(bb), float(scale),
                                ptr(al), ptr(dt), float(lower_bound), ptr(init), ptr(cu),
-                               N, B * T, H, K, V, ptr(hs), nh, ptr(out), ptr(fin), int(threads))
+                               N, B * T, H, K, V, ptr(hs), nh, ptr(out), ptr(fin), int(threads),
+                               int(flags))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return out, fin

@@ -177,3 +177,21 @@ def test_decode_checks():
     assert decode_call(scale=float("nan")) == INVALID
     assert decode_call(K=64, V=64) == UNSUPPORTED
     assert decode_call(lb=0.5) == UNSUPPORTED
+
+
+def fwd_ex_call(flags, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, scale=0.088, out=FAKE, ws=FAKE, ws_bytes=1 << 40,
+             A_log=FAKE, dt=FAKE, lb=-5.0, init=None, fin=None, cu=None, B=1, T=64, H=2, K=128, V=128, N=1)
+    a.update(over)
+    return kda._lib.kda_fwd_ex(a["q"], a["k"], a["v"], a["g"], a["b"], ctypes.c_float(a["scale"]), a["out"],
+                               a["ws"], a["ws_bytes"], a["A_log"], a["dt"], ctypes.c_float(a["lb"]), a["init"],
+                               a["fin"], a["cu"], a["B"], a["T"], a["H"], a["K"], a["V"], a["N"], flags, None)
+
+
+def test_fwd_ex_flag_checks():
+    assert fwd_ex_call(16) == INVALID                     # unknown bit
+    assert fwd_ex_call(1 << 31) == INVALID
+    assert fwd_ex_call(0, A_log=None) == INVALID          # gate parameters needed without GATE_GIVEN
+    assert fwd_ex_call(kda.FLAG_BETA_GIVEN, dt=None) == INVALID
+    assert fwd_ex_call(kda.FLAG_GATE_GIVEN, K=64, V=64, A_log=None, dt=None) == UNSUPPORTED
+    assert fwd_ex_call(kda.FLAG_STATE_VK, ws_bytes=8) == WORKSPACE
