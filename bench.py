@@ -124,9 +124,10 @@ def write_traffic(fwd_fetch, fwd_write, copy_fetch, copy_write, copy_bytes=2 << 
     for path, counter, fac, key in ((fwd_fetch, "FETCH_SIZE", ff, "read_bytes"),
                                     (fwd_write, "WRITE_SIZE", wf, "write_bytes")):
         for name, ks in per_kernel(path, counter).items():
-            if not name.startswith("kda::"):
+            m = re.search(r"(kda_\w+_kernel)", name)
+            if not m:
                 continue
-            short = re.search(r"(kda_\w+_kernel)", name).group(1)
+            short = m.group(1)
             kernels.setdefault(short, {})[key] = sum(ks) / len(ks) * 1024.0 * fac
     total = sum(v.get("read_bytes", 0.0) + v.get("write_bytes", 0.0) for v in kernels.values())
     doc = {"workload": "kda_fwd B=1 T=32768 H=96 K=V=128 (bench.py defaults)",
