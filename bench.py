@@ -232,6 +232,51 @@ def bench_decode(args):
     }), flush=True)
 
 
+def bench_bwd(args):
+    """Backward pass (kda_bwd: the gradients of every input) on the headline
+    workload, for a bf16 N(0,1) output gradient and an fp32 N(0,1) final-state
+    gradient.  Roofline view: the algorithmic HBM bytes of the call are the
+    inputs q, k, v, raw_gate, d_out (5 x 128 x 2 B per head-token) and raw_beta
+    (2 B), the outputs dq, dk, dv, d_raw_gate (4 x 128 x 2 B) and d_raw_beta
+    (2 B), plus the initial state, final-state gradient and initial-state
+    gradient (3 x 64 KiB fp32 per (sequence, head))."""
+    import torch
+
+    import chunked_gated_delta_amd as kda
+    import workloads
+
+    x = workloads.c3_headline(T=args.T, H=args.H)
+    x.initial_state = torch.zeros(1, x.H, x.K, x.V, dtype=torch.float32)
+    dev = torch.device("cuda:0")
+    d = lambda t: t.to(dev)  # noqa: E731
+    q, k, v, g, b, al, dt, init = (d(t) for t in (x.q, x.k, x.v, x.raw_gate, x.raw_beta, x.A_log, x.dt_bias,
+                                                  x.initial_state))
+    gen = torch.Generator().manual_seed(9)
+    d_out = d(torch.randn(1, x.T, x.H, x.V, generator=gen).to(torch.bfloat16))
+    d_fin = d(torch.randn(1, x.H, x.K, x.V, generator=gen))
+    dq, dk, dg = torch.empty_like(q), torch.empty_like(k), torch.empty_like(g)
+    dv, db = torch.empty_like(v), torch.empty_like(b)
+    dA, ddt, dinit = torch.empty_like(al), torch.empty_like(dt), torch.empty_like(init)
+    ws = torch.empty(kda.kda_bwd_workspace_size(x.T, x.H, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    ms = timed(lambda: kda.kda_bwd(q, k, v, g, b, x.scale, d_out, dq, dk, dv, dg, db, dA, ddt, ws, al, dt,
+                                   x.lower_bound, initial_state=init, d_final=d_fin, d_initial_state=dinit,
+                                   stream=sh), args.steps, args.warmup, stream)
+    ht = x.T * x.H
+    alg = ht * (9 * 128 * 2 + 2 * 2) + 3 * x.H * STATE_BYTES
+    gbs = alg / (ms / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "KDA backward (all input gradients) head-tokens/s", "value": ht / (ms / 1e3),
+        "unit": "head-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "dtype": "fp32 compute, bf16 io", "data": "synthetic",
+        "config": {"workload": f"kda_bwd B=1 T={x.T} H={x.H} K=V=128 chunk=64 lower_bound=-5, "
+                               "output and final-state gradients given"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +289,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--decode", type=int, default=0,
                     help="time the decode step for this many sequences (T=1) instead")
+    ap.add_argument("--bwd", action="store_true", help="time the backward pass (kda_bwd) instead")
     ap.add_argument("--kcp-shards", type=int, default=0,
                     help="time the split-sequence path with this many shards instead")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FWD_FETCH", "FWD_WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -266,6 +312,9 @@ def main():
         return
     if args.decode:
         bench_decode(args)
+        return
+    if args.bwd:
+        bench_bwd(args)
         return
 
     import torch

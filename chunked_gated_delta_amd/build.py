@@ -5,7 +5,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kda_api.hip", "kda_intra.hip", "kda_inter.hip", "kda_kcp.hip", "kda_decode.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kda_api.hip", "kda_intra.hip", "kda_inter.hip", "kda_kcp.hip", "kda_decode.hip", "kda_bwd.hip")]
 LIB = os.path.join(HERE, "libkda.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

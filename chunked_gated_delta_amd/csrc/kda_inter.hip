@@ -151,8 +151,9 @@ __device__ __forceinline__ void store_vt(__bf16* sVt, const uint4 (&vv)[2], int 
 
 // HAS_V = false runs the recurrence with V = 0 (the homogeneous part of the
 // chunk map, used for the per-shard affine map); WRITE_OUT = false computes
-// only the final state.
-template <bool HAS_V, bool WRITE_OUT>
+// only the final state; CKPT also stores every chunk's entering state and its
+// D tile for the backward pass.
+template <bool HAS_V, bool WRITE_OUT, bool CKPT = false>
 __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   __bf16* sVt = reinterpret_cast<__bf16*>(smem + OFF_VT);
@@ -255,6 +256,16 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     __builtin_amdgcn_sched_barrier(0);    \
   } while (0)
     uint4 vn[2];
+    if constexpr (CKPT) {
+      float* dst = a.states + ((size_t)gch * H + h) * KD * VD;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nn = 0; nn < 4; ++nn)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+            dst[(32 * w + 16 * mt + 4 * gq + ii) * VD + vs + 16 * nn + tl] = S[mt][nn][ii];
+    }
     if constexpr (HAS_V) KDA_ISSUE(load_v(vn, a.v, in1 ? c1 : c0, in1 ? chunk_len(c1) : L, H, h, vs, tid));
     KDA_ISSUE((load_ops<0, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
     KDA_TIMER_MARK(1);
@@ -285,6 +296,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
         if constexpr (WRITE_OUT) o = mfma_f16(cur.qg[kb], sb, o);
       }
       O[nn] = o;
+      if constexpr (CKPT) {
+        float* dst = a.dtile + ((size_t)gch * H + h) * CH * VD;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int i = 16 * w + 4 * gq + ii;
+          dst[i * VD + vs + col] = i < L ? u[ii] : 0.0f;
+        }
+      }
       // D^T hi/lo: lane holds tokens 16w + 4gq + 0..3 of column col
       f16x4 dh, dl;
 #pragma unroll
@@ -395,7 +414,9 @@ hipError_t launch_inter(const InterArgs& args, hipStream_t st) {
   InterArgs a = args;
   void* kargs[] = {(void*)&a};
   const void* fn;
-  if (a.v)
+  if (a.states)
+    fn = reinterpret_cast<const void*>(&kda_inter_kernel<true, false, true>);
+  else if (a.v)
     fn = a.out ? reinterpret_cast<const void*>(&kda_inter_kernel<true, true>)
                : reinterpret_cast<const void*>(&kda_inter_kernel<true, false>);
   else

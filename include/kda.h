@@ -206,6 +206,50 @@ kda_status_t kda_fwd_ex(const void* q, const void* k, const void* v, const void*
                         const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H, int64_t K,
                         int64_t V, int64_t N, unsigned flags, void* stream);
 
+/*
+ * Bytes of device workspace kda_bwd needs for T_total packed tokens, H heads
+ * and N sequences (more than kda_workspace_size: the backward keeps fp32
+ * per-chunk states, state gradients and chunk factors).  Returns 0 if any
+ * argument is < 1 (T_total may be 0).
+ */
+size_t kda_bwd_workspace_size(int64_t T_total, int64_t H, int64_t N);
+
+/*
+ * Gradients of kda_fwd.  The torchtitan page "[Kimi K3] allow KDA using inline
+ * Attention Gym reference eager implementation ..." (section "Results") runs
+ * the KDA kernel's forward and gradient against packed-versus-separate
+ * documents; the pages print no backward algorithm.  This computes the exact
+ * gradient of
+ *     loss = <d_out, out> + <d_final, final_state>
+ * of the kda_fwd call with the same inputs (flags 0), with respect to every
+ * input, by reverse-mode differentiation of the chunked algebra (fp32
+ * arithmetic; the forward states it needs are recomputed inside the call).
+ *
+ *   q, k, v, raw_gate, raw_beta, scale, A_log, dt_bias, lower_bound,
+ *   initial_state, cu_seqlens, B, T, H, K, V, N   exactly as for kda_fwd
+ *                (A_log and dt_bias are required)
+ *   d_out        bf16 [B, T, H, V]   gradient of out
+ *   d_final      fp32 [N, H, K, V]   gradient of final_state, or NULL for zero
+ *   dq, dk       bf16 [B, T, H, K]   written
+ *   dv           bf16 [B, T, H, V]   written
+ *   d_raw_gate   bf16 [B, T, H, K]   written
+ *   d_raw_beta   bf16 [B, T, H]      written
+ *   dA_log       fp32 [H]            written
+ *   d_dt_bias    fp32 [H, K]         written
+ *   d_initial_state fp32 [N, H, K, V] written, or NULL to skip; may equal d_final
+ *   workspace    device scratch of >= kda_bwd_workspace_size(B*T, H, N) bytes
+ *
+ * Outputs must not overlap the inputs or each other (except as stated).
+ * Same errors as kda_fwd; KDA_ERR_INVALID also for a NULL required output.
+ */
+kda_status_t kda_bwd(const void* q, const void* k, const void* v, const void* raw_gate,
+                     const void* raw_beta, float scale, const void* d_out, const float* d_final,
+                     void* dq, void* dk, void* dv, void* d_raw_gate, void* d_raw_beta, float* dA_log,
+                     float* d_dt_bias, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                     const float* A_log, const float* dt_bias, float lower_bound,
+                     const float* initial_state, const int32_t* cu_seqlens, int64_t B, int64_t T,
+                     int64_t H, int64_t K, int64_t V, int64_t N, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* kda_status_string(kda_status_t status);
 

@@ -195,3 +195,40 @@ def test_fwd_ex_flag_checks():
     assert fwd_ex_call(kda.FLAG_BETA_GIVEN, dt=None) == INVALID
     assert fwd_ex_call(kda.FLAG_GATE_GIVEN, K=64, V=64, A_log=None, dt=None) == UNSUPPORTED
     assert fwd_ex_call(kda.FLAG_STATE_VK, ws_bytes=8) == WORKSPACE
+
+
+def bwd_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, scale=0.088, dout=FAKE, dfin=None, dq=FAKE, dk=FAKE,
+             dv=FAKE, dg=FAKE, db=FAKE, dA=FAKE, ddt=FAKE, dinit=None, ws=FAKE, ws_bytes=1 << 40, A_log=FAKE,
+             dt=FAKE, lb=-5.0, init=None, cu=None, B=1, T=64, H=2, K=128, V=128, N=1)
+    a.update(over)
+    return kda._lib.kda_bwd(a["q"], a["k"], a["v"], a["g"], a["b"], ctypes.c_float(a["scale"]), a["dout"],
+                            a["dfin"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dA"], a["ddt"], a["dinit"],
+                            a["ws"], a["ws_bytes"], a["A_log"], a["dt"], ctypes.c_float(a["lb"]), a["init"],
+                            a["cu"], a["B"], a["T"], a["H"], a["K"], a["V"], a["N"], None)
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "g", "b", "dout", "dq", "dk", "dv", "dg", "db", "dA", "ddt",
+                                   "A_log", "dt"])
+def test_bwd_null_pointer_is_invalid(field):
+    assert bwd_call(**{field: None}) == INVALID
+
+
+def test_bwd_checks():
+    assert bwd_call(B=0) == INVALID
+    assert bwd_call(T=-1) == INVALID
+    assert bwd_call(scale=float("nan")) == INVALID
+    assert bwd_call(B=2, N=1) == INVALID                    # N must equal B without cu_seqlens
+    assert bwd_call(K=64, V=64) == UNSUPPORTED
+    assert bwd_call(lb=-6.0) == UNSUPPORTED
+    assert bwd_call(ws=None) == WORKSPACE
+    need = kda.kda_bwd_workspace_size(64, 2, 1)
+    assert bwd_call(ws_bytes=need - 1) == WORKSPACE
+    assert need > kda.kda_workspace_size(64, 2, 1)
+
+
+def test_bwd_workspace_size():
+    assert kda.kda_bwd_workspace_size(0, 2, 1) > 0
+    assert kda.kda_bwd_workspace_size(10, 0, 1) == 0
+    assert kda.kda_bwd_workspace_size(10, 2, 0) == 0
+    assert kda.kda_bwd_workspace_size(32768, 96, 1) > 20 * 10 ** 9 // 2

@@ -1,0 +1,175 @@
+"""Parity of kda_bwd (through the C ABI) against the fp64 gradient oracle.
+
+The oracle is torch autograd through the fp64 token recurrence
+(oracle/grad.py) at small sizes, and the chunked fp64 reverse-mode form
+(oracle/chunked.py, pinned to it) where the token loop's graph would not fit.
+Tolerance, per gradient: relative L2 <= 1e-2 and max-abs error <= 2e-2 of the
+reference's largest magnitude, all values finite.  Why 1e-2: the gradients
+are written in bf16 (relative rounding 2^-9) and the forward states they use
+come from the forward's fp16/bf16 operands (relative ~1e-3), so the expected
+error is a few 1e-3; the forward's own output bar is the same 1e-2.
+The varlen property test follows the torchtitan page's packed-versus-separate
+documents check ("Results": forward and gradient).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_gated_delta_amd as kda
+import workloads as W
+from oracle.chunked import chunked_bwd
+from oracle.grad import oracle_bwd
+
+pytestmark = pytest.mark.gpu
+
+REL, MAXREL = 1e-2, 2e-2
+DEV = "cuda:0"
+NAMES = ("dq", "dk", "dv", "d_raw_gate", "d_raw_beta", "dA_log", "d_dt_bias", "d_initial_state")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def d(t):
+    return None if t is None else t.to(DEV)
+
+
+def cotangents(x, seed, with_final=True):
+    g = torch.Generator().manual_seed(seed)
+    d_out = torch.randn(x.B, x.T, x.H, x.V, generator=g).to(torch.bfloat16)
+    d_fin = torch.randn(x.N, x.H, x.K, x.V, generator=g) if with_final else None
+    return d_out, d_fin
+
+
+def gpu_bwd(x, d_out, d_fin, with_dinit=True):
+    """Returns a dict of fp64 numpy gradients shaped like oracle_bwd's."""
+    B, T, H, K, V, N = x.B, x.T, x.H, x.K, x.V, x.N
+    nan_bf = lambda *s: torch.full(s, float("nan"), dtype=torch.bfloat16, device=DEV)  # noqa: E731
+    dq, dk, dg = nan_bf(B, T, H, K), nan_bf(B, T, H, K), nan_bf(B, T, H, K)
+    dv, db = nan_bf(B, T, H, V), nan_bf(B, T, H)
+    dA = torch.full((H,), float("nan"), device=DEV)
+    ddt = torch.full((H, K), float("nan"), device=DEV)
+    dinit = torch.full((N, H, K, V), float("nan"), device=DEV) if with_dinit else None
+    ws = torch.empty(kda.kda_bwd_workspace_size(B * T, H, N), dtype=torch.uint8, device=DEV)
+    print(f"kda_bwd {x.name} B={B} T={T} H={H} N={N}", flush=True)
+    kda.kda_bwd(d(x.q), d(x.k), d(x.v), d(x.raw_gate), d(x.raw_beta), x.scale, d(d_out), dq, dk, dv, dg, db,
+                dA, ddt, ws, d(x.A_log), d(x.dt_bias), x.lower_bound, initial_state=d(x.initial_state),
+                d_final=d(d_fin), d_initial_state=dinit, cu_seqlens=d(x.cu_seqlens))
+    torch.cuda.synchronize()
+    f = lambda t, *s: t.double().cpu().numpy().reshape(*s)  # noqa: E731
+    return {"dq": f(dq, B * T, H, K), "dk": f(dk, B * T, H, K), "dv": f(dv, B * T, H, V),
+            "d_raw_gate": f(dg, B * T, H, K), "d_raw_beta": f(db, B * T, H), "dA_log": f(dA, H),
+            "d_dt_bias": f(ddt, H, K), "d_initial_state": None if dinit is None else f(dinit, N, H, K, V)}
+
+
+def compare(got, ref, names=NAMES):
+    for n in names:
+        if ref.get(n) is None or got.get(n) is None:
+            continue
+        r, g = np.asarray(ref[n], dtype=np.float64), np.asarray(got[n], dtype=np.float64)
+        assert np.isfinite(g).all(), (n, "non-finite")
+        if r.size == 0:
+            continue
+        scale_ = max(np.linalg.norm(r), 1e-30)
+        rel = np.linalg.norm(g - r) / scale_
+        mx = np.abs(g - r).max() / max(np.abs(r).max(), 1e-30)
+        print(f"  {n}: rel_l2 {rel:.2e} max/maxref {mx:.2e}", flush=True)
+        assert rel <= REL and mx <= MAXREL, (n, rel, mx)
+
+
+def oracle(x, d_out, d_fin, chunked=False):
+    fn = chunked_bwd if chunked else oracle_bwd
+    return fn(x.q, x.k, x.v, x.raw_gate, x.raw_beta, x.scale, x.A_log, x.dt_bias, x.lower_bound,
+              d_out.double(), None if d_fin is None else d_fin.double(), x.initial_state, x.cu_seqlens)
+
+
+def test_bwd_one_tail_chunk():
+    x = W.random_inputs("bwd_T40", 201, 1, 40, 2)
+    d_out, d_fin = cotangents(x, 1)
+    compare(gpu_bwd(x, d_out, d_fin), oracle(x, d_out, d_fin))
+
+
+def test_bwd_reference_case_c1():
+    """3 full chunks and an 8-token tail, zero initial state, A_log = dt_bias = 0."""
+    x = W.c1_ref()
+    d_out, d_fin = cotangents(x, 2)
+    compare(gpu_bwd(x, d_out, d_fin, with_dinit=False), oracle(x, d_out, d_fin))
+
+
+def test_bwd_batch_with_state_and_no_final_gradient():
+    x = W.random_inputs("bwd_B2_T130", 202, 2, 130, 3)
+    d_out, _ = cotangents(x, 3, with_final=False)
+    compare(gpu_bwd(x, d_out, None), oracle(x, d_out, None))
+
+
+def test_bwd_varlen_with_empty_and_ragged_sequences():
+    lengths = [1, 0, 64, 70, 5, 0, 129]
+    x = W.random_inputs("bwd_varlen", 203, 1, sum(lengths), 2, lengths=lengths)
+    d_out, d_fin = cotangents(x, 4)
+    compare(gpu_bwd(x, d_out, d_fin), oracle(x, d_out, d_fin))
+
+
+def test_bwd_strong_decay_and_gate_parameters():
+    """A_log at ln 16 everywhere: most channels decay near the floor (exp(-5) per token)."""
+    x = W.random_inputs("bwd_decay", 204, 1, 192, 2, dt_bias_std=1.0)
+    x.A_log.fill_(float(np.log(16.0)))
+    d_out, d_fin = cotangents(x, 5)
+    compare(gpu_bwd(x, d_out, d_fin), oracle(x, d_out, d_fin))
+
+
+def test_bwd_tp_share_c2_sampled_heads():
+    """B=2, T=4096, H=12 on the GPU; heads 0 and 7 checked against the chunked fp64 backward."""
+    x = W.c2_tp_share()
+    d_out, d_fin = cotangents(x, 6)
+    got = gpu_bwd(x, d_out, d_fin)
+    for h in (0, 7):
+        xs = W.KdaInputs(name=f"c2_head{h}", q=x.q[:, :, h:h + 1].contiguous(), k=x.k[:, :, h:h + 1].contiguous(),
+                         v=x.v[:, :, h:h + 1].contiguous(), raw_gate=x.raw_gate[:, :, h:h + 1].contiguous(),
+                         raw_beta=x.raw_beta[:, :, h:h + 1].contiguous(), A_log=x.A_log[h:h + 1].contiguous(),
+                         dt_bias=x.dt_bias[h:h + 1].contiguous(),
+                         initial_state=x.initial_state[:, h:h + 1].contiguous(), cu_seqlens=None,
+                         scale=x.scale, lower_bound=x.lower_bound)
+        ref = oracle(xs, d_out[:, :, h:h + 1].contiguous(), d_fin[:, h:h + 1].contiguous(), chunked=True)
+        sub = {n: (None if got[n] is None else got[n][:, h:h + 1] if n in ("dq", "dk", "dv", "d_raw_gate",
+                                                                             "d_raw_beta", "d_initial_state")
+                   else got[n][h:h + 1]) for n in NAMES}
+        compare(sub, ref)
+
+
+def test_bwd_packed_equals_separate_documents():
+    """Gradients of a packed varlen call equal those of each document run alone (GPU vs GPU)."""
+    lengths = [300, 64, 1, 257]
+    x = W.random_inputs("bwd_pack", 205, 1, sum(lengths), 3, lengths=lengths)
+    d_out, d_fin = cotangents(x, 7)
+    packed = gpu_bwd(x, d_out, d_fin)
+    cu = [0] + list(np.cumsum(lengths))
+    dA_sum = np.zeros(x.H)
+    ddt_sum = np.zeros((x.H, x.K))
+    for n, (s, e) in enumerate(zip(cu[:-1], cu[1:])):
+        xs = W.KdaInputs(name=f"doc{n}", q=x.q[:, s:e].contiguous(), k=x.k[:, s:e].contiguous(),
+                         v=x.v[:, s:e].contiguous(), raw_gate=x.raw_gate[:, s:e].contiguous(),
+                         raw_beta=x.raw_beta[:, s:e].contiguous(), A_log=x.A_log, dt_bias=x.dt_bias,
+                         initial_state=x.initial_state[n:n + 1].contiguous(), cu_seqlens=None,
+                         scale=x.scale, lower_bound=x.lower_bound)
+        one = gpu_bwd(xs, d_out[:, s:e].contiguous(), d_fin[n:n + 1].contiguous())
+        for name in ("dq", "dk", "dv", "d_raw_gate", "d_raw_beta"):
+            np.testing.assert_allclose(packed[name][s:e], one[name], rtol=1e-2, atol=1e-2, err_msg=name)
+        np.testing.assert_allclose(packed["d_initial_state"][n], one["d_initial_state"][0], rtol=1e-4,
+                                   atol=1e-5)
+        dA_sum += one["dA_log"]
+        ddt_sum += one["d_dt_bias"]
+    np.testing.assert_allclose(packed["dA_log"], dA_sum, rtol=1e-3, atol=1e-3)
+    np.testing.assert_allclose(packed["d_dt_bias"], ddt_sum, rtol=1e-3, atol=1e-3)
+
+
+def test_bwd_zero_tokens():
+    x = W.random_inputs("bwd_empty", 206, 1, 0, 2)
+    d_out, d_fin = cotangents(x, 8)
+    got = gpu_bwd(x, d_out, d_fin)
+    np.testing.assert_array_equal(got["dA_log"], 0.0)
+    np.testing.assert_array_equal(got["d_dt_bias"], 0.0)
+    np.testing.assert_array_equal(got["d_initial_state"], d_fin.double().numpy())
