@@ -379,6 +379,11 @@ kda_status_t kda_bwd(const void* q, const void* k, const void* v, const void* ra
   ba.H = (int)H;
   ba.scale = scale;
   ba.lb = lower_bound;
+  ba.timers = nullptr;
+#ifdef KDA_PHASE_TIMERS
+  // timer builds only: 16 counters per workgroup of each backward kernel after the workspace
+  ba.timers = reinterpret_cast<unsigned long long*>(pr.ws + bl.total);
+#endif
   return launch_status(launch_bwd(ba, pr.max_chunks, st), "backward");
 }
 

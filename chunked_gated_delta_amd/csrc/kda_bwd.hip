@@ -40,16 +40,25 @@ constexpr int MP = CH + 4;  // pitch of [64][64] LDS tiles
 constexpr int VH = VD / 2;  // state columns per recurrence workgroup
 constexpr int DP = VH + 4;  // pitch of the recurrence kernel's LDS tiles
 
-// fp32 chunk record of the backward (offsets in floats)
-constexpr int BR_T = 0;                   // T = (I + diag(beta) KK)^-1, unit lower [64][64]
-constexpr int BR_KK = BR_T + CH * CH;     // KK = K^ K^T . decay, strictly lower     [64][64]
-constexpr int BR_AQK = BR_KK + CH * CH;   // A_qk, lower incl. diagonal              [64][64]
-constexpr int BR_W = BR_AQK + CH * CH;    // W = Tb KG                               [64][128]
-constexpr int BR_KT = BR_W + CH * KD;     // Kt = K^ exp(G_L - G)                    [64][128]
-constexpr int BR_QG = BR_KT + CH * KD;    // QG = Q^ exp(G)                          [64][128]
-constexpr int BR_GL = BR_QG + CH * KD;    // exp(G_L)                                [128]
-constexpr int BR_BETA = BR_GL + KD;       // beta                                    [64]
+// fp32 chunk record of the backward (offsets in floats).  The operands of the
+// reverse recurrence are stored in fp32 A-operand fragment order (frag32).
+constexpr int BR_T = 0;                   // T = (I + diag(beta) KK)^-1, unit lower, [64][64] row-major
+constexpr int BR_KK = BR_T + CH * CH;     // KK = K^ K^T . decay, strictly lower,     [64][64] row-major
+constexpr int BR_AQKT = BR_KK + CH * CH;  // A operand A_qk^T (rows i, contraction j), frag32
+constexpr int BR_WT = BR_AQKT + CH * CH;  // A operand W^T  (rows k, contraction i),   frag32
+constexpr int BR_KT = BR_WT + CH * KD;    // A operand Kt = K^ exp(G_L - G) (rows i, contraction k), frag32
+constexpr int BR_QGT = BR_KT + CH * KD;   // A operand QG^T = (Q^ exp(G))^T (rows k, contraction i), frag32
+constexpr int BR_GL = BR_QGT + CH * KD;   // exp(G_L)                                 [128]
+constexpr int BR_BETA = BR_GL + KD;       // beta                                     [64]
 static_assert(BR_BETA + CH == BWD_REC_FLOATS, "record size");
+
+// fp32 A-operand fragment order: element (r, kap) of an A operand with C
+// contraction columns lies in 16 x 16 tile (r / 16, kap / 16); inside it, lane
+// 16 ((kap / 4) % 4) + r % 16 holds kap % 4 of one float4, so one wave-wide
+// float4 load of a tile reads 1 KB of contiguous memory.
+__host__ __device__ constexpr int frag32(int r, int kap, int C) {
+  return ((((r >> 4) * (C >> 4) + (kap >> 4)) * 64 + ((kap >> 2) & 3) * 16 + (r & 15)) << 2) + (kap & 3);
+}
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
@@ -74,18 +83,22 @@ __device__ __forceinline__ void chunk_of(const ChunkMap& m, int64_t gch, int64_t
 
 // Per-token preparation of one chunk into LDS: q^, k^ (rows past the end are
 // zero), G = cumulative log2-decay (constant past the end), beta, the row
-// norms of q and k.  Thread t handles token t / 4 and channels 32 (t % 4)...
+// norms of q and k.  NTH threads: NTH / 64 per token, KD / (NTH / 64) channels
+// each.  sTmp needs NTH floats.
+template <int NTH>
 __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQn, float* sKn, float* sG,
                            float* sBeta, float* sRq, float* sRk, float* sTmp) {
+  constexpr int TPR = NTH / CH;  // threads per token
+  constexpr int CPT = KD / TPR;  // channels per thread
   const int t = threadIdx.x;
-  const int i = t >> 2;
-  const int cq = t & 3;
+  const int i = t / TPR;
+  const int part = t % TPR;
   const bool ok = i < L;
   const int64_t row = c0 + (ok ? i : L - 1);  // L >= 1: the clamped row is in range
-  const size_t base = ((size_t)row * a.H + h) * KD + 32 * cq;
-  float qv[32], kv[32], gv[32];
+  const size_t base = ((size_t)row * a.H + h) * KD + CPT * part;
+  float qv[CPT], kv[CPT], gv[CPT];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < CPT / 8; ++u) {
     float tq[8], tk[8], tg[8];
     unpack_bf16x8(reinterpret_cast<const uint4*>(a.q + base)[u], tq);
     unpack_bf16x8(reinterpret_cast<const uint4*>(a.k + base)[u], tk);
@@ -99,51 +112,58 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
   }
   float sq = 0.f, sk = 0.f;
 #pragma unroll
-  for (int c = 0; c < 32; ++c) {
+  for (int c = 0; c < CPT; ++c) {
     sq += qv[c] * qv[c];
     sk += kv[c] * kv[c];
   }
-  sq += __shfl_xor(sq, 1);
-  sq += __shfl_xor(sq, 2);
-  sk += __shfl_xor(sk, 1);
-  sk += __shfl_xor(sk, 2);
+#pragma unroll
+  for (int d = 1; d < TPR; d <<= 1) {
+    sq += __shfl_xor(sq, d);
+    sk += __shfl_xor(sk, d);
+  }
   const float rq = sqrtf(sq + L2_EPS), rk = sqrtf(sk + L2_EPS);
   const float iq = ok ? 1.0f / rq : 0.f, ik = ok ? 1.0f / rk : 0.f;
   const float al = expf(a.A_log[h]);
-  const float* dtb = a.dt_bias + (size_t)h * KD + 32 * cq;
+  const float* dtb = a.dt_bias + (size_t)h * KD + CPT * part;
 #pragma unroll
-  for (int c = 0; c < 32; c += 4) {
-    float4 qo, ko, go;
+  for (int c = 0; c < CPT; c += 4) {
     float gg[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) gg[e] = ok ? a.lb * sigmoidf(al * (gv[c + e] + dtb[c + e])) * LOG2E : 0.f;
-    qo = make_float4(qv[c] * iq, qv[c + 1] * iq, qv[c + 2] * iq, qv[c + 3] * iq);
-    ko = make_float4(kv[c] * ik, kv[c + 1] * ik, kv[c + 2] * ik, kv[c + 3] * ik);
-    go = make_float4(gg[0], gg[1], gg[2], gg[3]);
-    *reinterpret_cast<float4*>(sQn + i * QP + 32 * cq + c) = qo;
-    *reinterpret_cast<float4*>(sKn + i * QP + 32 * cq + c) = ko;
-    *reinterpret_cast<float4*>(sG + i * QP + 32 * cq + c) = go;
+    *reinterpret_cast<float4*>(sQn + i * QP + CPT * part + c) =
+        make_float4(qv[c] * iq, qv[c + 1] * iq, qv[c + 2] * iq, qv[c + 3] * iq);
+    *reinterpret_cast<float4*>(sKn + i * QP + CPT * part + c) =
+        make_float4(kv[c] * ik, kv[c + 1] * ik, kv[c + 2] * ik, kv[c + 3] * ik);
+    *reinterpret_cast<float4*>(sG + i * QP + CPT * part + c) = make_float4(gg[0], gg[1], gg[2], gg[3]);
   }
-  if (cq == 0) {
+  if (part == 0) {
     sBeta[i] = ok ? sigmoidf(bf2f(a.beta[(size_t)row * a.H + h])) : 0.f;
     sRq[i] = rq;
     sRk[i] = rk;
   }
   __syncthreads();
-  // inclusive cumulative sum over the 64 tokens: thread -> channel t % 128, half t / 128
+  // inclusive cumulative sum over the 64 tokens: thread -> channel t % 128,
+  // segment t / 128 of 64 / (NTH / 128) tokens
   {
-    const int c = t & 127;
-    const int hf = t >> 7;
+    constexpr int NSEG = NTH / KD;
+    constexpr int RS = CH / NSEG;
+    const int c = t % KD;
+    const int sg = t / KD;
     float run = 0.f;
-    for (int r = 32 * hf; r < 32 * hf + 32; ++r) {
+#pragma unroll 4
+    for (int r = RS * sg; r < RS * sg + RS; ++r) {
       run += sG[r * QP + c];
       sG[r * QP + c] = run;
     }
-    if (hf == 0) sTmp[c] = run;
+    sTmp[sg * KD + c] = run;
     __syncthreads();
-    if (hf == 1) {
-      const float off = sTmp[c];
-      for (int r = 32; r < 64; ++r) sG[r * QP + c] += off;
+    float off = 0.f;
+#pragma unroll
+    for (int u = 0; u < NSEG; ++u)
+      if (u < sg) off += sTmp[u * KD + c];
+    if (sg > 0) {
+#pragma unroll 4
+      for (int r = RS * sg; r < RS * sg + RS; ++r) sG[r * QP + c] += off;
     }
   }
   __syncthreads();
@@ -176,7 +196,7 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_prep_kernel(BwdArgs a) {
   chunk_of(a.map, gch, c0, L);
   float* br = a.br + (size_t)blockIdx.x * BWD_REC_FLOATS;
 
-  prep_chunk(a, c0, L, h, sQn, sKn, sG, sBeta, sRq, sRk, sTmp);
+  prep_chunk<NT>(a, c0, L, h, sQn, sKn, sG, sBeta, sRq, sRk, sTmp);
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -195,8 +215,10 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_prep_kernel(BwdArgs a) {
         sKK[i * MP + j] = 0.f;
         sAQ[i * MP + j] = 0.f;
         br[BR_KK + i * CH + j] = 0.f;
-        br[BR_AQK + i * CH + j] = 0.f;
       }
+      // A_qk^T tile (rows block b, contraction block w) is above the diagonal: zero
+      *reinterpret_cast<float4*>(br + BR_AQKT + frag32(16 * b + tl, 16 * w + 4 * gq, CH)) =
+          make_float4(0.f, 0.f, 0.f, 0.f);
       continue;
     }
     const int r = (b < w) ? 16 * b + 15 : 16 * w;
@@ -216,6 +238,7 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_prep_kernel(BwdArgs a) {
         aq = mfma_f32(el(qx, s) * fx, yb, aq);
       }
     }
+    float qk4[4];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int i = 16 * w + 4 * gq + ii, j = 16 * b + tl;
@@ -224,8 +247,11 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_prep_kernel(BwdArgs a) {
       sKK[i * MP + j] = kk;
       sAQ[i * MP + j] = qk;
       br[BR_KK + i * CH + j] = kk;
-      br[BR_AQK + i * CH + j] = qk;
+      qk4[ii] = qk;
     }
+    // A_qk^T[j][i]: rows j = 16b + tl, contraction i = 16w + 4gq + ii
+    *reinterpret_cast<float4*>(br + BR_AQKT + frag32(16 * b + tl, 16 * w + 4 * gq, CH)) =
+        make_float4(qk4[0], qk4[1], qk4[2], qk4[3]);
   }
   __syncthreads();
 
@@ -296,25 +322,33 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_prep_kernel(BwdArgs a) {
         acc = mfma_f32(av, bv, acc);
       }
     }
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) br[BR_W + (16 * w + 4 * gq + ii) * KD + 16 * n + tl] = acc[ii];
+    // W^T[k][i]: rows k = 16n + tl, contraction i = 16w + 4gq + ii
+    *reinterpret_cast<float4*>(br + BR_WT + frag32(16 * n + tl, 16 * w + 4 * gq, CH)) =
+        make_float4(acc[0], acc[1], acc[2], acc[3]);
   }
 
-  // ---- Kt, QG, exp(G_L), beta
+  // ---- Kt (thread: token tid / 4, 32 channels), QG^T (thread: channel tid / 2,
+  // 32 tokens), exp(G_L), beta
   {
     const int i = tid >> 2;
     const int cq = tid & 3;
 #pragma unroll
     for (int c = 32 * cq; c < 32 * cq + 32; c += 4) {
-      const float4 kn = ld4(sKn + i * QP + c), qn = ld4(sQn + i * QP + c), gg = ld4(sG + i * QP + c);
+      const float4 kn = ld4(sKn + i * QP + c), gg = ld4(sG + i * QP + c);
       const float4 gl = ld4(sG + (CH - 1) * QP + c);
-      float4 kt, qg;
+      float4 kt;
       kt.x = kn.x * fexp2(gl.x - gg.x); kt.y = kn.y * fexp2(gl.y - gg.y);
       kt.z = kn.z * fexp2(gl.z - gg.z); kt.w = kn.w * fexp2(gl.w - gg.w);
-      qg.x = qn.x * fexp2(gg.x); qg.y = qn.y * fexp2(gg.y);
-      qg.z = qn.z * fexp2(gg.z); qg.w = qn.w * fexp2(gg.w);
-      *reinterpret_cast<float4*>(br + BR_KT + i * KD + c) = kt;
-      *reinterpret_cast<float4*>(br + BR_QG + i * KD + c) = qg;
+      *reinterpret_cast<float4*>(br + BR_KT + frag32(i, c, KD)) = kt;
+    }
+    const int k = tid >> 1;
+    const int i0 = 32 * (tid & 1);
+#pragma unroll
+    for (int ib = i0; ib < i0 + 32; ib += 4) {
+      float q4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) q4[u] = sQn[(ib + u) * QP + k] * fexp2(sG[(ib + u) * QP + k]);
+      *reinterpret_cast<float4*>(br + BR_QGT + frag32(k, ib, CH)) = make_float4(q4[0], q4[1], q4[2], q4[3]);
     }
     if (tid < KD) br[BR_GL + tid] = fexp2(sG[(CH - 1) * QP + tid]);
     if (tid < CH) br[BR_BETA + tid] = sBeta[tid];
@@ -323,10 +357,45 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_prep_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // kda_bwd_dhu_kernel: per (sequence, head, V half), chunks in reverse order.
-// The state gradient dS (rows = channels 32w + 16mt + 4gq + ii, columns
-// vs + 16nn + tl) stays in registers.
+// The state gradient dS stays in MFMA accumulators: wave w holds channels
+// 32w + 16mt + 4gq + ii and, in "virtual tile" e, columns vs + 4 tl + e, so
+// that every LDS and global access of a state or V-wide row is a float4.
+// The next chunk's record operands (fragment order, one 1 KB block per wave
+// load) and dO rows are loaded one chunk ahead.
 // ---------------------------------------------------------------------------
 constexpr int DHU_FLOATS = KD * DP + 2 * CH * DP;
+
+struct DhuOps {
+  float4 kt[8];      // Kt, rows 16w + tl, contraction block t
+  float4 aq[4];      // A_qk^T, rows 16w + tl, contraction block jb (zero for jb < w)
+  float4 qg[2][4];   // QG^T, rows 32w + 16mt + tl, contraction block t
+  float4 wt[2][4];   // W^T
+  float4 gl[2];      // exp(G_L) of channels 32w + 16mt + 4gq + 0..3
+  uint4 dob[2];      // dO row tid / 4, columns vs + 16 (tid % 4) .. + 15 (zero past the end)
+};
+
+__device__ __forceinline__ void dhu_load(DhuOps& o, const float* br, const uint16_t* dorow, bool rowok, int w,
+                                         int lane, int gq) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) o.kt[t] = ld4(br + BR_KT + (((w * 8 + t) * 64 + lane) << 2));
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) o.aq[jb] = ld4(br + BR_AQKT + (((w * 4 + jb) * 64 + lane) << 2));
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      o.qg[mt][t] = ld4(br + BR_QGT + ((((2 * w + mt) * 4 + t) * 64 + lane) << 2));
+      o.wt[mt][t] = ld4(br + BR_WT + ((((2 * w + mt) * 4 + t) * 64 + lane) << 2));
+    }
+    o.gl[mt] = ld4(br + BR_GL + 32 * w + 16 * mt + 4 * gq);
+  }
+  if (rowok) {
+    o.dob[0] = reinterpret_cast<const uint4*>(dorow)[0];
+    o.dob[1] = reinterpret_cast<const uint4*>(dorow)[1];
+  } else {
+    o.dob[0] = o.dob[1] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
 
 __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float smem[DHU_FLOATS];
@@ -355,6 +424,8 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
   const int lane = tid & 63;
   const int tl = lane & 15;
   const int gq = lane >> 4;
+  const int orow = tid >> 2;          // dO staging: row and 16 columns
+  const int ocol = 16 * (tid & 3);
 
   f32x4 dS[2][4];
   {
@@ -362,119 +433,128 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nn = 0; nn < 4; ++nn)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          dS[mt][nn][ii] = src ? src[(32 * w + 16 * mt + 4 * gq + ii) * VD + vs + 16 * nn + tl] : 0.f;
+      for (int ii = 0; ii < 4; ++ii) {
+        const int kr = 32 * w + 16 * mt + 4 * gq + ii;
+        const float4 v4 = src ? ld4(src + kr * VD + vs + 4 * tl) : make_float4(0.f, 0.f, 0.f, 0.f);
+        dS[mt][0][ii] = v4.x;
+        dS[mt][1][ii] = v4.y;
+        dS[mt][2][ii] = v4.z;
+        dS[mt][3][ii] = v4.w;
+      }
+  }
+  auto chunk_start = [&](int ci) { return bos + (int64_t)ci * CH; };
+  auto dorow_of = [&](int ci, bool& ok) {
+    const int64_t c0 = chunk_start(ci);
+    ok = c0 + orow < eos;
+    return a.dout + ((size_t)(c0 + (ok ? orow : 0)) * H + h) * VD + vs + ocol;
+  };
+
+  DhuOps cur, nxt;
+  if (nch > 0) {
+    bool ok;
+    const uint16_t* dr = dorow_of(nch - 1, ok);
+    dhu_load(cur, a.br + ((size_t)(gfirst + nch - 1) * H + h) * BWD_REC_FLOATS, dr, ok, w, lane, gq);
   }
 
   for (int ci = nch - 1; ci >= 0; --ci) {
     const int64_t gch = gfirst + ci;
-    const int64_t c0 = bos + (int64_t)ci * CH;
-    const int L = (int)((eos - c0) < CH ? (eos - c0) : CH);
     const size_t it = (size_t)gch * H + h;
-    const float* br = a.br + it * BWD_REC_FLOATS;
+    {  // next (earlier) chunk's operands; the first chunk re-reads itself
+      const int cn = ci > 0 ? ci - 1 : ci;
+      bool ok;
+      const uint16_t* dr = dorow_of(cn, ok);
+      dhu_load(nxt, a.br + ((size_t)(gfirst + cn) * H + h) * BWD_REC_FLOATS, dr, ok, w, lane, gq);
+    }
 
     // dS' of this chunk: to the checkpoint buffer and to LDS
     float* dsg = a.dstates + it * KD * VD;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nn = 0; nn < 4; ++nn)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int kr = 32 * w + 16 * mt + 4 * gq + ii;
-          const int vc = 16 * nn + tl;
-          dsg[kr * VD + vs + vc] = dS[mt][nn][ii];
-          sdS[kr * DP + vc] = dS[mt][nn][ii];
-        }
-    // scale * dO tile (zero past the chunk end)
-    {
-      const int r = tid >> 2;
-      const int cg = 16 * (tid & 3);
-      float d[16];
-      if (r < L) {
-        const uint4* src = reinterpret_cast<const uint4*>(a.dout + ((size_t)(c0 + r) * H + h) * VD + vs + cg);
-        float t0[8], t1[8];
-        unpack_bf16x8(src[0], t0);
-        unpack_bf16x8(src[1], t1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          d[e] = t0[e] * a.scale;
-          d[8 + e] = t1[e] * a.scale;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) d[e] = 0.f;
+      for (int ii = 0; ii < 4; ++ii) {
+        const int kr = 32 * w + 16 * mt + 4 * gq + ii;
+        const float4 v4 = make_float4(dS[mt][0][ii], dS[mt][1][ii], dS[mt][2][ii], dS[mt][3][ii]);
+        *reinterpret_cast<float4*>(dsg + kr * VD + vs + 4 * tl) = v4;
+        *reinterpret_cast<float4*>(sdS + kr * DP + 4 * tl) = v4;
       }
+    // scale * dO tile
+    {
+      float t0[8], t1[8];
+      unpack_bf16x8(cur.dob[0], t0);
+      unpack_bf16x8(cur.dob[1], t1);
+      float* dst = sdO + orow * DP + ocol;
 #pragma unroll
-      for (int e = 0; e < 16; e += 4)
-        *reinterpret_cast<float4*>(sdO + r * DP + cg + e) = make_float4(d[e], d[e + 1], d[e + 2], d[e + 3]);
+      for (int e = 0; e < 8; e += 4) {
+        *reinterpret_cast<float4*>(dst + e) =
+            make_float4(t0[e] * a.scale, t0[e + 1] * a.scale, t0[e + 2] * a.scale, t0[e + 3] * a.scale);
+        *reinterpret_cast<float4*>(dst + 8 + e) =
+            make_float4(t1[e] * a.scale, t1[e + 1] * a.scale, t1[e + 2] * a.scale, t1[e + 3] * a.scale);
+      }
     }
     __syncthreads();
 
     // dD rows 16w.. = Kt dS' + A_qk^T (scale dO)
     f32x4 dD[4];
 #pragma unroll
-    for (int nn = 0; nn < 4; ++nn) dD[nn] = zero4();
+    for (int e = 0; e < 4; ++e) dD[e] = zero4();
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float4 kt = ld4(br + BR_KT + (16 * w + tl) * KD + 16 * t + 4 * gq);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int kap = 16 * t + 4 * gq + s;
-#pragma unroll
-        for (int nn = 0; nn < 4; ++nn) dD[nn] = mfma_f32(el(kt, s), sdS[kap * DP + 16 * nn + tl], dD[nn]);
-      }
-    }
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      if (jb < w) continue;  // A_qk[j][i] = 0 for j < i
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int kap = 16 * jb + 4 * gq + s;
-        const float av = br[BR_AQK + kap * CH + 16 * w + tl];
+        const float4 b4 = ld4(sdS + (16 * t + 4 * gq + s) * DP + 4 * tl);
+        const float av = el(cur.kt[t], s);
 #pragma unroll
-        for (int nn = 0; nn < 4; ++nn) dD[nn] = mfma_f32(av, sdO[kap * DP + 16 * nn + tl], dD[nn]);
+        for (int e = 0; e < 4; ++e) dD[e] = mfma_f32(av, el(b4, e), dD[e]);
       }
-    }
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const float4 b4 = ld4(sdO + (16 * jb + 4 * gq + s) * DP + 4 * tl);
+        const float av = el(cur.aq[jb], s);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dD[e] = mfma_f32(av, el(b4, e), dD[e]);
+      }
     float* ddg = a.ddtile + it * CH * VD;
 #pragma unroll
-    for (int nn = 0; nn < 4; ++nn)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int i = 16 * w + 4 * gq + ii;
-        ddg[i * VD + vs + 16 * nn + tl] = dD[nn][ii];
-        sdD[i * DP + 16 * nn + tl] = dD[nn][ii];
-      }
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = 16 * w + 4 * gq + ii;
+      const float4 v4 = make_float4(dD[0][ii], dD[1][ii], dD[2][ii], dD[3][ii]);
+      *reinterpret_cast<float4*>(ddg + i * VD + vs + 4 * tl) = v4;
+      *reinterpret_cast<float4*>(sdD + i * DP + 4 * tl) = v4;
+    }
     __syncthreads();
 
     // dS = Diag(exp(G_L)) dS' + QG^T (scale dO) - W^T dD
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const float4 gl = ld4(br + BR_GL + 32 * w + 16 * mt + 4 * gq);
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nn = 0; nn < 4; ++nn) {
-        dS[mt][nn][0] *= gl.x;
-        dS[mt][nn][1] *= gl.y;
-        dS[mt][nn][2] *= gl.z;
-        dS[mt][nn][3] *= gl.w;
+      for (int e = 0; e < 4; ++e) {
+        dS[mt][e][0] *= cur.gl[mt].x;
+        dS[mt][e][1] *= cur.gl[mt].y;
+        dS[mt][e][2] *= cur.gl[mt].z;
+        dS[mt][e][3] *= cur.gl[mt].w;
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int kap = 16 * t + 4 * gq + s;
-          const float aqg = br[BR_QG + kap * KD + 32 * w + 16 * mt + tl];
-          const float aw = -br[BR_W + kap * KD + 32 * w + 16 * mt + tl];
+      for (int s = 0; s < 4; ++s) {
+        const int kap = 16 * t + 4 * gq + s;
+        const float4 o4 = ld4(sdO + kap * DP + 4 * tl);
+        const float4 d4 = ld4(sdD + kap * DP + 4 * tl);
 #pragma unroll
-          for (int nn = 0; nn < 4; ++nn) {
-            dS[mt][nn] = mfma_f32(aqg, sdO[kap * DP + 16 * nn + tl], dS[mt][nn]);
-            dS[mt][nn] = mfma_f32(aw, sdD[kap * DP + 16 * nn + tl], dS[mt][nn]);
+        for (int mt = 0; mt < 2; ++mt) {
+          const float aqg = el(cur.qg[mt][t], s);
+          const float aw = -el(cur.wt[mt][t], s);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dS[mt][e] = mfma_f32(aqg, el(o4, e), dS[mt][e]);
+            dS[mt][e] = mfma_f32(aw, el(d4, e), dS[mt][e]);
           }
         }
-    }
+      }
     __syncthreads();
+    cur = nxt;
   }
 
   if (a.dinit) {
@@ -482,35 +562,50 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nn = 0; nn < 4; ++nn)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          dst[(32 * w + 16 * mt + 4 * gq + ii) * VD + vs + 16 * nn + tl] = dS[mt][nn][ii];
+      for (int ii = 0; ii < 4; ++ii) {
+        const int kr = 32 * w + 16 * mt + 4 * gq + ii;
+        *reinterpret_cast<float4*>(dst + kr * VD + vs + 4 * tl) =
+            make_float4(dS[mt][0][ii], dS[mt][1][ii], dS[mt][2][ii], dS[mt][3][ii]);
+      }
   }
 }
 
 // ---------------------------------------------------------------------------
-// kda_bwd_grad_kernel: per (chunk, head).  Wave w owns token block
-// 16w..16w+15 in the roles listed at each step.
+// kda_bwd_grad_kernel: per (chunk, head), 8 waves.  Wave (w, p) = (wave % 4,
+// wave / 4) owns token block 16w..16w+15 and half p of the work: channels
+// 64p..64p+63 of every token-by-channel product, V half p of Z, alternate
+// column blocks of the 64 x 64 products.  Two waves per SIMD hide each
+// other's memory latency.
+//
+// V index permutation: a float4 load gives a lane 4 consecutive v, so in a
+// 64-wide V half hv the A-operand row tl of "virtual tile" e is
+// v = 64 hv + 4 tl + e, and C row 4 gq + ii of that tile is
+// v = 64 hv + 16 gq + 4 ii + e.  Contractions over v use the same order, so
+// every v-operand is a float4 (or 16-bf16) load.
 // ---------------------------------------------------------------------------
-constexpr int GRAD_FLOATS = 3 * CH * QP + 3 * CH * MP + 4 * CH + NT + 4 * KD + KD + 4 * KD;
+constexpr int NT8 = 512;
+constexpr int GRAD_FLOATS = 3 * CH * QP + 3 * CH * MP + 4 * CH + NT8 + 4 * KD + KD + 4 * KD + 4 * CH;
+static_assert(GRAD_FLOATS * 4 <= 163840, "LDS");
 
-__global__ void __launch_bounds__(NT, 1) kda_bwd_grad_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(NT8, 1) kda_bwd_grad_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float smem[GRAD_FLOATS];
   float* sQn = smem;
   float* sKn = sQn + CH * QP;
   float* sG = sKn + CH * QP;
   float* sT = sG + CH * QP;
   float* sM1 = sT + CH * MP;   // dA_qk
-  float* sM2 = sM1 + CH * MP;  // dT, then X = dT T^T, then dKK
+  float* sM2 = sM1 + CH * MP;  // dTb -> dT, then X = dT T^T, then dKK
   float* sBeta = sM2 + CH * MP;
   float* sRq = sBeta + CH;
   float* sRk = sRq + CH;
-  float* sdB = sRk + CH;       // gradient of beta
-  float* sTmp = sdB + CH;      // [256]
-  float* sGLw = sTmp + NT;     // [4][128] per-wave sums of dKt . Kt
+  float* sdB = sRk + CH;       // gradient of beta (atomically accumulated)
+  float* sTmp = sdB + CH;      // [512]
+  float* sGLw = sTmp + NT8;    // [4][128] per-block sums of dKt . Kt, later of d dt_bias
   float* sGL2 = sGLw + 4 * KD; // [128] exp(G_L) sum_v dS' . S0
-  float* sCS = sGL2 + KD;      // [4][128] per-wave column totals
+  float* sCS = sGL2 + KD;      // [4][128] per-block column totals of dG
+  float* sDot = sCS + 4 * KD;  // [2][64][2] half-row dots q^.dq^, k^.dk^
+  // bf16 output staging, over sT / sM1 / sM2 once the pairwise products are done
+  uint16_t* sOut = reinterpret_cast<uint16_t*>(sT);  // [3][64][128]: dq, dk, d raw_gate
 
   const int H = a.H;
   const int64_t gch = blockIdx.x / H;
@@ -526,195 +621,246 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_grad_kernel(BwdArgs a) {
   const float* Dt = a.dtile + it * CH * VD;
   const float* dDt = a.ddtile + it * CH * VD;
 
-  prep_chunk(a, c0, L, h, sQn, sKn, sG, sBeta, sRq, sRk, sTmp);
-
+  KDA_TIMER_DECL
+  KDA_TIMER_MARK(0);
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  // loads that do not depend on the preparation, issued first
+  float4 tcp[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) tcp[u] = ld4(br + BR_T + 4 * (tid + NT8 * u));
+  float gl2 = 0.f;
+  {
+    const int c = tid >> 2;
+    const int v0 = 32 * (tid & 3);
+    float4 x[8], y[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      x[u] = ld4(dSn + c * VD + v0 + 4 * u);
+      y[u] = ld4(S0 + c * VD + v0 + 4 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) gl2 += x[u].x * y[u].x + x[u].y * y[u].y + x[u].z * y[u].z + x[u].w * y[u].w;
+    gl2 += __shfl_xor(gl2, 1);
+    gl2 += __shfl_xor(gl2, 2);
+  }
+  prep_chunk<NT8>(a, c0, L, h, sQn, sKn, sG, sBeta, sRq, sRk, sTmp);
+  KDA_TIMER_MARK(1);
+
+  const int wv = tid >> 6;
+  const int w = wv & 3;
+  const int p = wv >> 2;
   const int lane = tid & 63;
   const int tl = lane & 15;
   const int gq = lane >> 4;
   const int jw = 16 * w + tl;  // this lane's token as an A row / B column
 
-  for (int e = tid; e < CH * CH; e += NT) sT[(e >> 6) * MP + (e & 63)] = br[BR_T + e];
-  // exp(G_L) sum_v dS'[c][v] S0[c][v]: thread -> channel tid / 2, half of v
-  {
-    const int c = tid >> 1;
-    const int v0 = 64 * (tid & 1);
-    float acc = 0.f;
-#pragma unroll 4
-    for (int v = v0; v < v0 + 64; v += 4) {
-      const float4 x = ld4(dSn + c * VD + v), y = ld4(S0 + c * VD + v);
-      acc += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
-    }
-    acc += __shfl_xor(acc, 1);
-    if ((tid & 1) == 0) sGL2[c] = acc * fexp2(sG[(CH - 1) * QP + c]);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = 4 * (tid + NT8 * u);
+    *reinterpret_cast<float4*>(sT + (e >> 6) * MP + (e & 63)) = tcp[u];
   }
+  if ((tid & 3) == 0) sGL2[tid >> 2] = gl2 * fexp2(sG[(CH - 1) * QP + (tid >> 2)]);
+  for (int e = tid; e < CH * MP; e += NT8) {
+    sM1[e] = 0.f;
+    sM2[e] = 0.f;
+  }
+  if (tid < CH) sdB[tid] = 0.f;
   __syncthreads();
+  KDA_TIMER_MARK(2);
 
-  // ---- Z^T[:, block w] = V^T - S0^T KG^T   (rows v = 16m + 4gq + ii, column jw)
-  float kgb[8][4];  // KG[jw][16t + 4gq + s]
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const float4 kn = ld4(sKn + jw * QP + 16 * t + 4 * gq), gg = ld4(sG + jw * QP + 16 * t + 4 * gq);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) kgb[t][s] = el(kn, s) * fexp2(el(gg, s));
-  }
   const bool jok = jw < L;
   const size_t jrow = ((size_t)(c0 + (jok ? jw : 0)) * H + h);
-  f32x4 Zt[8];
+  const float bj = sBeta[jw];
+
+  // ---- Z^T, V half p: Z^T[v][jw] = V[jw][v] - sum_k S0[k][v] KG[jw][k]
+  f32x4 Zt[4];
+  {
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    f32x4 acc = zero4();
+    for (int e = 0; e < 4; ++e) Zt[e] = zero4();
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 8; ++t) {
+      const float4 kn = ld4(sKn + jw * QP + 16 * t + 4 * gq), gg = ld4(sG + jw * QP + 16 * t + 4 * gq);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc = mfma_f32(S0[(16 * t + 4 * gq + s) * VD + 16 * m + tl], kgb[t][s], acc);
-    // V[jw][16m + 4gq + ii]
-    float vv[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < 4; ++s) {
+        const float kg = el(kn, s) * fexp2(el(gg, s));
+        const float4 a4 = ld4(S0 + (16 * t + 4 * gq + s) * VD + 64 * p + 4 * tl);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Zt[e] = mfma_f32(el(a4, e), kg, Zt[e]);
+      }
+    }
+    float vv[16];
     if (jok) {
-      const uint2 raw = *reinterpret_cast<const uint2*>(a.v + jrow * VD + 16 * m + 4 * gq);
-      vv[0] = __uint_as_float(raw.x << 16);
-      vv[1] = __uint_as_float(raw.x & 0xffff0000u);
-      vv[2] = __uint_as_float(raw.y << 16);
-      vv[3] = __uint_as_float(raw.y & 0xffff0000u);
+      const uint4* src = reinterpret_cast<const uint4*>(a.v + jrow * VD + 64 * p + 16 * gq);
+      unpack_bf16x8(src[0], *reinterpret_cast<float(*)[8]>(vv));
+      unpack_bf16x8(src[1], *reinterpret_cast<float(*)[8]>(vv + 8));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) vv[r] = 0.f;
     }
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) Zt[m][ii] = vv[ii] - acc[ii];
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) Zt[e][ii] = vv[4 * ii + e] - Zt[e][ii];
   }
-
-  // ---- dv^T[:, block w] = dD^T Tb[:, block w]   (contraction over i >= 16w)
-  float tbb[4][4];
-  const float bj = sBeta[jw];
+  // ---- dTb[i][jw] for i >= 16w, V half p (atomically summed over p): dD Z^T
 #pragma unroll
-  for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) tbb[ib][s] = sT[(16 * ib + 4 * gq + s) * MP + jw] * bj;
-  f32x4 dvT[8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int ab = 0; ab < 4; ++ab) {
+    if (ab < w) continue;
     f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float4 a4 = ld4(dDt + (16 * ab + tl) * VD + 64 * p + 16 * gq + 4 * s);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = mfma_f32(el(a4, e), Zt[e][s], acc);
+    }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) atomicAdd(sM2 + (16 * ab + 4 * gq + ii) * MP + jw, acc[ii]);
+  }
+  KDA_TIMER_MARK(3);
+
+  // ---- dv^T, both V halves: dv[jw][v] = sum_{i >= jw} Tb[i][jw] dD[i][v]
+  f32x4 dvT[2][4];
+  {
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dvT[hv][e] = zero4();
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
       if (ib < w) continue;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc = mfma_f32(dDt[(16 * ib + 4 * gq + s) * VD + 16 * m + tl], tbb[ib][s], acc);
-    }
-    dvT[m] = acc;
-    if (jok) {
-      const uint32_t lo = (uint32_t)f2bf(acc[0]) | ((uint32_t)f2bf(acc[1]) << 16);
-      const uint32_t hi = (uint32_t)f2bf(acc[2]) | ((uint32_t)f2bf(acc[3]) << 16);
-      *reinterpret_cast<uint2*>(a.dv + jrow * VD + 16 * m + 4 * gq) = make_uint2(lo, hi);
-    }
-  }
-
-  // ---- scale * dO rows jw as A operands (contraction over v = 16m + 4gq + s)
-  float doa[8][4];
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    if (jok) {
-      const uint2 raw = *reinterpret_cast<const uint2*>(a.dout + jrow * VD + 16 * m + 4 * gq);
-      doa[m][0] = __uint_as_float(raw.x << 16) * a.scale;
-      doa[m][1] = __uint_as_float(raw.x & 0xffff0000u) * a.scale;
-      doa[m][2] = __uint_as_float(raw.y << 16) * a.scale;
-      doa[m][3] = __uint_as_float(raw.y & 0xffff0000u) * a.scale;
-    } else {
-      doa[m][0] = doa[m][1] = doa[m][2] = doa[m][3] = 0.f;
-    }
-  }
-
-  // ---- dQG, dKG, dKt (rows 16w + 4gq + ii, channels 16n + tl) and their
-  // elementwise contributions to dq^, dk^, dG
-  f32x4 dqh[8], dkh[8], dGa[8];
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    f32x4 aQ = zero4(), aK = zero4(), aT = zero4();
-    const int kc = 16 * n + tl;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const float4 s0 = ld4(S0 + kc * VD + 16 * m + 4 * gq);
-      const float4 dsn = ld4(dSn + kc * VD + 16 * m + 4 * gq);
-      const float4 dd = ld4(Dt + jw * VD + 16 * m + 4 * gq);
-#pragma unroll
       for (int s = 0; s < 4; ++s) {
-        aQ = mfma_f32(doa[m][s], el(s0, s), aQ);
-        aK = mfma_f32(-dvT[m][s], el(s0, s), aK);
-        aT = mfma_f32(el(dd, s), el(dsn, s), aT);
+        const int kap = 16 * ib + 4 * gq + s;
+        const float tb = sT[kap * MP + jw] * bj;
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv) {
+          const float4 a4 = ld4(dDt + kap * VD + 64 * hv + 4 * tl);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dvT[hv][e] = mfma_f32(el(a4, e), tb, dvT[hv][e]);
+        }
       }
     }
-    float glsum = 0.f;
-    const float gl2 = sG[(CH - 1) * QP + kc];
+    if (jok) {  // wave p writes V half p: 16 consecutive v per lane
+      uint32_t pk[8];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int j = 16 * w + 4 * gq + ii;
-      const float qn = sQn[j * QP + kc], kn = sKn[j * QP + kc], g2 = sG[j * QP + kc];
-      const float gam = fexp2(g2), el2 = fexp2(gl2 - g2);
-      const float kt = kn * el2;
-      dqh[n][ii] = aQ[ii] * gam;
-      dkh[n][ii] = aK[ii] * gam + aT[ii] * el2;
-      dGa[n][ii] = aQ[ii] * qn * gam + aK[ii] * kn * gam - aT[ii] * kt;
-      glsum += aT[ii] * kt;
+      for (int r = 0; r < 8; ++r) {
+        const int r0 = 2 * r, r1 = 2 * r + 1;  // r = 4 ii + e
+        const float x0 = p ? dvT[1][r0 & 3][r0 >> 2] : dvT[0][r0 & 3][r0 >> 2];
+        const float x1 = p ? dvT[1][r1 & 3][r1 >> 2] : dvT[0][r1 & 3][r1 >> 2];
+        pk[r] = (uint32_t)f2bf(x0) | ((uint32_t)f2bf(x1) << 16);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(a.dv + jrow * VD + 64 * p + 16 * gq);
+      dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
     }
-    glsum += __shfl_xor(glsum, 16);
-    glsum += __shfl_xor(glsum, 32);
-    if (gq == 0) sGLw[w * KD + kc] = glsum;
   }
+  KDA_TIMER_MARK(4);
 
-  // ---- dTb[i][block w] for i >= 16w = dD Z^T; dT = dTb diag(beta) -> sM2;
-  // column sums of dTb . T -> dbeta
-  {
-    float colsum = 0.f;
+  // ---- scale * dO[jw][v] as A operands, v = 64 hv + 16 gq + 4 ii + e
+  float doa[2][16];
 #pragma unroll
-    for (int ab = 0; ab < 4; ++ab) {
-      if (ab < w) {
+  for (int hv = 0; hv < 2; ++hv) {
+    if (jok) {
+      const uint4* src = reinterpret_cast<const uint4*>(a.dout + jrow * VD + 64 * hv + 16 * gq);
+      unpack_bf16x8(src[0], *reinterpret_cast<float(*)[8]>(doa[hv]));
+      unpack_bf16x8(src[1], *reinterpret_cast<float(*)[8]>(doa[hv] + 8));
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) sM2[(16 * ab + 4 * gq + ii) * MP + jw] = 0.f;
-        continue;
-      }
-      f32x4 acc = zero4();
+      for (int r = 0; r < 16; ++r) doa[hv][r] *= a.scale;
+    } else {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float4 dd = ld4(dDt + (16 * ab + tl) * VD + 16 * m + 4 * gq);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma_f32(el(dd, s), Zt[m][s], acc);
-      }
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int i = 16 * ab + 4 * gq + ii;
-        colsum += acc[ii] * sT[i * MP + jw];
-        sM2[i * MP + jw] = acc[ii] * bj;
-      }
+      for (int r = 0; r < 16; ++r) doa[hv][r] = 0.f;
     }
-    colsum += __shfl_xor(colsum, 16);
-    colsum += __shfl_xor(colsum, 32);
-    if (gq == 0) sdB[jw] = colsum;
   }
-
-  // ---- dA_qk[block w][j <= i] = scale dO D^T -> sM1
+  // ---- dA_qk[block w][block b] = scale dO D^T (j <= i), column blocks b <= w of parity p
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
+    if (b > w || (b & 1) != p) continue;
     f32x4 acc = zero4();
-    if (b <= w) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float4 dd = ld4(Dt + (16 * b + tl) * VD + 16 * m + 4 * gq);
+    for (int hv = 0; hv < 2; ++hv)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma_f32(doa[m][s], el(dd, s), acc);
+      for (int ii = 0; ii < 4; ++ii) {
+        const float4 d4 = ld4(Dt + (16 * b + tl) * VD + 64 * hv + 16 * gq + 4 * ii);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = mfma_f32(doa[hv][4 * ii + e], el(d4, e), acc);
       }
-    }
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int i = 16 * w + 4 * gq + ii, j = 16 * b + tl;
       sM1[i * MP + j] = (j <= i) ? acc[ii] : 0.f;
     }
   }
-  __syncthreads();
 
-  // ---- X = dT T^T, row block w, column blocks q <= w (in place in sM2)
-  {
-    f32x4 X[4];
+  // ---- dQG = scale dO S0^T, dKG = -dv S0^T, dKt = D dS'^T for channels 64p..64p+63,
+  // and their elementwise contributions to dq^, dk^, dG
+  f32x4 dqh[4], dkh[4], dGa[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      X[q] = zero4();
+  for (int nn = 0; nn < 4; ++nn) {
+    const int kc = 64 * p + 16 * nn + tl;
+    f32x4 aQ = zero4(), aK = zero4(), aT = zero4();
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const float4 s0 = ld4(S0 + kc * VD + 64 * hv + 16 * gq + 4 * ii);
+        const float4 dsn = ld4(dSn + kc * VD + 64 * hv + 16 * gq + 4 * ii);
+        const float4 d4 = ld4(Dt + jw * VD + 64 * hv + 16 * gq + 4 * ii);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          aQ = mfma_f32(doa[hv][4 * ii + e], el(s0, e), aQ);
+          aK = mfma_f32(-dvT[hv][e][ii], el(s0, e), aK);
+          aT = mfma_f32(el(d4, e), el(dsn, e), aT);
+        }
+      }
+    const int c = 64 * p + 16 * nn + tl;
+    float glsum = 0.f;
+    const float gl2c = sG[(CH - 1) * QP + c];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int j = 16 * w + 4 * gq + ii;
+      const float qn = sQn[j * QP + c], kn = sKn[j * QP + c], g2 = sG[j * QP + c];
+      const float gam = fexp2(g2), el2 = fexp2(gl2c - g2);
+      const float kt = kn * el2;
+      dqh[nn][ii] = aQ[ii] * gam;
+      dkh[nn][ii] = aK[ii] * gam + aT[ii] * el2;
+      dGa[nn][ii] = aQ[ii] * qn * gam + aK[ii] * kn * gam - aT[ii] * kt;
+      glsum += aT[ii] * kt;
+    }
+    glsum += __shfl_xor(glsum, 16);
+    glsum += __shfl_xor(glsum, 32);
+    if (gq == 0) sGLw[w * KD + c] = glsum;
+  }
+  KDA_TIMER_MARK(5);
+
+  __syncthreads();
+  KDA_TIMER_MARK(6);
+
+  // ---- dT = dTb diag(beta) in place; column sums of dTb . T -> dbeta (rows split by p)
+  {
+    float colsum = 0.f;
+#pragma unroll
+    for (int ab = 0; ab < 4; ++ab) {
+      if (ab < w || ((ab - w) & 1) != p) continue;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 16 * ab + 4 * gq + ii;
+        const float v = sM2[i * MP + jw];
+        colsum += v * sT[i * MP + jw];
+        sM2[i * MP + jw] = v * bj;
+      }
+    }
+    colsum += __shfl_xor(colsum, 16);
+    colsum += __shfl_xor(colsum, 32);
+    if (gq == 0) atomicAdd(sdB + jw, colsum);
+  }
+  __syncthreads();
+  // ---- X = dT T^T, row block w, column blocks q <= w of parity p
+  {
+    f32x4 X[2];
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const int q = 2 * qq + p;
+      X[qq] = zero4();
       if (q > w) continue;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
@@ -722,32 +868,35 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int kap = 16 * b + 4 * gq + s;
-          X[q] = mfma_f32(sM2[jw * MP + kap], sT[(16 * q + tl) * MP + kap], X[q]);
+          X[qq] = mfma_f32(sM2[jw * MP + kap], sT[(16 * q + tl) * MP + kap], X[qq]);
         }
       }
     }
+    __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (q <= w) {
+    for (int qq = 0; qq < 2; ++qq) {
+      const int q = 2 * qq + p;
+      if (q > w) continue;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) sM2[(16 * w + 4 * gq + ii) * MP + 16 * q + tl] = X[q][ii];
-      }
+      for (int ii = 0; ii < 4; ++ii) sM2[(16 * w + 4 * gq + ii) * MP + 16 * q + tl] = X[qq][ii];
+    }
   }
   __syncthreads();
   // ---- dA_kk[block w][m < a] = -T^T X; row sums of dA_kk . KK -> dbeta; dKK = dA_kk beta_a
-  f32x4 dkk[4];
   {
+    f32x4 dkk[2];
     float rows[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int qq = 0; qq < 2; ++qq) {
+      const int q = 2 * qq + p;
       f32x4 acc = zero4();
       if (q <= w) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          if (p < w) continue;
+        for (int pb = 0; pb < 4; ++pb) {
+          if (pb < w) continue;
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            const int kap = 16 * p + 4 * gq + s;
+            const int kap = 16 * pb + 4 * gq + s;
             acc = mfma_f32(-sT[kap * MP + jw], sM2[kap * MP + 16 * q + tl], acc);
           }
         }
@@ -755,11 +904,11 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int ar = 16 * w + 4 * gq + ii, mc = 16 * q + tl;
-        const float v = (mc < ar) ? acc[ii] : 0.f;
-        rows[ii] += v * br[BR_KK + ar * CH + mc];
+        const float v = (q <= w && mc < ar) ? acc[ii] : 0.f;
+        rows[ii] += v * br[BR_KK + ar * CH + (mc & 63)];
         acc[ii] = v * sBeta[ar];
       }
-      dkk[q] = acc;
+      dkk[qq] = acc;
     }
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
@@ -768,84 +917,101 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_grad_kernel(BwdArgs a) {
       r += __shfl_xor(r, 2);
       r += __shfl_xor(r, 4);
       r += __shfl_xor(r, 8);
-      if (tl == 0) sdB[16 * w + 4 * gq + ii] += r;
+      if (tl == 0) atomicAdd(sdB + 16 * w + 4 * gq + ii, r);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const int q = 2 * qq + p;
+      if (q > w) continue;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) sM2[(16 * w + 4 * gq + ii) * MP + 16 * q + tl] = dkk[qq][ii];
     }
   }
   __syncthreads();
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) sM2[(16 * w + 4 * gq + ii) * MP + 16 * q + tl] = dkk[q][ii];
-  __syncthreads();
+  KDA_TIMER_MARK(7);
 
   // ---- pairwise products, row role: i in block w, j in blocks b <= w
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     if (b > w) continue;
     const int r = (b < w) ? 16 * b + 15 : 16 * w;
+    float m1[4], m2[4];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int c = 16 * n + tl;
+    for (int s = 0; s < 4; ++s) {
+      m1[s] = sM1[jw * MP + 16 * b + 4 * gq + s];
+      m2[s] = sM2[jw * MP + 16 * b + 4 * gq + s];
+    }
+#pragma unroll
+    for (int nn = 0; nn < 4; ++nn) {
+      const int c = 64 * p + 16 * nn + tl;
       const float gr = sG[r * QP + c];
       f32x4 a1 = zero4(), a2 = zero4();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int kap = 16 * b + 4 * gq + s;
         const float y = sKn[kap * QP + c] * fexp2(gr - sG[kap * QP + c]);
-        a1 = mfma_f32(sM1[jw * MP + kap], y, a1);
-        a2 = mfma_f32(sM2[jw * MP + kap], y, a2);
+        a1 = mfma_f32(m1[s], y, a1);
+        a2 = mfma_f32(m2[s], y, a2);
       }
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int i = 16 * w + 4 * gq + ii;
         const float f = fexp2(sG[i * QP + c] - gr);
         const float v1 = a1[ii] * f, v2 = a2[ii] * f;
-        dqh[n][ii] += v1;
-        dkh[n][ii] += v2;
-        dGa[n][ii] += sQn[i * QP + c] * v1 + sKn[i * QP + c] * v2;
+        dqh[nn][ii] += v1;
+        dkh[nn][ii] += v2;
+        dGa[nn][ii] += sQn[i * QP + c] * v1 + sKn[i * QP + c] * v2;
       }
     }
   }
+  KDA_TIMER_MARK(8);
   // ---- pairwise products, column role: j in block w, i in blocks a >= w
 #pragma unroll
   for (int ab = 0; ab < 4; ++ab) {
     if (ab < w) continue;
     const int r = (ab > w) ? 16 * w + 15 : 16 * w;
+    float m1[4], m2[4];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int c = 16 * n + tl;
+    for (int s = 0; s < 4; ++s) {
+      m1[s] = sM1[(16 * ab + 4 * gq + s) * MP + jw];
+      m2[s] = sM2[(16 * ab + 4 * gq + s) * MP + jw];
+    }
+#pragma unroll
+    for (int nn = 0; nn < 4; ++nn) {
+      const int c = 64 * p + 16 * nn + tl;
       const float gr = sG[r * QP + c];
       f32x4 acc = zero4();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int kap = 16 * ab + 4 * gq + s;
         const float f = fexp2(sG[kap * QP + c] - gr);
-        acc = mfma_f32(sM1[kap * MP + jw], sQn[kap * QP + c] * f, acc);
-        acc = mfma_f32(sM2[kap * MP + jw], sKn[kap * QP + c] * f, acc);
+        acc = mfma_f32(m1[s], sQn[kap * QP + c] * f, acc);
+        acc = mfma_f32(m2[s], sKn[kap * QP + c] * f, acc);
       }
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int j = 16 * w + 4 * gq + ii;
         const float v = acc[ii] * fexp2(gr - sG[j * QP + c]);
-        dkh[n][ii] += v;
-        dGa[n][ii] -= sKn[j * QP + c] * v;
+        dkh[nn][ii] += v;
+        dGa[nn][ii] -= sKn[j * QP + c] * v;
       }
     }
   }
+  KDA_TIMER_MARK(9);
 
-  // ---- dG_L on the last token, then the reverse cumulative sum -> dg (log-decay gradient)
+  // ---- dG_L on the last token, then the reverse cumulative sum -> dg
   const int lastw = (L - 1) >> 4;
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const int c = 16 * n + tl;
+  for (int nn = 0; nn < 4; ++nn) {
+    const int c = 64 * p + 16 * nn + tl;
     if (w == lastw) {
       const float dgl = sGL2[c] + sGLw[c] + sGLw[KD + c] + sGLw[2 * KD + c] + sGLw[3 * KD + c];
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
-        if (16 * w + 4 * gq + ii == L - 1) dGa[n][ii] += dgl;
+        if (16 * w + 4 * gq + ii == L - 1) dGa[nn][ii] += dgl;
     }
-    // suffix sums within the lane's 4 rows, then over the later lane groups
-    f32x4 x = dGa[n];
+    f32x4 x = dGa[nn];
     x[2] += x[3];
     x[1] += x[2];
     x[0] += x[1];
@@ -854,17 +1020,42 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_grad_kernel(BwdArgs a) {
     const float off = (gq < 1 ? t1 : 0.f) + (gq < 2 ? t2 : 0.f) + (gq < 3 ? t3 : 0.f);
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) x[ii] += off;
-    dGa[n] = x;
-    if (gq == 0) sCS[w * KD + c] = x[0];  // the whole block's column total
+    dGa[nn] = x;
+    if (gq == 0) sCS[w * KD + c] = x[0];
+  }
+  // half-row dots q^.dq^ and k^.dk^ over this wave's 64 channels
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int j = 16 * w + 4 * gq + ii;
+    float dq_dot = 0.f, dk_dot = 0.f;
+#pragma unroll
+    for (int nn = 0; nn < 4; ++nn) {
+      const int c = 64 * p + 16 * nn + tl;
+      dq_dot += sQn[j * QP + c] * dqh[nn][ii];
+      dk_dot += sKn[j * QP + c] * dkh[nn][ii];
+    }
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      dq_dot += __shfl_xor(dq_dot, d);
+      dk_dot += __shfl_xor(dk_dot, d);
+    }
+    if (tl == 0) {
+      sDot[(p * CH + j) * 2] = dq_dot;
+      sDot[(p * CH + j) * 2 + 1] = dk_dot;
+    }
   }
   __syncthreads();
+  KDA_TIMER_MARK(10);
 
-  // ---- outputs: d raw_gate, dq, dk, d raw_beta; partial sums of d dt_bias, dA_log
+  // ---- outputs, staged in LDS: d raw_gate, dq, dk; partial sums of d dt_bias, dA_log
   const float al = expf(a.A_log[h]);
   float pA = 0.f;
+  uint16_t* oq = sOut;
+  uint16_t* ok_ = sOut + CH * KD;
+  uint16_t* og = sOut + 2 * CH * KD;
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const int c = 16 * n + tl;
+  for (int nn = 0; nn < 4; ++nn) {
+    const int c = 64 * p + 16 * nn + tl;
     float later = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -874,16 +1065,18 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int j = 16 * w + 4 * gq + ii;
-      const float dgv = dGa[n][ii] + later;  // natural-log gradient of g_j
+      const float dgv = dGa[nn][ii] + later;  // gradient of the natural-log decay g_j
+      float dgo = 0.f;
       if (j < L) {
         const size_t o = ((size_t)(c0 + j) * H + h) * KD + c;
         const float x = al * (bf2f(a.g[o]) + dtb);
         const float sg = sigmoidf(x);
         const float dx = dgv * a.lb * sg * (1.f - sg);
-        a.dg[o] = f2bf(dx * al);
-        pdt += dx * al;
+        dgo = dx * al;
+        pdt += dgo;
         pA += dx * x;
       }
+      og[j * KD + c] = f2bf(dgo);
     }
     pdt += __shfl_xor(pdt, 16);
     pdt += __shfl_xor(pdt, 32);
@@ -893,40 +1086,47 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
     const int j = 16 * w + 4 * gq + ii;
-    float dq_dot = 0.f, dk_dot = 0.f;
+    const float dq_dot = sDot[j * 2] + sDot[(CH + j) * 2];
+    const float dk_dot = sDot[j * 2 + 1] + sDot[(CH + j) * 2 + 1];
+    const float irq = 1.f / sRq[j], irk = 1.f / sRk[j];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      dq_dot += sQn[j * QP + 16 * n + tl] * dqh[n][ii];
-      dk_dot += sKn[j * QP + 16 * n + tl] * dkh[n][ii];
-    }
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
-      dq_dot += __shfl_xor(dq_dot, d);
-      dk_dot += __shfl_xor(dk_dot, d);
-    }
-    if (j < L) {
-      const float irq = 1.f / sRq[j], irk = 1.f / sRk[j];
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const int c = 16 * n + tl;
-        const size_t o = ((size_t)(c0 + j) * H + h) * KD + c;
-        a.dq[o] = f2bf((dqh[n][ii] - sQn[j * QP + c] * dq_dot) * irq);
-        a.dk[o] = f2bf((dkh[n][ii] - sKn[j * QP + c] * dk_dot) * irk);
-      }
+    for (int nn = 0; nn < 4; ++nn) {
+      const int c = 64 * p + 16 * nn + tl;
+      oq[j * KD + c] = f2bf((dqh[nn][ii] - sQn[j * QP + c] * dq_dot) * irq);
+      ok_[j * KD + c] = f2bf((dkh[nn][ii] - sKn[j * QP + c] * dk_dot) * irk);
     }
   }
-  // block reduction of pA
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) pA += __shfl_xor(pA, d);
-  if (lane == 0) sTmp[w] = pA;
-  if (lane < 16 && jw < L) {
+  if (lane == 0) sTmp[wv] = pA;
+  if (p == 0 && lane < 16 && jw < L) {
     const float b = sBeta[jw];
     a.dbeta[(size_t)(c0 + jw) * H + h] = f2bf(sdB[jw] * b * (1.f - b));
   }
   __syncthreads();
+  // 16-byte stores of the staged rows: thread -> (row, 16-byte column block)
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + NT8 * u;  // 0 .. 1023
+    const int row = e >> 4;
+    const int cb = 8 * (e & 15);
+    if (row < L) {
+      const size_t o = ((size_t)(c0 + row) * H + h) * KD + cb;
+      *reinterpret_cast<uint4*>(a.dq + o) = *reinterpret_cast<const uint4*>(oq + row * KD + cb);
+      *reinterpret_cast<uint4*>(a.dk + o) = *reinterpret_cast<const uint4*>(ok_ + row * KD + cb);
+      *reinterpret_cast<uint4*>(a.dg + o) = *reinterpret_cast<const uint4*>(og + row * KD + cb);
+    }
+  }
   float* part = a.part + it * (KD + 1);
   if (tid < KD) part[tid] = sGLw[tid] + sGLw[KD + tid] + sGLw[2 * KD + tid] + sGLw[3 * KD + tid];
-  if (tid == KD) part[KD] = sTmp[0] + sTmp[1] + sTmp[2] + sTmp[3];
+  if (tid == KD) {
+    float sA = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sA += sTmp[u];
+    part[KD] = sA;
+  }
+  KDA_TIMER_MARK(11);
+  KDA_TIMER_STORE(a.timers ? a.timers + (size_t)gridDim.x * 16 : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -963,7 +1163,7 @@ hipError_t launch_bwd(const BwdArgs& args, int64_t max_chunks, hipStream_t st) {
                       dim3(NT), kargs, 0, st);
   if (e != hipSuccess) return e;
   if (items > 0) {
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_bwd_grad_kernel), dim3((unsigned)items), dim3(NT),
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_bwd_grad_kernel), dim3((unsigned)items), dim3(NT8),
                         kargs, 0, st);
     if (e != hipSuccess) return e;
   }

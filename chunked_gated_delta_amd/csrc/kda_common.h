@@ -209,6 +209,7 @@ struct BwdArgs {
   int H;
   float scale;
   float lb;               // lower_bound
+  unsigned long long* timers;  // phase timers (KDA_PHASE_TIMERS builds only), else nullptr
 };
 constexpr int BWD_REC_FLOATS = 3 * CH * CH + 3 * CH * KD + KD + CH;  // 37056
 hipError_t launch_bwd(const BwdArgs& a, int64_t max_chunks, hipStream_t st);
