@@ -9,50 +9,12 @@
 #include <stdlib.h>
 
 #include "../../include/kda.h"
-#include "kda_common.h"
+#include "kda_host.h"
 
 namespace kda {
 namespace {
 
 constexpr int kMaxSortN = 16384;
-
-size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-
-struct Layout {
-  size_t choff, order, rec, total;
-};
-
-Layout workspace_layout(int64_t T_total, int64_t H, int64_t N) {
-  Layout l;
-  l.choff = 256;
-  l.order = l.choff + align256((size_t)(N + 1) * sizeof(int32_t));
-  l.rec = l.order + align256((size_t)N * sizeof(int32_t));
-  const size_t max_chunks = (size_t)(T_total / CH) + (size_t)N;
-  l.total = l.rec + max_chunks * (size_t)H * REC_BYTES;
-  return l;
-}
-
-// The backward pass keeps, after the forward's areas: the state entering and
-// the state gradient leaving every chunk, every chunk's D and dD, its fp32
-// factor record and its partial parameter-gradient sums.
-struct BwdLayout {
-  Layout fwd;
-  size_t states, dtile, dstates, ddtile, br, part, total;
-};
-
-BwdLayout bwd_layout(int64_t T_total, int64_t H, int64_t N) {
-  BwdLayout l;
-  l.fwd = workspace_layout(T_total, H, N);
-  const size_t items = ((size_t)(T_total / CH) + (size_t)N) * (size_t)H;
-  l.states = align256(l.fwd.total);
-  l.dtile = l.states + align256(items * KD * VD * 4);
-  l.dstates = l.dtile + align256(items * CH * VD * 4);
-  l.ddtile = l.dstates + align256(items * KD * VD * 4);
-  l.br = l.ddtile + align256(items * CH * VD * 4);
-  l.part = l.br + align256(items * BWD_REC_FLOATS * 4);
-  l.total = l.part + align256(items * (KD + 1) * 4);
-  return l;
-}
 
 // choff[n] = sum_{m<n} ceil(len_m / 64), choff[N] = total chunks (one block).
 __global__ void __launch_bounds__(1024) kda_chunk_offsets_kernel(const int32_t* __restrict__ cu, int N,
@@ -99,6 +61,8 @@ __global__ void kda_order_kernel(const int32_t* __restrict__ cu, int N, int32_t*
   order[rank] = i;
 }
 
+}  // namespace
+
 // The launch's own return code (not hipGetLastError, which also reports
 // errors left behind by earlier, unrelated runtime calls).  KDA_DEBUG=1 in the
 // environment prints the HIP error behind KDA_ERR_LAUNCH.
@@ -108,7 +72,6 @@ kda_status_t launch_status(hipError_t err, const char* what) {
   return KDA_ERR_LAUNCH;
 }
 
-}  // namespace
 }  // namespace kda
 
 using namespace kda;
@@ -118,11 +81,6 @@ extern "C" {
 size_t kda_workspace_size(int64_t T_total, int64_t H, int64_t N) {
   if (T_total < 0 || H < 1 || N < 1) return 0;
   return workspace_layout(T_total, H, N).total;
-}
-
-size_t kda_bwd_workspace_size(int64_t T_total, int64_t H, int64_t N) {
-  if (T_total < 0 || H < 1 || N < 1) return 0;
-  return bwd_layout(T_total, H, N).total;
 }
 
 int kda_is_supported(int64_t K, int64_t V, float lower_bound) {
@@ -143,17 +101,6 @@ const char* kda_status_string(kda_status_t s) {
 }  // extern "C"
 
 namespace kda {
-namespace {
-
-// What the intra-chunk pass of one call leaves for the inter-chunk passes.
-struct Prepared {
-  ChunkMap map;
-  int32_t* order;
-  char* rec;
-  char* ws;
-  Layout lay;
-  int64_t max_chunks;
-};
 
 // Argument checks shared by every entry point that runs the chunked forward,
 // then the varlen bookkeeping and the intra-chunk kernel on `st`.
@@ -161,7 +108,7 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
                      void* workspace, size_t workspace_bytes, const float* A_log,
                      const float* dt_bias, float lower_bound, const int32_t* cu_seqlens, int64_t B,
                      int64_t T, int64_t H, int64_t K, int64_t V, int64_t N, hipStream_t st,
-                     Prepared& pr, unsigned flags = 0) {
+                     Prepared& pr, unsigned flags) {
   if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID;
   if (flags & ~(unsigned)(FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM | FLAG_STATE_VK))
     return KDA_ERR_INVALID;
@@ -250,7 +197,6 @@ InterArgs inter_args(const Prepared& pr, int64_t H) {
   return xa;
 }
 
-}  // namespace
 }  // namespace kda
 
 extern "C" {
@@ -320,71 +266,6 @@ kda_status_t kda_shard_scan(const float* P, const float* R, const float* initial
   return launch_status(launch_shard_scan(P, R, initial_state, starts, final_state, (int)n_shards, (int)H,
                                          reinterpret_cast<hipStream_t>(stream)),
                        "shard scan");
-}
-
-kda_status_t kda_bwd(const void* q, const void* k, const void* v, const void* raw_gate,
-                     const void* raw_beta, float scale, const void* d_out, const float* d_final,
-                     void* dq, void* dk, void* dv, void* d_raw_gate, void* d_raw_beta, float* dA_log,
-                     float* d_dt_bias, float* d_initial_state, void* workspace, size_t workspace_bytes,
-                     const float* A_log, const float* dt_bias, float lower_bound,
-                     const float* initial_state, const int32_t* cu_seqlens, int64_t B, int64_t T,
-                     int64_t H, int64_t K, int64_t V, int64_t N, void* stream) {
-  if (B * T > 0 && (!v || !d_out || !dq || !dk || !dv || !d_raw_gate || !d_raw_beta)) return KDA_ERR_INVALID;
-  if (!dA_log || !d_dt_bias || !A_log || !dt_bias) return KDA_ERR_INVALID;
-  if (!(scale == scale)) return KDA_ERR_INVALID;
-  if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID;
-  if (B * T * H > ((int64_t)1 << 40) || N * H > ((int64_t)1 << 28) || N > ((int64_t)1 << 30))
-    return KDA_ERR_INVALID;
-  const BwdLayout bl = bwd_layout(B * T, H, N);
-  if (!workspace || workspace_bytes < bl.total) return KDA_ERR_WORKSPACE;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  Prepared pr;
-  const kda_status_t s = prepare(q, k, raw_gate, raw_beta, workspace, workspace_bytes, A_log, dt_bias,
-                                 lower_bound, cu_seqlens, B, T, H, K, V, N, st, pr);
-  if (s != KDA_SUCCESS) return s;
-  // forward recurrence, keeping the state entering each chunk and each chunk's D
-  InterArgs xa = inter_args(pr, H);
-  xa.v = static_cast<const uint16_t*>(v);
-  xa.init = initial_state;
-  xa.states = reinterpret_cast<float*>(pr.ws + bl.states);
-  xa.dtile = reinterpret_cast<float*>(pr.ws + bl.dtile);
-  if (launch_status(launch_inter(xa, st), "inter (checkpoints)") != KDA_SUCCESS) return KDA_ERR_LAUNCH;
-
-  BwdArgs ba;
-  ba.q = static_cast<const uint16_t*>(q);
-  ba.k = static_cast<const uint16_t*>(k);
-  ba.v = static_cast<const uint16_t*>(v);
-  ba.g = static_cast<const uint16_t*>(raw_gate);
-  ba.beta = static_cast<const uint16_t*>(raw_beta);
-  ba.A_log = A_log;
-  ba.dt_bias = dt_bias;
-  ba.dout = static_cast<const uint16_t*>(d_out);
-  ba.dfin = d_final;
-  ba.dq = static_cast<uint16_t*>(dq);
-  ba.dk = static_cast<uint16_t*>(dk);
-  ba.dv = static_cast<uint16_t*>(dv);
-  ba.dg = static_cast<uint16_t*>(d_raw_gate);
-  ba.dbeta = static_cast<uint16_t*>(d_raw_beta);
-  ba.dinit = d_initial_state;
-  ba.dA_log = dA_log;
-  ba.ddt = d_dt_bias;
-  ba.states = xa.states;
-  ba.dtile = xa.dtile;
-  ba.dstates = reinterpret_cast<float*>(pr.ws + bl.dstates);
-  ba.ddtile = reinterpret_cast<float*>(pr.ws + bl.ddtile);
-  ba.br = reinterpret_cast<float*>(pr.ws + bl.br);
-  ba.part = reinterpret_cast<float*>(pr.ws + bl.part);
-  ba.order = pr.order;
-  ba.map = pr.map;
-  ba.H = (int)H;
-  ba.scale = scale;
-  ba.lb = lower_bound;
-  ba.timers = nullptr;
-#ifdef KDA_PHASE_TIMERS
-  // timer builds only: 16 counters per workgroup of each backward kernel after the workspace
-  ba.timers = reinterpret_cast<unsigned long long*>(pr.ws + bl.total);
-#endif
-  return launch_status(launch_bwd(ba, pr.max_chunks, st), "backward");
 }
 
 }  // extern "C"

@@ -1,0 +1,44 @@
+// Internal declarations of the backward pass (kda_bwd.hip).  Not part of the C ABI.
+#pragma once
+
+#include "kda_common.h"
+
+namespace kda {
+
+// Backward pass (kda_bwd.hip).  Per-(chunk, head) buffers are indexed by
+// item = global chunk * H + head.
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* g;      // raw gate
+  const uint16_t* beta;   // raw beta
+  const float* A_log;
+  const float* dt_bias;
+  const uint16_t* dout;   // bf16 [tokens][H][V]
+  const float* dfin;      // [N][H][K][V] gradient of the final state, or nullptr
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  uint16_t* dg;           // gradient of the raw gate
+  uint16_t* dbeta;        // gradient of the raw beta
+  float* dinit;           // [N][H][K][V] or nullptr
+  float* dA_log;          // [H]
+  float* ddt;             // [H][K]
+  const float* states;    // [items][K][V] state entering each chunk
+  const float* dtile;     // [items][64][V] D of each chunk
+  float* dstates;         // [items][K][V] gradient of the state leaving each chunk
+  float* ddtile;          // [items][64][V] dD of each chunk
+  float* br;              // [items][BWD_REC_FLOATS] fp32 chunk factors
+  float* part;            // [items][K + 1] per-chunk partial sums of d dt_bias and dA_log
+  const int32_t* order;   // nullptr: identity order of sequences
+  ChunkMap map;
+  int H;
+  float scale;
+  float lb;               // lower_bound
+  unsigned long long* timers;  // phase timers (KDA_PHASE_TIMERS builds only), else nullptr
+};
+constexpr int BWD_REC_FLOATS = 3 * CH * CH + 3 * CH * KD + KD + CH;  // 37056
+hipError_t launch_bwd(const BwdArgs& a, int64_t max_chunks, hipStream_t st);
+
+}  // namespace kda

@@ -29,7 +29,10 @@
 // holds C[4 gq + ii][tl].  A C-layout tile therefore serves directly as the B
 // operand of a product that contracts over its rows.
 
-#include "kda_common.h"
+#include <stdio.h>
+
+#include "kda_bwd.h"
+#include "kda_host.h"
 
 namespace kda {
 namespace {
@@ -1172,3 +1175,107 @@ hipError_t launch_bwd(const BwdArgs& args, int64_t max_chunks, hipStream_t st) {
 }
 
 }  // namespace kda
+
+namespace kda {
+namespace {
+
+// The backward pass keeps, after the forward's areas: the state entering and
+// the state gradient leaving every chunk, every chunk's D and dD, its fp32
+// factor record and its partial parameter-gradient sums.
+struct BwdLayout {
+  Layout fwd;
+  size_t states, dtile, dstates, ddtile, br, part, total;
+};
+
+BwdLayout bwd_layout(int64_t T_total, int64_t H, int64_t N) {
+  BwdLayout l;
+  l.fwd = workspace_layout(T_total, H, N);
+  const size_t items = ((size_t)(T_total / CH) + (size_t)N) * (size_t)H;
+  l.states = align256(l.fwd.total);
+  l.dtile = l.states + align256(items * KD * VD * 4);
+  l.dstates = l.dtile + align256(items * CH * VD * 4);
+  l.ddtile = l.dstates + align256(items * KD * VD * 4);
+  l.br = l.ddtile + align256(items * CH * VD * 4);
+  l.part = l.br + align256(items * BWD_REC_FLOATS * 4);
+  l.total = l.part + align256(items * (KD + 1) * 4);
+  return l;
+}
+
+}  // namespace
+}  // namespace kda
+
+using namespace kda;
+
+extern "C" {
+
+size_t kda_bwd_workspace_size(int64_t T_total, int64_t H, int64_t N) {
+  if (T_total < 0 || H < 1 || N < 1) return 0;
+  return bwd_layout(T_total, H, N).total;
+}
+
+kda_status_t kda_bwd(const void* q, const void* k, const void* v, const void* raw_gate,
+                     const void* raw_beta, float scale, const void* d_out, const float* d_final,
+                     void* dq, void* dk, void* dv, void* d_raw_gate, void* d_raw_beta, float* dA_log,
+                     float* d_dt_bias, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                     const float* A_log, const float* dt_bias, float lower_bound,
+                     const float* initial_state, const int32_t* cu_seqlens, int64_t B, int64_t T,
+                     int64_t H, int64_t K, int64_t V, int64_t N, void* stream) {
+  if (B * T > 0 && (!v || !d_out || !dq || !dk || !dv || !d_raw_gate || !d_raw_beta)) return KDA_ERR_INVALID;
+  if (!dA_log || !d_dt_bias || !A_log || !dt_bias) return KDA_ERR_INVALID;
+  if (!(scale == scale)) return KDA_ERR_INVALID;
+  if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID;
+  if (B * T * H > ((int64_t)1 << 40) || N * H > ((int64_t)1 << 28) || N > ((int64_t)1 << 30))
+    return KDA_ERR_INVALID;
+  const BwdLayout bl = bwd_layout(B * T, H, N);
+  if (!workspace || workspace_bytes < bl.total) return KDA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Prepared pr;
+  const kda_status_t s = prepare(q, k, raw_gate, raw_beta, workspace, workspace_bytes, A_log, dt_bias,
+                                 lower_bound, cu_seqlens, B, T, H, K, V, N, st, pr);
+  if (s != KDA_SUCCESS) return s;
+  // forward recurrence, keeping the state entering each chunk and each chunk's D
+  InterArgs xa = inter_args(pr, H);
+  xa.v = static_cast<const uint16_t*>(v);
+  xa.init = initial_state;
+  xa.states = reinterpret_cast<float*>(pr.ws + bl.states);
+  xa.dtile = reinterpret_cast<float*>(pr.ws + bl.dtile);
+  if (launch_status(launch_inter(xa, st), "inter (checkpoints)") != KDA_SUCCESS) return KDA_ERR_LAUNCH;
+
+  BwdArgs ba;
+  ba.q = static_cast<const uint16_t*>(q);
+  ba.k = static_cast<const uint16_t*>(k);
+  ba.v = static_cast<const uint16_t*>(v);
+  ba.g = static_cast<const uint16_t*>(raw_gate);
+  ba.beta = static_cast<const uint16_t*>(raw_beta);
+  ba.A_log = A_log;
+  ba.dt_bias = dt_bias;
+  ba.dout = static_cast<const uint16_t*>(d_out);
+  ba.dfin = d_final;
+  ba.dq = static_cast<uint16_t*>(dq);
+  ba.dk = static_cast<uint16_t*>(dk);
+  ba.dv = static_cast<uint16_t*>(dv);
+  ba.dg = static_cast<uint16_t*>(d_raw_gate);
+  ba.dbeta = static_cast<uint16_t*>(d_raw_beta);
+  ba.dinit = d_initial_state;
+  ba.dA_log = dA_log;
+  ba.ddt = d_dt_bias;
+  ba.states = xa.states;
+  ba.dtile = xa.dtile;
+  ba.dstates = reinterpret_cast<float*>(pr.ws + bl.dstates);
+  ba.ddtile = reinterpret_cast<float*>(pr.ws + bl.ddtile);
+  ba.br = reinterpret_cast<float*>(pr.ws + bl.br);
+  ba.part = reinterpret_cast<float*>(pr.ws + bl.part);
+  ba.order = pr.order;
+  ba.map = pr.map;
+  ba.H = (int)H;
+  ba.scale = scale;
+  ba.lb = lower_bound;
+  ba.timers = nullptr;
+#ifdef KDA_PHASE_TIMERS
+  // timer builds only: 16 counters per workgroup of each backward kernel after the workspace
+  ba.timers = reinterpret_cast<unsigned long long*>(pr.ws + bl.total);
+#endif
+  return launch_status(launch_bwd(ba, pr.max_chunks, st), "backward");
+}
+
+}  // extern "C"
