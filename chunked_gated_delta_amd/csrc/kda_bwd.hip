@@ -173,18 +173,20 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
 }
 
 // ---------------------------------------------------------------------------
-// kda_bwd_prep_kernel: per (chunk, head), the chunk factors in fp32.
+// kda_bwd_prep_kernel: per (chunk, head), the chunk factors in fp32.  8 waves:
+// wave (w, p) = (wave % 4, wave / 4) owns row block w and the column blocks
+// (or channel tiles) of parity p.
 // ---------------------------------------------------------------------------
-constexpr int PREP_FLOATS = 3 * CH * QP + 3 * CH * MP + 3 * CH + NT;
+constexpr int NTP = 512;
+constexpr int PREP_FLOATS = 3 * CH * QP + 2 * CH * MP + 3 * CH + NTP;
 
-__global__ void __launch_bounds__(NT, 1) kda_bwd_prep_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float smem[PREP_FLOATS];
   float* sQn = smem;
   float* sKn = sQn + CH * QP;
   float* sG = sKn + CH * QP;
   float* sKK = sG + CH * QP;
-  float* sAQ = sKK + CH * MP;
-  float* sT = sAQ + CH * MP;
+  float* sT = sKK + CH * MP;
   float* sBeta = sT + CH * MP;
   float* sRq = sBeta + CH;
   float* sRk = sRq + CH;
@@ -199,24 +201,27 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_prep_kernel(BwdArgs a) {
   chunk_of(a.map, gch, c0, L);
   float* br = a.br + (size_t)blockIdx.x * BWD_REC_FLOATS;
 
-  prep_chunk<NT>(a, c0, L, h, sQn, sKn, sG, sBeta, sRq, sRk, sTmp);
+  prep_chunk<NTP>(a, c0, L, h, sQn, sKn, sG, sBeta, sRq, sRk, sTmp);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int wv = tid >> 6;
+  const int w = wv & 3;
+  const int p = wv >> 2;
   const int lane = tid & 63;
   const int tl = lane & 15;
   const int gq = lane >> 4;
 
-  // ---- KK and A_qk, row block w, column blocks b <= w.  Reference token r
-  // between i and j: the last token of block b (b < w), else the first of w.
+  // ---- KK and A_qk, row block w, column blocks b of parity p.  Reference
+  // token r between i and j: the last token of block b (b < w), else the
+  // first of w.  Blocks above the diagonal are zero.
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int bb = 0; bb < 2; ++bb) {
+    const int b = 2 * bb + p;
     if (b > w) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int i = 16 * w + 4 * gq + ii, j = 16 * b + tl;
         sKK[i * MP + j] = 0.f;
-        sAQ[i * MP + j] = 0.f;
         br[BR_KK + i * CH + j] = 0.f;
       }
       // A_qk^T tile (rows block b, contraction block w) is above the diagonal: zero
@@ -246,11 +251,9 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_prep_kernel(BwdArgs a) {
     for (int ii = 0; ii < 4; ++ii) {
       const int i = 16 * w + 4 * gq + ii, j = 16 * b + tl;
       const float kk = (b < w || j < i) ? ak[ii] : 0.f;
-      const float qk = (b < w || j <= i) ? aq[ii] : 0.f;
+      qk4[ii] = (b < w || j <= i) ? aq[ii] : 0.f;
       sKK[i * MP + j] = kk;
-      sAQ[i * MP + j] = qk;
       br[BR_KK + i * CH + j] = kk;
-      qk4[ii] = qk;
     }
     // A_qk^T[j][i]: rows j = 16b + tl, contraction i = 16w + 4gq + ii
     *reinterpret_cast<float4*>(br + BR_AQKT + frag32(16 * b + tl, 16 * w + 4 * gq, CH)) =
@@ -259,8 +262,9 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_prep_kernel(BwdArgs a) {
   __syncthreads();
 
   // ---- T = (I + diag(beta) KK)^-1.  Diagonal 16x16 blocks by forward
-  // substitution (lane tl owns column tl), zero upper blocks.
-  {
+  // substitution (waves with p = 0; lane tl owns column tl); waves with p = 1
+  // zero the upper blocks.
+  if (p == 0) {
     const int j = tl;
     float x[16];
 #pragma unroll
@@ -275,6 +279,7 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sT[(16 * w + i) * MP + 16 * w + j] = x[i];
     }
+  } else {
 #pragma unroll
     for (int b = 0; b < 4; ++b)
       if (b > w) {
@@ -283,10 +288,11 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_prep_kernel(BwdArgs a) {
       }
   }
   __syncthreads();
-  // off-diagonal blocks by diagonals: T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb
+  // off-diagonal blocks by diagonals: T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb,
+  // one 16 x 16 block per block row and level (waves with p = 0)
 #pragma unroll
   for (int d = 1; d < 4; ++d) {
-    if (w >= d) {
+    if (p == 0 && w >= d) {
       const int aa = w, bb = w - d;
       f32x4 X = zero4();
 #pragma unroll
@@ -307,36 +313,49 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_prep_kernel(BwdArgs a) {
     }
     __syncthreads();
   }
-  for (int e = tid; e < CH * CH; e += NT) br[BR_T + e] = sT[(e >> 6) * MP + (e & 63)];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = 4 * (tid + NTP * u);
+    *reinterpret_cast<float4*>(br + BR_T + e) = ld4(sT + (e >> 6) * MP + (e & 63));
+  }
 
-  // ---- W = Tb KG, row block w, contraction over tokens j < 16w + 16
+  // ---- W = Tb KG, row block w, channel tiles n of parity p; contraction over tokens j < 16w + 16
+  {
+    float tb[4][4];  // Tb[16w + tl][16 jb + 4 gq + s]
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      if (jb > w) continue;
+    for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int kap = 16 * jb + 4 * gq + s;
-        const int c = 16 * n + tl;
-        const float av = sT[(16 * w + tl) * MP + kap] * sBeta[kap];
-        const float bv = sKn[kap * QP + c] * fexp2(sG[kap * QP + c]);
-        acc = mfma_f32(av, bv, acc);
+        tb[jb][s] = sT[(16 * w + tl) * MP + kap] * sBeta[kap];
       }
+#pragma unroll
+    for (int n4 = 0; n4 < 4; ++n4) {
+      const int n = 2 * n4 + p;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        if (jb > w) continue;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int kap = 16 * jb + 4 * gq + s;
+          const int c = 16 * n + tl;
+          acc = mfma_f32(tb[jb][s], sKn[kap * QP + c] * fexp2(sG[kap * QP + c]), acc);
+        }
+      }
+      // W^T[k][i]: rows k = 16n + tl, contraction i = 16w + 4gq + ii
+      *reinterpret_cast<float4*>(br + BR_WT + frag32(16 * n + tl, 16 * w + 4 * gq, CH)) =
+          make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
-    // W^T[k][i]: rows k = 16n + tl, contraction i = 16w + 4gq + ii
-    *reinterpret_cast<float4*>(br + BR_WT + frag32(16 * n + tl, 16 * w + 4 * gq, CH)) =
-        make_float4(acc[0], acc[1], acc[2], acc[3]);
   }
 
-  // ---- Kt (thread: token tid / 4, 32 channels), QG^T (thread: channel tid / 2,
-  // 32 tokens), exp(G_L), beta
+  // ---- Kt (thread: token tid / 8, 16 channels), QG^T (thread: channel tid / 4,
+  // 16 tokens), exp(G_L), beta
   {
-    const int i = tid >> 2;
-    const int cq = tid & 3;
+    const int i = tid >> 3;
+    const int c8 = 16 * (tid & 7);
 #pragma unroll
-    for (int c = 32 * cq; c < 32 * cq + 32; c += 4) {
+    for (int c = c8; c < c8 + 16; c += 4) {
       const float4 kn = ld4(sKn + i * QP + c), gg = ld4(sG + i * QP + c);
       const float4 gl = ld4(sG + (CH - 1) * QP + c);
       float4 kt;
@@ -344,10 +363,10 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_prep_kernel(BwdArgs a) {
       kt.z = kn.z * fexp2(gl.z - gg.z); kt.w = kn.w * fexp2(gl.w - gg.w);
       *reinterpret_cast<float4*>(br + BR_KT + frag32(i, c, KD)) = kt;
     }
-    const int k = tid >> 1;
-    const int i0 = 32 * (tid & 1);
+    const int k = tid >> 2;
+    const int i0 = 16 * (tid & 3);
 #pragma unroll
-    for (int ib = i0; ib < i0 + 32; ib += 4) {
+    for (int ib = i0; ib < i0 + 16; ib += 4) {
       float q4[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) q4[u] = sQn[(ib + u) * QP + k] * fexp2(sG[(ib + u) * QP + k]);
@@ -1133,20 +1152,31 @@ __global__ void __launch_bounds__(NT8, 1) kda_bwd_grad_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// kda_bwd_reduce_kernel: per head, sum the per-chunk partials.
+// kda_bwd_reduce_kernel: per head, sum the per-chunk partials.  Thread t sums
+// column t % 129 over the chunks of residue t / 129 mod 4, then the four
+// partial sums meet in LDS.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(NT) kda_bwd_reduce_kernel(BwdArgs a) {
+constexpr int NTR = 4 * (KD + 1);
+
+__global__ void __launch_bounds__(NTR) kda_bwd_reduce_kernel(BwdArgs a) {
+  __shared__ float red[NTR];
   const int h = blockIdx.x;
   const int H = a.H;
   const int64_t nch = total_chunks(a.map);
   const int t = threadIdx.x;
-  if (t > KD) return;
+  const int col = t % (KD + 1);
+  const int rr = t / (KD + 1);
   float acc = 0.f;
-  for (int64_t g = 0; g < nch; ++g) acc += a.part[((size_t)g * H + h) * (KD + 1) + t];
-  if (t < KD)
-    a.ddt[(size_t)h * KD + t] = acc;
-  else
-    a.dA_log[h] = acc;
+  for (int64_t g = rr; g < nch; g += 4) acc += a.part[((size_t)g * H + h) * (KD + 1) + col];
+  red[t] = acc;
+  __syncthreads();
+  if (rr == 0) {
+    const float v = red[col] + red[(KD + 1) + col] + red[2 * (KD + 1) + col] + red[3 * (KD + 1) + col];
+    if (col < KD)
+      a.ddt[(size_t)h * KD + col] = v;
+    else
+      a.dA_log[h] = v;
+  }
 }
 
 }  // namespace
@@ -1157,7 +1187,7 @@ hipError_t launch_bwd(const BwdArgs& args, int64_t max_chunks, hipStream_t st) {
   const int64_t items = max_chunks * a.H;
   hipError_t e;
   if (items > 0) {
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_bwd_prep_kernel), dim3((unsigned)items), dim3(NT),
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_bwd_prep_kernel), dim3((unsigned)items), dim3(NTP),
                         kargs, 0, st);
     if (e != hipSuccess) return e;
   }
@@ -1170,7 +1200,7 @@ hipError_t launch_bwd(const BwdArgs& args, int64_t max_chunks, hipStream_t st) {
                         kargs, 0, st);
     if (e != hipSuccess) return e;
   }
-  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_bwd_reduce_kernel), dim3((unsigned)a.H), dim3(NT),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_bwd_reduce_kernel), dim3((unsigned)a.H), dim3(NTR),
                          kargs, 0, st);
 }
 
