@@ -173,3 +173,83 @@ def test_bwd_zero_tokens():
     np.testing.assert_array_equal(got["dA_log"], 0.0)
     np.testing.assert_array_equal(got["d_dt_bias"], 0.0)
     np.testing.assert_array_equal(got["d_initial_state"], d_fin.double().numpy())
+
+
+def test_bwd_near_collinear_c5():
+    """One key repeated along T = 16384 as both q and k (raw_beta 8, raw_gate -12): against the
+    chunked fp64 backward.  Two gradients need a bound other than the relative one:
+      * dq is exactly zero: the state stays k^ s^T, so dq^ is parallel to q^ and the L2 norm's
+        projection removes it (the fp64 reference holds ~1e-9 of rounding).  Its error is held to
+        1e-2 of the largest |dk|, the companion gradient of the same key.
+      * dA_log is a sum over every (token, channel) of d_raw_gate (raw_gate + dt_bias) whose terms
+        cancel to ~1e-8 of their magnitude here.  It is held to the summation error bound:
+        |error| <= 1e-2 * sum |term|, the terms taken from the oracle's own d_raw_gate.
+    Every other gradient, d dt_bias included, meets the relative bar."""
+    x = W.c5_collinear()
+    d_out, d_fin = cotangents(x, 9)
+    got = gpu_bwd(x, d_out, d_fin)
+    ref = oracle(x, d_out, d_fin, chunked=True)
+    compare(got, ref, names=tuple(n for n in NAMES if n not in ("dq", "dA_log")))
+    err = np.abs(got["dq"] - ref["dq"]).max()
+    print(f"  dq: max abs err {err:.2e} (|dk| max {np.abs(ref['dk']).max():.2e})", flush=True)
+    assert np.isfinite(got["dq"]).all() and err <= 1e-2 * np.abs(ref["dk"]).max()
+    z = (x.raw_gate.double().reshape(x.B * x.T, x.H, x.K) + x.dt_bias.double()).numpy()
+    bound = np.abs(ref["d_raw_gate"] * z).sum(axis=(0, 2))
+    err = np.abs(got["dA_log"] - ref["dA_log"])
+    print(f"  dA_log: err/bound {np.max(err / bound):.2e}", flush=True)
+    assert np.isfinite(got["dA_log"]).all() and (err <= 1e-2 * bound).all()
+
+
+def test_bwd_varlen_c4_sampled():
+    """The full C4 batch (16 packed sequences of lengths U[1, 8192], H = 32) on the GPU.  Sampled
+    outputs: for heads 5 and 30, the token gradients and initial-state gradient of sequences 6, 11
+    (the two shortest) and 14 (the longest) against the chunked fp64 backward of that sequence
+    alone (sequences are independent).  The parameter gradients, sums over every sequence, are
+    checked at C2 size and by the packed-versus-separate test."""
+    x = W.c4_varlen()
+    d_out, d_fin = cotangents(x, 10)
+    got = gpu_bwd(x, d_out, d_fin)
+    cu = x.cu_seqlens.tolist()
+    per_token = ("dq", "dk", "dv", "d_raw_gate", "d_raw_beta")
+    for n in (6, 11, 14):
+        s_, e_ = cu[n], cu[n + 1]
+        for h in (5, 30):
+            xs = W.KdaInputs(name=f"c4_seq{n}_head{h}", q=x.q[:, s_:e_, h:h + 1].contiguous(),
+                             k=x.k[:, s_:e_, h:h + 1].contiguous(), v=x.v[:, s_:e_, h:h + 1].contiguous(),
+                             raw_gate=x.raw_gate[:, s_:e_, h:h + 1].contiguous(),
+                             raw_beta=x.raw_beta[:, s_:e_, h:h + 1].contiguous(),
+                             A_log=x.A_log[h:h + 1].contiguous(), dt_bias=x.dt_bias[h:h + 1].contiguous(),
+                             initial_state=x.initial_state[n:n + 1, h:h + 1].contiguous(), cu_seqlens=None,
+                             scale=x.scale, lower_bound=x.lower_bound)
+            ref = oracle(xs, d_out[:, s_:e_, h:h + 1].contiguous(), d_fin[n:n + 1, h:h + 1].contiguous(),
+                         chunked=True)
+            sub = {k_: got[k_][s_:e_, h:h + 1] for k_ in per_token}
+            sub["d_initial_state"] = got["d_initial_state"][n:n + 1, h:h + 1]
+            compare(sub, ref, names=per_token + ("d_initial_state",))
+
+
+def test_bwd_final_state_gradient_only():
+    """d_out = 0: every gradient flows back from the final state alone."""
+    x = W.random_inputs("bwd_fin_only", 207, 1, 150, 2)
+    d_out, d_fin = cotangents(x, 11)
+    d_out = torch.zeros_like(d_out)
+    compare(gpu_bwd(x, d_out, d_fin), oracle(x, d_out, d_fin))
+
+
+def test_bwd_initial_state_gradient_in_place():
+    """d_initial_state may be the d_final buffer itself."""
+    x = W.random_inputs("bwd_inplace", 208, 2, 100, 2)
+    d_out, d_fin = cotangents(x, 12)
+    ref = gpu_bwd(x, d_out, d_fin)
+    B, T, H, K, V, N = x.B, x.T, x.H, x.K, x.V, x.N
+    bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=DEV)  # noqa: E731
+    dq, dk, dg, dv, db = bf(B, T, H, K), bf(B, T, H, K), bf(B, T, H, K), bf(B, T, H, V), bf(B, T, H)
+    dA, ddt = torch.empty(H, device=DEV), torch.empty(H, K, device=DEV)
+    buf = d(d_fin).clone()
+    ws = torch.empty(kda.kda_bwd_workspace_size(B * T, H, N), dtype=torch.uint8, device=DEV)
+    kda.kda_bwd(d(x.q), d(x.k), d(x.v), d(x.raw_gate), d(x.raw_beta), x.scale, d(d_out), dq, dk, dv, dg, db, dA,
+                ddt, ws, d(x.A_log), d(x.dt_bias), x.lower_bound, initial_state=d(x.initial_state), d_final=buf,
+                d_initial_state=buf)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(buf.double().cpu().numpy(), ref["d_initial_state"])
+    np.testing.assert_array_equal(dq.double().cpu().numpy().reshape(B * T, H, K), ref["dq"])
