@@ -41,26 +41,37 @@ constexpr int NT = 256;
 constexpr int QP = KD + 4;  // pitch (floats) of [64][128] LDS tiles
 constexpr int MP = CH + 4;  // pitch of [64][64] LDS tiles
 constexpr int VH = VD / 2;  // state columns per recurrence workgroup
-constexpr int DP = VH + 4;  // pitch of the recurrence kernel's LDS tiles
 
-// fp32 chunk record of the backward (offsets in floats).  The operands of the
-// reverse recurrence are stored in fp32 A-operand fragment order (frag32).
+// Chunk record of the backward (offsets in floats).  T and KK are fp32,
+// row-major.  The four operands of the reverse recurrence are bf16 hi/lo
+// pairs in the forward record's MFMA fragment order (frag_tc / frag_tt /
+// frag_ct): the hi array of a region, then its lo array.  The output scale is
+// folded into A_qk^T and QG^T, and W^T is stored negated.
 constexpr int BR_T = 0;                   // T = (I + diag(beta) KK)^-1, unit lower, [64][64] row-major
 constexpr int BR_KK = BR_T + CH * CH;     // KK = K^ K^T . decay, strictly lower,     [64][64] row-major
-constexpr int BR_AQKT = BR_KK + CH * CH;  // A operand A_qk^T (rows i, contraction j), frag32
-constexpr int BR_WT = BR_AQKT + CH * CH;  // A operand W^T  (rows k, contraction i),   frag32
-constexpr int BR_KT = BR_WT + CH * KD;    // A operand Kt = K^ exp(G_L - G) (rows i, contraction k), frag32
-constexpr int BR_QGT = BR_KT + CH * KD;   // A operand QG^T = (Q^ exp(G))^T (rows k, contraction i), frag32
+constexpr int BR_AQKT = BR_KK + CH * CH;  // scale A_qk^T (rows i, contraction j),  frag_tt, hi + lo
+constexpr int BR_WT = BR_AQKT + CH * CH;  // -W^T (rows k, contraction i),          frag_ct, hi + lo
+constexpr int BR_KT = BR_WT + CH * KD;    // Kt = K^ exp(G_L - G) (rows i, contraction k), frag_tc, hi + lo
+constexpr int BR_QGT = BR_KT + CH * KD;   // scale QG^T (rows k, contraction i),     frag_ct, hi + lo
 constexpr int BR_GL = BR_QGT + CH * KD;   // exp(G_L)                                 [128]
 constexpr int BR_BETA = BR_GL + KD;       // beta                                     [64]
 static_assert(BR_BETA + CH == BWD_REC_FLOATS, "record size");
 
-// fp32 A-operand fragment order: element (r, kap) of an A operand with C
-// contraction columns lies in 16 x 16 tile (r / 16, kap / 16); inside it, lane
-// 16 ((kap / 4) % 4) + r % 16 holds kap % 4 of one float4, so one wave-wide
-// float4 load of a tile reads 1 KB of contiguous memory.
-__host__ __device__ constexpr int frag32(int r, int kap, int C) {
-  return ((((r >> 4) * (C >> 4) + (kap >> 4)) * 64 + ((kap >> 2) & 3) * 16 + (r & 15)) << 2) + (kap & 3);
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Store x0..x3 (4 consecutive fragment elements starting at idx) of an n-element
+// bf16 hi/lo region: hi at idx, lo = x - hi at n + idx.
+__device__ __forceinline__ void store_hl4(float* region, int n, int idx, float x0, float x1, float x2, float x3) {
+  __bf16* hi = reinterpret_cast<__bf16*>(region);
+  const float x[4] = {x0, x1, x2, x3};
+  bf16x4 h, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = (__bf16)x[e];
+    l[e] = (__bf16)(x[e] - (float)h[e]);
+  }
+  *reinterpret_cast<bf16x4*>(hi + idx) = h;
+  *reinterpret_cast<bf16x4*>(hi + n + idx) = l;
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
@@ -225,8 +236,7 @@ __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
         br[BR_KK + i * CH + j] = 0.f;
       }
       // A_qk^T tile (rows block b, contraction block w) is above the diagonal: zero
-      *reinterpret_cast<float4*>(br + BR_AQKT + frag32(16 * b + tl, 16 * w + 4 * gq, CH)) =
-          make_float4(0.f, 0.f, 0.f, 0.f);
+      store_hl4(br + BR_AQKT, CH * CH, frag_tt(16 * b + tl, 16 * w + 4 * gq), 0.f, 0.f, 0.f, 0.f);
       continue;
     }
     const int r = (b < w) ? 16 * b + 15 : 16 * w;
@@ -255,9 +265,9 @@ __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
       sKK[i * MP + j] = kk;
       br[BR_KK + i * CH + j] = kk;
     }
-    // A_qk^T[j][i]: rows j = 16b + tl, contraction i = 16w + 4gq + ii
-    *reinterpret_cast<float4*>(br + BR_AQKT + frag32(16 * b + tl, 16 * w + 4 * gq, CH)) =
-        make_float4(qk4[0], qk4[1], qk4[2], qk4[3]);
+    // scale A_qk^T[j][i]: rows j = 16b + tl, contraction i = 16w + 4gq + ii
+    store_hl4(br + BR_AQKT, CH * CH, frag_tt(16 * b + tl, 16 * w + 4 * gq), a.scale * qk4[0], a.scale * qk4[1],
+              a.scale * qk4[2], a.scale * qk4[3]);
   }
   __syncthreads();
 
@@ -343,9 +353,8 @@ __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
           acc = mfma_f32(tb[jb][s], sKn[kap * QP + c] * fexp2(sG[kap * QP + c]), acc);
         }
       }
-      // W^T[k][i]: rows k = 16n + tl, contraction i = 16w + 4gq + ii
-      *reinterpret_cast<float4*>(br + BR_WT + frag32(16 * n + tl, 16 * w + 4 * gq, CH)) =
-          make_float4(acc[0], acc[1], acc[2], acc[3]);
+      // -W^T[k][i]: rows k = 16n + tl, contraction i = 16w + 4gq + ii
+      store_hl4(br + BR_WT, CH * KD, frag_ct(16 * n + tl, 16 * w + 4 * gq), -acc[0], -acc[1], -acc[2], -acc[3]);
     }
   }
 
@@ -361,7 +370,7 @@ __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
       float4 kt;
       kt.x = kn.x * fexp2(gl.x - gg.x); kt.y = kn.y * fexp2(gl.y - gg.y);
       kt.z = kn.z * fexp2(gl.z - gg.z); kt.w = kn.w * fexp2(gl.w - gg.w);
-      *reinterpret_cast<float4*>(br + BR_KT + frag32(i, c, KD)) = kt;
+      store_hl4(br + BR_KT, CH * KD, frag_tc(i, c), kt.x, kt.y, kt.z, kt.w);
     }
     const int k = tid >> 2;
     const int i0 = 16 * (tid & 3);
@@ -369,8 +378,8 @@ __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
     for (int ib = i0; ib < i0 + 16; ib += 4) {
       float q4[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) q4[u] = sQn[(ib + u) * QP + k] * fexp2(sG[(ib + u) * QP + k]);
-      *reinterpret_cast<float4*>(br + BR_QGT + frag32(k, ib, CH)) = make_float4(q4[0], q4[1], q4[2], q4[3]);
+      for (int u = 0; u < 4; ++u) q4[u] = a.scale * sQn[(ib + u) * QP + k] * fexp2(sG[(ib + u) * QP + k]);
+      store_hl4(br + BR_QGT, CH * KD, frag_ct(k, ib), q4[0], q4[1], q4[2], q4[3]);
     }
     if (tid < KD) br[BR_GL + tid] = fexp2(sG[(CH - 1) * QP + tid]);
     if (tid < CH) br[BR_BETA + tid] = sBeta[tid];
@@ -379,35 +388,53 @@ __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // kda_bwd_dhu_kernel: per (sequence, head, V half), chunks in reverse order.
-// The state gradient dS stays in MFMA accumulators: wave w holds channels
-// 32w + 16mt + 4gq + ii and, in "virtual tile" e, columns vs + 4 tl + e, so
-// that every LDS and global access of a state or V-wide row is a float4.
-// The next chunk's record operands (fragment order, one 1 KB block per wave
-// load) and dO rows are loaded one chunk ahead.
+// bf16 MFMA 16x16x32 with hi/lo splits on both sides of every product that
+// has an fp32 operand (3 passes), 2 passes where one side is the exact bf16
+// dO.  The state gradient dS stays in fp32 MFMA accumulators: wave w holds
+// channels 32w + 16mt + 4gq + ii, columns vs + 16nn + tl.  Its bf16 hi/lo
+// copy, the dO tile and dD hi/lo live in LDS column-major, so every B operand
+// is one 16-byte LDS read.  The next chunk's record operands and dO rows are
+// loaded one chunk ahead.
 // ---------------------------------------------------------------------------
-constexpr int DHU_FLOATS = KD * DP + 2 * CH * DP;
+constexpr int SPB = KD + 8;  // channel pitch of the [v][k] bf16 state copies
+constexpr int TPB = CH + 8;  // token pitch of the [v][i] bf16 tiles
+constexpr int DHU_BYTES = 2 * VH * SPB * 2 + 3 * VH * TPB * 2;
 
 struct DhuOps {
-  float4 kt[8];      // Kt, rows 16w + tl, contraction block t
-  float4 aq[4];      // A_qk^T, rows 16w + tl, contraction block jb (zero for jb < w)
-  float4 qg[2][4];   // QG^T, rows 32w + 16mt + tl, contraction block t
-  float4 wt[2][4];   // W^T
-  float4 gl[2];      // exp(G_L) of channels 32w + 16mt + 4gq + 0..3
-  uint4 dob[2];      // dO row tid / 4, columns vs + 16 (tid % 4) .. + 15 (zero past the end)
+  bf16x8 kth[4], ktl[4];          // Kt rows 16w + tl, channels 32kb + 8gq ..
+  bf16x8 aqh[2], aql[2];          // scale A_qk^T rows 16w + tl, tokens 32ks + 8gq ..
+  bf16x8 qgh[2][2], qgl[2][2];    // scale QG^T rows 32w + 16mt + tl, tokens 32ks + 8gq ..
+  bf16x8 wth[2][2], wtl[2][2];    // -W^T
+  float4 gl[2];                   // exp(G_L) of channels 32w + 16mt + 4gq + 0..3
+  uint4 dob[2];                   // dO row tid / 4, columns vs + 16 (tid % 4) .. + 15 (zero past the end)
 };
 
 __device__ __forceinline__ void dhu_load(DhuOps& o, const float* br, const uint16_t* dorow, bool rowok, int w,
                                          int lane, int gq) {
+  const bf16x8* kt = reinterpret_cast<const bf16x8*>(br + BR_KT) + lane;
+  const bf16x8* aq = reinterpret_cast<const bf16x8*>(br + BR_AQKT) + lane;
+  const bf16x8* qg = reinterpret_cast<const bf16x8*>(br + BR_QGT) + lane;
+  const bf16x8* wt = reinterpret_cast<const bf16x8*>(br + BR_WT) + lane;
+  constexpr int LO_TC = CH * KD / 8, LO_TT = CH * CH / 8;  // lo arrays, in 16-byte units
 #pragma unroll
-  for (int t = 0; t < 8; ++t) o.kt[t] = ld4(br + BR_KT + (((w * 8 + t) * 64 + lane) << 2));
+  for (int kb = 0; kb < 4; ++kb) {
+    o.kth[kb] = kt[(w * 4 + kb) * 64];
+    o.ktl[kb] = kt[LO_TC + (w * 4 + kb) * 64];
+  }
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) o.aq[jb] = ld4(br + BR_AQKT + (((w * 4 + jb) * 64 + lane) << 2));
+  for (int ks = 0; ks < 2; ++ks) {
+    o.aqh[ks] = aq[(w * 2 + ks) * 64];
+    o.aql[ks] = aq[LO_TT + (w * 2 + ks) * 64];
+  }
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      o.qg[mt][t] = ld4(br + BR_QGT + ((((2 * w + mt) * 4 + t) * 64 + lane) << 2));
-      o.wt[mt][t] = ld4(br + BR_WT + ((((2 * w + mt) * 4 + t) * 64 + lane) << 2));
+    for (int ks = 0; ks < 2; ++ks) {
+      const int f = ((2 * w + mt) * 2 + ks) * 64;
+      o.qgh[mt][ks] = qg[f];
+      o.qgl[mt][ks] = qg[LO_TC + f];
+      o.wth[mt][ks] = wt[f];
+      o.wtl[mt][ks] = wt[LO_TC + f];
     }
     o.gl[mt] = ld4(br + BR_GL + 32 * w + 16 * mt + 4 * gq);
   }
@@ -419,11 +446,46 @@ __device__ __forceinline__ void dhu_load(DhuOps& o, const float* br, const uint1
   }
 }
 
+// dO tile, transposed into sO[v][i] (2 tokens per dword).  Thread -> (token
+// tid / 4, columns 16 (tid % 4) .. + 15); lanes of tokens t, t ^ 1 (4 lanes
+// apart) trade half their columns, so each lane writes 8 packed dwords.
+__device__ __forceinline__ void store_dot(__bf16* sO, const uint4 (&vv)[2], int tid) {
+  const int t = tid >> 2;
+  const int cg = tid & 3;
+  const bool odd = t & 1;
+  const uint32_t wds[8] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w, vv[1].x, vv[1].y, vv[1].z, vv[1].w};
+  uint32_t mine[4], recv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    mine[j] = odd ? wds[4 + j] : wds[j];
+    recv[j] = (uint32_t)__shfl_xor((int)(odd ? wds[j] : wds[4 + j]), 4);
+  }
+  const int tp = t & ~1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = 16 * cg + (odd ? 8 : 0) + 2 * j;
+    const uint32_t lo = odd ? recv[j] : mine[j];  // token tp
+    const uint32_t hi = odd ? mine[j] : recv[j];  // token tp + 1
+    *reinterpret_cast<uint32_t*>(sO + c * TPB + tp) = (lo & 0xffffu) | (hi << 16);
+    *reinterpret_cast<uint32_t*>(sO + (c + 1) * TPB + tp) = (lo >> 16) | (hi & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ void split_hl4(const f32x4& x, bf16x4& h, bf16x4& l) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = (__bf16)x[e];
+    l[e] = (__bf16)(x[e] - (float)h[e]);
+  }
+}
+
 __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) float smem[DHU_FLOATS];
-  float* sdS = smem;             // [128 k][DP]  dS' columns of this half
-  float* sdO = sdS + KD * DP;    // [64 i][DP]   scale * dO
-  float* sdD = sdO + CH * DP;    // [64 i][DP]   dD
+  __shared__ __attribute__((aligned(16))) char smem[DHU_BYTES];
+  __bf16* sSh = reinterpret_cast<__bf16*>(smem);   // [64 v][SPB]  dS' hi
+  __bf16* sSl = sSh + VH * SPB;                     // [64 v][SPB]  dS' lo
+  __bf16* sO = sSl + VH * SPB;                      // [64 v][TPB]  dO (unscaled, exact)
+  __bf16* sDh = sO + VH * TPB;                      // [64 v][TPB]  dD hi
+  __bf16* sDl = sDh + VH * TPB;                     // [64 v][TPB]  dD lo
 
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
@@ -446,7 +508,7 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
   const int lane = tid & 63;
   const int tl = lane & 15;
   const int gq = lane >> 4;
-  const int orow = tid >> 2;          // dO staging: row and 16 columns
+  const int orow = tid >> 2;  // dO staging: row and 16 columns
   const int ocol = 16 * (tid & 3);
 
   f32x4 dS[2][4];
@@ -455,18 +517,13 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int kr = 32 * w + 16 * mt + 4 * gq + ii;
-        const float4 v4 = src ? ld4(src + kr * VD + vs + 4 * tl) : make_float4(0.f, 0.f, 0.f, 0.f);
-        dS[mt][0][ii] = v4.x;
-        dS[mt][1][ii] = v4.y;
-        dS[mt][2][ii] = v4.z;
-        dS[mt][3][ii] = v4.w;
-      }
+      for (int nn = 0; nn < 4; ++nn)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          dS[mt][nn][ii] = src ? src[(32 * w + 16 * mt + 4 * gq + ii) * VD + vs + 16 * nn + tl] : 0.f;
   }
-  auto chunk_start = [&](int ci) { return bos + (int64_t)ci * CH; };
   auto dorow_of = [&](int ci, bool& ok) {
-    const int64_t c0 = chunk_start(ci);
+    const int64_t c0 = bos + (int64_t)ci * CH;
     ok = c0 + orow < eos;
     return a.dout + ((size_t)(c0 + (ok ? orow : 0)) * H + h) * VD + vs + ocol;
   };
@@ -488,93 +545,82 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
       dhu_load(nxt, a.br + ((size_t)(gfirst + cn) * H + h) * BWD_REC_FLOATS, dr, ok, w, lane, gq);
     }
 
-    // dS' of this chunk: to the checkpoint buffer and to LDS
+    // dS' of this chunk: fp32 to the checkpoint buffer, bf16 hi/lo to LDS
     float* dsg = a.dstates + it * KD * VD;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int kr = 32 * w + 16 * mt + 4 * gq + ii;
-        const float4 v4 = make_float4(dS[mt][0][ii], dS[mt][1][ii], dS[mt][2][ii], dS[mt][3][ii]);
-        *reinterpret_cast<float4*>(dsg + kr * VD + vs + 4 * tl) = v4;
-        *reinterpret_cast<float4*>(sdS + kr * DP + 4 * tl) = v4;
-      }
-    // scale * dO tile
-    {
-      float t0[8], t1[8];
-      unpack_bf16x8(cur.dob[0], t0);
-      unpack_bf16x8(cur.dob[1], t1);
-      float* dst = sdO + orow * DP + ocol;
+      for (int nn = 0; nn < 4; ++nn) {
+        const int k0 = 32 * w + 16 * mt + 4 * gq;
+        const int col = 16 * nn + tl;
 #pragma unroll
-      for (int e = 0; e < 8; e += 4) {
-        *reinterpret_cast<float4*>(dst + e) =
-            make_float4(t0[e] * a.scale, t0[e + 1] * a.scale, t0[e + 2] * a.scale, t0[e + 3] * a.scale);
-        *reinterpret_cast<float4*>(dst + 8 + e) =
-            make_float4(t1[e] * a.scale, t1[e + 1] * a.scale, t1[e + 2] * a.scale, t1[e + 3] * a.scale);
+        for (int ii = 0; ii < 4; ++ii) dsg[(k0 + ii) * VD + vs + col] = dS[mt][nn][ii];
+        bf16x4 hv, lv;
+        split_hl4(dS[mt][nn], hv, lv);
+        *reinterpret_cast<bf16x4*>(sSh + col * SPB + k0) = hv;
+        *reinterpret_cast<bf16x4*>(sSl + col * SPB + k0) = lv;
       }
-    }
+    store_dot(sO, cur.dob, tid);
     __syncthreads();
 
-    // dD rows 16w.. = Kt dS' + A_qk^T (scale dO)
-    f32x4 dD[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dD[e] = zero4();
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const float4 b4 = ld4(sdS + (16 * t + 4 * gq + s) * DP + 4 * tl);
-        const float av = el(cur.kt[t], s);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dD[e] = mfma_f32(av, el(b4, e), dD[e]);
-      }
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const float4 b4 = ld4(sdO + (16 * jb + 4 * gq + s) * DP + 4 * tl);
-        const float av = el(cur.aq[jb], s);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dD[e] = mfma_f32(av, el(b4, e), dD[e]);
-      }
+    // dD rows 16w.. = Kt dS' + (scale A_qk^T) dO
     float* ddg = a.ddtile + it * CH * VD;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int i = 16 * w + 4 * gq + ii;
-      const float4 v4 = make_float4(dD[0][ii], dD[1][ii], dD[2][ii], dD[3][ii]);
-      *reinterpret_cast<float4*>(ddg + i * VD + vs + 4 * tl) = v4;
-      *reinterpret_cast<float4*>(sdD + i * DP + 4 * tl) = v4;
+    for (int nn = 0; nn < 4; ++nn) {
+      const int col = 16 * nn + tl;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(sSh + col * SPB + 32 * kb + 8 * gq);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(sSl + col * SPB + 32 * kb + 8 * gq);
+        acc = mfma_bf16(cur.kth[kb], bh, acc);
+        acc = mfma_bf16(cur.kth[kb], bl, acc);
+        acc = mfma_bf16(cur.ktl[kb], bh, acc);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 ob = *reinterpret_cast<const bf16x8*>(sO + col * TPB + 32 * ks + 8 * gq);
+        acc = mfma_bf16(cur.aqh[ks], ob, acc);
+        acc = mfma_bf16(cur.aql[ks], ob, acc);
+      }
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) ddg[(16 * w + 4 * gq + ii) * VD + vs + col] = acc[ii];
+      bf16x4 hv, lv;
+      split_hl4(acc, hv, lv);
+      *reinterpret_cast<bf16x4*>(sDh + col * TPB + 16 * w + 4 * gq) = hv;
+      *reinterpret_cast<bf16x4*>(sDl + col * TPB + 16 * w + 4 * gq) = lv;
     }
     __syncthreads();
 
-    // dS = Diag(exp(G_L)) dS' + QG^T (scale dO) - W^T dD
+    // dS = Diag(exp(G_L)) dS' + (scale QG^T) dO + (-W^T) dD
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int nn = 0; nn < 4; ++nn) {
+      const int col = 16 * nn + tl;
+      bf16x8 ob[2], dh[2], dl[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dS[mt][e][0] *= cur.gl[mt].x;
-        dS[mt][e][1] *= cur.gl[mt].y;
-        dS[mt][e][2] *= cur.gl[mt].z;
-        dS[mt][e][3] *= cur.gl[mt].w;
+      for (int ks = 0; ks < 2; ++ks) {
+        ob[ks] = *reinterpret_cast<const bf16x8*>(sO + col * TPB + 32 * ks + 8 * gq);
+        dh[ks] = *reinterpret_cast<const bf16x8*>(sDh + col * TPB + 32 * ks + 8 * gq);
+        dl[ks] = *reinterpret_cast<const bf16x8*>(sDl + col * TPB + 32 * ks + 8 * gq);
       }
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x4 st = dS[mt][nn];
+        st[0] *= cur.gl[mt].x;
+        st[1] *= cur.gl[mt].y;
+        st[2] *= cur.gl[mt].z;
+        st[3] *= cur.gl[mt].w;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int kap = 16 * t + 4 * gq + s;
-        const float4 o4 = ld4(sdO + kap * DP + 4 * tl);
-        const float4 d4 = ld4(sdD + kap * DP + 4 * tl);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const float aqg = el(cur.qg[mt][t], s);
-          const float aw = -el(cur.wt[mt][t], s);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            dS[mt][e] = mfma_f32(aqg, el(o4, e), dS[mt][e]);
-            dS[mt][e] = mfma_f32(aw, el(d4, e), dS[mt][e]);
-          }
+        for (int ks = 0; ks < 2; ++ks) {
+          st = mfma_bf16(cur.qgh[mt][ks], ob[ks], st);
+          st = mfma_bf16(cur.qgl[mt][ks], ob[ks], st);
+          st = mfma_bf16(cur.wth[mt][ks], dh[ks], st);
+          st = mfma_bf16(cur.wth[mt][ks], dl[ks], st);
+          st = mfma_bf16(cur.wtl[mt][ks], dh[ks], st);
         }
+        dS[mt][nn] = st;
       }
+    }
     __syncthreads();
     cur = nxt;
   }
@@ -584,11 +630,10 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int kr = 32 * w + 16 * mt + 4 * gq + ii;
-        *reinterpret_cast<float4*>(dst + kr * VD + vs + 4 * tl) =
-            make_float4(dS[mt][0][ii], dS[mt][1][ii], dS[mt][2][ii], dS[mt][3][ii]);
-      }
+      for (int nn = 0; nn < 4; ++nn)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          dst[(32 * w + 16 * mt + 4 * gq + ii) * VD + vs + 16 * nn + tl] = dS[mt][nn][ii];
   }
 }
 
