@@ -19,9 +19,12 @@
 //   kda_bwd_dhu_kernel     per (sequence, head, V half): the reverse recurrence -> dS', dD
 //   kda_bwd_grad_kernel    per (chunk, head): dq, dk, dv, d raw_gate, d raw_beta, partials
 //   kda_bwd_reduce_kernel  per head: dA_log and d dt_bias from the per-chunk partials
-// All arithmetic is fp32 (fp32 MFMA 16x16x4).  Exponents are kept in log2
-// units and every exp(G_i - G_j) factor is split at a reference token between
-// i and j (16-token sub-chunks), so no factor leaves fp32 range.
+// Arithmetic is fp32 throughout: fp32 MFMA 16x16x4, or bf16 MFMA 16x16x32 with
+// every fp32 operand split into a bf16 hi/lo pair (3 passes; 2 where the other
+// side is an exact bf16 input), which keeps about 16 significant bits per
+// operand.  Exponents are kept in log2 units and every exp(G_i - G_j) factor
+// is split at a reference token between i and j (16-token sub-chunks), so no
+// factor leaves fp32 range.
 //
 // fp32 MFMA convention used throughout: in k-step s of a 16-wide contraction
 // block starting at `base`, lane (gq = lane / 16, tl = lane % 16) supplies
@@ -72,6 +75,20 @@ __device__ __forceinline__ void store_hl4(float* region, int n, int idx, float x
   }
   *reinterpret_cast<bf16x4*>(hi + idx) = h;
   *reinterpret_cast<bf16x4*>(hi + n + idx) = l;
+}
+
+__device__ __forceinline__ void split_hl8(const float (&x)[8], bf16x8& h, bf16x8& l) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = (__bf16)x[e];
+    l[e] = (__bf16)(x[e] - (float)h[e]);
+  }
+}
+// 8 consecutive floats from global memory as a bf16 hi/lo pair
+__device__ __forceinline__ void ld_hl8(const float* p, bf16x8& h, bf16x8& l) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  split_hl8(x, h, l);
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
@@ -769,19 +786,33 @@ __global__ void __launch_bounds__(NT8, 1) kda_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) Zt[e][ii] = vv[4 * ii + e] - Zt[e][ii];
   }
-  // ---- dTb[i][jw] for i >= 16w, V half p (atomically summed over p): dD Z^T
+  // ---- dTb[i][jw] for i >= 16w, V half p (atomically summed over p): dD Z^T on
+  // bf16 MFMA, hi/lo on both sides.  k-step `half` takes v = 64p + 16gq + 8half + 0..7,
+  // which Zt holds as Zt[e8 % 4][2 half + e8 / 4].
+  {
+    bf16x8 zh[2], zl[2];
 #pragma unroll
-  for (int ab = 0; ab < 4; ++ab) {
-    if (ab < w) continue;
-    f32x4 acc = zero4();
+    for (int half = 0; half < 2; ++half) {
+      float zx[8];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const float4 a4 = ld4(dDt + (16 * ab + tl) * VD + 64 * p + 16 * gq + 4 * s);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc = mfma_f32(el(a4, e), Zt[e][s], acc);
+      for (int e8 = 0; e8 < 8; ++e8) zx[e8] = Zt[e8 & 3][2 * half + (e8 >> 2)];
+      split_hl8(zx, zh[half], zl[half]);
     }
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) atomicAdd(sM2 + (16 * ab + 4 * gq + ii) * MP + jw, acc[ii]);
+    for (int ab = 0; ab < 4; ++ab) {
+      if (ab < w) continue;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 ah, al;
+        ld_hl8(dDt + (16 * ab + tl) * VD + 64 * p + 16 * gq + 8 * half, ah, al);
+        acc = mfma_bf16(ah, zh[half], acc);
+        acc = mfma_bf16(ah, zl[half], acc);
+        acc = mfma_bf16(al, zh[half], acc);
+      }
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) atomicAdd(sM2 + (16 * ab + 4 * gq + ii) * MP + jw, acc[ii]);
+    }
   }
   KDA_TIMER_MARK(3);
 
@@ -823,21 +854,25 @@ __global__ void __launch_bounds__(NT8, 1) kda_bwd_grad_kernel(BwdArgs a) {
   }
   KDA_TIMER_MARK(4);
 
-  // ---- scale * dO[jw][v] as A operands, v = 64 hv + 16 gq + 4 ii + e
-  float doa[2][16];
+  // ---- bf16 MFMA operands over v for the products below.  k-step (hv, half)
+  // takes v = 64hv + 16gq + 8half + 0..7 in lane group gq:
+  //   dO[jw][v] (exact bf16, the scale is applied to the results),
+  //   -dv[jw][v] hi/lo (dvT holds it as dvT[hv][e8 % 4][2 half + e8 / 4]),
+  //   D[jw][v] hi/lo (loaded where it is used).
+  bf16x8 doA[2][2], dvh[2][2], dvl[2][2];
 #pragma unroll
-  for (int hv = 0; hv < 2; ++hv) {
-    if (jok) {
-      const uint4* src = reinterpret_cast<const uint4*>(a.dout + jrow * VD + 64 * hv + 16 * gq);
-      unpack_bf16x8(src[0], *reinterpret_cast<float(*)[8]>(doa[hv]));
-      unpack_bf16x8(src[1], *reinterpret_cast<float(*)[8]>(doa[hv] + 8));
+  for (int hv = 0; hv < 2; ++hv)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) doa[hv][r] *= a.scale;
-    } else {
+    for (int half = 0; half < 2; ++half) {
+      if (jok)
+        doA[hv][half] = *reinterpret_cast<const bf16x8*>(a.dout + jrow * VD + 64 * hv + 16 * gq + 8 * half);
+      else
+        doA[hv][half] = bf16x8{};
+      float x[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) doa[hv][r] = 0.f;
+      for (int e8 = 0; e8 < 8; ++e8) x[e8] = -dvT[hv][e8 & 3][2 * half + (e8 >> 2)];
+      split_hl8(x, dvh[hv][half], dvl[hv][half]);
     }
-  }
   // ---- dA_qk[block w][block b] = scale dO D^T (j <= i), column blocks b <= w of parity p
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -846,15 +881,16 @@ __global__ void __launch_bounds__(NT8, 1) kda_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int hv = 0; hv < 2; ++hv)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const float4 d4 = ld4(Dt + (16 * b + tl) * VD + 64 * hv + 16 * gq + 4 * ii);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc = mfma_f32(doa[hv][4 * ii + e], el(d4, e), acc);
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 bh, bl;
+        ld_hl8(Dt + (16 * b + tl) * VD + 64 * hv + 16 * gq + 8 * half, bh, bl);
+        acc = mfma_bf16(doA[hv][half], bh, acc);
+        acc = mfma_bf16(doA[hv][half], bl, acc);
       }
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int i = 16 * w + 4 * gq + ii, j = 16 * b + tl;
-      sM1[i * MP + j] = (j <= i) ? acc[ii] : 0.f;
+      sM1[i * MP + j] = (j <= i) ? acc[ii] * a.scale : 0.f;
     }
   }
 
@@ -868,17 +904,22 @@ __global__ void __launch_bounds__(NT8, 1) kda_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int hv = 0; hv < 2; ++hv)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const float4 s0 = ld4(S0 + kc * VD + 64 * hv + 16 * gq + 4 * ii);
-        const float4 dsn = ld4(dSn + kc * VD + 64 * hv + 16 * gq + 4 * ii);
-        const float4 d4 = ld4(Dt + jw * VD + 64 * hv + 16 * gq + 4 * ii);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          aQ = mfma_f32(doa[hv][4 * ii + e], el(s0, e), aQ);
-          aK = mfma_f32(-dvT[hv][e][ii], el(s0, e), aK);
-          aT = mfma_f32(el(d4, e), el(dsn, e), aT);
-        }
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 sh, sl, th, tl8, dah, dal;
+        ld_hl8(S0 + kc * VD + 64 * hv + 16 * gq + 8 * half, sh, sl);
+        ld_hl8(dSn + kc * VD + 64 * hv + 16 * gq + 8 * half, th, tl8);
+        ld_hl8(Dt + jw * VD + 64 * hv + 16 * gq + 8 * half, dah, dal);
+        aQ = mfma_bf16(doA[hv][half], sh, aQ);
+        aQ = mfma_bf16(doA[hv][half], sl, aQ);
+        aK = mfma_bf16(dvh[hv][half], sh, aK);
+        aK = mfma_bf16(dvh[hv][half], sl, aK);
+        aK = mfma_bf16(dvl[hv][half], sh, aK);
+        aT = mfma_bf16(dah, th, aT);
+        aT = mfma_bf16(dah, tl8, aT);
+        aT = mfma_bf16(dal, th, aT);
       }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) aQ[ii] *= a.scale;
     const int c = 64 * p + 16 * nn + tl;
     float glsum = 0.f;
     const float gl2c = sG[(CH - 1) * QP + c];
