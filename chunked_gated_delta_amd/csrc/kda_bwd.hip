@@ -32,15 +32,13 @@
 // holds C[4 gq + ii][tl].  A C-layout tile therefore serves directly as the B
 // operand of a product that contracts over its rows.
 
-#include <stdio.h>
-
 #include "kda_bwd.h"
 #include "kda_host.h"
 
 namespace kda {
 namespace {
 
-constexpr int NT = 256;
+constexpr int NT = 256;  // recurrence kernel: 4 waves
 constexpr int QP = KD + 4;  // pitch (floats) of [64][128] LDS tiles
 constexpr int MP = CH + 4;  // pitch of [64][64] LDS tiles
 constexpr int VH = VD / 2;  // state columns per recurrence workgroup
@@ -1355,6 +1353,7 @@ kda_status_t kda_bwd(const void* q, const void* k, const void* v, const void* ra
   xa.init = initial_state;
   xa.states = reinterpret_cast<float*>(pr.ws + bl.states);
   xa.dtile = reinterpret_cast<float*>(pr.ws + bl.dtile);
+  xa.timers = nullptr;  // (timer builds: the forward's counter area overlaps these checkpoints)
   if (launch_status(launch_inter(xa, st), "inter (checkpoints)") != KDA_SUCCESS) return KDA_ERR_LAUNCH;
 
   BwdArgs ba;
