@@ -13,7 +13,7 @@ import torch
 
 import workloads as W
 from oracle import oracle_fwd
-from oracle.grad import fwd_torch, oracle_bwd
+from oracle.grad import BETA_GIVEN, GATE_GIVEN, NO_QK_NORM, STATE_VK, fwd_torch, oracle_bwd
 
 NAMES = ("q", "k", "v", "raw_gate", "raw_beta", "A_log", "dt_bias", "initial_state")
 
@@ -83,3 +83,56 @@ def test_chunked_backward_equals_autograd(case):
             continue
         ref = np.asarray(a[n])
         assert np.abs(ref - np.asarray(b[n])).max() <= 1e-11 * max(1.0, np.abs(ref).max()), n
+
+
+def variant_inputs(seed, T, H, K, V, flags):
+    """Inputs in each variant's documented range (the same recipe as the forward variant pins)."""
+    x = W.random_inputs("grad_variant", seed, 1, T, H, K=K, V=V, init_std=0.5)
+    g = torch.Generator().manual_seed(seed + 500)
+    if flags & GATE_GIVEN:
+        x.raw_gate = (x.lower_bound * torch.sigmoid(torch.randn(x.raw_gate.shape, generator=g))).to(torch.bfloat16)
+    if flags & BETA_GIVEN:
+        x.raw_beta = torch.sigmoid(torch.randn(x.raw_beta.shape, generator=g)).to(torch.bfloat16)
+    if flags & NO_QK_NORM:
+        for name in ("q", "k"):
+            t = getattr(x, name).float()
+            setattr(x, name, (t / t.norm(dim=-1, keepdim=True)).to(torch.bfloat16))
+    return x
+
+
+@pytest.mark.parametrize("flags", [GATE_GIVEN, BETA_GIVEN, NO_QK_NORM, STATE_VK,
+                                   GATE_GIVEN | BETA_GIVEN | NO_QK_NORM | STATE_VK])
+def test_variant_forward_graph_and_gradients(flags):
+    """Under each variant flag the forward graph equals the C oracle's, and its gradients equal
+    central differences (the clamp of a given gate is never active at these inputs)."""
+    x = variant_inputs(120 + flags, 21, 2, 8, 8, flags)
+    ro, rf = oracle_fwd(x.q, x.k, x.v, x.raw_gate, x.raw_beta, x.scale, x.A_log, x.dt_bias, x.lower_bound,
+                        x.initial_state, flags=flags)
+    out, fin = fwd_torch(f64(x.q), f64(x.k), f64(x.v), f64(x.raw_gate), f64(x.raw_beta), x.scale, f64(x.A_log),
+                         f64(x.dt_bias), x.lower_bound, f64(x.initial_state), flags=flags)
+    assert np.abs(out.numpy() - ro).max() <= 1e-12
+    assert np.abs(fin.numpy() - rf).max() <= 1e-12
+    g = torch.Generator().manual_seed(5)
+    d_out = torch.randn(1, 21, 2, 8, generator=g, dtype=torch.float64)
+    d_fin = torch.randn(1, 2, 8, 8, generator=g, dtype=torch.float64)
+    grads = oracle_bwd(x.q, x.k, x.v, x.raw_gate, x.raw_beta, x.scale, x.A_log, x.dt_bias, x.lower_bound,
+                       d_out, d_fin, x.initial_state, flags=flags)
+    base = {n: f64(getattr(x, n)) for n in NAMES}
+
+    def loss(pp):
+        o, f = fwd_torch(pp["q"], pp["k"], pp["v"], pp["raw_gate"], pp["raw_beta"], x.scale, pp["A_log"],
+                         pp["dt_bias"], x.lower_bound, pp["initial_state"], flags=flags)
+        return float((o * d_out.reshape(o.shape)).sum() + (f * d_fin).sum())
+
+    key = {"q": "dq", "k": "dk", "v": "dv", "raw_gate": "d_raw_gate", "raw_beta": "d_raw_beta",
+           "A_log": "dA_log", "dt_bias": "d_dt_bias", "initial_state": "d_initial_state"}
+    h = 1e-6
+    for n in NAMES:
+        d = torch.randn(base[n].shape, generator=g, dtype=torch.float64)
+        plus = dict(base); plus[n] = base[n] + h * d
+        minus = dict(base); minus[n] = base[n] - h * d
+        fd = (loss(plus) - loss(minus)) / (2 * h)
+        an = float((torch.from_numpy(np.asarray(grads[key[n]])).reshape(d.shape) * d).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (flags, n, fd, an)
+    if flags & GATE_GIVEN:
+        assert not np.any(grads["dA_log"]) and not np.any(grads["d_dt_bias"])
