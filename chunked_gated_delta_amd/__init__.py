@@ -4,7 +4,7 @@ Argument marshalling only: every step of the forward pass runs in the HIP
 kernels behind the C ABI of include/kda.h.  The names mirror that header:
 ``kda_fwd``, ``kda_workspace_size``, ``kda_is_supported``, ``kda_shard_affine``,
 ``kda_shard_scan``, ``kda_decode``, ``kda_fwd_ex`` (with the ``FLAG_*`` variant bits),
-``kda_bwd`` and ``kda_bwd_workspace_size``.  PyTorch provides
+``kda_bwd``, ``kda_bwd_ex`` and ``kda_bwd_workspace_size``.  PyTorch provides
 device memory and the current stream; there is no CPU or PyTorch fallback, and
 importing this module fails if the library has not been built.
 """
@@ -21,7 +21,7 @@ import os
 import torch  # noqa: F401
 
 __all__ = ["kda_fwd", "kda_fwd_ex", "kda_workspace_size", "kda_is_supported", "kda_shard_affine",
-           "kda_shard_scan", "kda_decode", "kda_bwd", "kda_bwd_workspace_size", "KdaError", "STATUS", "library_path", "exported_symbols",
+           "kda_shard_scan", "kda_decode", "kda_bwd", "kda_bwd_ex", "kda_bwd_workspace_size", "KdaError", "STATUS", "library_path", "exported_symbols",
            "FLAG_GATE_GIVEN", "FLAG_BETA_GIVEN", "FLAG_NO_QK_NORM", "FLAG_STATE_VK"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +31,7 @@ STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERR_INVALID", 2: "KDA_ERR_UNSUPPORTED",
           3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_LAUNCH"}
 exported_symbols = ("kda_fwd", "kda_workspace_size", "kda_is_supported", "kda_status_string",
                     "kda_shard_affine", "kda_shard_scan", "kda_decode", "kda_fwd_ex", "kda_bwd",
-                    "kda_bwd_workspace_size")
+                    "kda_bwd_ex", "kda_bwd_workspace_size")
 # kda_fwd_ex variant bits (KDA_FLAG_* in include/kda.h)
 FLAG_GATE_GIVEN, FLAG_BETA_GIVEN, FLAG_NO_QK_NORM, FLAG_STATE_VK = 1, 2, 4, 8
 
@@ -76,6 +76,8 @@ _lib.kda_bwd_workspace_size.restype = ctypes.c_size_t
 _lib.kda_bwd.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                          ctypes.c_size_t, _P, _P, ctypes.c_float, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]
 _lib.kda_bwd.restype = ctypes.c_int
+_lib.kda_bwd_ex.argtypes = _lib.kda_bwd.argtypes[:-1] + [ctypes.c_uint, _P]
+_lib.kda_bwd_ex.restype = ctypes.c_int
 
 
 def kda_workspace_size(T: int, H: int, N: int) -> int:
@@ -231,25 +233,37 @@ def kda_bwd(q, k, v, raw_gate, raw_beta, scale, d_out, dq, dk, dv, d_raw_gate, d
     or None for zero).  Writes dq, dk, d_raw_gate (bf16 [B,T,H,K]), dv (bf16 [B,T,H,V]),
     d_raw_beta (bf16 [B,T,H]), dA_log (fp32 [H]), d_dt_bias (fp32 [H,K]) and, if given,
     d_initial_state (fp32 [N,H,K,V])."""
+    kda_bwd_ex(q, k, v, raw_gate, raw_beta, scale, d_out, dq, dk, dv, d_raw_gate, d_raw_beta, dA_log,
+               d_dt_bias, workspace, A_log, dt_bias, lower_bound, initial_state, d_final, d_initial_state,
+               cu_seqlens, flags=0, stream=stream, _name="kda_bwd")
+
+
+def kda_bwd_ex(q, k, v, raw_gate, raw_beta, scale, d_out, dq, dk, dv, d_raw_gate, d_raw_beta, dA_log,
+               d_dt_bias, workspace, A_log, dt_bias, lower_bound, initial_state=None, d_final=None,
+               d_initial_state=None, cu_seqlens=None, flags=0, stream=None, _name="kda_bwd_ex"):
+    """kda_bwd for the variants of kda_fwd_ex (an OR of the FLAG_* bits).  With
+    FLAG_GATE_GIVEN, A_log, dt_bias, dA_log and d_dt_bias may be None; with FLAG_STATE_VK
+    the states and their gradients are [N,H,V,K]."""
+    if not flags & FLAG_GATE_GIVEN and (A_log is None or dt_bias is None or dA_log is None or d_dt_bias is None):
+        raise ValueError("A_log, dt_bias, dA_log and d_dt_bias are required unless FLAG_GATE_GIVEN")
     B, T, H, K, V, N = _check_inputs(q, k, v, raw_gate, raw_beta, d_out, A_log, dt_bias, cu_seqlens)
-    if A_log is None or dt_bias is None:
-        raise ValueError("A_log and dt_bias are required")
     _check_inputs(q, dk, dv, d_raw_gate, d_raw_beta, None, None, None, None)
     if tuple(dq.shape) != tuple(q.shape) or dq.dtype != torch.bfloat16 or not dq.is_contiguous():
         raise ValueError("dq must be a contiguous bf16 tensor shaped like q")
-    _check_f32("initial_state", initial_state, (N, H, K, V))
-    _check_f32("d_final", d_final, (N, H, K, V))
-    _check_f32("d_initial_state", d_initial_state, (N, H, K, V))
+    st_shape = (N, H, V, K) if flags & FLAG_STATE_VK else (N, H, K, V)
+    _check_f32("initial_state", initial_state, st_shape)
+    _check_f32("d_final", d_final, st_shape)
+    _check_f32("d_initial_state", d_initial_state, st_shape)
     _check_f32("dA_log", dA_log, (H,))
     _check_f32("d_dt_bias", d_dt_bias, (H, K))
-    rc = _lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(raw_beta), float(scale), _ptr(d_out),
-                      _ptr(d_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(d_raw_gate), _ptr(d_raw_beta),
-                      _ptr(dA_log), _ptr(d_dt_bias), _ptr(d_initial_state), _ptr(workspace),
-                      workspace.numel() * workspace.element_size(), _ptr(A_log), _ptr(dt_bias),
-                      float(lower_bound), _ptr(initial_state), _ptr(cu_seqlens), B, T, H, K, V, N,
-                      _stream(stream, q.device))
+    rc = _lib.kda_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(raw_beta), float(scale), _ptr(d_out),
+                         _ptr(d_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(d_raw_gate), _ptr(d_raw_beta),
+                         _ptr(dA_log), _ptr(d_dt_bias), _ptr(d_initial_state), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _ptr(A_log), _ptr(dt_bias),
+                         float(lower_bound), _ptr(initial_state), _ptr(cu_seqlens), B, T, H, K, V, N,
+                         int(flags), _stream(stream, q.device))
     if rc != 0:
-        raise KdaError(rc, "kda_bwd")
+        raise KdaError(rc, _name)
 
 
 def raw_call(*args):

@@ -36,6 +36,7 @@ struct BwdArgs {
   int H;
   float scale;
   float lb;               // lower_bound
+  int flags;              // FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM | FLAG_STATE_VK
   unsigned long long* timers;  // phase timers (KDA_PHASE_TIMERS builds only), else nullptr
 };
 constexpr int BWD_REC_FLOATS = 3 * CH * CH + 3 * CH * KD + KD + CH;  // 37056

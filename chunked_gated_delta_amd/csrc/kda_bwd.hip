@@ -150,15 +150,24 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
     sq += __shfl_xor(sq, d);
     sk += __shfl_xor(sk, d);
   }
-  const float rq = sqrtf(sq + L2_EPS), rk = sqrtf(sk + L2_EPS);
+  const bool norm = !(a.flags & FLAG_NO_QK_NORM);
+  const bool gate_given = a.flags & FLAG_GATE_GIVEN;
+  const float rq = norm ? sqrtf(sq + L2_EPS) : 1.0f, rk = norm ? sqrtf(sk + L2_EPS) : 1.0f;
   const float iq = ok ? 1.0f / rq : 0.f, ik = ok ? 1.0f / rk : 0.f;
-  const float al = expf(a.A_log[h]);
-  const float* dtb = a.dt_bias + (size_t)h * KD + CPT * part;
+  // with the gate given, A_log and dt_bias may be absent and are not read
+  const float al = gate_given ? 0.f : expf(a.A_log[h]);
 #pragma unroll
   for (int c = 0; c < CPT; c += 4) {
     float gg[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) gg[e] = ok ? a.lb * sigmoidf(al * (gv[c + e] + dtb[c + e])) * LOG2E : 0.f;
+    for (int e = 0; e < 4; ++e) {
+      float gn;
+      if (gate_given)
+        gn = fminf(fmaxf(gv[c + e], a.lb), 0.f);
+      else
+        gn = a.lb * sigmoidf(al * (gv[c + e] + a.dt_bias[(size_t)h * KD + CPT * part + c + e]));
+      gg[e] = ok ? gn * LOG2E : 0.f;
+    }
     *reinterpret_cast<float4*>(sQn + i * QP + CPT * part + c) =
         make_float4(qv[c] * iq, qv[c + 1] * iq, qv[c + 2] * iq, qv[c + 3] * iq);
     *reinterpret_cast<float4*>(sKn + i * QP + CPT * part + c) =
@@ -166,7 +175,8 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
     *reinterpret_cast<float4*>(sG + i * QP + CPT * part + c) = make_float4(gg[0], gg[1], gg[2], gg[3]);
   }
   if (part == 0) {
-    sBeta[i] = ok ? sigmoidf(bf2f(a.beta[(size_t)row * a.H + h])) : 0.f;
+    const float rb = bf2f(a.beta[(size_t)row * a.H + h]);
+    sBeta[i] = ok ? ((a.flags & FLAG_BETA_GIVEN) ? rb : sigmoidf(rb)) : 0.f;
     sRq[i] = rq;
     sRk[i] = rk;
   }
@@ -527,6 +537,7 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
   const int ocol = 16 * (tid & 3);
 
   f32x4 dS[2][4];
+  const bool svk = a.flags & FLAG_STATE_VK;  // d_final / d_initial_state stored [V][K]
   {
     const float* src = a.dfin ? a.dfin + ((size_t)seq * H + h) * KD * VD : nullptr;
 #pragma unroll
@@ -535,7 +546,9 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
       for (int nn = 0; nn < 4; ++nn)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-          dS[mt][nn][ii] = src ? src[(32 * w + 16 * mt + 4 * gq + ii) * VD + vs + 16 * nn + tl] : 0.f;
+          dS[mt][nn][ii] = src ? src[svk ? (vs + 16 * nn + tl) * KD + 32 * w + 16 * mt + 4 * gq + ii
+                                         : (32 * w + 16 * mt + 4 * gq + ii) * VD + vs + 16 * nn + tl]
+                               : 0.f;
   }
   auto dorow_of = [&](int ci, bool& ok) {
     const int64_t c0 = bos + (int64_t)ci * CH;
@@ -648,7 +661,8 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
       for (int nn = 0; nn < 4; ++nn)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-          dst[(32 * w + 16 * mt + 4 * gq + ii) * VD + vs + 16 * nn + tl] = dS[mt][nn][ii];
+          dst[svk ? (vs + 16 * nn + tl) * KD + 32 * w + 16 * mt + 4 * gq + ii
+                  : (32 * w + 16 * mt + 4 * gq + ii) * VD + vs + 16 * nn + tl] = dS[mt][nn][ii];
   }
 }
 
@@ -1154,7 +1168,8 @@ __global__ void __launch_bounds__(NT8, 1) kda_bwd_grad_kernel(BwdArgs a) {
   KDA_TIMER_MARK(10);
 
   // ---- outputs, staged in LDS: d raw_gate, dq, dk; partial sums of d dt_bias, dA_log
-  const float al = expf(a.A_log[h]);
+  const bool gate_given = a.flags & FLAG_GATE_GIVEN;
+  const float al = gate_given ? 0.f : expf(a.A_log[h]);
   float pA = 0.f;
   uint16_t* oq = sOut;
   uint16_t* ok_ = sOut + CH * KD;
@@ -1166,7 +1181,7 @@ __global__ void __launch_bounds__(NT8, 1) kda_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (u > w) later += sCS[u * KD + c];
-    const float dtb = a.dt_bias[(size_t)h * KD + c];
+    const float dtb = gate_given ? 0.f : a.dt_bias[(size_t)h * KD + c];
     float pdt = 0.f;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
@@ -1175,12 +1190,18 @@ __global__ void __launch_bounds__(NT8, 1) kda_bwd_grad_kernel(BwdArgs a) {
       float dgo = 0.f;
       if (j < L) {
         const size_t o = ((size_t)(c0 + j) * H + h) * KD + c;
-        const float x = al * (bf2f(a.g[o]) + dtb);
-        const float sg = sigmoidf(x);
-        const float dx = dgv * a.lb * sg * (1.f - sg);
-        dgo = dx * al;
-        pdt += dgo;
-        pA += dx * x;
+        const float rg = bf2f(a.g[o]);
+        if (gate_given) {
+          // g = clamp(raw_gate, lower_bound, 0): the gradient passes inside the closed interval
+          dgo = (rg >= a.lb && rg <= 0.f) ? dgv : 0.f;
+        } else {
+          const float x = al * (rg + dtb);
+          const float sg = sigmoidf(x);
+          const float dx = dgv * a.lb * sg * (1.f - sg);
+          dgo = dx * al;
+          pdt += dgo;
+          pA += dx * x;
+        }
       }
       og[j * KD + c] = f2bf(dgo);
     }
@@ -1192,8 +1213,10 @@ __global__ void __launch_bounds__(NT8, 1) kda_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
     const int j = 16 * w + 4 * gq + ii;
-    const float dq_dot = sDot[j * 2] + sDot[(CH + j) * 2];
-    const float dk_dot = sDot[j * 2 + 1] + sDot[(CH + j) * 2 + 1];
+    // dq = dq^ when q is used without the L2 norm (the projection term and the row norm drop)
+    const bool norm = !(a.flags & FLAG_NO_QK_NORM);
+    const float dq_dot = norm ? sDot[j * 2] + sDot[(CH + j) * 2] : 0.f;
+    const float dk_dot = norm ? sDot[j * 2 + 1] + sDot[(CH + j) * 2 + 1] : 0.f;
     const float irq = 1.f / sRq[j], irk = 1.f / sRk[j];
 #pragma unroll
     for (int nn = 0; nn < 4; ++nn) {
@@ -1207,7 +1230,7 @@ __global__ void __launch_bounds__(NT8, 1) kda_bwd_grad_kernel(BwdArgs a) {
   if (lane == 0) sTmp[wv] = pA;
   if (p == 0 && lane < 16 && jw < L) {
     const float b = sBeta[jw];
-    a.dbeta[(size_t)(c0 + jw) * H + h] = f2bf(sdB[jw] * b * (1.f - b));
+    a.dbeta[(size_t)(c0 + jw) * H + h] = f2bf((a.flags & FLAG_BETA_GIVEN) ? sdB[jw] : sdB[jw] * b * (1.f - b));
   }
   __syncthreads();
   // 16-byte stores of the staged rows: thread -> (row, 16-byte column block)
@@ -1256,10 +1279,11 @@ __global__ void __launch_bounds__(NTR) kda_bwd_reduce_kernel(BwdArgs a) {
   __syncthreads();
   if (rr == 0) {
     const float v = red[col] + red[(KD + 1) + col] + red[2 * (KD + 1) + col] + red[3 * (KD + 1) + col];
-    if (col < KD)
-      a.ddt[(size_t)h * KD + col] = v;
-    else
+    if (col < KD) {
+      if (a.ddt) a.ddt[(size_t)h * KD + col] = v;
+    } else if (a.dA_log) {
       a.dA_log[h] = v;
+    }
   }
 }
 
@@ -1327,15 +1351,17 @@ size_t kda_bwd_workspace_size(int64_t T_total, int64_t H, int64_t N) {
   return bwd_layout(T_total, H, N).total;
 }
 
-kda_status_t kda_bwd(const void* q, const void* k, const void* v, const void* raw_gate,
-                     const void* raw_beta, float scale, const void* d_out, const float* d_final,
-                     void* dq, void* dk, void* dv, void* d_raw_gate, void* d_raw_beta, float* dA_log,
-                     float* d_dt_bias, float* d_initial_state, void* workspace, size_t workspace_bytes,
-                     const float* A_log, const float* dt_bias, float lower_bound,
-                     const float* initial_state, const int32_t* cu_seqlens, int64_t B, int64_t T,
-                     int64_t H, int64_t K, int64_t V, int64_t N, void* stream) {
+kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void* raw_gate,
+                        const void* raw_beta, float scale, const void* d_out, const float* d_final,
+                        void* dq, void* dk, void* dv, void* d_raw_gate, void* d_raw_beta, float* dA_log,
+                        float* d_dt_bias, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                        const float* A_log, const float* dt_bias, float lower_bound,
+                        const float* initial_state, const int32_t* cu_seqlens, int64_t B, int64_t T,
+                        int64_t H, int64_t K, int64_t V, int64_t N, unsigned flags, void* stream) {
+  if (flags & ~(unsigned)(FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM | FLAG_STATE_VK))
+    return KDA_ERR_INVALID;
   if (B * T > 0 && (!v || !d_out || !dq || !dk || !dv || !d_raw_gate || !d_raw_beta)) return KDA_ERR_INVALID;
-  if (!dA_log || !d_dt_bias || !A_log || !dt_bias) return KDA_ERR_INVALID;
+  if (!(flags & FLAG_GATE_GIVEN) && (!dA_log || !d_dt_bias || !A_log || !dt_bias)) return KDA_ERR_INVALID;
   if (!(scale == scale)) return KDA_ERR_INVALID;
   if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID;
   if (B * T * H > ((int64_t)1 << 40) || N * H > ((int64_t)1 << 28) || N > ((int64_t)1 << 30))
@@ -1345,12 +1371,13 @@ kda_status_t kda_bwd(const void* q, const void* k, const void* v, const void* ra
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   Prepared pr;
   const kda_status_t s = prepare(q, k, raw_gate, raw_beta, workspace, workspace_bytes, A_log, dt_bias,
-                                 lower_bound, cu_seqlens, B, T, H, K, V, N, st, pr);
+                                 lower_bound, cu_seqlens, B, T, H, K, V, N, st, pr, flags);
   if (s != KDA_SUCCESS) return s;
   // forward recurrence, keeping the state entering each chunk and each chunk's D
   InterArgs xa = inter_args(pr, H);
   xa.v = static_cast<const uint16_t*>(v);
   xa.init = initial_state;
+  xa.state_vk = (flags & FLAG_STATE_VK) ? 1 : 0;
   xa.states = reinterpret_cast<float*>(pr.ws + bl.states);
   xa.dtile = reinterpret_cast<float*>(pr.ws + bl.dtile);
   xa.timers = nullptr;  // (timer builds: the forward's counter area overlaps these checkpoints)
@@ -1385,12 +1412,25 @@ kda_status_t kda_bwd(const void* q, const void* k, const void* v, const void* ra
   ba.H = (int)H;
   ba.scale = scale;
   ba.lb = lower_bound;
+  ba.flags = (int)flags;
   ba.timers = nullptr;
 #ifdef KDA_PHASE_TIMERS
   // timer builds only: 16 counters per workgroup of each backward kernel after the workspace
   ba.timers = reinterpret_cast<unsigned long long*>(pr.ws + bl.total);
 #endif
   return launch_status(launch_bwd(ba, pr.max_chunks, st), "backward");
+}
+
+kda_status_t kda_bwd(const void* q, const void* k, const void* v, const void* raw_gate,
+                     const void* raw_beta, float scale, const void* d_out, const float* d_final,
+                     void* dq, void* dk, void* dv, void* d_raw_gate, void* d_raw_beta, float* dA_log,
+                     float* d_dt_bias, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                     const float* A_log, const float* dt_bias, float lower_bound,
+                     const float* initial_state, const int32_t* cu_seqlens, int64_t B, int64_t T,
+                     int64_t H, int64_t K, int64_t V, int64_t N, void* stream) {
+  return kda_bwd_ex(q, k, v, raw_gate, raw_beta, scale, d_out, d_final, dq, dk, dv, d_raw_gate, d_raw_beta,
+                    dA_log, d_dt_bias, d_initial_state, workspace, workspace_bytes, A_log, dt_bias, lower_bound,
+                    initial_state, cu_seqlens, B, T, H, K, V, N, 0u, stream);
 }
 
 }  // extern "C"

@@ -250,6 +250,26 @@ kda_status_t kda_bwd(const void* q, const void* k, const void* v, const void* ra
                      const float* initial_state, const int32_t* cu_seqlens, int64_t B, int64_t T,
                      int64_t H, int64_t K, int64_t V, int64_t N, void* stream);
 
+/*
+ * kda_bwd for the variants of kda_fwd_ex (any OR of the KDA_FLAG_* bits; other
+ * bits give KDA_ERR_INVALID): the gradients of the kda_fwd_ex call with the
+ * same inputs and flags.  With KDA_FLAG_GATE_GIVEN, d_raw_gate is the gradient
+ * with respect to the given decay, passed where raw_gate lies in
+ * [lower_bound, 0] and zero where the clamp is active; A_log and dt_bias are
+ * unused and may be NULL, and dA_log, d_dt_bias may be NULL (else zero-filled).
+ * With KDA_FLAG_BETA_GIVEN, d_raw_beta is the gradient with respect to beta;
+ * with KDA_FLAG_NO_QK_NORM, dq and dk are those of the unnormalised q, k; with
+ * KDA_FLAG_STATE_VK, initial_state, d_final and d_initial_state are [N, H, V, K].
+ * kda_bwd(...) == kda_bwd_ex(..., 0, stream).
+ */
+kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void* raw_gate,
+                        const void* raw_beta, float scale, const void* d_out, const float* d_final,
+                        void* dq, void* dk, void* dv, void* d_raw_gate, void* d_raw_beta, float* dA_log,
+                        float* d_dt_bias, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                        const float* A_log, const float* dt_bias, float lower_bound,
+                        const float* initial_state, const int32_t* cu_seqlens, int64_t B, int64_t T,
+                        int64_t H, int64_t K, int64_t V, int64_t N, unsigned flags, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* kda_status_string(kda_status_t status);
 

@@ -232,3 +232,23 @@ def test_bwd_workspace_size():
     assert kda.kda_bwd_workspace_size(10, 0, 1) == 0
     assert kda.kda_bwd_workspace_size(10, 2, 0) == 0
     assert kda.kda_bwd_workspace_size(32768, 96, 1) > 20 * 10 ** 9 // 2
+
+
+def bwd_ex_call(flags, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, scale=0.088, dout=FAKE, dfin=None, dq=FAKE, dk=FAKE,
+             dv=FAKE, dg=FAKE, db=FAKE, dA=FAKE, ddt=FAKE, dinit=None, ws=FAKE, ws_bytes=8, A_log=FAKE,
+             dt=FAKE, lb=-5.0, init=None, cu=None, B=1, T=64, H=2, K=128, V=128, N=1)
+    a.update(over)
+    return kda._lib.kda_bwd_ex(a["q"], a["k"], a["v"], a["g"], a["b"], ctypes.c_float(a["scale"]), a["dout"],
+                               a["dfin"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dA"], a["ddt"],
+                               a["dinit"], a["ws"], a["ws_bytes"], a["A_log"], a["dt"], ctypes.c_float(a["lb"]),
+                               a["init"], a["cu"], a["B"], a["T"], a["H"], a["K"], a["V"], a["N"], flags, None)
+
+
+def test_bwd_ex_flag_checks():
+    assert bwd_ex_call(16) == INVALID                       # unknown bit
+    assert bwd_ex_call(0, A_log=None) == INVALID            # gate parameters needed without GATE_GIVEN
+    assert bwd_ex_call(0, dA=None) == INVALID
+    # with the gate given they may be absent: the call then proceeds to the workspace check
+    assert bwd_ex_call(kda.FLAG_GATE_GIVEN, A_log=None, dt=None, dA=None, ddt=None) == WORKSPACE
+    assert bwd_ex_call(kda.FLAG_STATE_VK | kda.FLAG_NO_QK_NORM) == WORKSPACE
