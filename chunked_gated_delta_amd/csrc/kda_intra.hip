@@ -80,7 +80,10 @@ __device__ __forceinline__ float row_scan16(float x) {
 // The chunk table, A_log and the record base are also passed as separate
 // __restrict__ arguments: with no possible aliasing by the record stores, the
 // wave-uniform loads from them can go through the scalar unit and never wait
-// behind the vector memory queue.
+// behind the vector memory queue.  GATE_GIVEN is a template switch: a runtime
+// choice inside the per-element gate loop would split it into 32 branches and
+// keep the scan from interleaving.
+template <bool GATE_GIVEN>
 __global__ void __launch_bounds__(NTHREADS, 2)
     kda_intra_kernel(IntraArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ choff,
                      const float* __restrict__ A_log, char* __restrict__ recs) {
@@ -174,6 +177,12 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   locate(item, h, g, c0, L);
   issue(1, item, h, c0, L);
   issue(0, item, h, c0, L);
+  // Wait for the first item's loads here, once.  On the loop's back edge the
+  // prefetched loads are followed by the record stores; without this wait the
+  // entry path (no stores after its loads) makes the compiler's merged wait at
+  // the loop head a full vmcnt(0), which would also wait for every record
+  // store of the previous item to complete.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) only
   KDA_TIMER_DECL
 
   for (;;) {
@@ -248,7 +257,6 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   const float braw = __uint_as_float((uint32_t)braw16 << 16);
   const float beta =
       valid ? ((a.flags & FLAG_BETA_GIVEN) ? braw : __builtin_amdgcn_rcpf(1.0f + fexp2(-braw * LOG2E))) : 0.0f;
-  const bool gate_given = a.flags & FLAG_GATE_GIVEN;
 
   // log-decay in log2 units, inclusive scan over the sub-chunk's 16 tokens
 #pragma unroll
@@ -259,7 +267,7 @@ __global__ void __launch_bounds__(NTHREADS, 2)
     for (int e = 0; e < 8; ++e) {
       // log2 decay: lb2 * sigmoid(exp(A_log)(raw + dt)), or the given natural-log
       // decay clamped to [lower_bound, 0]
-      float g2 = gate_given ? fminf(fmaxf(gl[kb][e] * LOG2E, a.lb2), 0.0f)
+      float g2 = GATE_GIVEN ? fminf(fmaxf(gl[kb][e] * LOG2E, a.lb2), 0.0f)
                             : a.lb2 * __builtin_amdgcn_rcpf(1.0f + fexp2(gl[kb][e] * na + nb[e]));
       g2 = valid ? g2 : 0.0f;
       gl[kb][e] = row_scan16(g2);
@@ -371,6 +379,9 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   // wave w owns row-block w; lane holds C[16w + 4gq + ii][16b + tl]
   {
     const int i0 = 16 * w + 4 * gq;
+    // beta of this lane's four rows, read once (not inside the masked stores)
+    const float4 bi4 = *reinterpret_cast<const float4*>(sB + i0);
+    const float bi[4] = {bi4.x, bi4.y, bi4.z, bi4.w};
 #pragma unroll 1
     for (int b = 0; b <= w; ++b) {
       f32x4 akk = {0.f, 0.f, 0.f, 0.f};
@@ -415,7 +426,7 @@ __global__ void __launch_bounds__(NTHREADS, 2)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int i = i0 + ii;
-        sA[i * AP + j] = (j < i) ? akk[ii] * sB[i] : 0.0f;
+        sA[i * AP + j] = (j < i) ? akk[ii] * bi[ii] : 0.0f;
       }
       // A_qk came out transposed: lane holds row 16w + tl, columns 16b + 4gq + 0..3
       f16x4 q4;
@@ -431,16 +442,26 @@ __global__ void __launch_bounds__(NTHREADS, 2)
     }
     // T_ww = (I + A_ww)^-1 by forward substitution, lane cc < 16 owns column
     // cc.  This wave wrote A_ww just above and LDS operations of one wave
-    // complete in order, so no barrier is needed here.
+    // complete in order, so no barrier is needed here.  The block's lower
+    // triangle is read into registers first (36 16-byte reads), so the
+    // substitution chain never waits on LDS.
     if (lane < 16) {
       const int cc = lane;
       const float* Ab = sA + (16 * w) * AP + 16 * w;
+      float Ar[16][16];
+#pragma unroll
+      for (int i = 1; i < 16; ++i)
+#pragma unroll
+        for (int m4 = 0; m4 < i; m4 += 4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(Ab + i * AP + m4);
+          Ar[i][m4] = v4.x; Ar[i][m4 + 1] = v4.y; Ar[i][m4 + 2] = v4.z; Ar[i][m4 + 3] = v4.w;
+        }
       float x[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float s = (i == cc) ? 1.0f : 0.0f;
 #pragma unroll
-        for (int m = 0; m < i; ++m) s -= Ab[i * AP + m] * x[m];
+        for (int m = 0; m < i; ++m) s -= Ar[i][m] * x[m];
         x[i] = (i < cc) ? 0.0f : s;
       }
 #pragma unroll
@@ -569,7 +590,9 @@ hipError_t launch_intra(const IntraArgs& args, int64_t max_chunks, hipStream_t s
   const float* alog = a.A_log;
   char* recs = a.rec;
   void* kargs[] = {(void*)&a, (void*)&cu, (void*)&choff, (void*)&alog, (void*)&recs};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_intra_kernel), dim3((unsigned)grid),
+  const void* fn = (a.flags & FLAG_GATE_GIVEN) ? reinterpret_cast<const void*>(&kda_intra_kernel<true>)
+                                               : reinterpret_cast<const void*>(&kda_intra_kernel<false>);
+  return hipLaunchKernel(fn, dim3((unsigned)grid),
                          dim3(NTHREADS), kargs, 0, st);
 }
 
