@@ -474,32 +474,49 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   __syncthreads();
   KDA_TIMER_MARK(5);
 
-  // ============= off-diagonal blocks of T, row-block by row-block ==========
-  //     T_{b,b'} = -T_bb * sum_{m=b'}^{b-1} A_{b,m} T_{m,b'}   (fp32 MFMA)
-  for (int b = 1; b < 4; ++b) {
-    f32x4 res = {0.f, 0.f, 0.f, 0.f};
-    const int bp = w;  // wave w computes T_{b, w}
-    if (bp < b) {
-      f32x4 X = {0.f, 0.f, 0.f, 0.f};
-      for (int m = bp; m < b; ++m) {
+  // ============= off-diagonal blocks of T, column-block by column-block ====
+  //     T_{b,w} = -T_bb * sum_{m=w}^{b-1} A_{b,m} T_{m,w}   (fp32 MFMA)
+  // Wave w walks down its own column-block.  The blocks T_{m,w} it needs are
+  // its own earlier results, kept in registers in C layout (which is the
+  // B-operand layout); T_bb and the A blocks are final since the barrier
+  // above.  So the levels need no barrier between them.  Instruction s of a
+  // block product contracts over index 4gq + s: a lane's four A-operand values
+  // of one row are a single 16-byte LDS read.
+  {
+    f32x4 Tc[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const float av = sA[(16 * b + tl) * AP + 16 * m + 4 * s + gq];
-          const float tv = sA[(16 * m + 4 * s + gq) * AP + 16 * bp + tl];
-          X = mfma_f32(av, tv, X);
+    for (int ii = 0; ii < 4; ++ii) Tc[0][ii] = sA[(16 * w + 4 * gq + ii) * AP + 16 * w + tl];
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+      Tc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (w + d < 4) {
+        const int b = w + d;
+        const float* arow = sA + (16 * b + tl) * AP + 4 * gq;
+        f32x4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mm = 0; mm < d; ++mm) {
+          const float4 a4 = *reinterpret_cast<const float4*>(arow + 16 * (w + mm));
+          X = mfma_f32(a4.x, Tc[mm][0], X);
+          X = mfma_f32(a4.y, Tc[mm][1], X);
+          X = mfma_f32(a4.z, Tc[mm][2], X);
+          X = mfma_f32(a4.w, Tc[mm][3], X);
         }
-      }
-      // res = -T_bb X; X sits in C-layout, so k-step s uses rows {4g + s}
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const float av = sA[(16 * b + tl) * AP + 16 * b + 4 * gq + s];
-        res = mfma_f32(-av, X[s], res);
+        const float4 t4 = *reinterpret_cast<const float4*>(arow + 16 * b);
+        f32x4 r = {0.f, 0.f, 0.f, 0.f};
+        r = mfma_f32(-t4.x, X[0], r);
+        r = mfma_f32(-t4.y, X[1], r);
+        r = mfma_f32(-t4.z, X[2], r);
+        r = mfma_f32(-t4.w, X[3], r);
+        Tc[d] = r;
       }
     }
-    __syncthreads();
-    if (bp < b) {
+    __syncthreads();  // every wave is done reading A blocks that T overwrites
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) sA[(16 * b + 4 * gq + ii) * AP + 16 * bp + tl] = res[ii];
+    for (int d = 1; d < 4; ++d) {
+      if (w + d < 4) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) sA[(16 * (w + d) + 4 * gq + ii) * AP + 16 * w + tl] = Tc[d][ii];
+      }
     }
     __syncthreads();
   }
