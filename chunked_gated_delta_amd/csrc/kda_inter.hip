@@ -270,52 +270,79 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     KDA_ISSUE((load_ops<0, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
     KDA_TIMER_MARK(1);
 
-    // ---- U, D = U - W S, O = QG S (token rows 16w.., all 64 columns); the
-    // two products share each read of the state copy
-    f32x4 O[4];
+    // ---- U, D = U - W S, O = QG S (token rows 16w.., all 64 columns).  The
+    // B operands come in six groups of four 16-byte LDS reads (one per column
+    // tile): groups 0-1 the V tile (k-steps of U), groups 2-5 the state copy
+    // (k-blocks of W S and QG S).  Each group feeds eight independent MFMA
+    // chains and is read one group ahead, pinned there by a scheduling
+    // barrier (left alone, the scheduler sinks every read to its first use
+    // and waits for it there).  The two products share each state-copy read.
+    f32x4 O[4], u[4];
+#pragma unroll
+    for (int nn = 0; nn < 4; ++nn) {
+      u[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+      O[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    uint4 bq[2][4];
+    auto read_group = [&](int g, uint4(&dst)[4]) {
+#pragma unroll
+      for (int nn = 0; nn < 4; ++nn) {
+        const int col = 16 * nn + tl;
+        dst[nn] = g < 2 ? *reinterpret_cast<const uint4*>(sVt + col * TP + ((32 * g + 8 * gq) ^ vt_swz(col)))
+                        : *reinterpret_cast<const uint4*>(sSt + col * SP + 32 * (g - 2) + 8 * gq);
+      }
+    };
+    constexpr int G0 = HAS_V ? 0 : 2;
+    read_group(G0, bq[G0 & 1]);
+#pragma unroll
+    for (int g = G0; g < 6; ++g) {
+      if (g + 1 < 6) read_group(g + 1, bq[(g + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (g < 2) {
+        // Uniform control flow: every loaded operand register is consumed on
+        // every path, so no load is still outstanding when its register is
+        // reloaded (waves 0 and 1 multiply by zero for their upper k-step).
+        const bf16x8 th = g < ksmax ? cur.tbh[g] : bf16x8{};
+        const bf16x8 tlo = g < ksmax ? cur.tbl[g] : bf16x8{};
+#pragma unroll
+        for (int nn = 0; nn < 4; ++nn) {
+          const bf16x8 vb = __builtin_bit_cast(bf16x8, bq[g & 1][nn]);
+          u[nn] = mfma_bf16(th, vb, u[nn]);
+          u[nn] = mfma_bf16(tlo, vb, u[nn]);
+        }
+      } else {
+        const int kb = g - 2;
+#pragma unroll
+        for (int nn = 0; nn < 4; ++nn) {
+          const f16x8 sb = __builtin_bit_cast(f16x8, bq[g & 1][nn]);
+          u[nn] = mfma_f16(cur.nw[kb], sb, u[nn]);
+          if constexpr (WRITE_OUT) O[nn] = mfma_f16(cur.qg[kb], sb, O[nn]);
+        }
+      }
+      if (g == 2) KDA_ISSUE((load_ops<1, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
+      if (g == 3) KDA_ISSUE((load_ops<2, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
+    }
 #pragma unroll
     for (int nn = 0; nn < 4; ++nn) {
       const int col = 16 * nn + tl;
-      f32x4 u = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (HAS_V) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          // Uniform control flow: every loaded operand register is consumed on
-          // every path, so no load is still outstanding when its register is
-          // reloaded (waves 0 and 1 multiply by zero for their upper k-step).
-          const bf16x8 vb = *reinterpret_cast<const bf16x8*>(sVt + col * TP + ((32 * ks + 8 * gq) ^ vt_swz(col)));
-          u = mfma_bf16(ks < ksmax ? cur.tbh[ks] : bf16x8{}, vb, u);
-          u = mfma_bf16(ks < ksmax ? cur.tbl[ks] : bf16x8{}, vb, u);
-        }
-      }
-      f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const f16x8 sb = *reinterpret_cast<const f16x8*>(sSt + col * SP + 32 * kb + 8 * gq);
-        u = mfma_f16(cur.nw[kb], sb, u);
-        if constexpr (WRITE_OUT) o = mfma_f16(cur.qg[kb], sb, o);
-      }
-      O[nn] = o;
       if constexpr (CKPT) {
         float* dst = a.dtile + ((size_t)gch * H + h) * CH * VD;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int i = 16 * w + 4 * gq + ii;
-          dst[i * VD + vs + col] = i < L ? u[ii] : 0.0f;
+          dst[i * VD + vs + col] = i < L ? u[nn][ii] : 0.0f;
         }
       }
       // D^T hi/lo: lane holds tokens 16w + 4gq + 0..3 of column col
       f16x4 dh, dl;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const _Float16 hv = (_Float16)u[ii];
+        const _Float16 hv = (_Float16)u[nn][ii];
         dh[ii] = hv;
-        dl[ii] = (_Float16)(u[ii] - (float)hv);
+        dl[ii] = (_Float16)(u[nn][ii] - (float)hv);
       }
       *reinterpret_cast<f16x4*>(sDth + col * TP + 16 * w + 4 * gq) = dh;
       *reinterpret_cast<f16x4*>(sDtl + col * TP + 16 * w + 4 * gq) = dl;
-      if (nn == 0) KDA_ISSUE((load_ops<1, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
-      if (nn == 1) KDA_ISSUE((load_ops<2, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
     }
     KDA_TIMER_MARK(2);
     __syncthreads();
