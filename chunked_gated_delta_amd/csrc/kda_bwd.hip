@@ -58,8 +58,6 @@ constexpr int BR_GL = BR_QGT + CH * KD;   // exp(G_L)                           
 constexpr int BR_BETA = BR_GL + KD;       // beta                                     [64]
 static_assert(BR_BETA + CH == BWD_REC_FLOATS, "record size");
 
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
 // Store x0..x3 (4 consecutive fragment elements starting at idx) of an n-element
 // bf16 hi/lo region: hi at idx, lo = x - hi at n + idx.
 __device__ __forceinline__ void store_hl4(float* region, int n, int idx, float x0, float x1, float x2, float x3) {

@@ -316,7 +316,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
         for (int nn = 0; nn < 4; ++nn) {
           const f16x8 sb = __builtin_bit_cast(f16x8, bq[g & 1][nn]);
           u[nn] = mfma_f16(cur.nw[kb], sb, u[nn]);
-          if constexpr (WRITE_OUT) O[nn] = mfma_f16(cur.qg[kb], sb, O[nn]);
+          // O^T = S^T (QG)^T: lane holds token 16w + tl, columns 16nn + 4gq + 0..3
+          if constexpr (WRITE_OUT) O[nn] = mfma_f16(sb, cur.qg[kb], O[nn]);
         }
       }
       if (g == 2) KDA_ISSUE((load_ops<1, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
@@ -348,23 +349,37 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     __syncthreads();
     KDA_TIMER_MARK(3);
 
-    // ---- O += A_qk D; S = Diag(exp(G_L)) S + Kt^T D
+    // ---- O += A_qk D; S = Diag(exp(G_L)) S + Kt^T D.  The D^T hi/lo reads
+    // of a column tile are issued one tile ahead, like the groups above.
+    uint4 dq[2][4];
+    auto read_d = [&](int nn, uint4(&dst)[4]) {
+      const int col = 16 * nn + tl;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        dst[ks] = *reinterpret_cast<const uint4*>(sDth + col * TP + 32 * ks + 8 * gq);
+        dst[2 + ks] = *reinterpret_cast<const uint4*>(sDtl + col * TP + 32 * ks + 8 * gq);
+      }
+    };
+    read_d(0, dq[0]);
 #pragma unroll
     for (int nn = 0; nn < 4; ++nn) {
-      const int col = 16 * nn + tl;
+      if (nn + 1 < 4) read_d(nn + 1, dq[(nn + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
       f16x8 dh[2], dl[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        dh[ks] = *reinterpret_cast<const f16x8*>(sDth + col * TP + 32 * ks + 8 * gq);
-        dl[ks] = *reinterpret_cast<const f16x8*>(sDtl + col * TP + 32 * ks + 8 * gq);
+        dh[ks] = __builtin_bit_cast(f16x8, dq[nn & 1][ks]);
+        dl[ks] = __builtin_bit_cast(f16x8, dq[nn & 1][2 + ks]);
       }
       if constexpr (WRITE_OUT) {
+        // O^T += D^T (A_qk)^T; the lane's 4 consecutive bf16 columns of token
+        // row 16w + tl are staged in LDS with one 8-byte write
         f32x4 o = O[nn];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) o = mfma_f16(ks < ksmax ? cur.aqk[ks] : f16x8{}, dh[ks], o);
-        // output tile rows 16w + 4gq + ii, column col (staged for 16-byte stores)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) sO[(16 * w + 4 * gq + ii) * OP + col] = (__bf16)(o[ii] * a.scale);
+        for (int ks = 0; ks < 2; ++ks) o = mfma_f16(dh[ks], ks < ksmax ? cur.aqk[ks] : f16x8{}, o);
+        const bf16x4 ob = {(__bf16)(o[0] * a.scale), (__bf16)(o[1] * a.scale), (__bf16)(o[2] * a.scale),
+                           (__bf16)(o[3] * a.scale)};
+        *reinterpret_cast<bf16x4*>(sO + (16 * w + tl) * OP + 16 * nn + 4 * gq) = ob;
       }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
