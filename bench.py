@@ -38,7 +38,8 @@ BF16_DENSE_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
 BYTES_PER_HEAD_TOKEN = 4 * 128 * 2 + 2 + 128 * 2
 STATE_BYTES = 128 * 128 * 4
 KERNEL_SRCS = [os.path.join(ROOT, "chunked_gated_delta_amd", "csrc", f)
-               for f in ("kda_common.h", "kda_host.h", "kda_intra.hip", "kda_inter.hip", "kda_api.hip")]
+               for f in ("kda_common.h", "kda_host.h", "kda_intra.hip", "kda_inter.hip", "kda_api.hip")] + [
+    os.path.join(ROOT, "chunked_gated_delta_amd", "build.py")]  # compile flags shape the kernels too
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_fwd_c3_traffic.json")
 
 

@@ -202,17 +202,17 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
                               : ((a.init_identity && c == col) ? 1.0f : 0.0f);
         }
   }
-  auto store_st = [&]() {
+  // fp16 copy of the state's column tile nn (both row tiles of this wave)
+  auto store_st_tile = [&](int nn) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nn = 0; nn < 4; ++nn) {
-        const f16x4 hv = {(_Float16)S[mt][nn][0], (_Float16)S[mt][nn][1], (_Float16)S[mt][nn][2],
-                          (_Float16)S[mt][nn][3]};
-        *reinterpret_cast<f16x4*>(sSt + (16 * nn + tl) * SP + 32 * w + 16 * mt + 4 * gq) = hv;
-      }
+    for (int mt = 0; mt < 2; ++mt) {
+      const f16x4 hv = {(_Float16)S[mt][nn][0], (_Float16)S[mt][nn][1], (_Float16)S[mt][nn][2],
+                        (_Float16)S[mt][nn][3]};
+      *reinterpret_cast<f16x4*>(sSt + (16 * nn + tl) * SP + 32 * w + 16 * mt + 4 * gq) = hv;
+    }
   };
-  store_st();
+#pragma unroll
+  for (int nn = 0; nn < 4; ++nn) store_st_tile(nn);
   __bf16* sO = reinterpret_cast<__bf16*>(smem + OFF_O);
   // Record operands are prefetched one chunk ahead into two register sets
   // that alternate through the 2x unrolled loop below; the loads of chunk c+1
@@ -351,6 +351,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
 
     // ---- O += A_qk D; S = Diag(exp(G_L)) S + Kt^T D.  The D^T hi/lo reads
     // of a column tile are issued one tile ahead, like the groups above.
+    // Every wave finished reading the state copy and the V tile before the
+    // barrier above, so both are rewritten for the next chunk inside this
+    // phase: the fp16 copy of column tile nn - 1 while tile nn's MFMAs run,
+    // and the V tile at tile 2.
     uint4 dq[2][4];
     auto read_d = [&](int nn, uint4(&dst)[4]) {
       const int col = 16 * nn + tl;
@@ -365,6 +369,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     for (int nn = 0; nn < 4; ++nn) {
       if (nn + 1 < 4) read_d(nn + 1, dq[(nn + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
+      if (nn > 0) store_st_tile(nn - 1);
+      // past the end of the sequence this rewrites the current tile, which
+      // nothing reads
+      if constexpr (HAS_V)
+        if (nn == 2) store_vt(sVt, vn, tid, in1 ? chunk_len(c1) : L);
       f16x8 dh[2], dl[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -412,10 +421,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
       }
     }
     KDA_TIMER_MARK(4);
-    store_st();
-    // U of this chunk read sVt before the barrier above; past the end of the
-    // sequence this rewrites the current tile, which nothing reads
-    if constexpr (HAS_V) store_vt(sVt, vn, tid, in1 ? chunk_len(c1) : L);
+    store_st_tile(3);
     KDA_TIMER_MARK(5);
     __syncthreads();
     KDA_TIMER_MARK(6);
