@@ -60,7 +60,8 @@ constexpr int NFAC = 15;
 constexpr int OFF_FAC = OFF_TOT + 4 * KD * 4;          // f32 [NFAC][128] decay factors
 constexpr int OFF_NB = OFF_FAC + NFAC * KD * 4;        // f32 [128] gate offsets
 constexpr int OFF_B = OFF_NB + KD * 4;                 // f32 [64] beta
-constexpr int LDS_BYTES = OFF_B + CH * 4;
+constexpr int OFF_FLAG = OFF_B + CH * 4;               // int [4] row-block ready tags
+constexpr int LDS_BYTES = OFF_FLAG + 4 * 4;
 static_assert(LDS_BYTES <= 80 * 1024, "two workgroups per CU");
 
 // decay-factor rows (per channel, log2 units, P_w = prefix before sub-chunk w):
@@ -75,6 +76,36 @@ __device__ __forceinline__ float row_scan16(float x) {
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, true));
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, true));
   return x;
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bf16 hi/lo split of 8 floats, two at a time: hi = RNE(x), lo = RNE(x - hi).
+// Converting pairs (one packed conversion each) and reading hi back with a
+// shift or a mask takes 3 instructions per element, against 4 when every
+// element is converted on its own first.
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const f32x2 v = {x[2 * p], x[2 * p + 1]};
+    h[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    const f32x2 r = {x[2 * p] - __uint_as_float(h[p] << 16), x[2 * p + 1] - __uint_as_float(h[p] & 0xffff0000u)};
+    l[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+  }
+  hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8]) {
+  uint32_t h[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const f32x2 v = {x[2 * p], x[2 * p + 1]};
+    h[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
 }
 
 // The chunk table, A_log and the record base are also passed as separate
@@ -99,6 +130,7 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   float* sFac = reinterpret_cast<float*>(smem + OFF_FAC);
   float* sNB = reinterpret_cast<float*>(smem + OFF_NB);
   float* sB = reinterpret_cast<float*>(smem + OFF_B);
+  int* sFlag = reinterpret_cast<int*>(smem + OFF_FLAG);
 
   const int H = a.H;
 
@@ -113,6 +145,8 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   const int items = (int)(nchunk * H);
   int item = blockIdx.x;
   if (item >= items) return;
+  // row-block ready tags hold the item whose row they publish; no item is -1
+  if (threadIdx.x < 4) sFlag[threadIdx.x] = -1;
 
   // inputs of one item for this lane's token: channels 32kb + 8gq + e.  All
   // loads are unconditional: rows past the chunk end read the last valid row
@@ -324,48 +358,46 @@ __global__ void __launch_bounds__(NTHREADS, 2)
     unpack_bf16x8(pq[kb], qf);
     unpack_bf16x8(pk[kb], kf);
     bf16x8 krh, krl;
-    f16x8 qg, kth8, ktl8;
+    f16x8 qg, kg8, kth8, ktl8;
+    float xv[8], yv[8], qv[8], rv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int c = 32 * kb + 8 * gq + e;
       const float Gl = gl[kb][e];
       const float LF = fexp2(Gl);   // exp(G_t - P_w) <= 1
       const float E = fexp2(-Gl);   // exp(P_w - G_t) in [1, 2^116]
       const float kn = kf[e] * rk;
       const float qn = qf[e] * rq;
-      const float x = kn * LF;
-      const __bf16 xh = (__bf16)x;
-      kLFh[kb][e] = xh;
-      kLFl[kb][e] = (__bf16)(x - (float)xh);
-      const float y = kn * E;
-      const __bf16 yh = (__bf16)y;
-      kEh[kb][e] = yh;
-      kEl[kb][e] = (__bf16)(y - (float)yh);
-      const float ql = qn * LF;
-      qLF[kb][e] = (__bf16)ql;
-      const float rf = y * ET[e];    // k^ exp(P_{w+1} - G_t), |.| <= |k^|
-      const __bf16 rh = (__bf16)rf;
-      krh[e] = rh;
-      krl[e] = (__bf16)(rf - (float)rh);
-      sKG[c * TP + ti] = (_Float16)(x * EP[e]);   // k^ exp(G_t)
-      const float kt = y * EL[e];                  // k^ exp(G_L - G_t)
+      xv[e] = kn * LF;
+      yv[e] = kn * E;
+      qv[e] = qn * LF;
+      rv[e] = yv[e] * ET[e];                        // k^ exp(P_{w+1} - G_t), |.| <= |k^|
+      kg8[e] = (_Float16)(xv[e] * EP[e]);           // k^ exp(G_t)
+      const float kt = yv[e] * EL[e];               // k^ exp(G_L - G_t)
       const _Float16 kth = (_Float16)kt;
       kth8[e] = kth;
       ktl8[e] = (_Float16)(kt - (float)kth);
-      qg[e] = (_Float16)(ql * EP[e]);              // q^ exp(G_t)
+      qg[e] = (_Float16)(qv[e] * EP[e]);            // q^ exp(G_t)
     }
+    split_bf16x8(xv, kLFh[kb], kLFl[kb]);
+    split_bf16x8(yv, kEh[kb], kEl[kb]);
+    qLF[kb] = to_bf16x8(qv);
+    split_bf16x8(rv, krh, krl);
     *reinterpret_cast<f16x8*>(gQG + frag_tc(ti, 32 * kb + 8 * gq)) = qg;
-    // (K^ exp(G_L - G))^T hi/lo: f16 x 1 products summed in fp32 are exact
+    // (K^ exp(G_L - G))^T hi/lo and (K^ exp(G))^T: f16 x 1 products summed in
+    // fp32 are exact, so these transposes are exact
 #pragma unroll
     for (int sv = 0; sv < 2; ++sv) {
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
       const f32x4 th = mfma_f16(kth8, idt[sv], zero);
       const f32x4 tlo = mfma_f16(ktl8, idt[sv], zero);
+      const f32x4 tg = mfma_f16(kg8, idt[sv], zero);
       const int cc = 32 * kb + 16 * sv + tl;  // lane: channel cc, tokens 16w + 4gq + 0..3
       const f16x4 h4 = {(_Float16)th[0], (_Float16)th[1], (_Float16)th[2], (_Float16)th[3]};
       const f16x4 l4 = {(_Float16)tlo[0], (_Float16)tlo[1], (_Float16)tlo[2], (_Float16)tlo[3]};
+      const f16x4 g4 = {(_Float16)tg[0], (_Float16)tg[1], (_Float16)tg[2], (_Float16)tg[3]};
       *reinterpret_cast<f16x4*>(gKTH + frag_ct(cc, 16 * w + 4 * gq)) = h4;
       *reinterpret_cast<f16x4*>(gKTL + frag_ct(cc, 16 * w + 4 * gq)) = l4;
+      *reinterpret_cast<f16x4*>(sKG + cc * TP + 16 * w + 4 * gq) = g4;
     }
     if (w < 3) {
       *reinterpret_cast<bf16x8*>(sKRFh + ti * KP + 32 * kb + 8 * gq) = krh;
@@ -468,20 +500,26 @@ __global__ void __launch_bounds__(NTHREADS, 2)
       for (int i = 0; i < 16; ++i) sA[(16 * w + i) * AP + 16 * w + cc] = x[i];
     }
   }
+  // Publish row-block w (its A blocks and T_ww are in LDS).  LDS operations
+  // of one wave complete in order and the release orders the tag after them.
+  __hip_atomic_store(&sFlag[w], item, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   // The A operands of this item are dead: start the next item's loads (the
   // last item re-reads its own, so every path has the same loads in flight).
   issue(0, more ? next : item, h2, c02, L2);
-  __syncthreads();
   KDA_TIMER_MARK(5);
 
   // ============= off-diagonal blocks of T, column-block by column-block ====
   //     T_{b,w} = -T_bb * sum_{m=w}^{b-1} A_{b,m} T_{m,w}   (fp32 MFMA)
   // Wave w walks down its own column-block.  The blocks T_{m,w} it needs are
   // its own earlier results, kept in registers in C layout (which is the
-  // B-operand layout); T_bb and the A blocks are final since the barrier
-  // above.  So the levels need no barrier between them.  Instruction s of a
-  // block product contracts over index 4gq + s: a lane's four A-operand values
-  // of one row are a single 16-byte LDS read.
+  // B-operand layout); T_bb and the A blocks of row-block b are final once
+  // row-block b is published.  So no barrier separates this phase from
+  // the A phase or its levels from each other: the A work grows with the row
+  // index and this work with the column index, and the two now overlap.
+  // Every wave publishes its row before it waits for another, so the waits
+  // always end; the spin is bounded all the same.  Instruction s of a block
+  // product contracts over index 4gq + s: a lane's four A-operand values of
+  // one row are a single 16-byte LDS read.
   {
     f32x4 Tc[4];
 #pragma unroll
@@ -491,6 +529,10 @@ __global__ void __launch_bounds__(NTHREADS, 2)
       Tc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (w + d < 4) {
         const int b = w + d;
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+          if (__hip_atomic_load(&sFlag[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == item) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
         const float* arow = sA + (16 * b + tl) * AP + 4 * gq;
         f32x4 X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
