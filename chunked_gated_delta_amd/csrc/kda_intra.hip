@@ -508,22 +508,59 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   issue(0, more ? next : item, h2, c02, L2);
   KDA_TIMER_MARK(5);
 
-  // ============= off-diagonal blocks of T, column-block by column-block ====
+  // ======= T column-block by column-block, and T diag(b) from registers =====
   //     T_{b,w} = -T_bb * sum_{m=w}^{b-1} A_{b,m} T_{m,w}   (fp32 MFMA)
   // Wave w walks down its own column-block.  The blocks T_{m,w} it needs are
   // its own earlier results, kept in registers in C layout (which is the
   // B-operand layout); T_bb and the A blocks of row-block b are final once
-  // row-block b is published.  So no barrier separates this phase from
-  // the A phase or its levels from each other: the A work grows with the row
-  // index and this work with the column index, and the two now overlap.
-  // Every wave publishes its row before it waits for another, so the waits
-  // always end; the spin is bounded all the same.  Instruction s of a block
-  // product contracts over index 4gq + s: a lane's four A-operand values of
-  // one row are a single 16-byte LDS read.
+  // row-block b is published.  So no barrier separates this phase from the A
+  // phase or its levels from each other: the A work grows with the row index
+  // and this work with the column index, and the two overlap.  Every wave
+  // publishes its row before it waits for another, so the waits always end;
+  // the spin is bounded all the same.  Instruction s of a block product
+  // contracts over index 4gq + s: a lane's four A-operand values of one row
+  // are a single 16-byte LDS read.
+  //
+  // Each block is also formed transposed, T_{b,w}^T = X^T (-T_bb^T), whose C
+  // layout gives a lane four consecutive columns 16w + 4gq + 0..3 of row
+  // 16b + tl.  T diag(b) is formed from that right away: bf16 hi/lo 8-byte
+  // stores to the record, fp16 hi/lo kept in registers for the LDS copy that
+  // W reads (written after the barrier below, because that region still holds
+  // the A-phase right factors).  Odd waves also own the all-zero upper block
+  // (w - 1, w) that the readers of rows 0..15 and 32..47 load.
   {
+    const float4 bj4 = *reinterpret_cast<const float4*>(sB + 16 * w + 4 * gq);
+    const float bj[4] = {bj4.x, bj4.y, bj4.z, bj4.w};
+    f16x4 tbh16[5], tbl16[5];
+    auto emit = [&](int b, const f32x4& tt, f16x4& h16, f16x4& l16) {
+      const int i = 16 * b + tl;
+      float t[4];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int j = 16 * w + 4 * gq + ii;
+        t[ii] = (j < i) ? tt[ii] * bj[ii] : ((j == i) ? bj[ii] : 0.0f);
+        const _Float16 hv = (_Float16)t[ii];
+        h16[ii] = hv;
+        l16[ii] = (_Float16)(t[ii] - (float)hv);
+      }
+      uint32_t hb[2], lb[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const f32x2 v = {t[2 * p], t[2 * p + 1]};
+        hb[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+        const f32x2 r = {t[2 * p] - __uint_as_float(hb[p] << 16), t[2 * p + 1] - __uint_as_float(hb[p] & 0xffff0000u)};
+        lb[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+      }
+      *reinterpret_cast<uint2*>(gTBH + frag_tt(i, 16 * w + 4 * gq)) = make_uint2(hb[0], hb[1]);
+      *reinterpret_cast<uint2*>(gTBL + frag_tt(i, 16 * w + 4 * gq)) = make_uint2(lb[0], lb[1]);
+    };
     f32x4 Tc[4];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) Tc[0][ii] = sA[(16 * w + 4 * gq + ii) * AP + 16 * w + tl];
+    {
+      const float4 d4 = *reinterpret_cast<const float4*>(sA + (16 * w + tl) * AP + 16 * w + 4 * gq);
+      emit(w, f32x4{d4.x, d4.y, d4.z, d4.w}, tbh16[0], tbl16[0]);
+    }
 #pragma unroll
     for (int d = 1; d < 4; ++d) {
       Tc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -550,48 +587,33 @@ __global__ void __launch_bounds__(NTHREADS, 2)
         r = mfma_f32(-t4.z, X[2], r);
         r = mfma_f32(-t4.w, X[3], r);
         Tc[d] = r;
+        f32x4 tt = {0.f, 0.f, 0.f, 0.f};
+        tt = mfma_f32(X[0], -t4.x, tt);
+        tt = mfma_f32(X[1], -t4.y, tt);
+        tt = mfma_f32(X[2], -t4.z, tt);
+        tt = mfma_f32(X[3], -t4.w, tt);
+        emit(b, tt, tbh16[d], tbl16[d]);
       }
     }
-    __syncthreads();  // every wave is done reading A blocks that T overwrites
+    if (w & 1) emit(w - 1, f32x4{0.f, 0.f, 0.f, 0.f}, tbh16[4], tbl16[4]);
+    KDA_TIMER_MARK(6);
+    issue(1, more ? next : item, h2, c02, L2);
+    __syncthreads();  // every wave is done with the A phase's right factors
 #pragma unroll
-    for (int d = 1; d < 4; ++d) {
+    for (int d = 0; d < 4; ++d) {
       if (w + d < 4) {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) sA[(16 * (w + d) + 4 * gq + ii) * AP + 16 * w + tl] = Tc[d][ii];
+        const int i = 16 * (w + d) + tl;
+        *reinterpret_cast<f16x4*>(sTbh + i * TBP + 16 * w + 4 * gq) = tbh16[d];
+        *reinterpret_cast<f16x4*>(sTbl + i * TBP + 16 * w + 4 * gq) = tbl16[d];
       }
+    }
+    if (w & 1) {
+      const int i = 16 * (w - 1) + tl;
+      *reinterpret_cast<f16x4*>(sTbh + i * TBP + 16 * w + 4 * gq) = tbh16[4];
+      *reinterpret_cast<f16x4*>(sTbl + i * TBP + 16 * w + 4 * gq) = tbl16[4];
     }
     __syncthreads();
   }
-
-  KDA_TIMER_MARK(6);
-  issue(1, more ? next : item, h2, c02, L2);
-  // ======= T diag(b): fp16 hi/lo into LDS (for W), bf16 hi/lo to the record
-  for (int it = tid; it < CH * 8; it += NTHREADS) {
-    const int i = it >> 3;
-    const int j0 = (it & 7) * 8;
-    if (i < 32 && j0 >= 32) continue;  // all-zero fragment, read by no one
-    float t8[8], b8[8];
-    lds_f32x8(sA + i * AP + j0, t8);
-    lds_f32x8(sB + j0, b8);
-    f16x8 h16, l16;
-    bf16x8 hb, lb;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = j0 + e;
-      const float t = (j < i) ? t8[e] * b8[e] : ((j == i) ? b8[e] : 0.0f);
-      const _Float16 th = (_Float16)t;
-      h16[e] = th;
-      l16[e] = (_Float16)(t - (float)th);
-      const __bf16 tb = (__bf16)t;
-      hb[e] = tb;
-      lb[e] = (__bf16)(t - (float)tb);
-    }
-    *reinterpret_cast<f16x8*>(sTbh + i * TBP + j0) = h16;
-    *reinterpret_cast<f16x8*>(sTbl + i * TBP + j0) = l16;
-    *reinterpret_cast<bf16x8*>(gTBH + frag_tt(i, j0)) = hb;
-    *reinterpret_cast<bf16x8*>(gTBL + frag_tt(i, j0)) = lb;
-  }
-  __syncthreads();
   KDA_TIMER_MARK(7);
 
   // ======================= -W = -(T diag(b)) (K^ exp(G)) ===================
