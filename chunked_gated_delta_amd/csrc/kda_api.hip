@@ -17,14 +17,19 @@ namespace {
 constexpr int kMaxSortN = 16384;
 
 // choff[n] = sum_{m<n} ceil(len_m / 64), choff[N] = total chunks (one block).
+// Also zeroes the intra kernel's work-item counter.
 __global__ void __launch_bounds__(1024) kda_chunk_offsets_kernel(const int32_t* __restrict__ cu, int N,
-                                                                 int32_t* __restrict__ choff) {
+                                                                 int32_t* __restrict__ choff,
+                                                                 int32_t* __restrict__ claim) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t carry;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  if (tid == 0) carry = 0;
+  if (tid == 0) {
+    carry = 0;
+    *claim = 0;
+  }
   __syncthreads();
   for (int base = 0; base < N; base += 1024) {
     const int i = base + tid;
@@ -46,6 +51,10 @@ __global__ void __launch_bounds__(1024) kda_chunk_offsets_kernel(const int32_t* 
   }
   if (tid == 0) choff[N] = carry;
 }
+
+// Zeroes the intra kernel's work-item counter (a kernel rather than a memset,
+// so that a captured graph replays it as a kernel node).
+__global__ void kda_zero_claim_kernel(int32_t* __restrict__ claim) { *claim = 0; }
 
 // Longest-first processing order of the sequences: rank of sequence i = number
 // of sequences that are longer, or equally long with a smaller index.
@@ -128,10 +137,17 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
 
   pr.ws = static_cast<char*>(workspace);
   int32_t* choff = reinterpret_cast<int32_t*>(pr.ws + pr.lay.choff);
+  int32_t* claim = reinterpret_cast<int32_t*>(pr.ws + pr.lay.claim);
   pr.order = nullptr;
   int n32 = (int)N;
-  if (cu_seqlens) {
-    void* cargs[] = {(void*)&cu_seqlens, (void*)&n32, (void*)&choff};
+  if (!cu_seqlens) {
+    void* zargs[] = {(void*)&claim};
+    if (launch_status(hipLaunchKernel(reinterpret_cast<const void*>(&kda_zero_claim_kernel), dim3(1), dim3(1),
+                                      zargs, 0, st),
+                      "claim reset") != KDA_SUCCESS)
+      return KDA_ERR_LAUNCH;
+  } else {
+    void* cargs[] = {(void*)&cu_seqlens, (void*)&n32, (void*)&choff, (void*)&claim};
     if (launch_status(hipLaunchKernel(reinterpret_cast<const void*>(&kda_chunk_offsets_kernel), dim3(1),
                                       dim3(1024), cargs, 0, st),
                       "chunk offsets") != KDA_SUCCESS)
@@ -162,6 +178,7 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
   ia.A_log = A_log ? A_log : reinterpret_cast<const float*>(pr.rec);
   ia.dt_bias = dt_bias ? dt_bias : reinterpret_cast<const float*>(pr.rec);
   ia.flags = (int)(flags & (FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM));
+  ia.claim = claim;
   ia.rec = pr.rec;
   ia.map = pr.map;
   ia.H = (int)H;

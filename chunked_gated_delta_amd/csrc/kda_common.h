@@ -160,6 +160,7 @@ struct IntraArgs {
   int H;
   float lb2;        // lower_bound * log2(e)
   int flags;        // FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM
+  int* claim;       // work-item counter, zero when the kernel starts
   unsigned long long* timers;  // phase timers (KDA_PHASE_TIMERS builds only), else nullptr
 };
 struct InterArgs {

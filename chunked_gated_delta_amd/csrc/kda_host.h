@@ -10,11 +10,12 @@ namespace kda {
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct Layout {
-  size_t choff, order, rec, total;
+  size_t claim, choff, order, rec, total;
 };
 
 inline Layout workspace_layout(int64_t T_total, int64_t H, int64_t N) {
   Layout l;
+  l.claim = 0;  // the intra kernel's work-item counter (one int)
   l.choff = 256;
   l.order = l.choff + align256((size_t)(N + 1) * sizeof(int32_t));
   l.rec = l.order + align256((size_t)N * sizeof(int32_t));

@@ -60,8 +60,8 @@ constexpr int NFAC = 15;
 constexpr int OFF_FAC = OFF_TOT + 4 * KD * 4;          // f32 [NFAC][128] decay factors
 constexpr int OFF_NB = OFF_FAC + NFAC * KD * 4;        // f32 [128] gate offsets
 constexpr int OFF_B = OFF_NB + KD * 4;                 // f32 [64] beta
-constexpr int OFF_FLAG = OFF_B + CH * 4;               // int [4] row-block ready tags
-constexpr int LDS_BYTES = OFF_FLAG + 4 * 4;
+constexpr int OFF_FLAG = OFF_B + CH * 4;               // int [4] row-block ready tags, [4] claim
+constexpr int LDS_BYTES = OFF_FLAG + 8 * 4;
 static_assert(LDS_BYTES <= 80 * 1024, "two workgroups per CU");
 
 // decay-factor rows (per channel, log2 units, P_w = prefix before sub-chunk w):
@@ -131,6 +131,7 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   float* sNB = reinterpret_cast<float*>(smem + OFF_NB);
   float* sB = reinterpret_cast<float*>(smem + OFF_B);
   int* sFlag = reinterpret_cast<int*>(smem + OFF_FLAG);
+  int* sClaim = sFlag + 4;
 
   const int H = a.H;
 
@@ -143,8 +144,14 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   map.choff = choff;
   const int64_t nchunk = total_chunks(map);
   const int items = (int)(nchunk * H);
+  // The first two items of a workgroup are blockIdx.x and blockIdx.x + grid;
+  // after that it claims items from a counter (one claim per processed item,
+  // made an item ahead so that its latency stays hidden), so workgroups that
+  // run faster take more items and all finish together.  Claims only grow:
+  // once a workgroup's next item is past the end, so is every later claim.
   int item = blockIdx.x;
   if (item >= items) return;
+  int next = item + (int)gridDim.x;
   // row-block ready tags hold the item whose row they publish; no item is -1
   if (threadIdx.x < 4) sFlag[threadIdx.x] = -1;
 
@@ -245,8 +252,10 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   __bf16* gTBL = reinterpret_cast<__bf16*>(rec + REC_TBL);
   float* gGL = reinterpret_cast<float*>(rec + REC_GL);
   const bool valid = ti < L;
+  // claim the item after next (the value is shared before the operands barrier)
+  int claimed = 0;
+  if (threadIdx.x == 0) claimed = atomicAdd(a.claim, 1);
   // the next item's place (scalar table lookups, overlapped with this item)
-  const int next = item + (int)gridDim.x;
   const bool more = next < items;
   int h2, L2;
   int64_t g2, c02;
@@ -404,8 +413,10 @@ __global__ void __launch_bounds__(NTHREADS, 2)
       *reinterpret_cast<bf16x8*>(sKRFl + ti * KP + 32 * kb + 8 * gq) = krl;
     }
   }
+  if (threadIdx.x == 0) *sClaim = claimed;
   __syncthreads();
   KDA_TIMER_MARK(4);
+  const int next2 = __builtin_amdgcn_readfirstlane(*sClaim) + 2 * (int)gridDim.x;
 
   // ======================= A_kk and A_qk ==================================
   // wave w owns row-block w; lane holds C[16w + 4gq + ii][16b + tl]
@@ -647,6 +658,7 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   KDA_TIMER_MARK(8);
   if (!more) break;
   item = next;
+  next = next2;
   h = h2; g = g2; c0 = c02; L = L2;
   __syncthreads();  // LDS of this item is read above until the W phase
   KDA_TIMER_MARK(9);
