@@ -22,14 +22,21 @@ constexpr int NTHREADS = 256;
 constexpr int NV = 2;            // V slices per (sequence, head)
 constexpr int VT = VD / NV;      // 64 state columns per workgroup
 constexpr int TP = CH + 8;       // token pitch of [v][token] arrays (halves)
-constexpr int SP = KD + 8;       // channel pitch of the [v][channel] state copy
 
 constexpr int OFF_VT = 0;                          // bf16 [VT][TP]   V^T
-constexpr int OFF_ST = OFF_VT + VT * TP * 2;       // f16  [VT][SP]   S^T
-constexpr int OFF_DTH = OFF_ST + VT * SP * 2;      // f16  [VT][TP]   D^T hi
-constexpr int OFF_DTL = OFF_DTH + VT * TP * 2;     // f16  [VT][TP]   D^T lo
+// The state copy and D hi/lo are kept as B-operand fragments: fragment f holds
+// one 16-column tile x 32-k block, the 16 bytes (8 k) of MFMA lane l = 16gq + tl
+// split into two planes, bytes 0-7 at l*8 and bytes 8-15 at 512 + l*8.  A
+// lane's operand is then two 8-byte reads, and both the reads (64 contiguous
+// lanes) and the writes from the accumulator layout (4 consecutive k of one
+// column) are free of LDS bank conflicts on gfx950, where the row-pitched
+// layout doubled the read and write time.
+constexpr int FRAG = 1024;                         // bytes per fragment
+constexpr int OFF_ST = OFF_VT + VT * TP * 2;       // f16  16 fragments (nn, kb)   state copy
+constexpr int OFF_DTH = OFF_ST + 16 * FRAG;        // f16   8 fragments (nn, ks)   D hi
+constexpr int OFF_DTL = OFF_DTH + 8 * FRAG;        // f16   8 fragments (nn, ks)   D lo
 constexpr int OP = VT + 8;                         // token-row pitch of the output tile
-constexpr int OFF_O = OFF_DTL + VT * TP * 2;       // bf16 [CH][OP]   output staging
+constexpr int OFF_O = OFF_DTL + 8 * FRAG;          // bf16 [CH][OP]   output staging
 constexpr int LDS_BYTES = OFF_O + CH * OP * 2;
 
 // the record operands one wave needs per chunk
@@ -119,6 +126,20 @@ __device__ __forceinline__ void load_v(uint4 (&vv)[2], const uint16_t* v, int64_
 // over all banks instead of hitting 8 column groups in the same ones.
 __device__ __forceinline__ int vt_swz(int c) { return 8 * ((c >> 3) & 7); }
 
+// B operand of MFMA lane `lane` from fragment `frag` (two 8-byte plane reads)
+__device__ __forceinline__ uint4 frag_read(const char* base, int frag, int lane) {
+  const char* p = base + frag * FRAG + lane * 8;
+  const uint2 lo = *reinterpret_cast<const uint2*>(p);
+  const uint2 hi = *reinterpret_cast<const uint2*>(p + FRAG / 2);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// Store 4 consecutive k (k0 = 4 * q within the fragment's 32-k block, q = 0..7)
+// of column tl into fragment `frag`: MFMA lane 16 (q / 2) + tl, plane q % 2.
+__device__ __forceinline__ void frag_write4(char* base, int frag, int q, int tl, f16x4 v) {
+  *reinterpret_cast<f16x4*>(base + frag * FRAG + (q & 1) * (FRAG / 2) + (16 * (q >> 1) + tl) * 8) = v;
+}
+
 // Write the V tile transposed (column-major, 2 tokens per dword).  Lanes of
 // neighbouring tokens t, t^1 (lanes 4 apart) trade half their columns, so
 // each lane writes 8 packed dwords: the even token's lane columns
@@ -157,9 +178,9 @@ template <bool HAS_V, bool WRITE_OUT, bool CKPT = false>
 __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   __bf16* sVt = reinterpret_cast<__bf16*>(smem + OFF_VT);
-  _Float16* sSt = reinterpret_cast<_Float16*>(smem + OFF_ST);
-  _Float16* sDth = reinterpret_cast<_Float16*>(smem + OFF_DTH);
-  _Float16* sDtl = reinterpret_cast<_Float16*>(smem + OFF_DTL);
+  char* sSt = smem + OFF_ST;
+  char* sDth = smem + OFF_DTH;
+  char* sDtl = smem + OFF_DTL;
 
   // XCD-aware mapping: ids are dispatched round-robin over the 8 XCDs, so the
   // two V-halves of one (sequence, head) get ids with equal residue mod 8 and
@@ -208,7 +229,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     for (int mt = 0; mt < 2; ++mt) {
       const f16x4 hv = {(_Float16)S[mt][nn][0], (_Float16)S[mt][nn][1], (_Float16)S[mt][nn][2],
                         (_Float16)S[mt][nn][3]};
-      *reinterpret_cast<f16x4*>(sSt + (16 * nn + tl) * SP + 32 * w + 16 * mt + 4 * gq) = hv;
+      frag_write4(sSt, 4 * nn + w, 4 * mt + gq, tl, hv);
     }
   };
 #pragma unroll
@@ -289,7 +310,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
       for (int nn = 0; nn < 4; ++nn) {
         const int col = 16 * nn + tl;
         dst[nn] = g < 2 ? *reinterpret_cast<const uint4*>(sVt + col * TP + ((32 * g + 8 * gq) ^ vt_swz(col)))
-                        : *reinterpret_cast<const uint4*>(sSt + col * SP + 32 * (g - 2) + 8 * gq);
+                        : frag_read(sSt, 4 * nn + (g - 2), lane);
       }
     };
     constexpr int G0 = HAS_V ? 0 : 2;
@@ -342,8 +363,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
         dh[ii] = hv;
         dl[ii] = (_Float16)(u[nn][ii] - (float)hv);
       }
-      *reinterpret_cast<f16x4*>(sDth + col * TP + 16 * w + 4 * gq) = dh;
-      *reinterpret_cast<f16x4*>(sDtl + col * TP + 16 * w + 4 * gq) = dl;
+      frag_write4(sDth, 2 * nn + (w >> 1), 4 * (w & 1) + gq, tl, dh);
+      frag_write4(sDtl, 2 * nn + (w >> 1), 4 * (w & 1) + gq, tl, dl);
     }
     KDA_TIMER_MARK(2);
     __syncthreads();
@@ -357,11 +378,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     // and the V tile at tile 2.
     uint4 dq[2][4];
     auto read_d = [&](int nn, uint4(&dst)[4]) {
-      const int col = 16 * nn + tl;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        dst[ks] = *reinterpret_cast<const uint4*>(sDth + col * TP + 32 * ks + 8 * gq);
-        dst[2 + ks] = *reinterpret_cast<const uint4*>(sDtl + col * TP + 32 * ks + 8 * gq);
+        dst[ks] = frag_read(sDth, 2 * nn + ks, lane);
+        dst[2 + ks] = frag_read(sDtl, 2 * nn + ks, lane);
       }
     };
     read_d(0, dq[0]);
