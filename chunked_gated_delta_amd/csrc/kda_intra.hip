@@ -152,8 +152,9 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   int item = blockIdx.x;
   if (item >= items) return;
   int next = item + (int)gridDim.x;
-  // row-block ready tags hold the item whose row they publish; no item is -1
-  if (threadIdx.x < 4) sFlag[threadIdx.x] = -1;
+  // ready tags hold the item whose data they publish; no item is -1.  Tags
+  // 0-3: row-block b (its A blocks, and T_bb for b < 3); 5: A_33; 6: T_33.
+  if (threadIdx.x < 8) sFlag[threadIdx.x] = -1;
 
   // inputs of one item for this lane's token: channels 32kb + 8gq + e.  All
   // loads are unconditional: rows past the chunk end read the last valid row
@@ -418,15 +419,58 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   KDA_TIMER_MARK(4);
   const int next2 = __builtin_amdgcn_readfirstlane(*sClaim) + 2 * (int)gridDim.x;
 
+  // Wait until tag `t` holds this item (release/acquire on the LDS tag word).
+  // Tags 0-3 and 5 are published with no wait before them, and tag 6 only
+  // after tag 5, so every wait ends; the spin is bounded all the same.
+  auto wait_tag = [&](int t) {
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+      if (__hip_atomic_load(&sFlag[t], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == item) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  };
+  auto publish = [&](int t) { __hip_atomic_store(&sFlag[t], item, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); };
+  // T_bb = (I + A_bb)^-1 of diagonal block blk, in place, by forward
+  // substitution: lane cc < 16 owns column cc.  The block's lower triangle is
+  // read into registers first (36 16-byte reads), so the substitution chain
+  // never waits on LDS.
+  auto diag_inverse = [&](int blk) {
+    if (lane < 16) {
+      const int cc = lane;
+      const float* Ab = sA + (16 * blk) * AP + 16 * blk;
+      float Ar[16][16];
+#pragma unroll
+      for (int i = 1; i < 16; ++i)
+#pragma unroll
+        for (int m4 = 0; m4 < i; m4 += 4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(Ab + i * AP + m4);
+          Ar[i][m4] = v4.x; Ar[i][m4 + 1] = v4.y; Ar[i][m4 + 2] = v4.z; Ar[i][m4 + 3] = v4.w;
+        }
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float s = (i == cc) ? 1.0f : 0.0f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) s -= Ar[i][m] * x[m];
+        x[i] = (i < cc) ? 0.0f : s;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sA[(16 * blk + i) * AP + 16 * blk + cc] = x[i];
+    }
+  };
+
   // ======================= A_kk and A_qk ==================================
-  // wave w owns row-block w; lane holds C[16w + 4gq + ii][16b + tl]
+  // wave w owns row-block w; lane holds C[16w + 4gq + ii][16b + tl].  The
+  // diagonal block comes first: row-block 3 publishes it at once, and the
+  // role-0 wave, whose own A work is one block, inverts it while row-block 3
+  // computes its three off-diagonal blocks.
   {
     const int i0 = 16 * w + 4 * gq;
     // beta of this lane's four rows, read once (not inside the masked stores)
     const float4 bi4 = *reinterpret_cast<const float4*>(sB + i0);
     const float bi[4] = {bi4.x, bi4.y, bi4.z, bi4.w};
 #pragma unroll 1
-    for (int b = 0; b <= w; ++b) {
+    for (int it = 0; it <= w; ++it) {
+      const int b = it == 0 ? w : it - 1;
       f32x4 akk = {0.f, 0.f, 0.f, 0.f};
       f32x4 aqk = {0.f, 0.f, 0.f, 0.f};
       if (b == w) {
@@ -476,6 +520,7 @@ __global__ void __launch_bounds__(NTHREADS, 2)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) q4[ii] = (_Float16)((16 * b + 4 * gq + ii <= ti) ? aqk[ii] : 0.0f);
       *reinterpret_cast<f16x4*>(gAQK + frag_tt(ti, 16 * b + 4 * gq)) = q4;
+      if (w == 3 && it == 0) publish(5);  // A_33
     }
     // zero blocks above the diagonal; rows 0..31 skip tokens 32..63, a whole
     // record fragment that the reader never loads
@@ -483,37 +528,18 @@ __global__ void __launch_bounds__(NTHREADS, 2)
       const f16x4 z4 = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
       *reinterpret_cast<f16x4*>(gAQK + frag_tt(ti, 16 * b + 4 * gq)) = z4;
     }
-    // T_ww = (I + A_ww)^-1 by forward substitution, lane cc < 16 owns column
-    // cc.  This wave wrote A_ww just above and LDS operations of one wave
-    // complete in order, so no barrier is needed here.  The block's lower
-    // triangle is read into registers first (36 16-byte reads), so the
-    // substitution chain never waits on LDS.
-    if (lane < 16) {
-      const int cc = lane;
-      const float* Ab = sA + (16 * w) * AP + 16 * w;
-      float Ar[16][16];
-#pragma unroll
-      for (int i = 1; i < 16; ++i)
-#pragma unroll
-        for (int m4 = 0; m4 < i; m4 += 4) {
-          const float4 v4 = *reinterpret_cast<const float4*>(Ab + i * AP + m4);
-          Ar[i][m4] = v4.x; Ar[i][m4 + 1] = v4.y; Ar[i][m4 + 2] = v4.z; Ar[i][m4 + 3] = v4.w;
-        }
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = (i == cc) ? 1.0f : 0.0f;
-#pragma unroll
-        for (int m = 0; m < i; ++m) s -= Ar[i][m] * x[m];
-        x[i] = (i < cc) ? 0.0f : s;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sA[(16 * w + i) * AP + 16 * w + cc] = x[i];
-    }
+    // T_ww for w < 3 (T_33 is the role-0 wave's, below).  This wave wrote A_ww
+    // above and LDS operations of one wave complete in order.
+    if (w < 3) diag_inverse(w);
   }
-  // Publish row-block w (its A blocks and T_ww are in LDS).  LDS operations
-  // of one wave complete in order and the release orders the tag after them.
-  __hip_atomic_store(&sFlag[w], item, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  // Publish row-block w.  LDS operations of one wave complete in order and the
+  // release orders the tag after them.
+  publish(w);
+  if (w == 0) {
+    wait_tag(5);
+    diag_inverse(3);
+    publish(6);
+  }
   // The A operands of this item are dead: start the next item's loads (the
   // last item re-reads its own, so every path has the same loads in flight).
   issue(0, more ? next : item, h2, c02, L2);
@@ -523,14 +549,12 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   //     T_{b,w} = -T_bb * sum_{m=w}^{b-1} A_{b,m} T_{m,w}   (fp32 MFMA)
   // Wave w walks down its own column-block.  The blocks T_{m,w} it needs are
   // its own earlier results, kept in registers in C layout (which is the
-  // B-operand layout); T_bb and the A blocks of row-block b are final once
-  // row-block b is published.  So no barrier separates this phase from the A
-  // phase or its levels from each other: the A work grows with the row index
-  // and this work with the column index, and the two overlap.  Every wave
-  // publishes its row before it waits for another, so the waits always end;
-  // the spin is bounded all the same.  Instruction s of a block product
-  // contracts over index 4gq + s: a lane's four A-operand values of one row
-  // are a single 16-byte LDS read.
+  // B-operand layout); the A blocks of row-block b are final once tag b is
+  // published, and T_bb with it (T_33 with tag 6).  So no barrier separates
+  // this phase from the A phase or its levels from each other: the A work
+  // grows with the row index and this work with the column index, and the two
+  // overlap.  Instruction s of a block product contracts over index 4gq + s:
+  // a lane's four A-operand values of one row are a single 16-byte LDS read.
   //
   // Each block is also formed transposed, T_{b,w}^T = X^T (-T_bb^T), whose C
   // layout gives a lane four consecutive columns 16w + 4gq + 0..3 of row
@@ -565,6 +589,7 @@ __global__ void __launch_bounds__(NTHREADS, 2)
       *reinterpret_cast<uint2*>(gTBH + frag_tt(i, 16 * w + 4 * gq)) = make_uint2(hb[0], hb[1]);
       *reinterpret_cast<uint2*>(gTBL + frag_tt(i, 16 * w + 4 * gq)) = make_uint2(lb[0], lb[1]);
     };
+    if (w == 3) wait_tag(6);
     f32x4 Tc[4];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) Tc[0][ii] = sA[(16 * w + 4 * gq + ii) * AP + 16 * w + tl];
@@ -577,10 +602,8 @@ __global__ void __launch_bounds__(NTHREADS, 2)
       Tc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (w + d < 4) {
         const int b = w + d;
-        for (int spin = 0; spin < (1 << 22); ++spin) {
-          if (__hip_atomic_load(&sFlag[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == item) break;
-          __builtin_amdgcn_s_sleep(1);
-        }
+        wait_tag(b);
+        if (b == 3) wait_tag(6);
         const float* arow = sA + (16 * b + tl) * AP + 4 * gq;
         f32x4 X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
