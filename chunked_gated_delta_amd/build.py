@@ -17,11 +17,12 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
-# Per-source flags.  The inter-chunk kernel keeps its MFMA accumulators (the
-# state, U/D and O tiles) in arch VGPRs, where the VALU scales and converts them
-# without accumulator-register moves; its operand prefetch sets, which only feed
-# MFMAs, then go to the accumulator registers.
-SOURCE_FLAGS = {"kda_inter.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source flags.  The two recurrence kernels (forward inter-chunk, backward
+# state gradient) keep their MFMA accumulators in arch VGPRs, where the VALU
+# scales and converts them without accumulator-register moves; their operand
+# prefetch sets, which only feed MFMAs, then go to the accumulator registers.
+SOURCE_FLAGS = {"kda_inter.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "kda_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(extra_flags=(), out=LIB, sources=None) -> str:

@@ -419,9 +419,11 @@ __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
 // is one 16-byte LDS read.  The next chunk's record operands and dO rows are
 // loaded one chunk ahead.
 // ---------------------------------------------------------------------------
-constexpr int SPB = KD + 8;  // channel pitch of the [v][k] bf16 state copies
-constexpr int TPB = CH + 8;  // token pitch of the [v][i] bf16 tiles
-constexpr int DHU_BYTES = 2 * VH * SPB * 2 + 3 * VH * TPB * 2;
+constexpr int TPB = CH + 8;  // token pitch of the [v][i] bf16 dO tile
+// dS' hi/lo: 16 split-plane fragments each (column tile nn, k-block kb);
+// dD hi/lo: 8 each (nn, token block ks); then the dO tile
+constexpr int DHU_SH = 0, DHU_SL = 16 * FRAG, DHU_DH = 32 * FRAG, DHU_DL = 40 * FRAG, DHU_O = 48 * FRAG;
+constexpr int DHU_BYTES = DHU_O + VH * TPB * 2;
 
 struct DhuOps {
   bf16x8 kth[4], ktl[4];          // Kt rows 16w + tl, channels 32kb + 8gq ..
@@ -504,11 +506,11 @@ __device__ __forceinline__ void split_hl4(const f32x4& x, bf16x4& h, bf16x4& l) 
 
 __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DHU_BYTES];
-  __bf16* sSh = reinterpret_cast<__bf16*>(smem);   // [64 v][SPB]  dS' hi
-  __bf16* sSl = sSh + VH * SPB;                     // [64 v][SPB]  dS' lo
-  __bf16* sO = sSl + VH * SPB;                      // [64 v][TPB]  dO (unscaled, exact)
-  __bf16* sDh = sO + VH * TPB;                      // [64 v][TPB]  dD hi
-  __bf16* sDl = sDh + VH * TPB;                     // [64 v][TPB]  dD lo
+  char* sSh = smem + DHU_SH;                        // dS' hi, fragments (nn, kb)
+  char* sSl = smem + DHU_SL;                        // dS' lo
+  char* sDh = smem + DHU_DH;                        // dD hi, fragments (nn, ks)
+  char* sDl = smem + DHU_DL;                        // dD lo
+  __bf16* sO = reinterpret_cast<__bf16*>(smem + DHU_O);  // [64 v][TPB]  dO (unscaled, exact)
 
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
@@ -583,68 +585,108 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
         for (int ii = 0; ii < 4; ++ii) dsg[(k0 + ii) * VD + vs + col] = dS[mt][nn][ii];
         bf16x4 hv, lv;
         split_hl4(dS[mt][nn], hv, lv);
-        *reinterpret_cast<bf16x4*>(sSh + col * SPB + k0) = hv;
-        *reinterpret_cast<bf16x4*>(sSl + col * SPB + k0) = lv;
+        frag_write4(sSh, 4 * nn + w, 4 * mt + gq, tl, hv);
+        frag_write4(sSl, 4 * nn + w, 4 * mt + gq, tl, lv);
       }
     store_dot(sO, cur.dob, tid);
     __syncthreads();
 
-    // dD rows 16w.. = Kt dS' + (scale A_qk^T) dO
+    // dD rows 16w.. = Kt dS' + (scale A_qk^T) dO.  The B operands come in six
+    // groups of four (one per column tile): four k-blocks of dS' hi/lo, then
+    // two token blocks of dO.  Each group feeds four or eight independent MFMA
+    // chains and is read one group ahead behind a scheduling barrier, so one
+    // LDS latency is exposed per group instead of one per read.
     float* ddg = a.ddtile + it * CH * VD;
+    {
+      f32x4 acc[4];
 #pragma unroll
-    for (int nn = 0; nn < 4; ++nn) {
-      const int col = 16 * nn + tl;
-      f32x4 acc = zero4();
+      for (int nn = 0; nn < 4; ++nn) acc[nn] = zero4();
+      uint4 bq[2][4][2];
+      auto read_group = [&](int g, uint4(&dst)[4][2]) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(sSh + col * SPB + 32 * kb + 8 * gq);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(sSl + col * SPB + 32 * kb + 8 * gq);
-        acc = mfma_bf16(cur.kth[kb], bh, acc);
-        acc = mfma_bf16(cur.kth[kb], bl, acc);
-        acc = mfma_bf16(cur.ktl[kb], bh, acc);
+        for (int nn = 0; nn < 4; ++nn) {
+          if (g < 4) {
+            dst[nn][0] = frag_read(sSh, 4 * nn + g, lane);
+            dst[nn][1] = frag_read(sSl, 4 * nn + g, lane);
+          } else {
+            dst[nn][0] = *reinterpret_cast<const uint4*>(sO + (16 * nn + tl) * TPB + 32 * (g - 4) + 8 * gq);
+          }
+        }
+      };
+      read_group(0, bq[0]);
+#pragma unroll
+      for (int g = 0; g < 6; ++g) {
+        if (g + 1 < 6) read_group(g + 1, bq[(g + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nn = 0; nn < 4; ++nn) {
+          if (g < 4) {
+            const bf16x8 bh = __builtin_bit_cast(bf16x8, bq[g & 1][nn][0]);
+            const bf16x8 bl = __builtin_bit_cast(bf16x8, bq[g & 1][nn][1]);
+            acc[nn] = mfma_bf16(cur.kth[g], bh, acc[nn]);
+            acc[nn] = mfma_bf16(cur.kth[g], bl, acc[nn]);
+            acc[nn] = mfma_bf16(cur.ktl[g], bh, acc[nn]);
+          } else {
+            const bf16x8 ob = __builtin_bit_cast(bf16x8, bq[g & 1][nn][0]);
+            acc[nn] = mfma_bf16(cur.aqh[g - 4], ob, acc[nn]);
+            acc[nn] = mfma_bf16(cur.aql[g - 4], ob, acc[nn]);
+          }
+        }
       }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 ob = *reinterpret_cast<const bf16x8*>(sO + col * TPB + 32 * ks + 8 * gq);
-        acc = mfma_bf16(cur.aqh[ks], ob, acc);
-        acc = mfma_bf16(cur.aql[ks], ob, acc);
-      }
+      for (int nn = 0; nn < 4; ++nn) {
+        const int col = 16 * nn + tl;
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) ddg[(16 * w + 4 * gq + ii) * VD + vs + col] = acc[ii];
-      bf16x4 hv, lv;
-      split_hl4(acc, hv, lv);
-      *reinterpret_cast<bf16x4*>(sDh + col * TPB + 16 * w + 4 * gq) = hv;
-      *reinterpret_cast<bf16x4*>(sDl + col * TPB + 16 * w + 4 * gq) = lv;
+        for (int ii = 0; ii < 4; ++ii) ddg[(16 * w + 4 * gq + ii) * VD + vs + col] = acc[nn][ii];
+        bf16x4 hv, lv;
+        split_hl4(acc[nn], hv, lv);
+        frag_write4(sDh, 2 * nn + (w >> 1), 4 * (w & 1) + gq, tl, hv);
+        frag_write4(sDl, 2 * nn + (w >> 1), 4 * (w & 1) + gq, tl, lv);
+      }
     }
     __syncthreads();
 
-    // dS = Diag(exp(G_L)) dS' + (scale QG^T) dO + (-W^T) dD
-#pragma unroll
-    for (int nn = 0; nn < 4; ++nn) {
-      const int col = 16 * nn + tl;
-      bf16x8 ob[2], dh[2], dl[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        ob[ks] = *reinterpret_cast<const bf16x8*>(sO + col * TPB + 32 * ks + 8 * gq);
-        dh[ks] = *reinterpret_cast<const bf16x8*>(sDh + col * TPB + 32 * ks + 8 * gq);
-        dl[ks] = *reinterpret_cast<const bf16x8*>(sDl + col * TPB + 32 * ks + 8 * gq);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        f32x4 st = dS[mt][nn];
-        st[0] *= cur.gl[mt].x;
-        st[1] *= cur.gl[mt].y;
-        st[2] *= cur.gl[mt].z;
-        st[3] *= cur.gl[mt].w;
+    // dS = Diag(exp(G_L)) dS' + (scale QG^T) dO + (-W^T) dD; a column tile's six
+    // B operands are read one tile ahead
+    {
+      uint4 dq[2][6];
+      auto read_tile = [&](int nn, uint4(&dst)[6]) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          st = mfma_bf16(cur.qgh[mt][ks], ob[ks], st);
-          st = mfma_bf16(cur.qgl[mt][ks], ob[ks], st);
-          st = mfma_bf16(cur.wth[mt][ks], dh[ks], st);
-          st = mfma_bf16(cur.wth[mt][ks], dl[ks], st);
-          st = mfma_bf16(cur.wtl[mt][ks], dh[ks], st);
+          dst[ks] = *reinterpret_cast<const uint4*>(sO + (16 * nn + tl) * TPB + 32 * ks + 8 * gq);
+          dst[2 + ks] = frag_read(sDh, 2 * nn + ks, lane);
+          dst[4 + ks] = frag_read(sDl, 2 * nn + ks, lane);
         }
-        dS[mt][nn] = st;
+      };
+      read_tile(0, dq[0]);
+#pragma unroll
+      for (int nn = 0; nn < 4; ++nn) {
+        if (nn + 1 < 4) read_tile(nn + 1, dq[(nn + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 ob[2], dh[2], dl[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          ob[ks] = __builtin_bit_cast(bf16x8, dq[nn & 1][ks]);
+          dh[ks] = __builtin_bit_cast(bf16x8, dq[nn & 1][2 + ks]);
+          dl[ks] = __builtin_bit_cast(bf16x8, dq[nn & 1][4 + ks]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          f32x4 st = dS[mt][nn];
+          st[0] *= cur.gl[mt].x;
+          st[1] *= cur.gl[mt].y;
+          st[2] *= cur.gl[mt].z;
+          st[3] *= cur.gl[mt].w;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            st = mfma_bf16(cur.qgh[mt][ks], ob[ks], st);
+            st = mfma_bf16(cur.qgl[mt][ks], ob[ks], st);
+            st = mfma_bf16(cur.wth[mt][ks], dh[ks], st);
+            st = mfma_bf16(cur.wth[mt][ks], dl[ks], st);
+            st = mfma_bf16(cur.wtl[mt][ks], dh[ks], st);
+          }
+          dS[mt][nn] = st;
+        }
       }
     }
     __syncthreads();

@@ -126,6 +126,30 @@ __device__ __forceinline__ void lds_f32x8(const float* src, float (&d)[8]) {
   d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
 }
 
+// Split-plane B-operand fragments in LDS.  Fragment f holds one 16-column
+// tile x 32-k block of a 16-bit operand: the 16 bytes (8 k) of MFMA lane
+// l = 16gq + tl, split into two planes, bytes 0-7 at l*8 and bytes 8-15 at
+// 512 + l*8.  A lane's operand is two 8-byte reads, and both the reads (64
+// contiguous lanes) and the writes from the accumulator layout (4 consecutive
+// k of one column) are free of LDS bank conflicts on gfx950, where row-pitched
+// layouts doubled the read and the write time.
+constexpr int FRAG = 1024;  // bytes per fragment
+
+__device__ __forceinline__ uint4 frag_read(const char* base, int frag, int lane) {
+  const char* p = base + frag * FRAG + lane * 8;
+  const uint2 lo = *reinterpret_cast<const uint2*>(p);
+  const uint2 hi = *reinterpret_cast<const uint2*>(p + FRAG / 2);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// Store 4 consecutive k (k0 = 4q within the fragment's 32-k block, q = 0..7)
+// of column tl into fragment `frag`: MFMA lane 16 (q / 2) + tl, plane q % 2.
+template <typename V4>
+__device__ __forceinline__ void frag_write4(char* base, int frag, int q, int tl, V4 v) {
+  static_assert(sizeof(V4) == 8, "4 x 16-bit");
+  *reinterpret_cast<V4*>(base + frag * FRAG + (q & 1) * (FRAG / 2) + (16 * (q >> 1) + tl) * 8) = v;
+}
+
 // Optional per-phase cycle counters, compiled out unless KDA_PHASE_TIMERS is
 // defined: thread 0 of each workgroup accumulates cycle-counter deltas between
 // phase marks and stores them to timers[blockIdx.x * 16 + i].

@@ -24,14 +24,8 @@ constexpr int VT = VD / NV;      // 64 state columns per workgroup
 constexpr int TP = CH + 8;       // token pitch of [v][token] arrays (halves)
 
 constexpr int OFF_VT = 0;                          // bf16 [VT][TP]   V^T
-// The state copy and D hi/lo are kept as B-operand fragments: fragment f holds
-// one 16-column tile x 32-k block, the 16 bytes (8 k) of MFMA lane l = 16gq + tl
-// split into two planes, bytes 0-7 at l*8 and bytes 8-15 at 512 + l*8.  A
-// lane's operand is then two 8-byte reads, and both the reads (64 contiguous
-// lanes) and the writes from the accumulator layout (4 consecutive k of one
-// column) are free of LDS bank conflicts on gfx950, where the row-pitched
-// layout doubled the read and write time.
-constexpr int FRAG = 1024;                         // bytes per fragment
+// The state copy and D hi/lo are kept as split-plane B-operand fragments
+// (frag_read / frag_write4).
 constexpr int OFF_ST = OFF_VT + VT * TP * 2;       // f16  16 fragments (nn, kb)   state copy
 constexpr int OFF_DTH = OFF_ST + 16 * FRAG;        // f16   8 fragments (nn, ks)   D hi
 constexpr int OFF_DTL = OFF_DTH + 8 * FRAG;        // f16   8 fragments (nn, ks)   D lo
@@ -125,20 +119,6 @@ __device__ __forceinline__ void load_v(uint4 (&vv)[2], const uint16_t* v, int64_
 // tokens stays one 16-byte read, while the packed 2-token writes below spread
 // over all banks instead of hitting 8 column groups in the same ones.
 __device__ __forceinline__ int vt_swz(int c) { return 8 * ((c >> 3) & 7); }
-
-// B operand of MFMA lane `lane` from fragment `frag` (two 8-byte plane reads)
-__device__ __forceinline__ uint4 frag_read(const char* base, int frag, int lane) {
-  const char* p = base + frag * FRAG + lane * 8;
-  const uint2 lo = *reinterpret_cast<const uint2*>(p);
-  const uint2 hi = *reinterpret_cast<const uint2*>(p + FRAG / 2);
-  return make_uint4(lo.x, lo.y, hi.x, hi.y);
-}
-
-// Store 4 consecutive k (k0 = 4 * q within the fragment's 32-k block, q = 0..7)
-// of column tl into fragment `frag`: MFMA lane 16 (q / 2) + tl, plane q % 2.
-__device__ __forceinline__ void frag_write4(char* base, int frag, int q, int tl, f16x4 v) {
-  *reinterpret_cast<f16x4*>(base + frag * FRAG + (q & 1) * (FRAG / 2) + (16 * (q >> 1) + tl) * 8) = v;
-}
 
 // Write the V tile transposed (column-major, 2 tokens per dword).  Lanes of
 // neighbouring tokens t, t^1 (lanes 4 apart) trade half their columns, so
