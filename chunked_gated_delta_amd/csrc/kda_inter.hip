@@ -19,19 +19,25 @@ namespace kda {
 namespace {
 
 constexpr int NTHREADS = 256;
-constexpr int NV = 2;            // V slices per (sequence, head)
-constexpr int VT = VD / NV;      // 64 state columns per workgroup
 constexpr int TP = CH + 8;       // token pitch of [v][token] arrays (halves)
 
-constexpr int OFF_VT = 0;                          // bf16 [VT][TP]   V^T
-// The state copy and D hi/lo are kept as split-plane B-operand fragments
-// (frag_read / frag_write4).
-constexpr int OFF_ST = OFF_VT + VT * TP * 2;       // f16  16 fragments (nn, kb)   state copy
-constexpr int OFF_DTH = OFF_ST + 16 * FRAG;        // f16   8 fragments (nn, ks)   D hi
-constexpr int OFF_DTL = OFF_DTH + 8 * FRAG;        // f16   8 fragments (nn, ks)   D lo
-constexpr int OP = VT + 8;                         // token-row pitch of the output tile
-constexpr int OFF_O = OFF_DTL + 8 * FRAG;          // bf16 [CH][OP]   output staging
-constexpr int LDS_BYTES = OFF_O + CH * OP * 2;
+// A workgroup owns NN 16-column tiles of the state (VT = 16 NN columns; NN = 4
+// normally, 2 or 1 when there are too few (sequence, head) chains to fill the
+// GPU).  LDS carve-up: the V tile, then the state copy and D hi/lo as
+// split-plane B-operand fragments (frag_read / frag_write4), then the output
+// staging tile.
+template <int NN>
+struct Cfg {
+  static constexpr int VT = 16 * NN;                     // state columns per workgroup
+  static constexpr int NV = VD / VT;                     // V slices per (sequence, head)
+  static constexpr int OFF_VT = 0;                       // bf16 [VT][TP]   V^T
+  static constexpr int OFF_ST = OFF_VT + VT * TP * 2;    // f16  4 NN fragments (nn, kb)   state copy
+  static constexpr int OFF_DTH = OFF_ST + 4 * NN * FRAG; // f16  2 NN fragments (nn, ks)   D hi
+  static constexpr int OFF_DTL = OFF_DTH + 2 * NN * FRAG;// f16  2 NN fragments (nn, ks)   D lo
+  static constexpr int OP = VT + 8;                      // token-row pitch of the output tile
+  static constexpr int OFF_O = OFF_DTL + 2 * NN * FRAG;  // bf16 [CH][OP]   output staging
+  static constexpr int LDS_BYTES = OFF_O + CH * OP * 2;
+};
 
 // the record operands one wave needs per chunk
 struct Ops {
@@ -101,17 +107,31 @@ __device__ __forceinline__ void load_ops_all(Ops& o, const char* rec, int w, int
   load_ops<4, HAS_V, WRITE_OUT>(o, rec, w, lane, gq, ksmax);
 }
 
-// V tile of a chunk: thread -> (token tid/4, columns 16*(tid%4) .. +15).  Rows
-// past the chunk end are loaded from the clamped last row and zeroed only when
-// written to LDS, so issuing the prefetch never waits for its data.
-__device__ __forceinline__ void load_v(uint4 (&vv)[2], const uint16_t* v, int64_t c0, int L, int H,
-                                       int h, int vs, int tid) {
+// V tile of a chunk: thread -> (token tid/4, columns 4NN*(tid%4) .. +4NN-1),
+// held as 2NN packed dwords.  Rows past the chunk end are loaded from the
+// clamped last row and zeroed only when written to LDS, so issuing the
+// prefetch never waits for its data.
+template <int NN>
+struct VRow {
+  uint32_t d[2 * NN];
+};
+template <int NN>
+__device__ __forceinline__ void load_v(VRow<NN>& vv, const uint16_t* v, int64_t c0, int L, int H, int h,
+                                       int vs, int tid) {
   const int t = tid >> 2;
   const int cg = tid & 3;
   const int tc = t < L ? t : L - 1;  // L >= 1: the clamped row is inside the sequence
-  const uint4* src = reinterpret_cast<const uint4*>(v + ((c0 + tc) * H + h) * VD + vs + 16 * cg);
-  vv[0] = src[0];
-  vv[1] = src[1];
+  const uint16_t* row = v + ((c0 + tc) * H + h) * VD + vs + 4 * NN * cg;
+  if constexpr (NN == 1) {
+    const uint2 x = *reinterpret_cast<const uint2*>(row);
+    vv.d[0] = x.x; vv.d[1] = x.y;
+  } else {
+#pragma unroll
+    for (int u = 0; u < NN / 2; ++u) {
+      const uint4 x = reinterpret_cast<const uint4*>(row)[u];
+      vv.d[4 * u] = x.x; vv.d[4 * u + 1] = x.y; vv.d[4 * u + 2] = x.z; vv.d[4 * u + 3] = x.w;
+    }
+  }
 }
 
 // Token slot of V^T: token t of column c sits at t ^ vt_swz(c).  The XOR
@@ -122,25 +142,25 @@ __device__ __forceinline__ int vt_swz(int c) { return 8 * ((c >> 3) & 7); }
 
 // Write the V tile transposed (column-major, 2 tokens per dword).  Lanes of
 // neighbouring tokens t, t^1 (lanes 4 apart) trade half their columns, so
-// each lane writes 8 packed dwords: the even token's lane columns
-// 16cg + 0..7, the odd token's lane columns 16cg + 8..15.
-__device__ __forceinline__ void store_vt(__bf16* sVt, const uint4 (&vv)[2], int tid, int L) {
+// each lane writes 2NN packed dwords: the even token's lane columns
+// 4NN cg + 0..2NN-1, the odd token's lane columns 4NN cg + 2NN..4NN-1.
+template <int NN>
+__device__ __forceinline__ void store_vt(__bf16* sVt, const VRow<NN>& vv, int tid, int L) {
   const int t = tid >> 2;
   const int cg = tid & 3;
   const bool keep = t < L;
   const bool odd = t & 1;
-  const uint32_t wds[8] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w, vv[1].x, vv[1].y, vv[1].z, vv[1].w};
-  uint32_t mine[4], recv[4];
+  uint32_t mine[NN], recv[NN];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    mine[j] = keep ? (odd ? wds[4 + j] : wds[j]) : 0u;
-    const uint32_t send = keep ? (odd ? wds[j] : wds[4 + j]) : 0u;
+  for (int j = 0; j < NN; ++j) {
+    mine[j] = keep ? (odd ? vv.d[NN + j] : vv.d[j]) : 0u;
+    const uint32_t send = keep ? (odd ? vv.d[j] : vv.d[NN + j]) : 0u;
     recv[j] = (uint32_t)__shfl_xor((int)send, 4);
   }
   const int tp = t & ~1;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = 16 * cg + (odd ? 8 : 0) + 2 * j;
+  for (int j = 0; j < NN; ++j) {
+    const int c = 4 * NN * cg + (odd ? 2 * NN : 0) + 2 * j;
     const uint32_t lo = odd ? recv[j] : mine[j];  // token tp
     const uint32_t hi = odd ? mine[j] : recv[j];  // token tp + 1
     const uint32_t d0 = (lo & 0xffffu) | (hi << 16);           // column c
@@ -154,16 +174,18 @@ __device__ __forceinline__ void store_vt(__bf16* sVt, const uint4 (&vv)[2], int 
 // chunk map, used for the per-shard affine map); WRITE_OUT = false computes
 // only the final state; CKPT also stores every chunk's entering state and its
 // D tile for the backward pass.
-template <bool HAS_V, bool WRITE_OUT, bool CKPT = false>
+template <bool HAS_V, bool WRITE_OUT, bool CKPT = false, int NN = 4>
 __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
-  __bf16* sVt = reinterpret_cast<__bf16*>(smem + OFF_VT);
-  char* sSt = smem + OFF_ST;
-  char* sDth = smem + OFF_DTH;
-  char* sDtl = smem + OFF_DTL;
+  using C = Cfg<NN>;
+  constexpr int NV = C::NV, VT = C::VT, OP = C::OP;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  __bf16* sVt = reinterpret_cast<__bf16*>(smem + C::OFF_VT);
+  char* sSt = smem + C::OFF_ST;
+  char* sDth = smem + C::OFF_DTH;
+  char* sDtl = smem + C::OFF_DTL;
 
   // XCD-aware mapping: ids are dispatched round-robin over the 8 XCDs, so the
-  // two V-halves of one (sequence, head) get ids with equal residue mod 8 and
+  // V slices of one (sequence, head) get ids with equal residue mod 8 and
   // read the chunk records through the same L2.
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
@@ -188,13 +210,13 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
   const int ksmax = (w >= 2) ? 2 : 1;  // token rows 16w.. only see tokens <= 16w + 15
 
   // state rows (channels) 32w + 16mt + 4gq + ii, columns vs + 16n + tl
-  f32x4 S[2][4];
+  f32x4 S[2][NN];
   {
     const float* src = a.init ? a.init + ((int64_t)seq * H + h) * KD * VD : nullptr;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nn = 0; nn < 4; ++nn)
+      for (int nn = 0; nn < NN; ++nn)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int c = 32 * w + 16 * mt + 4 * gq + ii;
@@ -213,8 +235,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     }
   };
 #pragma unroll
-  for (int nn = 0; nn < 4; ++nn) store_st_tile(nn);
-  __bf16* sO = reinterpret_cast<__bf16*>(smem + OFF_O);
+  for (int nn = 0; nn < NN; ++nn) store_st_tile(nn);
+  __bf16* sO = reinterpret_cast<__bf16*>(smem + C::OFF_O);
   // Record operands are prefetched one chunk ahead into two register sets
   // that alternate through the 2x unrolled loop below; the loads of chunk c+1
   // are spread over chunk c's step.
@@ -226,14 +248,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
   auto chunk_len = [&](int64_t c) { return (int)((eos - c) < CH ? (eos - c) : CH); };
   const bool odd = ((eos - bos + CH - 1) / CH) & 1;
   if (bos < eos) {
-    uint4 v0[2];
+    VRow<NN> v0;
     if constexpr (HAS_V) load_v(v0, a.v, bos, chunk_len(bos), H, h, vs, tid);
     const char* r0 = a.rec + ((size_t)gfirst * H + h) * REC_BYTES;
     if (odd)
       load_ops_all<HAS_V, WRITE_OUT>(opsA, r0, w, lane, gq, ksmax);
     else
       load_ops_all<HAS_V, WRITE_OUT>(opsB, r0, w, lane, gq, ksmax);
-    if constexpr (HAS_V) store_vt(sVt, v0, tid, chunk_len(bos));
+    if constexpr (HAS_V) store_vt<NN>(sVt, v0, tid, chunk_len(bos));
   }
   __syncthreads();
 
@@ -256,13 +278,13 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     stmt;                                 \
     __builtin_amdgcn_sched_barrier(0);    \
   } while (0)
-    uint4 vn[2];
+    VRow<NN> vn;
     if constexpr (CKPT) {
       float* dst = a.states + ((size_t)gch * H + h) * KD * VD;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nn = 0; nn < 4; ++nn)
+        for (int nn = 0; nn < NN; ++nn)
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii)
             dst[(32 * w + 16 * mt + 4 * gq + ii) * VD + vs + 16 * nn + tl] = S[mt][nn][ii];
@@ -278,16 +300,16 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     // chains and is read one group ahead, pinned there by a scheduling
     // barrier (left alone, the scheduler sinks every read to its first use
     // and waits for it there).  The two products share each state-copy read.
-    f32x4 O[4], u[4];
+    f32x4 O[NN], u[NN];
 #pragma unroll
-    for (int nn = 0; nn < 4; ++nn) {
+    for (int nn = 0; nn < NN; ++nn) {
       u[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
       O[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    uint4 bq[2][4];
-    auto read_group = [&](int g, uint4(&dst)[4]) {
+    uint4 bq[2][NN];
+    auto read_group = [&](int g, uint4(&dst)[NN]) {
 #pragma unroll
-      for (int nn = 0; nn < 4; ++nn) {
+      for (int nn = 0; nn < NN; ++nn) {
         const int col = 16 * nn + tl;
         dst[nn] = g < 2 ? *reinterpret_cast<const uint4*>(sVt + col * TP + ((32 * g + 8 * gq) ^ vt_swz(col)))
                         : frag_read(sSt, 4 * nn + (g - 2), lane);
@@ -306,7 +328,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
         const bf16x8 th = g < ksmax ? cur.tbh[g] : bf16x8{};
         const bf16x8 tlo = g < ksmax ? cur.tbl[g] : bf16x8{};
 #pragma unroll
-        for (int nn = 0; nn < 4; ++nn) {
+        for (int nn = 0; nn < NN; ++nn) {
           const bf16x8 vb = __builtin_bit_cast(bf16x8, bq[g & 1][nn]);
           u[nn] = mfma_bf16(th, vb, u[nn]);
           u[nn] = mfma_bf16(tlo, vb, u[nn]);
@@ -314,7 +336,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
       } else {
         const int kb = g - 2;
 #pragma unroll
-        for (int nn = 0; nn < 4; ++nn) {
+        for (int nn = 0; nn < NN; ++nn) {
           const f16x8 sb = __builtin_bit_cast(f16x8, bq[g & 1][nn]);
           u[nn] = mfma_f16(cur.nw[kb], sb, u[nn]);
           // O^T = S^T (QG)^T: lane holds token 16w + tl, columns 16nn + 4gq + 0..3
@@ -325,7 +347,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
       if (g == 3) KDA_ISSUE((load_ops<2, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
     }
 #pragma unroll
-    for (int nn = 0; nn < 4; ++nn) {
+    for (int nn = 0; nn < NN; ++nn) {
       const int col = 16 * nn + tl;
       if constexpr (CKPT) {
         float* dst = a.dtile + ((size_t)gch * H + h) * CH * VD;
@@ -366,14 +388,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     };
     read_d(0, dq[0]);
 #pragma unroll
-    for (int nn = 0; nn < 4; ++nn) {
-      if (nn + 1 < 4) read_d(nn + 1, dq[(nn + 1) & 1]);
+    for (int nn = 0; nn < NN; ++nn) {
+      if (nn + 1 < NN) read_d(nn + 1, dq[(nn + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
       if (nn > 0) store_st_tile(nn - 1);
       // past the end of the sequence this rewrites the current tile, which
       // nothing reads
       if constexpr (HAS_V)
-        if (nn == 2) store_vt(sVt, vn, tid, in1 ? chunk_len(c1) : L);
+        if (nn == (NN > 2 ? 2 : NN - 1)) store_vt<NN>(sVt, vn, tid, in1 ? chunk_len(c1) : L);
       f16x8 dh[2], dl[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -406,14 +428,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
         S[mt][nn] = s;
       }
       if (nn == 0) KDA_ISSUE((load_ops<3, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
-      if (nn == 1) KDA_ISSUE((load_ops<4, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
+      if (nn == (NN > 1 ? 1 : 0)) KDA_ISSUE((load_ops<4, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
     }
 #undef KDA_ISSUE
-    // this wave's 16 output rows: lane -> row 16w + lane/4, 16 columns per lane
+    // this wave's 16 output rows: NN lanes per row, 16 columns per lane
     if constexpr (WRITE_OUT) {
-      const int orow = 16 * w + (lane >> 2);
-      const int ocol = 16 * (lane & 3);
-      if (orow < L) {
+      const int orow = 16 * w + lane / NN;
+      const int ocol = 16 * (lane % NN);
+      if (lane < 16 * NN && orow < L) {
         const uint4* srcp = reinterpret_cast<const uint4*>(sO + orow * OP + ocol);
         uint4* dstp = reinterpret_cast<uint4*>(a.out + ((c0 + orow) * H + h) * VD + vs + ocol);
         dstp[0] = srcp[0];
@@ -421,7 +443,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
       }
     }
     KDA_TIMER_MARK(4);
-    store_st_tile(3);
+    store_st_tile(NN - 1);
     KDA_TIMER_MARK(5);
     __syncthreads();
     KDA_TIMER_MARK(6);
@@ -444,7 +466,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nn = 0; nn < 4; ++nn)
+      for (int nn = 0; nn < NN; ++nn)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int c = 32 * w + 16 * mt + 4 * gq + ii;
@@ -456,20 +478,43 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
 
 }  // namespace
 
+// Column tiles per workgroup of the output-producing forward.  Each
+// (sequence, head) chain is a sequential walk over its chunks, so with few
+// chains the 64-column slices leave most CUs idle; narrower slices give each
+// chain more workgroups (every one re-reads the chunk's record, through the
+// L2 of its XCD).  Wide slices stay in use once the chains alone fill half
+// the CUs.
+int inter_tiles(int64_t chains, int cus) {
+  if (chains * 2 >= cus / 2) return 4;
+  if (chains * 4 >= cus / 2) return 2;
+  return 1;
+}
+
 hipError_t launch_inter(const InterArgs& args, hipStream_t st) {
   const int64_t items = (int64_t)args.map.N * args.H;
-  const int64_t grid = (items + 7) / 8 * 8 * NV;
   InterArgs a = args;
   void* kargs[] = {(void*)&a};
+  int nn = 4;
+  if (a.v && a.out && !a.states) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    nn = inter_tiles(items, cus);
+  }
   const void* fn;
   if (a.states)
     fn = reinterpret_cast<const void*>(&kda_inter_kernel<true, false, true>);
   else if (a.v)
-    fn = a.out ? reinterpret_cast<const void*>(&kda_inter_kernel<true, true>)
-               : reinterpret_cast<const void*>(&kda_inter_kernel<true, false>);
+    fn = !a.out    ? reinterpret_cast<const void*>(&kda_inter_kernel<true, false>)
+         : nn == 1 ? reinterpret_cast<const void*>(&kda_inter_kernel<true, true, false, 1>)
+         : nn == 2 ? reinterpret_cast<const void*>(&kda_inter_kernel<true, true, false, 2>)
+                   : reinterpret_cast<const void*>(&kda_inter_kernel<true, true>);
   else
     fn = a.out ? reinterpret_cast<const void*>(&kda_inter_kernel<false, true>)
                : reinterpret_cast<const void*>(&kda_inter_kernel<false, false>);
+  // ids 8m + x (x = XCD) cover the VD / (16 nn) slices of items 8(m / slices) + x
+  const int64_t grid = (items + 7) / 8 * 8 * (VD / (16 * nn));
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(NTHREADS), kargs, 0, st);
 }
 

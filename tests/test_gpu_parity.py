@@ -253,3 +253,24 @@ def test_zero_tokens_copies_the_state():
                 x.A_log.to(dev), x.dt_bias.to(dev), x.lower_bound, x.initial_state.to(dev), fin)
     torch.cuda.synchronize()
     assert torch.equal(fin.cpu(), x.initial_state)
+
+
+@pytest.mark.parametrize("H", [40, 64])
+def test_slice_width_changes_no_bit(H):
+    """With few (sequence, head) chains the inter-chunk recurrence runs in narrower
+    V slices per workgroup (on 256 CUs: H=2 gives 16 columns, H=40 gives 32, H=64
+    the full 64).  Each output column is computed the same way at every width, so
+    the two-head subset, run at H=2, reproduces the wide run bit for bit."""
+    x = W.random_inputs(f"slices_H{H}", 300 + H, 1, 129, H)
+    o, f = run_gpu(x)
+    ro, rf = oracle(x)
+    check(o, f, ro, rf, x.name)
+    p = [0, H - 1]
+    y = W.random_inputs(f"slices_H{H}", 300 + H, 1, 129, H)
+    for name in ("q", "k", "v", "raw_gate", "raw_beta"):
+        setattr(y, name, getattr(x, name)[:, :, p].contiguous())
+    y.A_log = x.A_log[p].contiguous()
+    y.dt_bias = x.dt_bias[p].contiguous()
+    y.initial_state = x.initial_state[:, p].contiguous()
+    o2, f2 = run_gpu(y)
+    assert np.array_equal(o2, o[:, p]) and np.array_equal(f2, f[:, p])
