@@ -78,9 +78,16 @@ def cpu_baseline(x, heads):
                x.lower_bound, x.initial_state, x.cu_seqlens, heads=heads, want_final=True)
     dt = time.perf_counter() - t0
     ht = x.B * x.T * len(heads)
+    # the same recurrence on one host thread, over the first head only
+    t1 = time.perf_counter()
+    oracle_fwd(x.q, x.k, x.v, x.raw_gate, x.raw_beta, x.scale, x.A_log, x.dt_bias,
+               x.lower_bound, x.initial_state, x.cu_seqlens, heads=heads[:1], want_final=True, threads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": ht / dt, "unit": "head-tokens/s", "cores": oracle_threads(), "kind": "oracle",
             "sample": f"fp64 token recurrence over heads 0..{len(heads) - 1} of {x.H}, all "
-                      f"{x.T} tokens ({ht} head-tokens, {dt:.1f} s)"}
+                      f"{x.T} tokens ({ht} head-tokens, {dt:.1f} s)",
+            "single_core_value": x.B * x.T / dt1,
+            "single_core_sample": f"head 0, all {x.T} tokens, one thread ({dt1:.2f} s)"}
 
 
 def copy_calibration(gib: float = 2.0):
