@@ -274,3 +274,15 @@ def test_slice_width_changes_no_bit(H):
     y.initial_state = x.initial_state[:, p].contiguous()
     o2, f2 = run_gpu(y)
     assert np.array_equal(o2, o[:, p]) and np.array_equal(f2, f[:, p])
+
+
+@pytest.mark.parametrize("H", [2, 10, 20])
+def test_varlen_at_every_slice_width(H):
+    """Packed sequences with ragged tails and an empty one, at the head counts that pick
+    16-, 32- and 64-column slices (4 sequences: 8, 40 and 80 (sequence, head) pairs)."""
+    lengths = [130, 0, 64, 77]
+    x = W.random_inputs(f"varlen_slices_H{H}", 400 + H, 1, sum(lengths), H, lengths=lengths)
+    o, f = run_gpu(x)
+    ro, rf = oracle(x)
+    check(o, f, ro, rf, x.name)
+    assert np.array_equal(f[1], x.initial_state[1].double().numpy())
