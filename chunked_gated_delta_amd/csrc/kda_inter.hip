@@ -9,9 +9,10 @@
 // sequence; its fp16 copy, the chunk's V tile and D live in LDS in
 // column-major form so that every B operand is one 16-byte LDS read.
 //
-// One workgroup (4 waves) per (sequence, head, V-half).  Wave w computes the
-// token rows 16w..16w+15 of U, D and O (its A operands are 16-byte global
-// loads from the record) and the state rows (channels) 32w..32w+31.
+// One workgroup (4 waves) per (sequence, head, V slice of 16 NN columns;
+// NN = 4 gives the two V halves).  Wave w computes the token rows
+// 16w..16w+15 of U, D and O (its A operands are 16-byte global loads from the
+// record) and the state rows (channels) 32w..32w+31 of the slice.
 
 #include "kda_common.h"
 
@@ -293,10 +294,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     KDA_ISSUE((load_ops<0, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
     KDA_TIMER_MARK(1);
 
-    // ---- U, D = U - W S, O = QG S (token rows 16w.., all 64 columns).  The
-    // B operands come in six groups of four 16-byte LDS reads (one per column
+    // ---- U, D = U - W S, O = QG S (token rows 16w.., all VT columns).  The
+    // B operands come in six groups of NN 16-byte LDS reads (one per column
     // tile): groups 0-1 the V tile (k-steps of U), groups 2-5 the state copy
-    // (k-blocks of W S and QG S).  Each group feeds eight independent MFMA
+    // (k-blocks of W S and QG S).  Each group feeds 2 NN independent MFMA
     // chains and is read one group ahead, pinned there by a scheduling
     // barrier (left alone, the scheduler sinks every read to its first use
     // and waits for it there).  The two products share each state-copy read.
@@ -377,7 +378,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
     // Every wave finished reading the state copy and the V tile before the
     // barrier above, so both are rewritten for the next chunk inside this
     // phase: the fp16 copy of column tile nn - 1 while tile nn's MFMAs run,
-    // and the V tile at tile 2.
+    // and the V tile at tile 2 (the last tile when NN < 3).
     uint4 dq[2][4];
     auto read_d = [&](int nn, uint4(&dst)[4]) {
 #pragma unroll

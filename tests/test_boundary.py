@@ -28,6 +28,24 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(kda.exported_symbols)
 
 
+def test_import_fails_loudly_without_the_library(tmp_path):
+    """The binding has no fallback: a package copy without libkda.so refuses to import."""
+    import shutil
+    import subprocess
+    import sys
+
+    pkg = tmp_path / "chunked_gated_delta_amd"
+    pkg.mkdir()
+    src = os.path.join(ROOT, "chunked_gated_delta_amd")
+    for name in os.listdir(src):
+        if name.endswith(".py"):
+            shutil.copy(os.path.join(src, name), pkg)
+    r = subprocess.run([sys.executable, "-c", "import chunked_gated_delta_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "libkda.so is missing" in r.stderr
+
+
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(kda.library_path)
     for name in declared_functions():
