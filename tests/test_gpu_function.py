@@ -1,0 +1,67 @@
+"""The differentiable wrapper ``kda_chunk`` (chunked_gated_delta_amd.function) through
+torch autograd: its forward equals kda_fwd bit for bit, and the gradients autograd
+delivers match the fp64 gradient oracle with the backward's tolerances."""
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_gated_delta_amd as kda
+import workloads as W
+from gpu_run import run_gpu
+from test_gpu_bwd import compare, cotangents, oracle
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("lengths", [None, [70, 0, 5, 64]])
+def test_autograd_through_the_wrapper(lengths):
+    from chunked_gated_delta_amd.function import kda_chunk
+
+    T = 130 if lengths is None else sum(lengths)
+    x = W.random_inputs("fn", 61, 1, T, 3, lengths=lengths)
+    leaf = lambda t: t.to(DEV).requires_grad_(True)  # noqa: E731
+    q, k, v, g, b = (leaf(t) for t in (x.q, x.k, x.v, x.raw_gate, x.raw_beta))
+    al, dt, init = leaf(x.A_log), leaf(x.dt_bias), leaf(x.initial_state)
+    cu = None if x.cu_seqlens is None else x.cu_seqlens.to(DEV)
+    print(f"kda_chunk {x.name} T={T} lengths={lengths}", flush=True)
+    out, fin = kda_chunk(q, k, v, g, b, al, dt, scale=x.scale, lower_bound=x.lower_bound,
+                         initial_state=init, cu_seqlens=cu)
+    o_ref, f_ref = run_gpu(x)
+    assert np.array_equal(out.detach().double().cpu().numpy().reshape(o_ref.shape), o_ref)
+    assert np.array_equal(fin.detach().double().cpu().numpy(), f_ref)
+
+    d_out, d_fin = cotangents(x, 62)
+    loss = (out.float() * d_out.to(DEV).float()).sum() + (fin * d_fin.to(DEV)).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    B, H, K, V, N = x.B, x.H, x.K, x.V, x.N
+    f = lambda t, *s: t.grad.double().cpu().numpy().reshape(*s)  # noqa: E731
+    got = {"dq": f(q, B * T, H, K), "dk": f(k, B * T, H, K), "dv": f(v, B * T, H, V),
+           "d_raw_gate": f(g, B * T, H, K), "d_raw_beta": f(b, B * T, H), "dA_log": f(al, H),
+           "d_dt_bias": f(dt, H, K), "d_initial_state": f(init, N, H, K, V)}
+    compare(got, oracle(x, d_out, d_fin))
+
+
+def test_q_and_k_as_one_tensor_sum_their_gradients():
+    """With q and k the same leaf, autograd adds dq and dk."""
+    from chunked_gated_delta_amd.function import kda_chunk
+
+    x = W.random_inputs("fn_qk", 63, 1, 100, 2)
+    x.k = x.q
+    qk = x.q.to(DEV).requires_grad_(True)
+    v, g, b = x.v.to(DEV), x.raw_gate.to(DEV), x.raw_beta.to(DEV)
+    al, dt, init = x.A_log.to(DEV), x.dt_bias.to(DEV), x.initial_state.to(DEV)
+    out, fin = kda_chunk(qk, qk, v, g, b, al, dt, scale=x.scale, lower_bound=x.lower_bound, initial_state=init)
+    d_out, d_fin = cotangents(x, 64)
+    ((out.float() * d_out.to(DEV).float()).sum() + (fin * d_fin.to(DEV)).sum()).backward()
+    ref = oracle(x, d_out, d_fin)
+    got = qk.grad.double().cpu().numpy().reshape(x.T, x.H, x.K)
+    compare({"dq": got}, {"dq": ref["dq"] + ref["dk"]}, names=("dq",))
