@@ -22,7 +22,7 @@ import torch  # noqa: F401
 
 __all__ = ["kda_fwd", "kda_fwd_ex", "kda_workspace_size", "kda_is_supported", "kda_shard_affine",
            "kda_shard_scan", "kda_decode", "kda_bwd", "kda_bwd_ex", "kda_bwd_workspace_size", "KdaError", "STATUS", "library_path", "exported_symbols",
-           "FLAG_GATE_GIVEN", "FLAG_BETA_GIVEN", "FLAG_NO_QK_NORM", "FLAG_STATE_VK"]
+           "FLAG_GATE_GIVEN", "FLAG_BETA_GIVEN", "FLAG_NO_QK_NORM", "FLAG_STATE_VK", "FLAG_REUSE_RECORDS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkda.so")
@@ -34,6 +34,8 @@ exported_symbols = ("kda_fwd", "kda_workspace_size", "kda_is_supported", "kda_st
                     "kda_bwd_ex", "kda_bwd_workspace_size")
 # kda_fwd_ex variant bits (KDA_FLAG_* in include/kda.h)
 FLAG_GATE_GIVEN, FLAG_BETA_GIVEN, FLAG_NO_QK_NORM, FLAG_STATE_VK = 1, 2, 4, 8
+# kda_fwd_ex only: reuse the chunk records the previous call left in the workspace
+FLAG_REUSE_RECORDS = 16
 
 
 class KdaError(RuntimeError):
@@ -154,7 +156,9 @@ def kda_fwd(q, k, v, raw_gate, raw_beta, scale, out, workspace, A_log, dt_bias, 
 def kda_fwd_ex(q, k, v, raw_gate, raw_beta, scale, out, workspace, A_log, dt_bias, lower_bound,
                initial_state=None, final_state=None, cu_seqlens=None, flags=0, stream=None):
     """kda_fwd with variant flags (an OR of the FLAG_* bits).  With FLAG_GATE_GIVEN,
-    A_log and dt_bias may be None; with FLAG_STATE_VK the states are [N,H,V,K]."""
+    A_log and dt_bias may be None; with FLAG_STATE_VK the states are [N,H,V,K];
+    FLAG_REUSE_RECORDS skips the intra-chunk pass and uses the records that the
+    previous call on this workspace (same inputs but v and the states) left there."""
     if out is None:
         raise ValueError("out is required")
     if not flags & FLAG_GATE_GIVEN and (A_log is None or dt_bias is None):

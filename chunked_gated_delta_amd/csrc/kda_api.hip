@@ -119,7 +119,8 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
                      int64_t T, int64_t H, int64_t K, int64_t V, int64_t N, hipStream_t st,
                      Prepared& pr, unsigned flags) {
   if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID;
-  if (flags & ~(unsigned)(FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM | FLAG_STATE_VK))
+  if (flags & ~(unsigned)(FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM | FLAG_STATE_VK |
+                          FLAG_REUSE_RECORDS))
     return KDA_ERR_INVALID;
   // token arrays may be NULL only when there are no tokens (empty tensors)
   if (B * T > 0 && (!q || !k || !raw_gate || !raw_beta)) return KDA_ERR_INVALID;
@@ -166,6 +167,7 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
   pr.map.T = T;
   pr.map.N = (int)N;
   pr.rec = pr.ws + pr.lay.rec;
+  if (flags & FLAG_REUSE_RECORDS) return KDA_SUCCESS;  // the records are already in the workspace
 
   IntraArgs ia;
   ia.q = static_cast<const uint16_t*>(q);

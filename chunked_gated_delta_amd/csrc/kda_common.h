@@ -170,6 +170,7 @@ constexpr int FLAG_GATE_GIVEN = 1;   // raw_gate holds the natural-log decay g
 constexpr int FLAG_BETA_GIVEN = 2;   // raw_beta holds beta
 constexpr int FLAG_NO_QK_NORM = 4;   // q, k used without L2 normalisation
 constexpr int FLAG_STATE_VK = 8;     // states stored transposed, [N, H, V, K]
+constexpr int FLAG_REUSE_RECORDS = 16;  // the workspace already holds this call's chunk records
 
 // Host-side launchers (defined next to their kernels).
 struct IntraArgs {

@@ -195,6 +195,20 @@ kda_status_t kda_decode(const void* q, const void* k, const void* v, const void*
 #define KDA_FLAG_STATE_VK 8u
 
 /*
+ * KDA_FLAG_REUSE_RECORDS (kda_fwd_ex only): skip the intra-chunk pass and use
+ * the per-(chunk, head) records that the previous call on this workspace left
+ * there, for the second pass of the split-sequence flow (the KCP item of the
+ * torchtitan PR page, "Summary"): kda_shard_affine, kda_shard_scan, then
+ * kda_fwd_ex over the same shard batch from the scanned entering states.  The
+ * records depend on q, k, raw_gate, raw_beta, A_log, dt_bias, lower_bound,
+ * cu_seqlens, B, T, H, N and the GATE_GIVEN, BETA_GIVEN and NO_QK_NORM bits,
+ * not on v or the states.  The caller guarantees that all of these equal those
+ * of the call that wrote the records and that the workspace is unchanged since;
+ * nothing checks it, and other records give wrong results.
+ */
+#define KDA_FLAG_REUSE_RECORDS 16u
+
+/*
  * kda_fwd with variant flags (any OR of the KDA_FLAG_* bits; other bits give
  * KDA_ERR_INVALID).  Every other argument is as for kda_fwd, and
  * kda_fwd(...) == kda_fwd_ex(..., 0, stream).

@@ -207,8 +207,10 @@ def fwd_ex_call(flags, **over):
 
 
 def test_fwd_ex_flag_checks():
-    assert fwd_ex_call(16) == INVALID                     # unknown bit
+    assert fwd_ex_call(32) == INVALID                     # unknown bit
     assert fwd_ex_call(1 << 31) == INVALID
+    # reusing the workspace's records is a known bit: the call proceeds to the workspace check
+    assert fwd_ex_call(kda.FLAG_REUSE_RECORDS, ws_bytes=8) == WORKSPACE
     assert fwd_ex_call(0, A_log=None) == INVALID          # gate parameters needed without GATE_GIVEN
     assert fwd_ex_call(kda.FLAG_BETA_GIVEN, dt=None) == INVALID
     assert fwd_ex_call(kda.FLAG_GATE_GIVEN, K=64, V=64, A_log=None, dt=None) == UNSUPPORTED
@@ -264,7 +266,8 @@ def bwd_ex_call(flags, **over):
 
 
 def test_bwd_ex_flag_checks():
-    assert bwd_ex_call(16) == INVALID                       # unknown bit
+    assert bwd_ex_call(32) == INVALID                       # unknown bit
+    assert bwd_ex_call(kda.FLAG_REUSE_RECORDS) == INVALID   # the backward always builds its records
     assert bwd_ex_call(0, A_log=None) == INVALID            # gate parameters needed without GATE_GIVEN
     assert bwd_ex_call(0, dA=None) == INVALID
     # with the gate given they may be absent: the call then proceeds to the workspace check

@@ -118,3 +118,29 @@ def test_scan_matches_fp64_fold(n):
     rs, rf = oracle_shard_fold(P.double().numpy(), R.double().numpy(), S0.double().numpy())
     assert metrics(starts.double().cpu().numpy(), rs)["rel_l2"] <= 1e-5
     assert metrics(fin.double().cpu().numpy(), rf)["rel_l2"] <= 1e-5
+
+
+def test_forward_reusing_the_shard_records_is_exact():
+    """kda_fwd_ex with FLAG_REUSE_RECORDS on the workspace kda_shard_affine filled gives
+    the same bits as a kda_fwd call that rebuilds the records."""
+    x = W.random_inputs("kcp-reuse", 44, 1, 3000, 3)
+    cu = [0, 640, 1000, 1001, 3000]
+    n = len(cu) - 1
+    cut = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    P = torch.empty(n, x.H, x.K, x.K, device=DEV)
+    R = torch.empty(n, x.H, x.K, x.V, device=DEV)
+    ws = torch.empty(kda.kda_workspace_size(x.T, x.H, n), dtype=torch.uint8, device=DEV)
+    args = (d(x.q), d(x.k), d(x.v), d(x.raw_gate), d(x.raw_beta))
+    al, dt = d(x.A_log), d(x.dt_bias)
+    print("kda_shard_affine + scan + kda_fwd_ex(REUSE_RECORDS)", flush=True)
+    kda.kda_shard_affine(*args, ws, al, dt, x.lower_bound, P, R, cu_seqlens=cut)
+    starts = torch.empty(n, x.H, x.K, x.V, device=DEV)
+    kda.kda_shard_scan(P, R, starts, initial_state=d(x.initial_state[0].contiguous()))
+    out_r, fin_r = torch.empty_like(args[2]), torch.empty(n, x.H, x.K, x.V, device=DEV)
+    kda.kda_fwd_ex(*args, x.scale, out_r, ws, al, dt, x.lower_bound, starts, fin_r, cut,
+                   flags=kda.FLAG_REUSE_RECORDS)
+    out_f, fin_f = torch.empty_like(out_r), torch.empty_like(fin_r)
+    ws2 = torch.empty_like(ws)
+    kda.kda_fwd(*args, x.scale, out_f, ws2, al, dt, x.lower_bound, starts, fin_f, cut)
+    torch.cuda.synchronize()
+    assert torch.equal(out_r, out_f) and torch.equal(fin_r, fin_f)
