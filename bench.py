@@ -277,11 +277,19 @@ def bench_bwd(args):
     ms = timed(lambda: kda.kda_bwd(q, k, v, g, b, x.scale, d_out, dq, dk, dv, dg, db, dA, ddt, ws, al, dt,
                                    x.lower_bound, initial_state=init, d_final=d_fin, d_initial_state=dinit,
                                    stream=sh), args.steps, args.warmup, stream)
+    # the same gradients on the records a forward call left in this workspace
+    out, fin = torch.empty_like(v), torch.empty_like(init)
+    kda.kda_fwd(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, init, fin, stream=sh)
+    ms_reuse = timed(lambda: kda.kda_bwd_ex(q, k, v, g, b, x.scale, d_out, dq, dk, dv, dg, db, dA, ddt, ws, al,
+                                            dt, x.lower_bound, initial_state=init, d_final=d_fin,
+                                            d_initial_state=dinit, flags=kda.FLAG_REUSE_RECORDS, stream=sh),
+                     args.steps, args.warmup, stream)
     ht = x.T * x.H
     alg = ht * (9 * 128 * 2 + 2 * 2) + 3 * x.H * STATE_BYTES
     gbs = alg / (ms / 1e3) / 1e9
     print(json.dumps({
         "metric": "KDA backward (all input gradients) head-tokens/s", "value": ht / (ms / 1e3),
+        "ms_reusing_forward_records": ms_reuse,
         "unit": "head-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "dtype": "fp32 compute, bf16 io", "data": "synthetic",
         "config": {"workload": f"kda_bwd B=1 T={x.T} H={x.H} K=V=128 chunk=64 lower_bound=-5, "

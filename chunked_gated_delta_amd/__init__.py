@@ -34,7 +34,7 @@ exported_symbols = ("kda_fwd", "kda_workspace_size", "kda_is_supported", "kda_st
                     "kda_bwd_ex", "kda_bwd_workspace_size")
 # kda_fwd_ex variant bits (KDA_FLAG_* in include/kda.h)
 FLAG_GATE_GIVEN, FLAG_BETA_GIVEN, FLAG_NO_QK_NORM, FLAG_STATE_VK = 1, 2, 4, 8
-# kda_fwd_ex only: reuse the chunk records the previous call left in the workspace
+# kda_fwd_ex, kda_bwd_ex: reuse the chunk records the previous call left in the workspace
 FLAG_REUSE_RECORDS = 16
 
 

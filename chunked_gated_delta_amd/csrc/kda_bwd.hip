@@ -1398,7 +1398,8 @@ kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void*
                         const float* A_log, const float* dt_bias, float lower_bound,
                         const float* initial_state, const int32_t* cu_seqlens, int64_t B, int64_t T,
                         int64_t H, int64_t K, int64_t V, int64_t N, unsigned flags, void* stream) {
-  if (flags & ~(unsigned)(FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM | FLAG_STATE_VK))
+  if (flags & ~(unsigned)(FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM | FLAG_STATE_VK |
+                          FLAG_REUSE_RECORDS))
     return KDA_ERR_INVALID;
   if (B * T > 0 && (!v || !d_out || !dq || !dk || !dv || !d_raw_gate || !d_raw_beta)) return KDA_ERR_INVALID;
   if (!(flags & FLAG_GATE_GIVEN) && (!dA_log || !d_dt_bias || !A_log || !dt_bias)) return KDA_ERR_INVALID;

@@ -195,7 +195,7 @@ kda_status_t kda_decode(const void* q, const void* k, const void* v, const void*
 #define KDA_FLAG_STATE_VK 8u
 
 /*
- * KDA_FLAG_REUSE_RECORDS (kda_fwd_ex only): skip the intra-chunk pass and use
+ * KDA_FLAG_REUSE_RECORDS (kda_fwd_ex, kda_bwd_ex): skip the intra-chunk pass and use
  * the per-(chunk, head) records that the previous call on this workspace left
  * there, for the second pass of the split-sequence flow (the KCP item of the
  * torchtitan PR page, "Summary"): kda_shard_affine, kda_shard_scan, then
@@ -274,6 +274,10 @@ kda_status_t kda_bwd(const void* q, const void* k, const void* v, const void* ra
  * With KDA_FLAG_BETA_GIVEN, d_raw_beta is the gradient with respect to beta;
  * with KDA_FLAG_NO_QK_NORM, dq and dk are those of the unnormalised q, k; with
  * KDA_FLAG_STATE_VK, initial_state, d_final and d_initial_state are [N, H, V, K].
+ * With KDA_FLAG_REUSE_RECORDS the gradients use the chunk records that a
+ * kda_fwd / kda_fwd_ex call with the same inputs and flags left at the start of
+ * this workspace (the backward workspace begins with the forward's layout), and
+ * the intra-chunk pass is skipped; the conditions are those of kda_fwd_ex.
  * kda_bwd(...) == kda_bwd_ex(..., 0, stream).
  */
 kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void* raw_gate,

@@ -267,7 +267,7 @@ def bwd_ex_call(flags, **over):
 
 def test_bwd_ex_flag_checks():
     assert bwd_ex_call(32) == INVALID                       # unknown bit
-    assert bwd_ex_call(kda.FLAG_REUSE_RECORDS) == INVALID   # the backward always builds its records
+    assert bwd_ex_call(kda.FLAG_REUSE_RECORDS) == WORKSPACE  # a known bit: on to the workspace check
     assert bwd_ex_call(0, A_log=None) == INVALID            # gate parameters needed without GATE_GIVEN
     assert bwd_ex_call(0, dA=None) == INVALID
     # with the gate given they may be absent: the call then proceeds to the workspace check

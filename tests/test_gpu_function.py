@@ -21,8 +21,8 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-@pytest.mark.parametrize("lengths", [None, [70, 0, 5, 64]])
-def test_autograd_through_the_wrapper(lengths):
+@pytest.mark.parametrize("lengths,reuse", [(None, False), ([70, 0, 5, 64], False), ([70, 0, 5, 64], True)])
+def test_autograd_through_the_wrapper(lengths, reuse):
     from chunked_gated_delta_amd.function import kda_chunk
 
     T = 130 if lengths is None else sum(lengths)
@@ -33,7 +33,7 @@ def test_autograd_through_the_wrapper(lengths):
     cu = None if x.cu_seqlens is None else x.cu_seqlens.to(DEV)
     print(f"kda_chunk {x.name} T={T} lengths={lengths}", flush=True)
     out, fin = kda_chunk(q, k, v, g, b, al, dt, scale=x.scale, lower_bound=x.lower_bound,
-                         initial_state=init, cu_seqlens=cu)
+                         initial_state=init, cu_seqlens=cu, reuse_records=reuse)
     o_ref, f_ref = run_gpu(x)
     assert np.array_equal(out.detach().double().cpu().numpy().reshape(o_ref.shape), o_ref)
     assert np.array_equal(fin.detach().double().cpu().numpy(), f_ref)
@@ -65,3 +65,35 @@ def test_q_and_k_as_one_tensor_sum_their_gradients():
     ref = oracle(x, d_out, d_fin)
     got = qk.grad.double().cpu().numpy().reshape(x.T, x.H, x.K)
     compare({"dq": got}, {"dq": ref["dq"] + ref["dk"]}, names=("dq",))
+
+
+def test_backward_on_the_forward_records_is_exact():
+    """kda_bwd_ex with FLAG_REUSE_RECORDS after kda_fwd on the same (backward-sized)
+    workspace gives the same bits as kda_bwd rebuilding the records."""
+    x = W.random_inputs("fn_reuse", 65, 1, 300, 3, lengths=[100, 200])
+    t = {n: getattr(x, n).to(DEV) for n in ("q", "k", "v", "raw_gate", "raw_beta", "A_log", "dt_bias",
+                                             "initial_state", "cu_seqlens")}
+    d_out, d_fin = (c.to(DEV) for c in cotangents(x, 66))
+    B, T, H, K, V, N = x.B, x.T, x.H, x.K, x.V, x.N
+    size = kda.kda_bwd_workspace_size(B * T, H, N)
+
+    def grads(ws, flags):
+        gs = [torch.empty_like(t[n]) for n in ("q", "k", "v", "raw_gate", "raw_beta", "A_log", "dt_bias",
+                                                "initial_state")]
+        kda.kda_bwd_ex(t["q"], t["k"], t["v"], t["raw_gate"], t["raw_beta"], x.scale, d_out, gs[0], gs[1], gs[2],
+                       gs[3], gs[4], gs[5], gs[6], ws, t["A_log"], t["dt_bias"], x.lower_bound,
+                       initial_state=t["initial_state"], d_final=d_fin, d_initial_state=gs[7],
+                       cu_seqlens=t["cu_seqlens"], flags=flags)
+        return gs
+
+    ws = torch.empty(size, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(t["v"])
+    fin = torch.empty(N, H, K, V, device=DEV)
+    print("kda_fwd then kda_bwd_ex(REUSE_RECORDS) on one workspace", flush=True)
+    kda.kda_fwd(t["q"], t["k"], t["v"], t["raw_gate"], t["raw_beta"], x.scale, out, ws, t["A_log"], t["dt_bias"],
+                x.lower_bound, t["initial_state"], fin, t["cu_seqlens"])
+    reused = grads(ws, kda.FLAG_REUSE_RECORDS)
+    fresh = grads(torch.empty(size, dtype=torch.uint8, device=DEV), 0)
+    torch.cuda.synchronize()
+    for a, b in zip(reused, fresh):
+        assert torch.equal(a, b)
