@@ -53,7 +53,9 @@ typedef enum {
  * Bytes of device workspace kda_fwd needs for T_total packed tokens, H heads
  * and N sequences (the page's get_workspace_size(T, H, 1) for one sequence).
  * The caller allocates it (any alignment >= 256 bytes) and passes it to
- * kda_fwd.  Its contents are scratch: undefined before and after a call.
+ * kda_fwd.  Its contents are scratch: undefined before a call, and afterwards
+ * meaningful only as the chunk records that KDA_FLAG_REUSE_RECORDS lets a
+ * following call with the same inputs reuse.
  * Returns 0 if any argument is < 1 (T_total may be 0).
  */
 size_t kda_workspace_size(int64_t T_total, int64_t H, int64_t N);
