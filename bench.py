@@ -78,12 +78,13 @@ def cpu_baseline(x, heads):
                x.lower_bound, x.initial_state, x.cu_seqlens, heads=heads, want_final=True)
     dt = time.perf_counter() - t0
     ht = x.B * x.T * len(heads)
+    cores = oracle_threads()  # before the one-thread run below changes the OpenMP default
     # the same recurrence on one host thread, over the first head only
     t1 = time.perf_counter()
     oracle_fwd(x.q, x.k, x.v, x.raw_gate, x.raw_beta, x.scale, x.A_log, x.dt_bias,
                x.lower_bound, x.initial_state, x.cu_seqlens, heads=heads[:1], want_final=True, threads=1)
     dt1 = time.perf_counter() - t1
-    return {"value": ht / dt, "unit": "head-tokens/s", "cores": oracle_threads(), "kind": "oracle",
+    return {"value": ht / dt, "unit": "head-tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"fp64 token recurrence over heads 0..{len(heads) - 1} of {x.H}, all "
                       f"{x.T} tokens ({ht} head-tokens, {dt:.1f} s)",
             "single_core_value": x.B * x.T / dt1,

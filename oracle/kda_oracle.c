@@ -102,13 +102,14 @@ int kda_oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   for (int64_t i = 0; i < n_heads; ++i)
     if (heads[i] < 0 || heads[i] >= H) return -1;
 #ifdef _OPENMP
-  if (n_threads > 0) omp_set_num_threads(n_threads);
+  /* the thread count applies to this call only (no process-wide OpenMP setting) */
+  const int nt = n_threads > 0 ? n_threads : omp_get_max_threads();
 #else
   (void)n_threads;
 #endif
 
   int64_t jobs = N * n_heads;
-#pragma omp parallel
+#pragma omp parallel num_threads(nt)
   {
     double* S = (double*)malloc(sizeof(double) * K * V);
     double* qh = (double*)malloc(sizeof(double) * K);
