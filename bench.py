@@ -324,8 +324,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (the KDA forward shards heads and "
-              "sequences with no exchange; multi-GPU runs are out of scope)", file=sys.stderr)
+        print("bench.py: only --gpus 1 is supported; the library runs on one GPU (its forward "
+              "would shard heads and sequences across GPUs with no exchange, which is not built)",
+              file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
