@@ -286,3 +286,15 @@ def test_varlen_at_every_slice_width(H):
     ro, rf = oracle(x)
     check(o, f, ro, rf, x.name)
     assert np.array_equal(f[1], x.initial_state[1].double().numpy())
+
+
+@pytest.mark.parametrize("N", [300, 3000])
+def test_many_short_sequences(N):
+    """Hundreds to thousands of packed sequences of 0-70 (N = 300) or 0-5 tokens
+    (N = 3000), empty ones included, through the longest-first sequence order."""
+    g = np.random.default_rng(N)
+    lengths = [int(v) for v in g.integers(0, 6 if N > 1000 else 71, size=N)]
+    x = W.random_inputs(f"many_N{N}", 700 + N % 97, 1, sum(lengths), 2, lengths=lengths)
+    o, f = run_gpu(x)
+    ro, rf = oracle(x)
+    check(o, f, ro, rf, x.name)
