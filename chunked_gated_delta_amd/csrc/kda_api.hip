@@ -52,6 +52,20 @@ __global__ void __launch_bounds__(1024) kda_chunk_offsets_kernel(const int32_t* 
   if (tid == 0) choff[N] = carry;
 }
 
+// Shard offsets of a split forward: N sequences of T tokens (nc chunks) cut
+// into S shards of cs chunks; shard i = n S + s starts at token n T + s cs 64
+// and at global chunk n nc + s cs (the intra kernel's numbering).
+__global__ void kda_shard_map_kernel(int32_t* __restrict__ scu, int32_t* __restrict__ schoff, int N, int S,
+                                     int T, int nc, int cs) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int ns = N * S;
+  if (i > ns) return;
+  const int n = i < ns ? i / S : N;
+  const int sh = i < ns ? i - n * S : 0;
+  scu[i] = n * T + sh * cs * CH;
+  schoff[i] = n * nc + sh * cs;
+}
+
 // Zeroes the intra kernel's work-item counter (a kernel rather than a memset,
 // so that a captured graph replays it as a kernel node).
 __global__ void kda_zero_claim_kernel(int32_t* __restrict__ claim) { *claim = 0; }
@@ -216,6 +230,67 @@ InterArgs inter_args(const Prepared& pr, int64_t H) {
   return xa;
 }
 
+// The recurrence of a prepared forward (records built for the N sequences of
+// T tokens) on shards: R and P of every shard (the shard passes of
+// kda_shard_affine), their fold per sequence, then the forward over the
+// shards from the folded states.  The records are indexed by global chunk, so
+// the shard map reuses them as they are.  Not for in-place states (the fold
+// reads initial_state while it writes final_state).
+kda_status_t split_forward(const Prepared& pr, const void* v, void* out, const float* initial_state,
+                           float* final_state, float scale, int64_t T, int64_t H, int64_t N, hipStream_t st) {
+  const SplitPlan sp = split_plan(T, H, N);
+  const int64_t ns = N * sp.S;
+  const int64_t nc = (T + CH - 1) / CH;
+  int32_t* scu = reinterpret_cast<int32_t*>(pr.ws + pr.lay.scu);
+  int32_t* schoff = reinterpret_cast<int32_t*>(pr.ws + pr.lay.schoff);
+  float* sP = reinterpret_cast<float*>(pr.ws + pr.lay.sP);
+  float* sR = reinterpret_cast<float*>(pr.ws + pr.lay.sR);
+  float* sstart = reinterpret_cast<float*>(pr.ws + pr.lay.sstart);
+  float* sfin = reinterpret_cast<float*>(pr.ws + pr.lay.sfin);
+  int n32 = (int)N, s32 = (int)sp.S, t32 = (int)T, nc32 = (int)nc, cs32 = (int)sp.cs;
+  void* margs[] = {(void*)&scu, (void*)&schoff, (void*)&n32, (void*)&s32, (void*)&t32, (void*)&nc32, (void*)&cs32};
+  if (launch_status(hipLaunchKernel(reinterpret_cast<const void*>(&kda_shard_map_kernel),
+                                    dim3((unsigned)((ns + 1 + 255) / 256)), dim3(256), margs, 0, st),
+                    "shard map") != KDA_SUCCESS)
+    return KDA_ERR_LAUNCH;
+  ChunkMap m2;
+  m2.cu = scu;
+  m2.choff = schoff;
+  m2.T = T;
+  m2.N = (int)ns;
+  auto shard_args = [&]() {
+    InterArgs x = inter_args(pr, H);
+    x.map = m2;
+    x.order = nullptr;
+    x.timers = nullptr;
+    return x;
+  };
+  InterArgs xr = shard_args();  // R: from a zero state, with V
+  xr.v = static_cast<const uint16_t*>(v);
+  xr.fin = sR;
+  if (launch_status(launch_inter(xr, st), "inter (shard R)") != KDA_SUCCESS) return KDA_ERR_LAUNCH;
+  InterArgs xp = shard_args();  // P: V = 0 from the identity
+  xp.fin = sP;
+  xp.init_identity = 1;
+  if (launch_status(launch_inter(xp, st), "inter (shard P)") != KDA_SUCCESS) return KDA_ERR_LAUNCH;
+  const size_t kv = (size_t)KD * VD;
+  for (int64_t n = 0; n < N; ++n) {
+    const size_t sh = (size_t)n * sp.S * H * kv, sq = (size_t)n * H * kv;
+    if (launch_status(launch_shard_scan(sP + sh, sR + sh, initial_state ? initial_state + sq : nullptr,
+                                        sstart + sh, final_state ? final_state + sq : nullptr, (int)sp.S,
+                                        (int)H, st),
+                      "shard fold") != KDA_SUCCESS)
+      return KDA_ERR_LAUNCH;
+  }
+  InterArgs xf = shard_args();  // the outputs, from the folded entering states
+  xf.v = static_cast<const uint16_t*>(v);
+  xf.out = static_cast<uint16_t*>(out);
+  xf.init = sstart;
+  xf.fin = sfin;
+  xf.scale = scale;
+  return launch_status(launch_inter(xf, st), "inter (shards)");
+}
+
 }  // namespace kda
 
 extern "C" {
@@ -233,6 +308,9 @@ kda_status_t kda_fwd_ex(const void* q, const void* k, const void* v, const void*
   const kda_status_t s = prepare(q, k, raw_gate, raw_beta, workspace, workspace_bytes, A_log, dt_bias,
                                  lower_bound, cu_seqlens, B, T, H, K, V, N, st, pr, flags);
   if (s != KDA_SUCCESS) return s;
+  const bool split = pr.lay.S > 1 && !cu_seqlens && !(flags & FLAG_STATE_VK) && T > 0 &&
+                     B * T < ((int64_t)1 << 31) && !(initial_state && initial_state == final_state);
+  if (split) return split_forward(pr, v, out, initial_state, final_state, scale, T, H, N, st);
   InterArgs xa = inter_args(pr, H);
   xa.v = static_cast<const uint16_t*>(v);
   xa.out = static_cast<uint16_t*>(out);

@@ -9,10 +9,39 @@ namespace kda {
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// A forward with few (sequence, head) chains and long sequences runs its
+// recurrence on shards: each of the N sequences is cut into S shards of cs
+// whole chunks, the per-shard affine maps S -> P S + R are folded, and the
+// forward runs over the shards from the folded entering states.  Three passes
+// over chains S times shorter, on S times more workgroups.  Only without
+// cu_seqlens, where the host knows every length (T per sequence).
+constexpr int64_t kSplitChains = 128;   // aim: about this many (shard, head) chains
+constexpr int64_t kMinShardChunks = 32;  // shards of at least 2048 tokens
+constexpr int64_t kMinShards = 4;        // below 4 shards the three passes do not pay
+struct SplitPlan {
+  int64_t S;   // shards per sequence (1: no split)
+  int64_t cs;  // chunks per shard (the last one of a sequence may be shorter)
+};
+inline SplitPlan split_plan(int64_t T, int64_t H, int64_t N) {
+  const int64_t nc = (T + CH - 1) / CH;
+  if (T <= 0 || H < 1 || N < 1) return {1, nc};
+  const int64_t a = kSplitChains / (N * H), b = nc / kMinShardChunks;
+  const int64_t S = a < b ? a : b;
+  if (S < kMinShards) return {1, nc};
+  const int64_t cs = (nc + S - 1) / S;
+  return {(nc + cs - 1) / cs, cs};
+}
+
 struct Layout {
   size_t claim, choff, order, rec, total;
+  // shard areas (split forwards only): shard offsets in tokens and in chunks
+  // [N S + 1], and the per-shard P, R, entering and final states
+  int64_t S;
+  size_t scu, schoff, sP, sR, sstart, sfin;
 };
 
+// T_total / N is the per-sequence length the split plan assumes; calls with
+// cu_seqlens never split and need only the first areas.
 inline Layout workspace_layout(int64_t T_total, int64_t H, int64_t N) {
   Layout l;
   l.claim = 0;  // the intra kernel's work-item counter (one int)
@@ -21,6 +50,18 @@ inline Layout workspace_layout(int64_t T_total, int64_t H, int64_t N) {
   l.rec = l.order + align256((size_t)N * sizeof(int32_t));
   const size_t max_chunks = (size_t)(T_total / CH) + (size_t)N;
   l.total = l.rec + max_chunks * (size_t)H * REC_BYTES;
+  l.S = N > 0 ? split_plan(T_total / N, H, N).S : 1;
+  l.scu = l.schoff = l.sP = l.sR = l.sstart = l.sfin = l.total;
+  if (l.S > 1) {
+    const size_t ns = (size_t)(N * l.S), st = ns * (size_t)H * KD * VD * sizeof(float);
+    l.scu = align256(l.total);
+    l.schoff = l.scu + align256((ns + 1) * sizeof(int32_t));
+    l.sP = l.schoff + align256((ns + 1) * sizeof(int32_t));
+    l.sR = l.sP + st;  // P is [ns, H, K, K] with K == V
+    l.sstart = l.sR + st;
+    l.sfin = l.sstart + st;
+    l.total = l.sfin + st;
+  }
   return l;
 }
 
@@ -44,6 +85,10 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
 
 // Inter-chunk arguments for the prepared call (no v, outputs or states set).
 InterArgs inter_args(const Prepared& pr, int64_t H);
+
+// The forward's recurrence on shards (split_plan), after prepare().
+kda_status_t split_forward(const Prepared& pr, const void* v, void* out, const float* initial_state,
+                           float* final_state, float scale, int64_t T, int64_t H, int64_t N, hipStream_t st);
 
 // KDA_SUCCESS, or KDA_ERR_LAUNCH for a failed launch (KDA_DEBUG=1 prints why).
 kda_status_t launch_status(hipError_t err, const char* what);

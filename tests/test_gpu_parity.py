@@ -298,3 +298,22 @@ def test_many_short_sequences(N):
     o, f = run_gpu(x)
     ro, rf = oracle(x)
     check(o, f, ro, rf, x.name)
+
+
+@pytest.mark.parametrize("B,T,H,init,lb", [(1, 25600, 1, False, -5.0), (2, 16000, 2, True, -5.0),
+                                             (1, 16421, 3, True, -0.01), (1, 20000, 1, True, -0.002)])
+def test_long_sequences_with_few_heads_run_on_shards(B, T, H, init, lb):
+    """Few (sequence, head) pairs and long sequences: the forward cuts every sequence into
+    shards of at least 32 chunks (here 12, 7, 8 and 9 per sequence, ragged last shards
+    included), folds their affine maps and runs the shards from the folded states.  With
+    lower_bound -5 the state forgets a shard's start within it; the small lower bounds
+    keep it, so the fold carries the state across shards.  An in-place state update takes
+    the unsplit path, so the same inputs are checked both ways."""
+    x = W.random_inputs(f"split_B{B}_T{T}_H{H}", 800 + T % 97, B, T, H, init_std=0.1 if init else None,
+                        lower_bound=lb)
+    o, f = run_gpu(x)
+    ro, rf = oracle(x)
+    check(o, f, ro, rf, x.name + " (shards)")
+    if init:
+        o2, f2 = run_gpu(x, in_place=True)
+        check(o2, f2, ro, rf, x.name + " (in place, unsplit)")
