@@ -70,6 +70,10 @@ def test_workspace_size():
     assert kda.kda_workspace_size(10, 2, 0) == 0
     # room for a processing order of all N sequences
     assert kda.kda_workspace_size(10 ** 6, 1, 10 ** 5) >= 4 * 10 ** 5
+    # a long sequence with few heads runs on shards: room for their P, R, entering and
+    # final states (16 shards x 8 heads x 4 x 64 KiB) beyond the chunk records
+    records = (262144 // 64 + 1) * 8 * 90624
+    assert kda.kda_workspace_size(262144, 8, 1) >= records + 16 * 8 * 4 * 65536
 
 
 def test_is_supported():
