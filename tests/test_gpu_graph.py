@@ -28,9 +28,11 @@ def dev(x):
             for n in ("q", "k", "v", "raw_gate", "raw_beta", "A_log", "dt_bias", "initial_state", "cu_seqlens")}
 
 
-@pytest.mark.parametrize("lengths", [None, [130, 0, 64, 77]])
-def test_forward_replays_match_eager_calls(lengths):
-    T = 200 if lengths is None else sum(lengths)
+@pytest.mark.parametrize("lengths,T", [(None, 200), ([130, 0, 64, 77], None), (None, 8192)])
+def test_forward_replays_match_eager_calls(lengths, T):
+    """T = 8192 with 3 heads runs the recurrence on 4 shards per sequence (shard map,
+    R and P passes, fold, forward): every launch of that path is captured too."""
+    T = sum(lengths) if lengths is not None else T
     xs = [W.random_inputs(f"graph_{i}", 500 + i, 1, T, 3, lengths=lengths) for i in range(3)]
     x0 = xs[0]
     st = dev(x0)  # the captured (static) input buffers
