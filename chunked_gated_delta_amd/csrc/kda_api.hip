@@ -230,14 +230,14 @@ InterArgs inter_args(const Prepared& pr, int64_t H) {
   return xa;
 }
 
-// The recurrence of a prepared forward (records built for the N sequences of
-// T tokens) on shards: R and P of every shard (the shard passes of
-// kda_shard_affine), their fold per sequence, then the forward over the
-// shards from the folded states.  The records are indexed by global chunk, so
-// the shard map reuses them as they are.  Not for in-place states (the fold
-// reads initial_state while it writes final_state).
-kda_status_t split_forward(const Prepared& pr, const void* v, void* out, const float* initial_state,
-                           float* final_state, float scale, int64_t T, int64_t H, int64_t N, hipStream_t st) {
+// The shard states of a prepared call (records built for the N sequences of
+// T tokens, split_plan(T, H, N).S > 1): the shard map, R and P of every shard
+// (the shard passes of kda_shard_affine), and their fold per sequence, which
+// leaves the entering state of every shard in the workspace (lay.sstart) and
+// writes final_state if given.  The records are indexed by global chunk, so
+// the shard map reuses them as they are.  `m2` receives the shard map.
+kda_status_t shard_states(const Prepared& pr, const void* v, const float* initial_state, float* final_state,
+                          int64_t T, int64_t H, int64_t N, hipStream_t st, ChunkMap& m2) {
   const SplitPlan sp = split_plan(T, H, N);
   const int64_t ns = N * sp.S;
   const int64_t nc = (T + CH - 1) / CH;
@@ -246,30 +246,21 @@ kda_status_t split_forward(const Prepared& pr, const void* v, void* out, const f
   float* sP = reinterpret_cast<float*>(pr.ws + pr.lay.sP);
   float* sR = reinterpret_cast<float*>(pr.ws + pr.lay.sR);
   float* sstart = reinterpret_cast<float*>(pr.ws + pr.lay.sstart);
-  float* sfin = reinterpret_cast<float*>(pr.ws + pr.lay.sfin);
   int n32 = (int)N, s32 = (int)sp.S, t32 = (int)T, nc32 = (int)nc, cs32 = (int)sp.cs;
   void* margs[] = {(void*)&scu, (void*)&schoff, (void*)&n32, (void*)&s32, (void*)&t32, (void*)&nc32, (void*)&cs32};
   if (launch_status(hipLaunchKernel(reinterpret_cast<const void*>(&kda_shard_map_kernel),
                                     dim3((unsigned)((ns + 1 + 255) / 256)), dim3(256), margs, 0, st),
                     "shard map") != KDA_SUCCESS)
     return KDA_ERR_LAUNCH;
-  ChunkMap m2;
   m2.cu = scu;
   m2.choff = schoff;
   m2.T = T;
   m2.N = (int)ns;
-  auto shard_args = [&]() {
-    InterArgs x = inter_args(pr, H);
-    x.map = m2;
-    x.order = nullptr;
-    x.timers = nullptr;
-    return x;
-  };
-  InterArgs xr = shard_args();  // R: from a zero state, with V
+  InterArgs xr = shard_inter_args(pr, H, m2);  // R: from a zero state, with V
   xr.v = static_cast<const uint16_t*>(v);
   xr.fin = sR;
   if (launch_status(launch_inter(xr, st), "inter (shard R)") != KDA_SUCCESS) return KDA_ERR_LAUNCH;
-  InterArgs xp = shard_args();  // P: V = 0 from the identity
+  InterArgs xp = shard_inter_args(pr, H, m2);  // P: V = 0 from the identity
   xp.fin = sP;
   xp.init_identity = 1;
   if (launch_status(launch_inter(xp, st), "inter (shard P)") != KDA_SUCCESS) return KDA_ERR_LAUNCH;
@@ -282,11 +273,30 @@ kda_status_t split_forward(const Prepared& pr, const void* v, void* out, const f
                       "shard fold") != KDA_SUCCESS)
       return KDA_ERR_LAUNCH;
   }
-  InterArgs xf = shard_args();  // the outputs, from the folded entering states
+  return KDA_SUCCESS;
+}
+
+InterArgs shard_inter_args(const Prepared& pr, int64_t H, const ChunkMap& m2) {
+  InterArgs x = inter_args(pr, H);
+  x.map = m2;
+  x.order = nullptr;
+  x.timers = nullptr;
+  return x;
+}
+
+// The forward's recurrence on shards: the shard states, then the forward over
+// the shards from them.  Not for in-place states (the fold reads
+// initial_state while it writes final_state).
+kda_status_t split_forward(const Prepared& pr, const void* v, void* out, const float* initial_state,
+                           float* final_state, float scale, int64_t T, int64_t H, int64_t N, hipStream_t st) {
+  ChunkMap m2;
+  const kda_status_t s = shard_states(pr, v, initial_state, final_state, T, H, N, st, m2);
+  if (s != KDA_SUCCESS) return s;
+  InterArgs xf = shard_inter_args(pr, H, m2);  // the outputs, from the folded entering states
   xf.v = static_cast<const uint16_t*>(v);
   xf.out = static_cast<uint16_t*>(out);
-  xf.init = sstart;
-  xf.fin = sfin;
+  xf.init = reinterpret_cast<const float*>(pr.ws + pr.lay.sstart);
+  xf.fin = reinterpret_cast<float*>(pr.ws + pr.lay.sfin);
   xf.scale = scale;
   return launch_status(launch_inter(xf, st), "inter (shards)");
 }
@@ -308,8 +318,7 @@ kda_status_t kda_fwd_ex(const void* q, const void* k, const void* v, const void*
   const kda_status_t s = prepare(q, k, raw_gate, raw_beta, workspace, workspace_bytes, A_log, dt_bias,
                                  lower_bound, cu_seqlens, B, T, H, K, V, N, st, pr, flags);
   if (s != KDA_SUCCESS) return s;
-  const bool split = pr.lay.S > 1 && !cu_seqlens && !(flags & FLAG_STATE_VK) && T > 0 &&
-                     B * T < ((int64_t)1 << 31) && !(initial_state && initial_state == final_state);
+  const bool split = use_split(pr, cu_seqlens, flags, B, T) && !(initial_state && initial_state == final_state);
   if (split) return split_forward(pr, v, out, initial_state, final_state, scale, T, H, N, st);
   InterArgs xa = inter_args(pr, H);
   xa.v = static_cast<const uint16_t*>(v);

@@ -1414,11 +1414,21 @@ kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void*
   const kda_status_t s = prepare(q, k, raw_gate, raw_beta, workspace, workspace_bytes, A_log, dt_bias,
                                  lower_bound, cu_seqlens, B, T, H, K, V, N, st, pr, flags);
   if (s != KDA_SUCCESS) return s;
-  // forward recurrence, keeping the state entering each chunk and each chunk's D
+  // forward recurrence, keeping the state entering each chunk and each chunk's D;
+  // with few long chains it runs on shards from their folded entering states,
+  // which writes the same per-chunk checkpoints
   InterArgs xa = inter_args(pr, H);
   xa.v = static_cast<const uint16_t*>(v);
   xa.init = initial_state;
   xa.state_vk = (flags & FLAG_STATE_VK) ? 1 : 0;
+  if (use_split(pr, cu_seqlens, flags, B, T)) {
+    ChunkMap m2;
+    const kda_status_t ss = shard_states(pr, v, initial_state, nullptr, T, H, N, st, m2);
+    if (ss != KDA_SUCCESS) return ss;
+    xa = shard_inter_args(pr, H, m2);
+    xa.v = static_cast<const uint16_t*>(v);
+    xa.init = reinterpret_cast<const float*>(pr.ws + pr.lay.sstart);
+  }
   xa.states = reinterpret_cast<float*>(pr.ws + bl.states);
   xa.dtile = reinterpret_cast<float*>(pr.ws + bl.dtile);
   xa.timers = nullptr;  // (timer builds: the forward's counter area overlaps these checkpoints)

@@ -86,6 +86,22 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
 // Inter-chunk arguments for the prepared call (no v, outputs or states set).
 InterArgs inter_args(const Prepared& pr, int64_t H);
 
+// Whether a prepared call runs its recurrence on shards (split_plan): only
+// without cu_seqlens, with the [K][V] state layout and a token count that fits
+// the int32 shard offsets.
+inline bool use_split(const Prepared& pr, const int32_t* cu_seqlens, unsigned flags, int64_t B, int64_t T) {
+  return pr.lay.S > 1 && !cu_seqlens && !(flags & FLAG_STATE_VK) && T > 0 && B * T < ((int64_t)1 << 31);
+}
+
+// Inter-chunk arguments over the shard map m2 (no v, outputs or states set).
+InterArgs shard_inter_args(const Prepared& pr, int64_t H, const ChunkMap& m2);
+
+// After prepare(): the shard map (into m2), the shards' R and P and their
+// fold, leaving every shard's entering state at pr.ws + pr.lay.sstart and
+// writing final_state (if not NULL; it must not overlap initial_state).
+kda_status_t shard_states(const Prepared& pr, const void* v, const float* initial_state, float* final_state,
+                          int64_t T, int64_t H, int64_t N, hipStream_t st, ChunkMap& m2);
+
 // The forward's recurrence on shards (split_plan), after prepare().
 kda_status_t split_forward(const Prepared& pr, const void* v, void* out, const float* initial_state,
                            float* final_state, float scale, int64_t T, int64_t H, int64_t N, hipStream_t st);

@@ -253,3 +253,12 @@ def test_bwd_initial_state_gradient_in_place():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(buf.double().cpu().numpy(), ref["d_initial_state"])
     np.testing.assert_array_equal(dq.double().cpu().numpy().reshape(B * T, H, K), ref["dq"])
+
+
+def test_bwd_long_sequence_with_few_heads_checkpoints_on_shards():
+    """T = 8192 with 2 heads: the checkpointing forward pass runs on 4 shards per sequence
+    from their folded entering states (lower_bound -0.01, so the state carries across
+    shards); the gradients still match the chunked fp64 oracle."""
+    x = W.random_inputs("bwd_split", 231, 1, 8192, 2, lower_bound=-0.01)
+    d_out, d_fin = cotangents(x, 232)
+    compare(gpu_bwd(x, d_out, d_fin), oracle(x, d_out, d_fin, chunked=True))
