@@ -40,6 +40,21 @@ struct BwdArgs {
   unsigned long long* timers;  // phase timers (KDA_PHASE_TIMERS builds only), else nullptr
 };
 constexpr int BWD_REC_FLOATS = 3 * CH * CH + 3 * CH * KD + KD + CH;  // 37056
-hipError_t launch_bwd(const BwdArgs& a, int64_t max_chunks, hipStream_t st);
+
+// The reverse recurrence on shards (sequences of the same length split into
+// S shards each, map m2 over the same global chunks): a pass from a zero
+// leaving gradient gives each shard's own entering-state gradient B_r (into
+// `b`), the reverse fold with the shard maps P (`P`, [N S][H][K][K]) gives
+// every shard's leaving gradient (into `ends`) and d_initial_state, and a
+// second pass from those writes the per-chunk gradients.
+struct BwdShards {
+  ChunkMap m2;
+  int64_t N, S;
+  const float* P;
+  float* b;     // [N S][H][K][V]
+  float* ends;  // [N S][H][K][V]
+};
+// `sh` == nullptr: one reverse pass over whole sequences
+hipError_t launch_bwd(const BwdArgs& a, int64_t max_chunks, const BwdShards* sh, hipStream_t st);
 
 }  // namespace kda

@@ -573,16 +573,19 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
       dhu_load(nxt, a.br + ((size_t)(gfirst + cn) * H + h) * BWD_REC_FLOATS, dr, ok, w, lane, gq);
     }
 
-    // dS' of this chunk: fp32 to the checkpoint buffer, bf16 hi/lo to LDS
-    float* dsg = a.dstates + it * KD * VD;
+    // dS' of this chunk: fp32 to the checkpoint buffer (unless only the
+    // entering gradient is wanted), bf16 hi/lo to LDS
+    float* dsg = a.dstates ? a.dstates + it * KD * VD : nullptr;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nn = 0; nn < 4; ++nn) {
         const int k0 = 32 * w + 16 * mt + 4 * gq;
         const int col = 16 * nn + tl;
+        if (dsg) {
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) dsg[(k0 + ii) * VD + vs + col] = dS[mt][nn][ii];
+          for (int ii = 0; ii < 4; ++ii) dsg[(k0 + ii) * VD + vs + col] = dS[mt][nn][ii];
+        }
         bf16x4 hv, lv;
         split_hl4(dS[mt][nn], hv, lv);
         frag_write4(sSh, 4 * nn + w, 4 * mt + gq, tl, hv);
@@ -596,7 +599,7 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
     // two token blocks of dO.  Each group feeds four or eight independent MFMA
     // chains and is read one group ahead behind a scheduling barrier, so one
     // LDS latency is exposed per group instead of one per read.
-    float* ddg = a.ddtile + it * CH * VD;
+    float* ddg = a.ddtile ? a.ddtile + it * CH * VD : nullptr;
     {
       f32x4 acc[4];
 #pragma unroll
@@ -636,8 +639,10 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
 #pragma unroll
       for (int nn = 0; nn < 4; ++nn) {
         const int col = 16 * nn + tl;
+        if (ddg) {
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) ddg[(16 * w + 4 * gq + ii) * VD + vs + col] = acc[nn][ii];
+          for (int ii = 0; ii < 4; ++ii) ddg[(16 * w + 4 * gq + ii) * VD + vs + col] = acc[nn][ii];
+        }
         bf16x4 hv, lv;
         split_hl4(acc[nn], hv, lv);
         frag_write4(sDh, 2 * nn + (w >> 1), 4 * (w & 1) + gq, tl, hv);
@@ -1329,7 +1334,15 @@ __global__ void __launch_bounds__(NTR) kda_bwd_reduce_kernel(BwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& args, int64_t max_chunks, hipStream_t st) {
+hipError_t launch_dhu(const BwdArgs& args, hipStream_t st) {
+  BwdArgs a = args;
+  void* kargs[] = {(void*)&a};
+  const int64_t seqs = (int64_t)a.map.N * a.H;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_bwd_dhu_kernel),
+                         dim3((unsigned)((seqs + 7) / 8 * 8 * 2)), dim3(NT), kargs, 0, st);
+}
+
+hipError_t launch_bwd(const BwdArgs& args, int64_t max_chunks, const BwdShards* sh, hipStream_t st) {
   BwdArgs a = args;
   void* kargs[] = {(void*)&a};
   const int64_t items = max_chunks * a.H;
@@ -1339,9 +1352,31 @@ hipError_t launch_bwd(const BwdArgs& args, int64_t max_chunks, hipStream_t st) {
                         kargs, 0, st);
     if (e != hipSuccess) return e;
   }
-  const int64_t seqs = (int64_t)a.map.N * a.H;
-  e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_bwd_dhu_kernel), dim3((unsigned)((seqs + 7) / 8 * 8 * 2)),
-                      dim3(NT), kargs, 0, st);
+  if (!sh) {
+    e = launch_dhu(a, st);
+  } else {
+    BwdArgs a1 = a;  // each shard's own entering gradient, no per-chunk stores
+    a1.map = sh->m2;
+    a1.order = nullptr;
+    a1.dfin = nullptr;
+    a1.dinit = sh->b;
+    a1.dstates = nullptr;
+    a1.ddtile = nullptr;
+    e = launch_dhu(a1, st);
+    const size_t kv = (size_t)KD * VD;
+    for (int64_t n = 0; n < sh->N && e == hipSuccess; ++n) {
+      const size_t o = (size_t)(n * sh->S * a.H) * kv, oq = (size_t)(n * a.H) * kv;
+      e = launch_shard_scan_rev(sh->P + o, sh->b + o, a.dfin ? a.dfin + oq : nullptr, sh->ends + o,
+                                a.dinit ? a.dinit + oq : nullptr, (int)sh->S, a.H, st);
+    }
+    if (e != hipSuccess) return e;
+    BwdArgs a2 = a;  // the per-chunk gradients from every shard's leaving gradient
+    a2.map = sh->m2;
+    a2.order = nullptr;
+    a2.dfin = sh->ends;
+    a2.dinit = nullptr;
+    e = launch_dhu(a2, st);
+  }
   if (e != hipSuccess) return e;
   if (items > 0) {
     e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_bwd_grad_kernel), dim3((unsigned)items), dim3(NT8),
@@ -1421,8 +1456,9 @@ kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void*
   xa.v = static_cast<const uint16_t*>(v);
   xa.init = initial_state;
   xa.state_vk = (flags & FLAG_STATE_VK) ? 1 : 0;
-  if (use_split(pr, cu_seqlens, flags, B, T)) {
-    ChunkMap m2;
+  const bool split = use_split(pr, cu_seqlens, flags, B, T);
+  ChunkMap m2;
+  if (split) {
     const kda_status_t ss = shard_states(pr, v, initial_state, nullptr, T, H, N, st, m2);
     if (ss != KDA_SUCCESS) return ss;
     xa = shard_inter_args(pr, H, m2);
@@ -1469,7 +1505,19 @@ kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void*
   // timer builds only: 16 counters per workgroup of each backward kernel after the workspace
   ba.timers = reinterpret_cast<unsigned long long*>(pr.ws + bl.total);
 #endif
-  return launch_status(launch_bwd(ba, pr.max_chunks, st), "backward");
+  // with shards, the reverse recurrence runs on them too: the shard maps P
+  // are still in the workspace, R's area (consumed by the fold) takes each
+  // shard's own entering gradient and the final-state area the leaving ones
+  BwdShards sh;
+  if (split) {
+    sh.m2 = m2;
+    sh.N = N;
+    sh.S = split_plan(T, H, N).S;
+    sh.P = reinterpret_cast<const float*>(pr.ws + pr.lay.sP);
+    sh.b = reinterpret_cast<float*>(pr.ws + pr.lay.sR);
+    sh.ends = reinterpret_cast<float*>(pr.ws + pr.lay.sfin);
+  }
+  return launch_status(launch_bwd(ba, pr.max_chunks, split ? &sh : nullptr, st), "backward");
 }
 
 kda_status_t kda_bwd(const void* q, const void* k, const void* v, const void* raw_gate,

@@ -209,5 +209,8 @@ hipError_t launch_intra(const IntraArgs& a, int64_t max_chunks, hipStream_t st);
 hipError_t launch_inter(const InterArgs& a, hipStream_t st);
 hipError_t launch_shard_scan(const float* P, const float* R, const float* init, float* starts, float* fin,
                              int n_shards, int H, hipStream_t st);
+// the backward's reverse fold: ends[r] = gradient leaving shard r, dinit = P_0^T g_0 + B_0
+hipError_t launch_shard_scan_rev(const float* P, const float* B, const float* dfin, float* ends, float* dinit,
+                                 int n_shards, int H, hipStream_t st);
 
 }  // namespace kda

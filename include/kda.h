@@ -245,6 +245,10 @@ size_t kda_bwd_workspace_size(int64_t T_total, int64_t H, int64_t N);
  * of the kda_fwd call with the same inputs (flags 0), with respect to every
  * input, by reverse-mode differentiation of the chunked algebra (fp32
  * arithmetic; the forward states it needs are recomputed inside the call).
+ * Where kda_fwd splits sequences into shards inside the call, both the
+ * recomputed forward recurrence and the reverse one run on those shards, the
+ * reverse one from leaving gradients folded in reverse shard order; results
+ * match the unsplit path up to rounding order.
  *
  *   q, k, v, raw_gate, raw_beta, scale, A_log, dt_bias, lower_bound,
  *   initial_state, cu_seqlens, B, T, H, K, V, N   exactly as for kda_fwd

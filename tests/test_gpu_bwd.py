@@ -257,8 +257,27 @@ def test_bwd_initial_state_gradient_in_place():
 
 def test_bwd_long_sequence_with_few_heads_checkpoints_on_shards():
     """T = 8192 with 2 heads: the checkpointing forward pass runs on 4 shards per sequence
-    from their folded entering states (lower_bound -0.01, so the state carries across
+    from their folded entering states, and the reverse recurrence on the same shards from
+    their folded leaving gradients (lower_bound -0.01, so state and gradient carry across
     shards); the gradients still match the chunked fp64 oracle."""
     x = W.random_inputs("bwd_split", 231, 1, 8192, 2, lower_bound=-0.01)
     d_out, d_fin = cotangents(x, 232)
     compare(gpu_bwd(x, d_out, d_fin), oracle(x, d_out, d_fin, chunked=True))
+
+
+def test_bwd_two_long_sequences_fold_each_on_its_own_shards():
+    """Two sequences of 8192 tokens, one head: 4 shards each, both folds (forward states and
+    reverse gradients) per sequence, with the slowest decay (lower_bound -0.002) so that a
+    shard's gradient reaches far back; every gradient matches the chunked fp64 oracle."""
+    x = W.random_inputs("bwd_split2", 233, 2, 8192, 1, lower_bound=-0.002)
+    d_out, d_fin = cotangents(x, 234)
+    compare(gpu_bwd(x, d_out, d_fin), oracle(x, d_out, d_fin, chunked=True))
+
+
+def test_bwd_split_ragged_tail_without_state_gradients():
+    """T = 8229 (a 37-token tail in the last of 4 shards) with no final-state gradient and
+    no d_initial_state requested: the reverse fold starts from zero and writes nothing for
+    the initial state, and the gradients still match the chunked fp64 oracle."""
+    x = W.random_inputs("bwd_split_tail", 235, 1, 8229, 2, lower_bound=-0.01)
+    d_out, _ = cotangents(x, 236, with_final=False)
+    compare(gpu_bwd(x, d_out, None, with_dinit=False), oracle(x, d_out, None, chunked=True))
