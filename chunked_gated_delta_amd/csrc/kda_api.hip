@@ -52,18 +52,33 @@ __global__ void __launch_bounds__(1024) kda_chunk_offsets_kernel(const int32_t* 
   if (tid == 0) choff[N] = carry;
 }
 
-// Shard offsets of a split forward: N sequences of T tokens (nc chunks) cut
-// into S shards of cs chunks; shard i = n S + s starts at token n T + s cs 64
-// and at global chunk n nc + s cs (the intra kernel's numbering).
-__global__ void kda_shard_map_kernel(int32_t* __restrict__ scu, int32_t* __restrict__ schoff, int N, int S,
-                                     int T, int nc, int cs) {
+// Shard offsets of a split forward, shard i = n S + s of sequence n.
+// Without cu: N sequences of T tokens (nc chunks) cut into S shards of cs
+// chunks; shard i starts at token n T + s cs 64 and at global chunk
+// n nc + s cs (the intra kernel's numbering).  With cu (and the chunk
+// offsets choff of the intra kernel's varlen numbering): sequence n of
+// nc_n chunks is cut into S shards of ceil(nc_n / S) chunks, the last ones
+// shorter or empty.
+__global__ void kda_shard_map_kernel(int32_t* __restrict__ scu, int32_t* __restrict__ schoff,
+                                     const int32_t* __restrict__ cu, const int32_t* __restrict__ choff, int N,
+                                     int S, int T, int nc, int cs) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int ns = N * S;
   if (i > ns) return;
   const int n = i < ns ? i / S : N;
   const int sh = i < ns ? i - n * S : 0;
-  scu[i] = n * T + sh * cs * CH;
-  schoff[i] = n * nc + sh * cs;
+  if (cu) {
+    const int bos = cu[n];
+    const int len = i < ns ? cu[n + 1] - bos : 0;
+    const int ncn = (len + CH - 1) / CH;
+    const int csn = (ncn + S - 1) / S;
+    const int c = sh * csn < ncn ? sh * csn : ncn;
+    scu[i] = bos + (c < ncn ? c * CH : len);
+    schoff[i] = choff[n] + c;
+  } else {
+    scu[i] = n * T + sh * cs * CH;
+    schoff[i] = n * nc + sh * cs;
+  }
 }
 
 // Zeroes the intra kernel's work-item counter (a kernel rather than a memset,
@@ -238,16 +253,20 @@ InterArgs inter_args(const Prepared& pr, int64_t H) {
 // the shard map reuses them as they are.  `m2` receives the shard map.
 kda_status_t shard_states(const Prepared& pr, const void* v, const float* initial_state, float* final_state,
                           int64_t T, int64_t H, int64_t N, hipStream_t st, ChunkMap& m2) {
-  const SplitPlan sp = split_plan(T, H, N);
+  // varlen calls take S from the mean length and cut each sequence by its own
+  const SplitPlan sp = pr.map.cu ? SplitPlan{pr.lay.S, 0} : split_plan(T, H, N);
   const int64_t ns = N * sp.S;
-  const int64_t nc = (T + CH - 1) / CH;
+  const int64_t nc = pr.map.cu ? 0 : (T + CH - 1) / CH;
   int32_t* scu = reinterpret_cast<int32_t*>(pr.ws + pr.lay.scu);
   int32_t* schoff = reinterpret_cast<int32_t*>(pr.ws + pr.lay.schoff);
   float* sP = reinterpret_cast<float*>(pr.ws + pr.lay.sP);
   float* sR = reinterpret_cast<float*>(pr.ws + pr.lay.sR);
   float* sstart = reinterpret_cast<float*>(pr.ws + pr.lay.sstart);
+  const int32_t* cu = pr.map.cu;
+  const int32_t* choff = pr.map.choff;
   int n32 = (int)N, s32 = (int)sp.S, t32 = (int)T, nc32 = (int)nc, cs32 = (int)sp.cs;
-  void* margs[] = {(void*)&scu, (void*)&schoff, (void*)&n32, (void*)&s32, (void*)&t32, (void*)&nc32, (void*)&cs32};
+  void* margs[] = {(void*)&scu,  (void*)&schoff, (void*)&cu,   (void*)&choff, (void*)&n32,
+                   (void*)&s32,  (void*)&t32,    (void*)&nc32, (void*)&cs32};
   if (launch_status(hipLaunchKernel(reinterpret_cast<const void*>(&kda_shard_map_kernel),
                                     dim3((unsigned)((ns + 1 + 255) / 256)), dim3(256), margs, 0, st),
                     "shard map") != KDA_SUCCESS)
@@ -318,7 +337,7 @@ kda_status_t kda_fwd_ex(const void* q, const void* k, const void* v, const void*
   const kda_status_t s = prepare(q, k, raw_gate, raw_beta, workspace, workspace_bytes, A_log, dt_bias,
                                  lower_bound, cu_seqlens, B, T, H, K, V, N, st, pr, flags);
   if (s != KDA_SUCCESS) return s;
-  const bool split = use_split(pr, cu_seqlens, flags, B, T) && !(initial_state && initial_state == final_state);
+  const bool split = use_split(pr, flags, B, T) && !(initial_state && initial_state == final_state);
   if (split) return split_forward(pr, v, out, initial_state, final_state, scale, T, H, N, st);
   InterArgs xa = inter_args(pr, H);
   xa.v = static_cast<const uint16_t*>(v);

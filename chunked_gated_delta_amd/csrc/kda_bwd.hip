@@ -1456,7 +1456,7 @@ kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void*
   xa.v = static_cast<const uint16_t*>(v);
   xa.init = initial_state;
   xa.state_vk = (flags & FLAG_STATE_VK) ? 1 : 0;
-  const bool split = use_split(pr, cu_seqlens, flags, B, T);
+  const bool split = use_split(pr, flags, B, T);
   ChunkMap m2;
   if (split) {
     const kda_status_t ss = shard_states(pr, v, initial_state, nullptr, T, H, N, st, m2);
@@ -1512,7 +1512,7 @@ kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void*
   if (split) {
     sh.m2 = m2;
     sh.N = N;
-    sh.S = split_plan(T, H, N).S;
+    sh.S = pr.lay.S;
     sh.P = reinterpret_cast<const float*>(pr.ws + pr.lay.sP);
     sh.b = reinterpret_cast<float*>(pr.ws + pr.lay.sR);
     sh.ends = reinterpret_cast<float*>(pr.ws + pr.lay.sfin);

@@ -40,8 +40,8 @@ struct Layout {
   size_t scu, schoff, sP, sR, sstart, sfin;
 };
 
-// T_total / N is the per-sequence length the split plan assumes; calls with
-// cu_seqlens never split and need only the first areas.
+// T_total / N is the per-sequence length the split plan assumes (the mean
+// length of a varlen call, whose shards follow each sequence's own length).
 inline Layout workspace_layout(int64_t T_total, int64_t H, int64_t N) {
   Layout l;
   l.claim = 0;  // the intra kernel's work-item counter (one int)
@@ -86,11 +86,11 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
 // Inter-chunk arguments for the prepared call (no v, outputs or states set).
 InterArgs inter_args(const Prepared& pr, int64_t H);
 
-// Whether a prepared call runs its recurrence on shards (split_plan): only
-// without cu_seqlens, with the [K][V] state layout and a token count that fits
-// the int32 shard offsets.
-inline bool use_split(const Prepared& pr, const int32_t* cu_seqlens, unsigned flags, int64_t B, int64_t T) {
-  return pr.lay.S > 1 && !cu_seqlens && !(flags & FLAG_STATE_VK) && T > 0 && B * T < ((int64_t)1 << 31);
+// Whether a prepared call runs its recurrence on shards (split_plan of the
+// mean sequence length): only with the [K][V] state layout and a token count
+// that fits the int32 shard offsets.
+inline bool use_split(const Prepared& pr, unsigned flags, int64_t B, int64_t T) {
+  return pr.lay.S > 1 && !(flags & FLAG_STATE_VK) && T > 0 && B * T < ((int64_t)1 << 31);
 }
 
 // Inter-chunk arguments over the shard map m2 (no v, outputs or states set).

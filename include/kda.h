@@ -94,10 +94,12 @@ int kda_is_supported(int64_t K, int64_t V, float lower_bound);
  *   B, T, H, K, V, N sizes as above (T >= 0; B, H, N >= 1)
  *   stream      hipStream_t as void*
  *
- * With few (sequence, head) pairs and long sequences (no cu_seqlens, states
- * not in place), the call runs its recurrence on shards of each sequence and
- * folds their affine maps (the kda_shard_affine / kda_shard_scan algebra) to
- * shorten the sequential chain; kda_workspace_size already covers it.
+ * With few (sequence, head) pairs and long sequences (states not in place, not
+ * KDA_FLAG_STATE_VK), the call runs its recurrence on shards of each sequence
+ * and folds their affine maps (the kda_shard_affine / kda_shard_scan algebra)
+ * to shorten the sequential chain.  The shard count follows the mean length
+ * T_total / N; with cu_seqlens each sequence is cut by its own length.
+ * kda_workspace_size already covers it.
  *
  * Returns KDA_SUCCESS after enqueueing the work, or an error status.
  */

@@ -281,3 +281,13 @@ def test_bwd_split_ragged_tail_without_state_gradients():
     x = W.random_inputs("bwd_split_tail", 235, 1, 8229, 2, lower_bound=-0.01)
     d_out, _ = cotangents(x, 236, with_final=False)
     compare(gpu_bwd(x, d_out, None, with_dinit=False), oracle(x, d_out, None, chunked=True))
+
+
+def test_bwd_varlen_long_sequences_on_shards():
+    """Two packed sequences of 9000 and 7500 tokens, 2 heads: the mean length gives 4 shards
+    per sequence, each cut by its own length; both recurrences run on them and every
+    gradient matches the chunked fp64 oracle."""
+    lengths = [9000, 7500]
+    x = W.random_inputs("bwd_split_varlen", 237, 1, sum(lengths), 2, lengths=lengths, lower_bound=-0.01)
+    d_out, d_fin = cotangents(x, 238)
+    compare(gpu_bwd(x, d_out, d_fin), oracle(x, d_out, d_fin, chunked=True))

@@ -317,3 +317,18 @@ def test_long_sequences_with_few_heads_run_on_shards(B, T, H, init, lb):
     if init:
         o2, f2 = run_gpu(x, in_place=True)
         check(o2, f2, ro, rf, x.name + " (in place, unsplit)")
+
+
+@pytest.mark.parametrize("lengths,H,lb", [([12000, 5000], 2, -0.01), ([33000, 0, 100, 64], 1, -0.002)])
+def test_varlen_long_sequences_run_on_shards_of_their_own_length(lengths, H, lb):
+    """Packed sequences whose mean length calls for 4 shards: each sequence is cut into 4
+    shards of its own length (47 and 20 chunks; 0, 1 and 1 chunks, so empty shards and an
+    empty sequence too), the folds carry the state across them, and the outputs and final
+    states match the oracle and the unsplit in-place path."""
+    x = W.random_inputs(f"split_varlen_{len(lengths)}_H{H}", 900 + len(lengths), 1, sum(lengths), H,
+                        lengths=lengths, init_std=0.1, lower_bound=lb)
+    o, f = run_gpu(x)
+    ro, rf = oracle(x)
+    check(o, f, ro, rf, x.name + " (shards)")
+    o2, f2 = run_gpu(x, in_place=True)
+    check(o2, f2, ro, rf, x.name + " (in place, unsplit)")
