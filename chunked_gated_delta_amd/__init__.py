@@ -4,7 +4,8 @@ Argument marshalling only: every step of the forward pass runs in the HIP
 kernels behind the C ABI of include/kda.h.  The names mirror that header:
 ``kda_fwd``, ``kda_workspace_size``, ``kda_is_supported``, ``kda_shard_affine``,
 ``kda_shard_scan``, ``kda_decode``, ``kda_fwd_ex`` (with the ``FLAG_*`` variant bits),
-``kda_bwd``, ``kda_bwd_ex`` and ``kda_bwd_workspace_size``.  PyTorch provides
+``kda_bwd``, ``kda_bwd_ex``, ``kda_bwd_workspace_size`` and
+``kda_workspace_faults`` (with the ``FAULT_*`` bits).  PyTorch provides
 device memory and the current stream; there is no CPU or PyTorch fallback, and
 importing this module fails if the library has not been built.
 """
@@ -21,7 +22,8 @@ import os
 import torch  # noqa: F401
 
 __all__ = ["kda_fwd", "kda_fwd_ex", "kda_workspace_size", "kda_is_supported", "kda_shard_affine",
-           "kda_shard_scan", "kda_decode", "kda_bwd", "kda_bwd_ex", "kda_bwd_workspace_size", "KdaError", "STATUS", "library_path", "exported_symbols",
+           "kda_shard_scan", "kda_decode", "kda_bwd", "kda_bwd_ex", "kda_bwd_workspace_size",
+           "kda_workspace_faults", "FAULT_WAIT_TIMEOUT", "FAULT_GATE_RANGE", "FAULT_QK_NORM", "KdaError", "STATUS", "library_path", "exported_symbols",
            "FLAG_GATE_GIVEN", "FLAG_BETA_GIVEN", "FLAG_NO_QK_NORM", "FLAG_STATE_VK", "FLAG_REUSE_RECORDS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,11 +33,13 @@ STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERR_INVALID", 2: "KDA_ERR_UNSUPPORTED",
           3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_LAUNCH"}
 exported_symbols = ("kda_fwd", "kda_workspace_size", "kda_is_supported", "kda_status_string",
                     "kda_shard_affine", "kda_shard_scan", "kda_decode", "kda_fwd_ex", "kda_bwd",
-                    "kda_bwd_ex", "kda_bwd_workspace_size")
+                    "kda_bwd_ex", "kda_bwd_workspace_size", "kda_workspace_faults")
 # kda_fwd_ex variant bits (KDA_FLAG_* in include/kda.h)
 FLAG_GATE_GIVEN, FLAG_BETA_GIVEN, FLAG_NO_QK_NORM, FLAG_STATE_VK = 1, 2, 4, 8
 # kda_fwd_ex, kda_bwd_ex: reuse the chunk records the previous call left in the workspace
 FLAG_REUSE_RECORDS = 16
+# fault-word bits (KDA_FAULT_* in include/kda.h), read by kda_workspace_faults
+FAULT_WAIT_TIMEOUT, FAULT_GATE_RANGE, FAULT_QK_NORM = 1, 2, 4
 
 
 class KdaError(RuntimeError):
@@ -80,6 +84,8 @@ _lib.kda_bwd.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P,
 _lib.kda_bwd.restype = ctypes.c_int
 _lib.kda_bwd_ex.argtypes = _lib.kda_bwd.argtypes[:-1] + [ctypes.c_uint, _P]
 _lib.kda_bwd_ex.restype = ctypes.c_int
+_lib.kda_workspace_faults.argtypes = [_P, ctypes.POINTER(ctypes.c_uint32), _P]
+_lib.kda_workspace_faults.restype = ctypes.c_int
 
 
 def kda_workspace_size(T: int, H: int, N: int) -> int:
@@ -268,6 +274,16 @@ def kda_bwd_ex(q, k, v, raw_gate, raw_beta, scale, d_out, dq, dk, dv, d_raw_gate
                          int(flags), _stream(stream, q.device))
     if rc != 0:
         raise KdaError(rc, _name)
+
+
+def kda_workspace_faults(workspace, stream=None) -> int:
+    """The fault word (an OR of the FAULT_* bits) of the last call on ``workspace``,
+    read after the work enqueued on ``stream`` has finished (this synchronises it)."""
+    word = ctypes.c_uint32(0)
+    rc = _lib.kda_workspace_faults(_ptr(workspace), ctypes.byref(word), _stream(stream, workspace.device))
+    if rc != 0:
+        raise KdaError(rc, "kda_workspace_faults")
+    return int(word.value)
 
 
 def raw_call(*args):

@@ -17,7 +17,8 @@ namespace {
 constexpr int kMaxSortN = 16384;
 
 // choff[n] = sum_{m<n} ceil(len_m / 64), choff[N] = total chunks (one block).
-// Also zeroes the intra kernel's work-item counter.
+// Also zeroes the intra kernel's work-item counter and the call's fault word
+// (claim[0], claim[1]).
 __global__ void __launch_bounds__(1024) kda_chunk_offsets_kernel(const int32_t* __restrict__ cu, int N,
                                                                  int32_t* __restrict__ choff,
                                                                  int32_t* __restrict__ claim) {
@@ -28,7 +29,8 @@ __global__ void __launch_bounds__(1024) kda_chunk_offsets_kernel(const int32_t* 
   const int wv = tid >> 6;
   if (tid == 0) {
     carry = 0;
-    *claim = 0;
+    claim[0] = 0;
+    claim[1] = 0;
   }
   __syncthreads();
   for (int base = 0; base < N; base += 1024) {
@@ -81,9 +83,13 @@ __global__ void kda_shard_map_kernel(int32_t* __restrict__ scu, int32_t* __restr
   }
 }
 
-// Zeroes the intra kernel's work-item counter (a kernel rather than a memset,
-// so that a captured graph replays it as a kernel node).
-__global__ void kda_zero_claim_kernel(int32_t* __restrict__ claim) { *claim = 0; }
+// Zeroes the intra kernel's work-item counter and the call's fault word (a
+// kernel rather than a memset, so that a captured graph replays it as a
+// kernel node).
+__global__ void kda_zero_claim_kernel(int32_t* __restrict__ claim) {
+  claim[0] = 0;
+  claim[1] = 0;
+}
 
 // Longest-first processing order of the sequences: rank of sequence i = number
 // of sequences that are longer, or equally long with a smaller index.
@@ -118,11 +124,23 @@ extern "C" {
 
 size_t kda_workspace_size(int64_t T_total, int64_t H, int64_t N) {
   if (T_total < 0 || H < 1 || N < 1) return 0;
-  return workspace_layout(T_total, H, N).total;
+  return workspace_bound(T_total, H, N);
 }
 
 int kda_is_supported(int64_t K, int64_t V, float lower_bound) {
   return K == KD && V == VD && lower_bound >= -5.0f && lower_bound <= 0.0f;
+}
+
+kda_status_t kda_workspace_faults(const void* workspace, uint32_t* faults, void* stream) {
+  if (!workspace || !faults) return KDA_ERR_INVALID;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint32_t word = 0;
+  hipError_t e = hipMemcpyAsync(&word, static_cast<const char*>(workspace) + workspace_layout(0, 1, 1).faults,
+                                sizeof word, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return launch_status(e, "fault word copy");
+  *faults = word;
+  return KDA_SUCCESS;
 }
 
 const char* kda_status_string(kda_status_t s) {
@@ -210,10 +228,12 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
   ia.dt_bias = dt_bias ? dt_bias : reinterpret_cast<const float*>(pr.rec);
   ia.flags = (int)(flags & (FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM));
   ia.claim = claim;
+  ia.faults = reinterpret_cast<unsigned*>(pr.ws + pr.lay.faults);
   ia.rec = pr.rec;
   ia.map = pr.map;
   ia.H = (int)H;
   ia.lb2 = lower_bound * LOG2E;
+  ia.lb = lower_bound;
   ia.timers = nullptr;
 #ifdef KDA_PHASE_TIMERS
   // timer builds only: the caller extends the workspace by 16 counters per

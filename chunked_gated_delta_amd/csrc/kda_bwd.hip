@@ -1423,7 +1423,16 @@ extern "C" {
 
 size_t kda_bwd_workspace_size(int64_t T_total, int64_t H, int64_t N) {
   if (T_total < 0 || H < 1 || N < 1) return 0;
-  return bwd_layout(T_total, H, N).total;
+  // the largest layout of any call with N' <= N sequences: only N' with
+  // N' H <= kSplitChains / kMinShards can split (which moves the later areas
+  // up by a shard area), and above those the layout grows with N'
+  size_t best = bwd_layout(T_total, H, N).total;
+  const int64_t top = N < kSplitChains / kMinShards ? N : kSplitChains / kMinShards;
+  for (int64_t n = 1; n <= top; ++n) {
+    const size_t t = bwd_layout(T_total, H, n).total;
+    if (t > best) best = t;
+  }
+  return best;
 }
 
 kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void* raw_gate,

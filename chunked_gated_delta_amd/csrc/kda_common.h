@@ -172,6 +172,13 @@ constexpr int FLAG_NO_QK_NORM = 4;   // q, k used without L2 normalisation
 constexpr int FLAG_STATE_VK = 8;     // states stored transposed, [N, H, V, K]
 constexpr int FLAG_REUSE_RECORDS = 16;  // the workspace already holds this call's chunk records
 
+// Fault bits a call ORs into the workspace's fault word (same values as the
+// KDA_FAULT_* constants of the C ABI): conditions the kernels detect on the
+// device, where no status can be returned.
+constexpr unsigned FAULT_WAIT_TIMEOUT = 1u;  // a bounded wait gave up; results are invalid
+constexpr unsigned FAULT_GATE_RANGE = 2u;    // FLAG_GATE_GIVEN: a decay outside [lower_bound, 0]
+constexpr unsigned FAULT_QK_NORM = 4u;       // FLAG_NO_QK_NORM: a q or k row with |x|^2 > 1 + 1/16
+
 // Host-side launchers (defined next to their kernels).
 struct IntraArgs {
   const uint16_t* q;
@@ -184,8 +191,10 @@ struct IntraArgs {
   ChunkMap map;
   int H;
   float lb2;        // lower_bound * log2(e)
+  float lb;         // lower_bound
   int flags;        // FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM
   int* claim;       // work-item counter, zero when the kernel starts
+  unsigned* faults; // the call's fault word (FAULT_* bits)
   unsigned long long* timers;  // phase timers (KDA_PHASE_TIMERS builds only), else nullptr
 };
 struct InterArgs {

@@ -33,7 +33,7 @@ inline SplitPlan split_plan(int64_t T, int64_t H, int64_t N) {
 }
 
 struct Layout {
-  size_t claim, choff, order, rec, total;
+  size_t claim, faults, choff, order, rec, base, total;  // base: end of the records
   // shard areas (split forwards only): shard offsets in tokens and in chunks
   // [N S + 1], and the per-shard P, R, entering and final states
   int64_t S;
@@ -44,12 +44,14 @@ struct Layout {
 // length of a varlen call, whose shards follow each sequence's own length).
 inline Layout workspace_layout(int64_t T_total, int64_t H, int64_t N) {
   Layout l;
-  l.claim = 0;  // the intra kernel's work-item counter (one int)
+  l.claim = 0;   // the intra kernel's work-item counter (one int)
+  l.faults = 4;  // the call's fault word (FAULT_* bits)
   l.choff = 256;
   l.order = l.choff + align256((size_t)(N + 1) * sizeof(int32_t));
   l.rec = l.order + align256((size_t)N * sizeof(int32_t));
   const size_t max_chunks = (size_t)(T_total / CH) + (size_t)N;
   l.total = l.rec + max_chunks * (size_t)H * REC_BYTES;
+  l.base = l.total;
   l.S = N > 0 ? split_plan(T_total / N, H, N).S : 1;
   l.scu = l.schoff = l.sP = l.sR = l.sstart = l.sfin = l.total;
   if (l.S > 1) {
@@ -63,6 +65,25 @@ inline Layout workspace_layout(int64_t T_total, int64_t H, int64_t N) {
     l.total = l.sfin + st;
   }
   return l;
+}
+
+// The workspace size reported to callers: the largest layout of any call
+// with N' <= N sequences over the same T_total tokens, so that one size bought
+// for an upper bound on the batch serves every smaller one.  The base part
+// (records and tables) grows with N; the shard area does not (it follows the
+// mean length), but only N' H <= kSplitChains / kMinShards chains can split,
+// so the maximum of the shard area runs over at most 32 values of N'.
+inline size_t workspace_bound(int64_t T_total, int64_t H, int64_t N) {
+  const Layout l = workspace_layout(T_total, H, N);
+  size_t shards = 0;
+  const int64_t top = N < kSplitChains / kMinShards ? N : kSplitChains / kMinShards;
+  for (int64_t n = 1; n <= top; ++n) {
+    const Layout m = workspace_layout(T_total, H, n);
+    const size_t a = m.total - m.base;
+    if (a > shards) shards = a;
+  }
+  const size_t bound = l.base + shards;
+  return bound > l.total ? bound : l.total;
 }
 
 // What the intra-chunk pass of one call leaves for the inter-chunk passes.

@@ -296,12 +296,27 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   ssk += xor_lane(ssk, 16);
   ssk += xor_lane(ssk, 32);
   const bool qk_norm = !(a.flags & FLAG_NO_QK_NORM);
+  // without the in-kernel norm the caller keeps |q|, |k| <= 1 (the fp16
+  // operands assume unit scale); a row beyond that is recorded, not rejected
+  if (!qk_norm && __any(valid && (ssq > 1.0625f || ssk > 1.0625f)) && lane == 0)
+    atomicOr(a.faults, FAULT_QK_NORM);
   const float rq = valid ? (qk_norm ? __builtin_amdgcn_rsqf(ssq + L2_EPS) : 1.0f) : 0.0f;
   const float rk = valid ? (qk_norm ? __builtin_amdgcn_rsqf(ssk + L2_EPS) : 1.0f) : 0.0f;
   const float braw = __uint_as_float((uint32_t)braw16 << 16);
   const float beta =
       valid ? ((a.flags & FLAG_BETA_GIVEN) ? braw : __builtin_amdgcn_rcpf(1.0f + fexp2(-braw * LOG2E))) : 0.0f;
 
+  // a given decay outside [lower_bound, 0] is outside the call's contract: it
+  // is recorded in the fault word (and saturated below, so every decay ratio
+  // stays in range)
+  if constexpr (GATE_GIVEN) {
+    bool bad = false;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bad |= !(gl[kb][e] >= a.lb && gl[kb][e] <= 0.0f);
+    if (__any(valid && bad) && lane == 0) atomicOr(a.faults, FAULT_GATE_RANGE);
+  }
   // log-decay in log2 units, inclusive scan over the sub-chunk's 16 tokens
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -421,10 +436,15 @@ __global__ void __launch_bounds__(NTHREADS, 2)
 
   // Wait until tag `t` holds this item (release/acquire on the LDS tag word).
   // Tags 0-3 and 5 are published with no wait before them, and tag 6 only
-  // after tag 5, so every wait ends; the spin is bounded all the same.
+  // after tag 5, so every wait ends; the spin is bounded all the same, and a
+  // wait that gives up marks the call's results invalid in the fault word.
   auto wait_tag = [&](int t) {
-    for (int spin = 0; spin < (1 << 22); ++spin) {
+    for (int spin = 0;; ++spin) {
       if (__hip_atomic_load(&sFlag[t], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == item) break;
+      if (spin == (1 << 22)) {
+        if (lane == 0) atomicOr(a.faults, FAULT_WAIT_TIMEOUT);
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
   };

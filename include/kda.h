@@ -187,14 +187,20 @@ kda_status_t kda_decode(const void* q, const void* k, const void* v, const void*
  * Variants of kda_fwd (kda_fwd_ex `flags`), the in-kernel switches of the
  * chunk_kda call on the instagit FlashKDA page ("Usage Examples"):
  *   KDA_FLAG_GATE_GIVEN  (use_gate_in_kernel off) raw_gate already holds the
- *       natural-log decay g, bf16; values are clamped to [lower_bound, 0]
- *       (lower_bound keeps its [-5, 0] range and role as the decay floor).
+ *       natural-log decay g, bf16.  Every g must lie in [lower_bound, 0]: the
+ *       range the in-kernel gate maps into, which the page's chunk_kda call
+ *       bounds with safe_gate=True and lower_bound.  That is the caller's
+ *       contract (checking it on the host would need the data): a value
+ *       outside it sets KDA_FAULT_GATE_RANGE in the workspace's fault word
+ *       (kda_workspace_faults), and the results are then unspecified.
  *       A_log and dt_bias are unused and may be NULL.
  *   KDA_FLAG_BETA_GIVEN  (use_beta_sigmoid_in_kernel off) raw_beta already
  *       holds beta; keep it in [0, 1] for the documented accuracy.
  *   KDA_FLAG_NO_QK_NORM  (use_qk_l2norm_in_kernel off) q and k are used as
  *       given; the caller keeps |k|, |q| <= 1 (the rule is only stable for
  *       beta |k|^2 <= 2, and the kernel's fp16 operands assume unit scale).
+ *       A row with |q|^2 or |k|^2 above 1 + 1/16 sets KDA_FAULT_QK_NORM in
+ *       the fault word; the call still runs, at unspecified accuracy.
  *   KDA_FLAG_STATE_VK    (transpose_state_layout) initial_state and
  *       final_state are stored transposed, [N, H, V, K]: S[k][v] at v*K + k.
  */
@@ -281,8 +287,8 @@ kda_status_t kda_bwd(const void* q, const void* k, const void* v, const void* ra
  * kda_bwd for the variants of kda_fwd_ex (any OR of the KDA_FLAG_* bits; other
  * bits give KDA_ERR_INVALID): the gradients of the kda_fwd_ex call with the
  * same inputs and flags.  With KDA_FLAG_GATE_GIVEN, d_raw_gate is the gradient
- * with respect to the given decay, passed where raw_gate lies in
- * [lower_bound, 0] and zero where the clamp is active; A_log and dt_bias are
+ * with respect to the given decay (which must lie in [lower_bound, 0], as for
+ * kda_fwd_ex); A_log and dt_bias are
  * unused and may be NULL, and dA_log, d_dt_bias may be NULL (else zero-filled).
  * With KDA_FLAG_BETA_GIVEN, d_raw_beta is the gradient with respect to beta;
  * with KDA_FLAG_NO_QK_NORM, dq and dk are those of the unnormalised q, k; with
@@ -300,6 +306,30 @@ kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void*
                         const float* A_log, const float* dt_bias, float lower_bound,
                         const float* initial_state, const int32_t* cu_seqlens, int64_t B, int64_t T,
                         int64_t H, int64_t K, int64_t V, int64_t N, unsigned flags, void* stream);
+
+/*
+ * Faults the kernels of a kda_fwd / kda_fwd_ex / kda_shard_affine / kda_bwd /
+ * kda_bwd_ex call detect on the device, where no status can be returned.
+ * Each such call clears the fault word of its workspace when it starts and
+ * ORs these bits into it:
+ *   KDA_FAULT_WAIT_TIMEOUT  a bounded wait between waves gave up: the call's
+ *                           results are invalid
+ *   KDA_FAULT_GATE_RANGE    KDA_FLAG_GATE_GIVEN with a decay outside
+ *                           [lower_bound, 0]
+ *   KDA_FAULT_QK_NORM       KDA_FLAG_NO_QK_NORM with |q|^2 or |k|^2 > 1 + 1/16
+ */
+#define KDA_FAULT_WAIT_TIMEOUT 1u
+#define KDA_FAULT_GATE_RANGE 2u
+#define KDA_FAULT_QK_NORM 4u
+
+/*
+ * Read the fault word of the last call on `workspace` (a device buffer passed
+ * to one of the calls above) into *faults, after the work already enqueued on
+ * `stream` (hipStream_t as void*) has finished: unlike every other entry
+ * point, this one synchronises the stream.  Returns KDA_ERR_INVALID for NULL
+ * arguments, KDA_ERR_LAUNCH if the copy fails, else KDA_SUCCESS.
+ */
+kda_status_t kda_workspace_faults(const void* workspace, uint32_t* faults, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* kda_status_string(kda_status_t status);

@@ -43,7 +43,8 @@ def brute_fwd(q, k, v, raw_gate, raw_beta, scale, A_log, dt_bias, lower_bound,
               beta_given=False, no_qk_norm=False):
     """One sequence (B=1), one head.  Returns (out [T][V], final [K][V]) as Decimals.
 
-    gate_given: raw_gate is the log-decay g itself (clamped to [lower_bound, 0]);
+    gate_given: raw_gate is the log-decay g itself, which must lie in [lower_bound, 0]
+    (other values raise ValueError);
     beta_given: raw_beta is beta itself; no_qk_norm: q, k are used unnormalised."""
     getcontext().prec = digits
     _, T, H, K = q.shape
@@ -63,15 +64,17 @@ def brute_fwd(q, k, v, raw_gate, raw_beta, scale, A_log, dt_bias, lower_bound,
         r = Decimal(1) / (sum((x * x for x in xs), Decimal(0)) + EPS).sqrt()
         return [x * r for x in xs]
 
-    def clamp_gate(x):
-        return lb if x < lb else (Decimal(0) if x > 0 else x)
+    def given_gate(x):
+        if x < lb or x > 0:
+            raise ValueError("given gate outside [lower_bound, 0]")
+        return x
 
     qn = [norm(qf[t]) for t in range(T)]
     kn = [norm(kf[t]) for t in range(T)]
     beta = [_dec(bf[t]) if beta_given else _sig(_dec(bf[t])) for t in range(T)]
     gm = al.exp()
     if gate_given:
-        alpha = [[clamp_gate(_dec(gf[t, c])).exp() for c in range(K)] for t in range(T)]
+        alpha = [[given_gate(_dec(gf[t, c])).exp() for c in range(K)] for t in range(T)]
     else:
         alpha = [[(lb * _sig(gm * (_dec(gf[t, c]) + dt[c]))).exp() for c in range(K)]
                  for t in range(T)]

@@ -33,8 +33,8 @@ def fwd_torch(q, k, v, raw_gate, raw_beta, scale, A_log, dt_bias, lower_bound, i
     """fp64 token recurrence on fp64 tensors (differentiable).  Shapes as oracle_fwd:
     q, k, raw_gate [B, T, H, K]; v [B, T, H, V]; raw_beta [B, T, H]; A_log [H]; dt_bias [H, K];
     initial_state [N, H, K, V] ([N, H, V, K] with STATE_VK) or None.  ``flags`` are the variant
-    switches of oracle_fwd: GATE_GIVEN (raw_gate is the natural-log decay, clamped to
-    [lower_bound, 0]), BETA_GIVEN (raw_beta is beta), NO_QK_NORM, STATE_VK (transposed states).
+    switches of oracle_fwd: GATE_GIVEN (raw_gate is the natural-log decay, in
+    [lower_bound, 0]; other values raise ValueError), BETA_GIVEN (raw_beta is beta), NO_QK_NORM, STATE_VK (transposed states).
     Returns (out [B*T, H, V], final [N, H, K, V] or [N, H, V, K])."""
     B, T, H, K = q.shape
     V = v.shape[-1]
@@ -47,6 +47,8 @@ def fwd_torch(q, k, v, raw_gate, raw_beta, scale, A_log, dt_bias, lower_bound, i
         cu = [int(x) for x in cu_seqlens]
         bounds = [(cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
     vk = bool(flags & STATE_VK)
+    if flags & GATE_GIVEN and not bool(((gf >= lower_bound) & (gf <= 0.0)).all()):
+        raise ValueError("given gate outside [lower_bound, 0]")
     a = None if flags & GATE_GIVEN else torch.exp(A_log)[:, None]          # [H, 1]
     outs, fins = [], []
     for n, (s, e) in enumerate(bounds):
@@ -62,7 +64,7 @@ def fwd_torch(q, k, v, raw_gate, raw_beta, scale, A_log, dt_bias, lower_bound, i
                 kh = kf[t] / torch.sqrt((kf[t] * kf[t]).sum(-1, keepdim=True) + EPS)
             beta = bf[t] if flags & BETA_GIVEN else torch.sigmoid(bf[t])            # [H]
             if flags & GATE_GIVEN:
-                alpha = torch.exp(torch.clamp(gf[t], min=lower_bound, max=0.0))
+                alpha = torch.exp(gf[t])
             else:
                 alpha = torch.exp(lower_bound * torch.sigmoid(a * (gf[t] + dt_bias)))   # [H, K]
             S = alpha[:, :, None] * S

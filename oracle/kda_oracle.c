@@ -31,8 +31,12 @@
  *
  * Variants (the chunk_kda flags on the same page, each switching one in-kernel
  * step off), selected by the bits of `flags`:
- *   ORACLE_GATE_GIVEN  raw_gate already holds g (natural-log decay; values are
- *                      clamped to [lower_bound, 0]); A_log, dt_bias unused
+ *   ORACLE_GATE_GIVEN  raw_gate already holds g (natural-log decay), which must
+ *                      lie in [lower_bound, 0]: the range the in-kernel gate
+ *                      maps into, read as the bound that safe_gate=True with
+ *                      lower_bound puts on the decay.  A value outside it is
+ *                      not an input of the method; the call is rejected (-2).
+ *                      A_log, dt_bias unused
  *   ORACLE_BETA_GIVEN  raw_beta already holds beta (no sigmoid)
  *   ORACLE_NO_QK_NORM  q^ = q, k^ = k (no L2 normalisation)
  *   ORACLE_STATE_VK    initial/final states stored transposed, [N, H, V, K]
@@ -87,7 +91,7 @@ int kda_oracle_threads(void) {
  * cu_seqlens int32 [N+1] (host); heads: the n_heads head indices to evaluate.
  * out: fp64 [T_total, n_heads, V]; final_state: fp64 [N, n_heads, K, V] (may be NULL).
  * n_threads <= 0 keeps the OpenMP default; flags: ORACLE_* bits above.
- * Returns 0, or -1 on bad sizes.
+ * Returns 0, -1 on bad sizes, or -2 for a given gate outside [lower_bound, 0].
  */
 int kda_oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                    const uint16_t* raw_gate, const uint16_t* raw_beta, double scale,
@@ -101,6 +105,11 @@ int kda_oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
   for (int64_t i = 0; i < n_heads; ++i)
     if (heads[i] < 0 || heads[i] >= H) return -1;
+  if (flags & ORACLE_GATE_GIVEN)
+    for (int64_t i = 0; i < T_total * H * K; ++i) {
+      const double g = widen_bf16(raw_gate[i]);
+      if (!(g >= lower_bound && g <= 0.0)) return -2;
+    }
 #ifdef _OPENMP
   /* the thread count applies to this call only (no process-wide OpenMP setting) */
   const int nt = n_threads > 0 ? n_threads : omp_get_max_threads();
@@ -139,7 +148,7 @@ int kda_oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
           double rg = widen_bf16(raw_gate[th * K + c]);
           double g;
           if (flags & ORACLE_GATE_GIVEN)
-            g = rg < lower_bound ? lower_bound : (rg > 0.0 ? 0.0 : rg);
+            g = rg; /* checked above to lie in [lower_bound, 0] */
           else
             g = lower_bound * sigmoid(gate_mul * (rg + (double)dt_bias[h * K + c]));
           alpha[c] = exp(g);

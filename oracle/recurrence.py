@@ -67,8 +67,8 @@ def oracle_fwd(q, k, v, raw_gate, raw_beta, scale, A_log, dt_bias, lower_bound,
                want_final: bool = True, flags: int = 0):
     """Run the fp64 recurrence.
 
-    flags: GATE_GIVEN (raw_gate holds the log-decay g, clamped to
-    [lower_bound, 0]), BETA_GIVEN (raw_beta holds beta), NO_QK_NORM (no L2
+    flags: GATE_GIVEN (raw_gate holds the log-decay g, which must lie in
+    [lower_bound, 0]; other values raise ValueError), BETA_GIVEN (raw_beta holds beta), NO_QK_NORM (no L2
     norm of q, k), STATE_VK (states stored transposed, [N, H, V, K]).
 
     q, k, raw_gate: bf16 [B, T, H, K]; v: bf16 [B, T, H, V]; raw_beta: bf16 [B, T, H];
@@ -101,15 +101,25 @@ def oracle_fwd(q, k, v, raw_gate, raw_beta, scale, A_log, dt_bias, lower_bound,
                                ptr(al), ptr(dt), float(lower_bound), ptr(init), ptr(cu),
                                N, B * T, H, K, V, ptr(hs), nh, ptr(out), ptr(fin), int(threads),
                                int(flags))
+    if rc == -2:
+        raise ValueError("given gate outside [lower_bound, 0]")
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return out, fin
 
 
 def metrics(x: np.ndarray, ref: np.ndarray) -> dict:
-    """Whole-tensor comparison: rel-L2 = |x-ref|_2/|ref|_2, max-abs, finiteness."""
+    """Whole-tensor comparison of a result x with its reference ref (same shape):
+    rel-L2 = |x-ref|_2/|ref|_2 (|x-ref|_2 itself when ref is all zero), max-abs
+    = max |x-ref|, and whether every element of x is finite.  A shape mismatch
+    or a non-finite reference raises ValueError: no broadcasting, and a broken
+    reference never passes as a comparison."""
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    if x.shape != ref.shape:
+        raise ValueError(f"metrics: shape {x.shape} != reference shape {ref.shape}")
+    if not np.isfinite(ref).all():
+        raise ValueError("metrics: the reference holds non-finite values")
     finite = bool(np.isfinite(x).all())
     d = x - ref
     nref = float(np.linalg.norm(ref.ravel()))

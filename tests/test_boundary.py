@@ -277,3 +277,24 @@ def test_bwd_ex_flag_checks():
     # with the gate given they may be absent: the call then proceeds to the workspace check
     assert bwd_ex_call(kda.FLAG_GATE_GIVEN, A_log=None, dt=None, dA=None, ddt=None) == WORKSPACE
     assert bwd_ex_call(kda.FLAG_STATE_VK | kda.FLAG_NO_QK_NORM) == WORKSPACE
+
+
+def test_fault_word_query_rejects_null_arguments():
+    lib = ctypes.CDLL(kda.library_path)
+    lib.kda_workspace_faults.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32), ctypes.c_void_p]
+    word = ctypes.c_uint32(7)
+    assert lib.kda_workspace_faults(None, ctypes.byref(word), None) == 1
+    assert lib.kda_workspace_faults(FAKE, None, None) == 1
+    assert word.value == 7  # untouched on rejection
+    assert (kda.FAULT_WAIT_TIMEOUT, kda.FAULT_GATE_RANGE, kda.FAULT_QK_NORM) == (1, 2, 4)
+
+
+def test_workspace_sizes_grow_with_the_batch():
+    """A size bought for an upper bound on the sequence count serves every smaller
+    batch over the same tokens: the shard area of a call that splits (few chains)
+    can exceed what more sequences need, so the reported size takes the maximum."""
+    for T, H in ((65536, 1), (262144, 8), (20000, 2), (4096, 12)):
+        fw = [kda.kda_workspace_size(T, H, n) for n in range(1, 41)]
+        bw = [kda.kda_bwd_workspace_size(T, H, n) for n in range(1, 41)]
+        assert all(a <= b for a, b in zip(fw, fw[1:])), (T, H, fw)
+        assert all(a <= b for a, b in zip(bw, bw[1:])), (T, H, bw)

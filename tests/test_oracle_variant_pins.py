@@ -5,7 +5,10 @@ switches named on the instagit FlashKDA page ("Usage Examples").
     agrees with the fp64 recurrence under every flag and all of them at once;
   * the transposed state layout is the same computation with the states
     stored [N, H, V, K]: outputs equal and states transposed, exactly;
-  * a given gate outside [lower_bound, 0] acts as its clamped value.
+  * a given gate is a natural-log decay: the decay factor exp(g) of a given g
+    equals the in-kernel gate's once g holds that gate's value, and a value
+    outside [lower_bound, 0] (no such gate maps there) is rejected by every
+    oracle form.
 """
 
 import numpy as np
@@ -59,16 +62,41 @@ def test_transposed_state_layout_is_a_pure_relayout():
     assert np.array_equal(fin_t.reshape(1, 2, 12, 16), np.swapaxes(fin, -1, -2))
 
 
-def test_given_gate_is_clamped_to_its_range():
-    x = variant_inputs(92, 40, 2, 16, 16, GATE_GIVEN)
-    lo = x.raw_gate.clone()
-    lo[0, ::3] = -8.0   # below lower_bound = -5
-    lo[0, 1::3] = 0.75  # above 0
-    clamped = lo.clone()
-    clamped[0, ::3] = x.lower_bound
-    clamped[0, 1::3] = 0.0
-    a = oracle_fwd(x.q, x.k, x.v, lo, x.raw_beta, x.scale, x.A_log, x.dt_bias, x.lower_bound, x.initial_state,
-                   flags=GATE_GIVEN)
-    b = oracle_fwd(x.q, x.k, x.v, clamped, x.raw_beta, x.scale, x.A_log, x.dt_bias, x.lower_bound,
+def test_given_gate_equals_the_in_kernel_gate_it_stands_for():
+    """A given gate is the natural-log decay g of the same recurrence.  With A_log = 0,
+    dt_bias = 0 and raw_gate in {-100, 0, 100}, the in-kernel gate lower_bound *
+    sigmoid(raw_gate) is, in fp64, 0 to within 2e-43 (so exp(g) == 1.0 exactly),
+    exactly lower_bound / 2, and exactly lower_bound; handing over g in {0,
+    lower_bound / 2, lower_bound} (exact in bf16) must give the same bits, which also
+    shows that both ends of [lower_bound, 0] are accepted."""
+    x = W.random_inputs("variant", 93, 1, 48, 2, K=16, V=16, init_std=0.5)
+    x.A_log = torch.zeros_like(x.A_log)
+    x.dt_bias = torch.zeros_like(x.dt_bias)
+    pick = torch.randint(0, 3, x.raw_gate.shape, generator=torch.Generator().manual_seed(94))
+    raw = torch.tensor([100.0, 0.0, -100.0])[pick].to(torch.bfloat16)
+    given = torch.tensor([x.lower_bound, x.lower_bound / 2, 0.0])[pick].to(torch.bfloat16)
+    assert set(given.double().unique().tolist()) == {x.lower_bound, x.lower_bound / 2, 0.0}
+    a = oracle_fwd(x.q, x.k, x.v, raw, x.raw_beta, x.scale, x.A_log, x.dt_bias, x.lower_bound,
+                   x.initial_state)
+    b = oracle_fwd(x.q, x.k, x.v, given, x.raw_beta, x.scale, x.A_log, x.dt_bias, x.lower_bound,
                    x.initial_state, flags=GATE_GIVEN)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_given_gate_outside_its_range_is_rejected():
+    x = variant_inputs(92, 40, 2, 16, 16, GATE_GIVEN)
+    for bad in (-8.0, 0.75):
+        lo = x.raw_gate.clone()
+        lo[0, 7, 1, 3] = bad
+        with pytest.raises(ValueError):
+            oracle_fwd(x.q, x.k, x.v, lo, x.raw_beta, x.scale, x.A_log, x.dt_bias, x.lower_bound,
+                       x.initial_state, flags=GATE_GIVEN)
+        with pytest.raises(ValueError):
+            brute_fwd(x.q[:, :8], x.k[:, :8], x.v[:, :8], lo[:, :8], x.raw_beta[:, :8], x.scale, x.A_log,
+                      x.dt_bias, x.lower_bound, x.initial_state, head=1, gate_given=True)
+    # the boundary values themselves are inside the range
+    ok = x.raw_gate.clone()
+    ok[0, 0] = x.lower_bound
+    ok[0, 1] = 0.0
+    oracle_fwd(x.q, x.k, x.v, ok, x.raw_beta, x.scale, x.A_log, x.dt_bias, x.lower_bound, x.initial_state,
+               flags=GATE_GIVEN)
