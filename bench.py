@@ -1,20 +1,33 @@
 """Benchmark of the KDA chunked forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3|c2|c4]
 
-One step is one kda_fwd call (every kernel of the forward pass) over the
-throughput headline workload: B=1, T=32768, H=96, K=V=128, bf16 q/k/v/raw_gate
-and raw_beta ~N(0,1), A_log ~U(0, ln 16), dt_bias ~N(0, 0.1), lower_bound -5,
-scale K^-0.5, a zero fp32 initial state, final state written.  Inputs are
-synthetic (seeded, tests/workloads.py) and resident in HBM before timing
-starts.  Prints one JSON line.
+One step is one kda_fwd call (every kernel of the forward pass).  The default
+workload is the throughput headline (--config c3): B=1, T=32768, H=96,
+K=V=128, bf16 q/k/v/raw_gate and raw_beta ~N(0,1), A_log ~U(0, ln 16),
+dt_bias ~N(0, 0.1), lower_bound -5, scale K^-0.5, a zero fp32 initial state,
+final state written.  --config c2 is one tensor-parallel rank's share (B=2,
+T=4096, H=12, initial states ~N(0, 0.1)); --config c4 the packed varlen batch
+(16 sequences of U[1, 8192] tokens, H=32, per-sequence initial states).
+Inputs are synthetic (seeded, tests/workloads.py) and resident in HBM before
+timing starts.  Prints one JSON line.
+
+Timing: W untimed warm-up steps, then K timed steps between two device
+synchronisations (`value` and `ms_per_step` come from that wall clock), each
+launch also bracketed by HIP events on its stream; the roofline uses the
+median of those per-launch event times.  A workload whose inputs and outputs
+fit in the 256 MB Infinity Cache (C2) is run cold: 512 MB are written
+between launches (outside the events), and `value` then comes from the median
+event time.  The loaded shader clock is sampled while the forward runs back to
+back and reported with its fraction of the maximum; a fraction below 0.70
+marks the line (`clock.gate`), since such a row measures the power cap rather
+than the kernel.
 
 Roofline: the forward kernel is HBM-bound.  Its algorithmic traffic is
 1282 bytes per head-token (q, k, v, raw_gate: 4 x 128 x 2 B; raw_beta 2 B;
 out 128 x 2 B) plus 2 x 64 KiB of fp32 state I/O per (sequence, head); the
-achieved rate is that byte count divided by the average device time of one
-forward (its intra-chunk and inter-chunk kernels back to back), measured with
-HIP events recorded on the launch stream around every timed launch.  ``traffic`` is the measured HBM bytes per launch from rocprofv3
+achieved rate is that byte count divided by the median device time of one
+forward.  ``traffic`` is the measured HBM bytes per launch from rocprofv3
 FETCH_SIZE / WRITE_SIZE counters (profiles/), reported only while the kernel
 source is unchanged since the counters were taken.
 
@@ -91,6 +104,27 @@ def cpu_baseline(x, heads):
             "single_core_sample": f"head 0, all {x.T} tokens, one thread ({dt1:.2f} s)"}
 
 
+def cpu_baseline_bwd(x, T_sample, heads):
+    """Time the gradient oracle (fp64 autograd through the token recurrence) on the
+    first T_sample tokens of `heads`: it is orders of magnitude slower than the C
+    recurrence, so the sample is small; the rate is head-tokens of gradients per second."""
+    import torch
+
+    from oracle.grad import oracle_bwd
+
+    sl = lambda t: t[:, :T_sample][:, :, heads].contiguous()  # noqa: E731
+    gen = torch.Generator().manual_seed(9)
+    d_out = torch.randn(1, T_sample, len(heads), x.V, generator=gen).to(torch.bfloat16)
+    t0 = time.perf_counter()
+    oracle_bwd(sl(x.q), sl(x.k), sl(x.v), sl(x.raw_gate), x.raw_beta[:, :T_sample][:, :, heads].contiguous(),
+               x.scale, x.A_log[heads], x.dt_bias[heads], x.lower_bound, d_out)
+    dt = time.perf_counter() - t0
+    ht = T_sample * len(heads)
+    return {"value": ht / dt, "unit": "head-tokens/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"fp64 autograd of the token recurrence, heads {heads}, first {T_sample} tokens "
+                      f"({ht} head-tokens, {dt:.1f} s)"}
+
+
 def copy_calibration(gib: float = 2.0):
     """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
     import torch
@@ -152,7 +186,7 @@ def write_traffic(fwd_fetch, fwd_write, copy_fetch, copy_write, copy_bytes=2 << 
 
 
 def timed(fn, steps, warmup, stream):
-    """Average device time (ms) of fn() over `steps` launches, HIP events on `stream`."""
+    """Median device time (ms) of fn() over `steps` launches, HIP events on `stream`."""
     import torch
 
     for _ in range(warmup):
@@ -164,7 +198,7 @@ def timed(fn, steps, warmup, stream):
         fn()
         b.record(stream)
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / steps
+    return median([a.elapsed_time(b) for a, b in evs])
 
 
 def bench_kcp(args):
@@ -211,7 +245,31 @@ def bench_kcp(args):
                                f"T={x.T} H={x.H} K=V=128 cut into {n} equal shards", "shards": n},
         "ms": {"shard_affine": t_aff, "shard_scan": t_scan, "forward_reusing_records": t_reuse,
                "forward_recomputing_records": t_fwd, "total": total},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_kcp(x, n, list(range(min(4, x.H)))),
     }), flush=True)
+
+
+def cpu_baseline_kcp(x, n, heads):
+    """The fp64 oracle of the same split: each shard's (P, R) from the token recurrence,
+    then the fp64 fold and the forward from the folded states, on `heads`."""
+    import numpy as np
+
+    from oracle import oracle_fwd, oracle_shard_affine, oracle_shard_fold, oracle_threads
+
+    cut = np.array([i * x.T // n for i in range(n + 1)], dtype=np.int32)
+    t0 = time.perf_counter()
+    P, R = oracle_shard_affine(x.q, x.k, x.v, x.raw_gate, x.raw_beta, x.A_log, x.dt_bias, x.lower_bound,
+                               cu_seqlens=cut, heads=heads)
+    starts, _ = oracle_shard_fold(P, R)
+    sub = lambda t: t[:, :, heads].contiguous()  # noqa: E731
+    oracle_fwd(sub(x.q), sub(x.k), sub(x.v), sub(x.raw_gate), x.raw_beta[:, :, heads].contiguous(), x.scale,
+               x.A_log[heads], x.dt_bias[heads], x.lower_bound,
+               __import__("torch").from_numpy(starts.astype(np.float32)), cut)
+    dt = time.perf_counter() - t0
+    ht = x.T * len(heads)
+    return {"value": ht / dt, "unit": "head-tokens/s", "cores": oracle_threads(), "kind": "oracle",
+            "sample": f"fp64 shard maps, fold and forward over heads 0..{len(heads) - 1} of {x.H}, all "
+                      f"{x.T} tokens in {n} shards ({ht} head-tokens, {dt:.1f} s)"}
 
 
 def bench_decode(args):
@@ -244,6 +302,8 @@ def bench_decode(args):
         "config": {"workload": f"kda_decode B={x.B} T=1 H={x.H} K=V=128, in-place fp32 state"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg},
+        "cpu_baseline": None if args.no_cpu_baseline else dict(
+            cpu_baseline(x, list(range(x.H))), unit="sequence-heads/s"),
     }), flush=True)
 
 
@@ -297,7 +357,171 @@ def bench_bwd(args):
                                "output and final-state gradients given"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_bwd(x, 256, [0, 1]),
     }), flush=True)
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def read_sclk():
+    """(current, maximum) shader clock in MHz from the driver's DPM table in sysfs
+    (the level marked '*' is the current one), or None where it is not readable."""
+    import glob
+
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            lines = open(path).read().strip().splitlines()
+        except OSError:
+            continue
+        levels, cur = [], None
+        for ln in lines:
+            m = re.search(r"(\d+)\s*[Mm][Hh]z", ln)
+            if not m:
+                continue
+            levels.append(int(m.group(1)))
+            if "*" in ln:
+                cur = int(m.group(1))
+        if levels and cur is not None:
+            return cur, max(levels), path
+    return None
+
+
+def loaded_clock(step, seconds=1.0):
+    """Sample the shader clock while `step` runs back to back for about `seconds`."""
+    import threading
+
+    import torch
+
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            r = read_sclk()
+            if r is not None:
+                samples.append(r)
+            time.sleep(0.02)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return {"sclk_mhz": None, "max_mhz": None, "frac": None,
+                "gate": "not measured: no readable pp_dpm_sclk"}
+    cur = median([c for c, _, _ in samples])
+    mx = max(m for _, m, _ in samples)
+    frac = cur / mx
+    return {"sclk_mhz": cur, "max_mhz": mx, "frac": frac, "samples": len(samples), "source": samples[0][2],
+            "gate": "pass" if frac >= 0.70 else "FAIL: loaded clock below 0.70 of max, row not valid"}
+
+
+CONFIGS = {
+    "c3": "kda_fwd B=1 T={T} H={H} K=V=128 chunk=64 lower_bound=-5 zero initial state, final state written",
+    "c2": "kda_fwd B=2 T=4096 H=12 K=V=128 (one TP8 rank's share of H=96) lower_bound=-5, initial and final "
+          "states, run cold (MALL flushed between launches)",
+    "c4": "kda_fwd varlen: 16 packed sequences of U[1, 8192] tokens ({T} in all), H=32, K=V=128, "
+          "lower_bound=-5, per-sequence initial and final states",
+}
+
+
+def bench_forward(args):
+    import torch
+
+    import chunked_gated_delta_amd as kda
+    import workloads
+
+    if args.config == "c3":
+        x = workloads.c3_headline(T=args.T, H=args.H)
+        x.initial_state = torch.zeros(1, x.H, x.K, x.V, dtype=torch.float32)
+        x.cu_seqlens = torch.tensor([0, x.T], dtype=torch.int32)
+    elif args.config == "c2":
+        x = workloads.c2_tp_share()
+    else:
+        x = workloads.c4_varlen()
+    dev = torch.device("cuda:0")
+    d = lambda t: None if t is None else t.to(dev)  # noqa: E731
+    q, k, v, g, b = d(x.q), d(x.k), d(x.v), d(x.raw_gate), d(x.raw_beta)
+    al, dt, init, cu = d(x.A_log), d(x.dt_bias), d(x.initial_state), d(x.cu_seqlens)
+    out = torch.empty_like(v)
+    fin = torch.empty_like(init)
+    ws = torch.empty(kda.kda_workspace_size(x.B * x.T, x.H, x.N), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    head_tokens = x.B * x.T * x.H
+    alg_bytes = head_tokens * BYTES_PER_HEAD_TOKEN + 2 * x.N * x.H * STATE_BYTES
+    cold = alg_bytes < (256 << 20)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if cold else None
+
+    def step():
+        kda.kda_fwd(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, init, fin, cu, stream=sh)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if cold:
+            flush.zero_()
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    med_s = median(kern_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    value = head_tokens / (med_s if cold else wall / args.steps)
+    clock = loaded_clock(step) if not args.no_clock else None
+
+    achieved = alg_bytes / med_s / 1e9
+    flops = head_tokens * algorithmic_flops_per_head_token()
+    headline = args.config == "c3" and x.T == 32768 and x.H == 96
+    line = {
+        "metric": "KDA fwd head-tokens/s at H=96 T=32K bf16; % of MFMA/HBM roofline" if headline else
+                  f"KDA fwd head-tokens/s ({args.config}); % of HBM roofline",
+        "value": value,
+        "unit": "head-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": CONFIGS[args.config].format(T=x.B * x.T, H=x.H),
+                   "B": x.B, "T": x.T, "H": x.H, "K": 128, "V": 128, "N": x.N},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic() if headline else None,
+                     "kernel": "kda_fwd (every kernel of one forward)",
+                     "median_kernel_ms": med_s * 1e3,
+                     "mean_kernel_ms": sum(kern_ms) / len(kern_ms),
+                     "min_kernel_ms": min(kern_ms),
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "mfma": {"achieved_tflops": flops / med_s / 1e12, "peak_tflops": BF16_DENSE_TFLOPS,
+                 "frac": flops / med_s / 1e12 / BF16_DENSE_TFLOPS,
+                 "algorithmic_flops_per_launch": flops},
+        "clock": clock,
+        "cold": cold,
+    }
+    if not args.no_cpu_baseline:
+        heads = list(range(min(args.cpu_heads, x.H)))
+        line["cpu_baseline"] = cpu_baseline(x, heads)
+    print(json.dumps(line), flush=True)
 
 
 def main():
@@ -307,7 +531,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--T", type=int, default=32768)
     ap.add_argument("--H", type=int, default=96)
+    ap.add_argument("--config", choices=["c3", "c2", "c4"], default="c3",
+                    help="forward workload: c3 headline (default), c2 one TP8 rank's share, c4 packed varlen")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true", help="skip the loaded-clock probe")
     ap.add_argument("--cpu-heads", type=int, default=96)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--decode", type=int, default=0,
@@ -341,79 +568,7 @@ def main():
         bench_bwd(args)
         return
 
-    import torch
-
-    import chunked_gated_delta_amd as kda
-    import workloads
-
-    x = workloads.c3_headline(T=args.T, H=args.H)
-    x.initial_state = torch.zeros(1, x.H, x.K, x.V, dtype=torch.float32)
-    dev = torch.device("cuda:0")
-    d = lambda t: None if t is None else t.to(dev)  # noqa: E731
-    q, k, v, g, b = d(x.q), d(x.k), d(x.v), d(x.raw_gate), d(x.raw_beta)
-    al, dt, init = d(x.A_log), d(x.dt_bias), d(x.initial_state)
-    cu = torch.tensor([0, x.T], dtype=torch.int32, device=dev)
-    out = torch.empty_like(v)
-    fin = torch.empty_like(init)
-    ws = torch.empty(kda.kda_workspace_size(x.T, x.H, 1), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    sh = stream.cuda_stream
-
-    def step():
-        kda.kda_fwd(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, init, fin, cu,
-                    stream=sh)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    avg_kern_s = sum(kern_ms) / len(kern_ms) / 1e3
-    ms_per_step = wall / args.steps * 1e3
-    head_tokens = x.B * x.T * x.H
-    value = head_tokens / (wall / args.steps)
-
-    alg_bytes = head_tokens * BYTES_PER_HEAD_TOKEN + 2 * x.N * x.H * STATE_BYTES
-    achieved = alg_bytes / avg_kern_s / 1e9
-    flops = head_tokens * algorithmic_flops_per_head_token()
-    line = {
-        "metric": "KDA fwd head-tokens/s at H=96 T=32K bf16; % of MFMA/HBM roofline",
-        "value": value,
-        "unit": "head-tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"kda_fwd B=1 T={x.T} H={x.H} K=V=128 chunk=64 lower_bound=-5 "
-                               "zero initial state, final state written",
-                   "B": 1, "T": x.T, "H": x.H, "K": 128, "V": 128},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "kda_fwd (intra-chunk + inter-chunk kernels, one forward)",
-                     "avg_kernel_ms": avg_kern_s * 1e3,
-                     "algorithmic_bytes_per_launch": alg_bytes},
-        "mfma": {"achieved_tflops": flops / avg_kern_s / 1e12, "peak_tflops": BF16_DENSE_TFLOPS,
-                 "frac": flops / avg_kern_s / 1e12 / BF16_DENSE_TFLOPS,
-                 "algorithmic_flops_per_launch": flops},
-    }
-    if not args.no_cpu_baseline:
-        heads = list(range(min(args.cpu_heads, x.H)))
-        line["cpu_baseline"] = cpu_baseline(x, heads)
-    print(json.dumps(line), flush=True)
+    bench_forward(args)
 
 
 if __name__ == "__main__":
