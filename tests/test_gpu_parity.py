@@ -83,6 +83,42 @@ def test_c5_near_collinear_keys():
     check(o, f, ro, rf, x.name)
 
 
+def test_c5_near_collinear_keys_on_the_unsplit_chain():
+    """C5 through the unsplit 256-chunk recurrence: an in-place state update and the
+    transposed state layout both take it (the call above runs on 8 shards), and so
+    does every call with 32 or more (sequence, head) chains."""
+    import chunked_gated_delta_amd as kda
+    x = W.c5_collinear()
+    ro, rf = oracle(x)
+    o, f = run_gpu(x, in_place=True)
+    check(o, f, ro, rf, x.name + " (in place, unsplit)")
+    dev = "cuda:0"
+    d = lambda t: t.to(dev)  # noqa: E731
+    out = torch.full_like(d(x.v), float("nan"))
+    fin = torch.full((1, 1, 128, 128), float("nan"), device=dev)
+    ws = torch.empty(kda.kda_workspace_size(x.T, 1, 1), dtype=torch.uint8, device=dev)
+    qk = d(x.q)
+    kda.kda_fwd_ex(qk, qk, d(x.v), d(x.raw_gate), d(x.raw_beta), x.scale, out, ws, d(x.A_log), d(x.dt_bias),
+                   x.lower_bound, d(x.initial_state), fin, d(x.cu_seqlens), flags=kda.FLAG_STATE_VK)
+    torch.cuda.synchronize()
+    check(out.double().cpu().numpy().reshape(x.T, 1, 128), fin.double().cpu().numpy().swapaxes(-1, -2), ro, rf,
+          x.name + " (transposed state, unsplit)")
+
+
+@pytest.mark.parametrize("T", [32768, 65536])
+def test_c5_near_collinear_keys_longer_than_the_page(T):
+    """The page's stress case at 2x and 4x its length, on the split path (16 and 32 shards)
+    and on the unsplit chain (in place).  With one repeated key and almost no decay the
+    16-bit rounding of the state-update operands is the same every chunk, so its error
+    adds up coherently along T (until the decay, 3e-5 per token, forgets it)."""
+    x = W.c5_collinear(T=T)
+    ro, rf = oracle(x)
+    o, f = run_gpu(x)
+    check(o, f, ro, rf, x.name + f" T={T} (shards)")
+    o2, f2 = run_gpu(x, in_place=True)
+    check(o2, f2, ro, rf, x.name + f" T={T} (in place, unsplit)")
+
+
 def test_c3_headline_sampled_heads():
     """Full-size headline launch; the oracle recomputes three sampled heads."""
     x = W.c3_headline()

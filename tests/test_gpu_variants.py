@@ -61,10 +61,12 @@ def test_variant_matches_oracle(flags):
     check(variant_inputs(101, 1000, 4, 128, 128, flags, init_std=0.1), flags)
 
 
-def test_given_gate_without_gate_parameters_and_out_of_range():
+def test_given_gate_without_gate_parameters_and_at_its_range_ends():
+    """A_log and dt_bias absent; the given decays include both ends of [lower_bound, 0]
+    (values outside it break the call's contract: test_gpu_faults.py)."""
     x = variant_inputs(102, 777, 3, 128, 128, GATE_GIVEN, init_std=0.1)
-    x.raw_gate[0, ::5] = -8.0
-    x.raw_gate[0, 1::5] = 0.75
+    x.raw_gate[0, ::5] = x.lower_bound
+    x.raw_gate[0, 1::5] = 0.0
     check(x, GATE_GIVEN, drop_gate_params=True)
 
 
