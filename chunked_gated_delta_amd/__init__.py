@@ -4,8 +4,8 @@ Argument marshalling only: every step of the forward pass runs in the HIP
 kernels behind the C ABI of include/kda.h.  The names mirror that header:
 ``kda_fwd``, ``kda_workspace_size``, ``kda_is_supported``, ``kda_shard_affine``,
 ``kda_shard_scan``, ``kda_decode``, ``kda_fwd_ex`` (with the ``FLAG_*`` variant bits),
-``kda_bwd``, ``kda_bwd_ex``, ``kda_bwd_workspace_size`` and
-``kda_workspace_faults`` (with the ``FAULT_*`` bits).  PyTorch provides
+``kda_bwd``, ``kda_bwd_ex``, ``kda_bwd_workspace_size``,
+``kda_workspace_faults`` (with the ``FAULT_*`` bits) and ``kda_fwd_noalloc``.  PyTorch provides
 device memory and the current stream; there is no CPU or PyTorch fallback, and
 importing this module fails if the library has not been built.
 """
@@ -23,7 +23,7 @@ import torch  # noqa: F401
 
 __all__ = ["kda_fwd", "kda_fwd_ex", "kda_workspace_size", "kda_is_supported", "kda_shard_affine",
            "kda_shard_scan", "kda_decode", "kda_bwd", "kda_bwd_ex", "kda_bwd_workspace_size",
-           "kda_workspace_faults", "FAULT_WAIT_TIMEOUT", "FAULT_GATE_RANGE", "FAULT_QK_NORM", "KdaError", "STATUS", "library_path", "exported_symbols",
+           "kda_workspace_faults", "kda_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "FAULT_WAIT_TIMEOUT", "FAULT_GATE_RANGE", "FAULT_QK_NORM", "KdaError", "STATUS", "library_path", "exported_symbols",
            "FLAG_GATE_GIVEN", "FLAG_BETA_GIVEN", "FLAG_NO_QK_NORM", "FLAG_STATE_VK", "FLAG_REUSE_RECORDS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,13 +33,15 @@ STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERR_INVALID", 2: "KDA_ERR_UNSUPPORTED",
           3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_LAUNCH"}
 exported_symbols = ("kda_fwd", "kda_workspace_size", "kda_is_supported", "kda_status_string",
                     "kda_shard_affine", "kda_shard_scan", "kda_decode", "kda_fwd_ex", "kda_bwd",
-                    "kda_bwd_ex", "kda_bwd_workspace_size", "kda_workspace_faults")
+                    "kda_bwd_ex", "kda_bwd_workspace_size", "kda_workspace_faults", "kda_fwd_noalloc")
 # kda_fwd_ex variant bits (KDA_FLAG_* in include/kda.h)
 FLAG_GATE_GIVEN, FLAG_BETA_GIVEN, FLAG_NO_QK_NORM, FLAG_STATE_VK = 1, 2, 4, 8
 # kda_fwd_ex, kda_bwd_ex: reuse the chunk records the previous call left in the workspace
 FLAG_REUSE_RECORDS = 16
 # fault-word bits (KDA_FAULT_* in include/kda.h), read by kda_workspace_faults
 FAULT_WAIT_TIMEOUT, FAULT_GATE_RANGE, FAULT_QK_NORM = 1, 2, 4
+# size of the static device scratch behind kda_fwd_noalloc (KDA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 160 << 20
 
 
 class KdaError(RuntimeError):
@@ -86,6 +88,9 @@ _lib.kda_bwd_ex.argtypes = _lib.kda_bwd.argtypes[:-1] + [ctypes.c_uint, _P]
 _lib.kda_bwd_ex.restype = ctypes.c_int
 _lib.kda_workspace_faults.argtypes = [_P, ctypes.POINTER(ctypes.c_uint32), _P]
 _lib.kda_workspace_faults.restype = ctypes.c_int
+_lib.kda_fwd_noalloc.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_float, _P, _P, _P,
+                                 _I64, _I64, _I64, _I64, _I64, _I64, _P]
+_lib.kda_fwd_noalloc.restype = ctypes.c_int
 
 
 def kda_workspace_size(T: int, H: int, N: int) -> int:
@@ -157,6 +162,23 @@ def kda_fwd(q, k, v, raw_gate, raw_beta, scale, out, workspace, A_log, dt_bias, 
                       _ptr(final_state), _ptr(cu_seqlens), B, T, H, K, V, N, _stream(stream, q.device))
     if rc != 0:
         raise KdaError(rc)
+
+
+def kda_fwd_noalloc(q, k, v, raw_gate, raw_beta, scale, out, A_log, dt_bias, lower_bound,
+                    initial_state=None, final_state=None, cu_seqlens=None, stream=None):
+    """kda_fwd without a workspace: the library's static per-GPU scratch of
+    NOALLOC_SCRATCH_BYTES is used instead (calls larger than it raise KdaError with
+    KDA_ERR_WORKSPACE; calls that overlap on one GPU race)."""
+    if out is None:
+        raise ValueError("out is required")
+    B, T, H, K, V, N = _check_inputs(q, k, v, raw_gate, raw_beta, out, A_log, dt_bias, cu_seqlens)
+    _check_f32("initial_state", initial_state, (N, H, K, V))
+    _check_f32("final_state", final_state, (N, H, K, V))
+    rc = _lib.kda_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(raw_beta), float(scale),
+                              _ptr(out), _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
+                              _ptr(final_state), _ptr(cu_seqlens), B, T, H, K, V, N, _stream(stream, q.device))
+    if rc != 0:
+        raise KdaError(rc, "kda_fwd_noalloc")
 
 
 def kda_fwd_ex(q, k, v, raw_gate, raw_beta, scale, out, workspace, A_log, dt_bias, lower_bound,

@@ -331,6 +331,35 @@ kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void*
  */
 kda_status_t kda_workspace_faults(const void* workspace, uint32_t* faults, void* stream);
 
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  kda_fwd
+ * with the same arguments minus the workspace, whose scratch (counter, fault
+ * word, varlen tables, chunk records) is instead a static device array of
+ * KDA_NOALLOC_SCRATCH_BYTES inside the library.  Every GPU the library runs on
+ * holds its own copy of that array until the process ends.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).
+ *
+ * Limits and sharing:
+ *   - the call's workspace layout must fit: kda_workspace_size-sized calls up
+ *     to KDA_NOALLOC_SCRATCH_BYTES (e.g. B=2, T=4096, H=12 needs about 142 MB);
+ *     larger calls return KDA_ERR_WORKSPACE before any device work;
+ *   - every call on one GPU uses that GPU's one array: calls that overlap on a
+ *     GPU (different streams, host threads or processes sharing a context)
+ *     race and give wrong results; serialise them;
+ *   - the array keeps the last call's contents, which no call depends on (the
+ *     kernels clear the counter and fault word themselves);
+ *   - kda_workspace_faults is not available for it (the array has no host
+ *     handle); the kernels' bounded waits are the same as kda_fwd's.
+ * Arguments, layouts, results and other errors are those of kda_fwd.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)160 << 20)
+kda_status_t kda_fwd_noalloc(const void* q, const void* k, const void* v, const void* raw_gate,
+                             const void* raw_beta, float scale, void* out, const float* A_log,
+                             const float* dt_bias, float lower_bound, const float* initial_state,
+                             float* final_state, const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H,
+                             int64_t K, int64_t V, int64_t N, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* kda_status_string(kda_status_t status);
 

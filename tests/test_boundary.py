@@ -298,3 +298,19 @@ def test_workspace_sizes_grow_with_the_batch():
         bw = [kda.kda_bwd_workspace_size(T, H, n) for n in range(1, 41)]
         assert all(a <= b for a, b in zip(fw, fw[1:])), (T, H, fw)
         assert all(a <= b for a, b in zip(bw, bw[1:])), (T, H, bw)
+
+
+def test_noalloc_refuses_bad_and_oversized_calls_on_the_host():
+    lib = ctypes.CDLL(kda.library_path)
+    P, I64, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    lib.kda_fwd_noalloc.argtypes = [P, P, P, P, P, F, P, P, P, F, P, P, P, I64, I64, I64, I64, I64, I64, P]
+
+    def call(B, T, H, N):
+        return lib.kda_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, FAKE, -5.0, None, None, None,
+                                   B, T, H, 128, 128, N, None)
+
+    assert call(0, 64, 2, 1) == 1           # INVALID
+    assert call(1, 64, 0, 1) == 1
+    assert call(1, 32768, 96, 1) == 3       # WORKSPACE: 4.4 GB of records do not fit the scratch
+    assert call(1, 1 << 20, 2, 1) == 3
+    assert kda.NOALLOC_SCRATCH_BYTES == 160 << 20
