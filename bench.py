@@ -51,7 +51,8 @@ BF16_DENSE_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
 BYTES_PER_HEAD_TOKEN = 4 * 128 * 2 + 2 + 128 * 2
 STATE_BYTES = 128 * 128 * 4
 KERNEL_SRCS = [os.path.join(ROOT, "chunked_gated_delta_amd", "csrc", f)
-               for f in ("kda_common.h", "kda_host.h", "kda_intra.hip", "kda_inter.hip", "kda_api.hip")] + [
+               for f in ("kda_common.h", "kda_host.h", "kda_intra.hip", "kda_inter.hip", "kda_chain.h",
+                         "kda_chain.hip", "kda_api.hip")] + [
     os.path.join(ROOT, "chunked_gated_delta_amd", "build.py")]  # compile flags shape the kernels too
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_fwd_c3_traffic.json")
 
@@ -340,7 +341,8 @@ def bench_bwd(args):
                                    stream=sh), args.steps, args.warmup, stream)
     # the same gradients on the records a forward call left in this workspace
     out, fin = torch.empty_like(v), torch.empty_like(init)
-    kda.kda_fwd(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, init, fin, stream=sh)
+    kda.kda_fwd_ex(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, init, fin, flags=kda.FLAG_KEEP_RECORDS,
+                   stream=sh)
     ms_reuse = timed(lambda: kda.kda_bwd_ex(q, k, v, g, b, x.scale, d_out, dq, dk, dv, dg, db, dA, ddt, ws, al,
                                             dt, x.lower_bound, initial_state=init, d_final=d_fin,
                                             d_initial_state=dinit, flags=kda.FLAG_REUSE_RECORDS, stream=sh),

@@ -24,7 +24,8 @@ import torch  # noqa: F401
 __all__ = ["kda_fwd", "kda_fwd_ex", "kda_workspace_size", "kda_is_supported", "kda_shard_affine",
            "kda_shard_scan", "kda_decode", "kda_bwd", "kda_bwd_ex", "kda_bwd_workspace_size",
            "kda_workspace_faults", "kda_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "FAULT_WAIT_TIMEOUT", "FAULT_GATE_RANGE", "FAULT_QK_NORM", "KdaError", "STATUS", "library_path", "exported_symbols",
-           "FLAG_GATE_GIVEN", "FLAG_BETA_GIVEN", "FLAG_NO_QK_NORM", "FLAG_STATE_VK", "FLAG_REUSE_RECORDS"]
+           "FLAG_GATE_GIVEN", "FLAG_BETA_GIVEN", "FLAG_NO_QK_NORM", "FLAG_STATE_VK", "FLAG_REUSE_RECORDS",
+           "FLAG_KEEP_RECORDS", "FLAG_SINGLE_LAUNCH", "FAULT_PLACEMENT"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkda.so")
@@ -38,8 +39,12 @@ exported_symbols = ("kda_fwd", "kda_workspace_size", "kda_is_supported", "kda_st
 FLAG_GATE_GIVEN, FLAG_BETA_GIVEN, FLAG_NO_QK_NORM, FLAG_STATE_VK = 1, 2, 4, 8
 # kda_fwd_ex, kda_bwd_ex: reuse the chunk records the previous call left in the workspace
 FLAG_REUSE_RECORDS = 16
+# kda_fwd_ex: leave every chunk record in the workspace, for a later FLAG_REUSE_RECORDS call
+FLAG_KEEP_RECORDS = 32
+# kda_fwd_ex: one-sequence calls with >= 16 heads run as one producer/chain launch
+FLAG_SINGLE_LAUNCH = 64
 # fault-word bits (KDA_FAULT_* in include/kda.h), read by kda_workspace_faults
-FAULT_WAIT_TIMEOUT, FAULT_GATE_RANGE, FAULT_QK_NORM = 1, 2, 4
+FAULT_WAIT_TIMEOUT, FAULT_GATE_RANGE, FAULT_QK_NORM, FAULT_PLACEMENT = 1, 2, 4, 8
 # size of the static device scratch behind kda_fwd_noalloc (KDA_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 160 << 20
 
@@ -185,7 +190,8 @@ def kda_fwd_ex(q, k, v, raw_gate, raw_beta, scale, out, workspace, A_log, dt_bia
                initial_state=None, final_state=None, cu_seqlens=None, flags=0, stream=None):
     """kda_fwd with variant flags (an OR of the FLAG_* bits).  With FLAG_GATE_GIVEN,
     A_log and dt_bias may be None; with FLAG_STATE_VK the states are [N,H,V,K];
-    FLAG_REUSE_RECORDS skips the intra-chunk pass and uses the records that the
+    FLAG_KEEP_RECORDS leaves every chunk record in the workspace, and
+    FLAG_REUSE_RECORDS skips the intra-chunk pass and uses the records that such a
     previous call on this workspace (same inputs but v and the states) left there."""
     if out is None:
         raise ValueError("out is required")

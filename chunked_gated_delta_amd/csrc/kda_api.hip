@@ -164,10 +164,10 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
                      void* workspace, size_t workspace_bytes, const float* A_log,
                      const float* dt_bias, float lower_bound, const int32_t* cu_seqlens, int64_t B,
                      int64_t T, int64_t H, int64_t K, int64_t V, int64_t N, hipStream_t st,
-                     Prepared& pr, unsigned flags) {
+                     Prepared& pr, unsigned flags, bool run_intra) {
   if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID;
   if (flags & ~(unsigned)(FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM | FLAG_STATE_VK |
-                          FLAG_REUSE_RECORDS))
+                          FLAG_REUSE_RECORDS | FLAG_KEEP_RECORDS | FLAG_SINGLE_LAUNCH))
     return KDA_ERR_INVALID;
   // token arrays may be NULL only when there are no tokens (empty tensors)
   if (B * T > 0 && (!q || !k || !raw_gate || !raw_beta)) return KDA_ERR_INVALID;
@@ -214,9 +214,8 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
   pr.map.T = T;
   pr.map.N = (int)N;
   pr.rec = pr.ws + pr.lay.rec;
-  if (flags & FLAG_REUSE_RECORDS) return KDA_SUCCESS;  // the records are already in the workspace
 
-  IntraArgs ia;
+  IntraArgs& ia = pr.ia;
   ia.q = static_cast<const uint16_t*>(q);
   ia.k = static_cast<const uint16_t*>(k);
   ia.g = static_cast<const uint16_t*>(raw_gate);
@@ -240,7 +239,23 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
   // workgroup of each kernel, intra first
   ia.timers = reinterpret_cast<unsigned long long*>(pr.ws + pr.lay.total);
 #endif
+  // with REUSE the records are already in the workspace
+  if (!run_intra || (flags & FLAG_REUSE_RECORDS)) return KDA_SUCCESS;
   return launch_status(launch_intra(ia, pr.max_chunks, st), "intra");
+}
+
+// Whether a prepared forward runs as the fused pipeline: one sequence of at
+// least one token, enough heads, its records not wanted afterwards (KEEP) and
+// not given (REUSE), not split into shards, on a GPU of 8 equal XCDs.
+static bool use_fused(const Prepared& pr, unsigned flags, int64_t T_total, bool split) {
+  if (!(flags & FLAG_SINGLE_LAUNCH) || !pr.lay.fused || split || T_total < 1 ||
+      (flags & (FLAG_REUSE_RECORDS | FLAG_KEEP_RECORDS)))
+    return false;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return false;
+  return cus >= 192 && cus % 8 == 0;
 }
 
 InterArgs inter_args(const Prepared& pr, int64_t H) {
@@ -355,9 +370,41 @@ kda_status_t kda_fwd_ex(const void* q, const void* k, const void* v, const void*
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   Prepared pr;
   const kda_status_t s = prepare(q, k, raw_gate, raw_beta, workspace, workspace_bytes, A_log, dt_bias,
-                                 lower_bound, cu_seqlens, B, T, H, K, V, N, st, pr, flags);
+                                 lower_bound, cu_seqlens, B, T, H, K, V, N, st, pr, flags, false);
   if (s != KDA_SUCCESS) return s;
   const bool split = use_split(pr, flags, B, T) && !(initial_state && initial_state == final_state);
+  if (use_fused(pr, flags, B * T, split)) {
+    // one sequence: its bounds are [0, B T) with or without cu_seqlens
+    ChunkMap m1;
+    m1.cu = nullptr;
+    m1.choff = nullptr;
+    m1.T = B * T;
+    m1.N = 1;
+    IntraArgs ia = pr.ia;
+    ia.map = m1;
+    ChainArgs ca;
+    ca.v = static_cast<const uint16_t*>(v);
+    ca.out = static_cast<uint16_t*>(out);
+    ca.init = initial_state;
+    ca.fin = final_state;
+    ca.state_vk = (flags & FLAG_STATE_VK) ? 1 : 0;
+    ca.rec = pr.rec;
+    ca.order = nullptr;
+    ca.map = m1;
+    ca.H = (int)H;
+    ca.scale = scale;
+    FusedArgs fa;
+    fa.ringbuf = pr.ws + pr.lay.fring;
+    fa.flags = reinterpret_cast<int*>(pr.ws + pr.lay.fflags);
+    fa.consumed = reinterpret_cast<int*>(pr.ws + pr.lay.fcons);
+    fa.claims = reinterpret_cast<int*>(pr.ws + pr.lay.fclaims);
+    fa.faults = reinterpret_cast<unsigned*>(pr.ws + pr.lay.faults);
+    fa.nchunk = (int)((B * T + CH - 1) / CH);
+    return launch_status(launch_fused(ia, ca, fa, st), "fused");
+  }
+  if (!(flags & FLAG_REUSE_RECORDS) &&
+      launch_status(launch_intra(pr.ia, pr.max_chunks, st), "intra") != KDA_SUCCESS)
+    return KDA_ERR_LAUNCH;
   if (split) return split_forward(pr, v, out, initial_state, final_state, scale, T, H, N, st);
   InterArgs xa = inter_args(pr, H);
   xa.v = static_cast<const uint16_t*>(v);

@@ -28,6 +28,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 //   NW   : -W = -T diag(beta) (K^ * exp(G))      f16  [64 tok][128 ch]
 //   QG   : Q^ * exp(G)                           f16  [64 tok][128 ch]
 //   KTH/L: (K^ * exp(G_L - G))^T  hi / lo        f16  [128 ch][64 tok]
+//          (the lo half is stored times KT_LO_SCALE, see below)
 //   AQK  : A_qk (zero above the diagonal)        f16  [64 tok][64 tok]
 //   TBH/L: T diag(beta) (zero above diagonal)    bf16 [64 tok][64 tok] hi / lo
 //   GL   : exp(G_L) per channel                  f32  [128]
@@ -42,6 +43,16 @@ constexpr size_t REC_TBL = REC_TBH + CH * CH * 2;
 constexpr size_t REC_GL = REC_TBL + CH * CH * 2;
 constexpr size_t REC_BYTES = REC_GL + KD * 4;  // 90624
 static_assert(REC_BYTES % 256 == 0, "record alignment");
+
+// The lo half of the fp16 hi/lo split of Kt is stored times 2^11.  A lo part
+// is at most half an fp16 ulp of its hi part (2^-11 of it), which puts it in
+// the fp16 subnormal range (below 2^-14) for every |Kt| < 1/8: there its
+// error is an absolute 2^-25 instead of 11 bits relative.  With one key
+// repeated at every position that error is the same in every chunk and adds
+// up along the sequence.  Scaled by 2^11 the lo part keeps 11 bits wherever
+// the hi part is normal; the reader multiplies its pass by KT_LO_UNSCALE.
+constexpr float KT_LO_SCALE = 2048.0f;
+constexpr float KT_LO_UNSCALE = 1.0f / 2048.0f;
 
 // Element index (in 16-bit units) of the fragment-ordered record arrays.  The
 // reader's lane l = 16 gq + tl of wave w loads 8 consecutive k elements:
@@ -126,6 +137,26 @@ __device__ __forceinline__ void lds_f32x8(const float* src, float (&d)[8]) {
   d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
 }
 
+// Buffer loads and stores: a 128-bit descriptor (scalar registers) per array
+// and one lane offset, every element's place a compile-time or wave-uniform
+// offset, instead of a 64-bit address per load.  The last argument of the
+// load and store builtins is the cache policy: 0 for the default, SC1
+// (device scope) for data that another CU writes while this kernel runs: such
+// a load misses this CU's L1 and reads the L2 that CUs of one XCD share,
+// where a store has landed once the writer's s_waitcnt vmcnt(0) returned.
+// (Workgroup scope, SC0, may still hit a stale line of this CU's L1.)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int BUF_DESC3 = 0x00020000;  // raw 32-bit buffer, no format conversion
+constexpr int SC1 = 16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, BUF_DESC3);
+}
+template <typename T, int POLICY = 0>
+__device__ __forceinline__ T bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY));
+}
+
 // Split-plane B-operand fragments in LDS.  Fragment f holds one 16-column
 // tile x 32-k block of a 16-bit operand: the 16 bytes (8 k) of MFMA lane
 // l = 16gq + tl, split into two planes, bytes 0-7 at l*8 and bytes 8-15 at
@@ -171,6 +202,8 @@ constexpr int FLAG_BETA_GIVEN = 2;   // raw_beta holds beta
 constexpr int FLAG_NO_QK_NORM = 4;   // q, k used without L2 normalisation
 constexpr int FLAG_STATE_VK = 8;     // states stored transposed, [N, H, V, K]
 constexpr int FLAG_REUSE_RECORDS = 16;  // the workspace already holds this call's chunk records
+constexpr int FLAG_KEEP_RECORDS = 32;   // leave every chunk record in the workspace (for REUSE)
+constexpr int FLAG_SINGLE_LAUNCH = 64;  // one-sequence calls: the one-launch producer/chain pipeline
 
 // Fault bits a call ORs into the workspace's fault word (same values as the
 // KDA_FAULT_* constants of the C ABI): conditions the kernels detect on the
@@ -178,6 +211,36 @@ constexpr int FLAG_REUSE_RECORDS = 16;  // the workspace already holds this call
 constexpr unsigned FAULT_WAIT_TIMEOUT = 1u;  // a bounded wait gave up; results are invalid
 constexpr unsigned FAULT_GATE_RANGE = 2u;    // FLAG_GATE_GIVEN: a decay outside [lower_bound, 0]
 constexpr unsigned FAULT_QK_NORM = 4u;       // FLAG_NO_QK_NORM: a q or k row with |x|^2 > 1 + 1/16
+constexpr unsigned FAULT_PLACEMENT = 8u;     // a fused-pipeline workgroup ran on another XCD than planned
+
+// The fused forward pipeline (one sequence): per XCD, intra-chunk producer
+// workgroups hand the chunk records of that XCD's heads (h = xcd + 8 l) to one
+// chain workgroup per head through a ring of FUSED_RING records per head, in
+// that XCD's L2.  The per-head and per-XCD words sit FUSED_LINE bytes apart
+// (one L2 line each).
+constexpr int FUSED_LINE = 128;
+constexpr int FUSED_RING = 8;
+struct IntraFused {
+  int xcd = 0;               // the producer's XCD
+  int hx = 0;                // heads of that XCD
+  int ring = 1;              // ring slots per head
+  char* ringbuf = nullptr;   // [H][ring] records
+  const int* consumed = nullptr;  // per head: chunks its chain has finished reading
+  int* flags = nullptr;      // [chunks][H]: 0 not ready, 1 in the ring, 2 in the record area
+  int H = 0;
+  int nchunk = 0;
+};
+struct ChainFused {
+  const char* ringbuf = nullptr;  // [H][ring] records
+  int ring = 1;
+  const int* flags = nullptr;     // [chunks][H] ready flags
+  int* consumed = nullptr;        // per head (FUSED_LINE apart)
+  unsigned* faults = nullptr;
+  int nchunk = 0;
+};
+// Polls of one ready flag before a chain gives up on it (about a second: each
+// poll is an L2 round trip plus a 256-cycle sleep).
+constexpr int FUSED_SPIN_LIMIT = 1 << 21;
 
 // Host-side launchers (defined next to their kernels).
 struct IntraArgs {
@@ -214,7 +277,35 @@ struct InterArgs {
   float* states;         // [chunks][H][K][V] state entering every chunk (fp32)
   float* dtile;          // [chunks][H][64][V] the chunk's D = U - W S (rows past the chunk end zero)
 };
+// The chain kernel: the inter-chunk recurrence with one workgroup per
+// (sequence, head), all 128 columns (same results as the inter kernel).
+struct ChainArgs {
+  const uint16_t* v;
+  uint16_t* out;
+  const float* init;     // nullptr: zero state
+  float* fin;            // nullptr: not written
+  int state_vk;          // states stored transposed, S[c][j] at j * K + c
+  const char* rec;       // records [chunks][H]
+  const int32_t* order;  // nullptr: identity order of sequences
+  ChunkMap map;
+  int H;
+  float scale;
+};
 hipError_t launch_intra(const IntraArgs& a, int64_t max_chunks, hipStream_t st);
+hipError_t launch_chain(const ChainArgs& a, hipStream_t st);
+// The fused pipeline over one sequence: intra-chunk producers and one chain
+// workgroup per head in a single persistent launch (`fz` carries the ring,
+// flags, consumed counters, per-XCD claim counters and the fault word, all
+// cleared by the launcher first).  Needs 8 XCDs of equal size and N == 1.
+struct FusedArgs {
+  char* ringbuf;
+  int* flags;      // [chunks][H]
+  int* consumed;   // [H] FUSED_LINE apart
+  int* claims;     // [8] FUSED_LINE apart
+  unsigned* faults;
+  int nchunk;
+};
+hipError_t launch_fused(const IntraArgs& ia, const ChainArgs& ca, const FusedArgs& fa, hipStream_t st);
 hipError_t launch_inter(const InterArgs& a, hipStream_t st);
 hipError_t launch_shard_scan(const float* P, const float* R, const float* init, float* starts, float* fin,
                              int n_shards, int H, hipStream_t st);

@@ -32,12 +32,22 @@ inline SplitPlan split_plan(int64_t T, int64_t H, int64_t N) {
   return {(nc + cs - 1) / cs, cs};
 }
 
+// The fused pipeline (one launch of intra-chunk producers and per-head
+// chains, records handed over through a ring in L2) serves calls with one
+// sequence and at least this many heads (two per XCD).
+constexpr int64_t kFusedMinHeads = 16;
+
 struct Layout {
   size_t claim, faults, choff, order, rec, base, total;  // base: end of the records
   // shard areas (split forwards only): shard offsets in tokens and in chunks
   // [N S + 1], and the per-shard P, R, entering and final states
   int64_t S;
   size_t scu, schoff, sP, sR, sstart, sfin;
+  // fused-pipeline areas (N == 1, H >= kFusedMinHeads): the ring of
+  // FUSED_RING records per head, ready flags [chunks][H], consumed counters
+  // [H] and per-XCD claim counters [8] (FUSED_LINE apart)
+  bool fused;
+  size_t fring, fflags, fcons, fclaims;
 };
 
 // T_total / N is the per-sequence length the split plan assumes (the mean
@@ -63,6 +73,15 @@ inline Layout workspace_layout(int64_t T_total, int64_t H, int64_t N) {
     l.sstart = l.sR + st;
     l.sfin = l.sstart + st;
     l.total = l.sfin + st;
+  }
+  l.fused = N == 1 && H >= kFusedMinHeads;
+  l.fring = l.fflags = l.fcons = l.fclaims = l.total;
+  if (l.fused) {
+    l.fring = align256(l.total);
+    l.fflags = l.fring + (size_t)H * FUSED_RING * REC_BYTES;
+    l.fcons = l.fflags + align256(max_chunks * (size_t)H * 4);
+    l.fclaims = l.fcons + align256((size_t)H * FUSED_LINE);
+    l.total = l.fclaims + 8 * FUSED_LINE;
   }
   return l;
 }
@@ -94,15 +113,16 @@ struct Prepared {
   char* ws;
   Layout lay;
   int64_t max_chunks;
+  IntraArgs ia;  // the intra-chunk pass's arguments
 };
 
 // Argument checks shared by every entry point that runs the chunked forward,
-// then the varlen bookkeeping and the intra-chunk kernel on `st`.
+// then the varlen bookkeeping and (run_intra) the intra-chunk kernel on `st`.
 kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const void* raw_beta,
                      void* workspace, size_t workspace_bytes, const float* A_log,
                      const float* dt_bias, float lower_bound, const int32_t* cu_seqlens, int64_t B,
                      int64_t T, int64_t H, int64_t K, int64_t V, int64_t N, hipStream_t st,
-                     Prepared& pr, unsigned flags = 0);
+                     Prepared& pr, unsigned flags = 0, bool run_intra = true);
 
 // Inter-chunk arguments for the prepared call (no v, outputs or states set).
 InterArgs inter_args(const Prepared& pr, int64_t H);

@@ -4,7 +4,8 @@
 //     U = T diag(b) V                       (bf16 hi/lo x exact bf16 V, 2 passes)
 //     D = U - W S                           (fp16 W, fp16 copy of S)
 //     O = scale [ (Q exp(G)) S + A_qk D ]   -> bf16 output
-//     S = Diag(exp(G_L)) S + (K exp(G_L - G))^T D   (fp16 hi/lo x fp16 hi/lo, 3 passes)
+//     S = Diag(exp(G_L)) S + (K exp(G_L - G))^T D   (fp16 hi/lo x fp16 hi/lo, 3 passes;
+//                                                   the Kt lo pass accumulates on its own)
 // The state S is fp32 and stays in MFMA accumulator registers for the whole
 // sequence; its fp16 copy, the chunk's V tile and D live in LDS in
 // column-major form so that every B operand is one 16-byte LDS read.
@@ -420,12 +421,16 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
         s[1] *= cur.gl[mt].y;
         s[2] *= cur.gl[mt].z;
         s[3] *= cur.gl[mt].w;
+        // the Kt lo pass in its own accumulator: the record holds lo * 2^11
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           s = mfma_f16(cur.kth[mt][ks], dh[ks], s);
           s = mfma_f16(cur.kth[mt][ks], dl[ks], s);
-          s = mfma_f16(cur.ktl[mt][ks], dh[ks], s);
+          c = mfma_f16(cur.ktl[mt][ks], dh[ks], c);
         }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) s[ii] = __builtin_fmaf(c[ii], KT_LO_UNSCALE, s[ii]);
         S[mt][nn] = s;
       }
       if (nn == 0) KDA_ISSUE((load_ops<3, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));

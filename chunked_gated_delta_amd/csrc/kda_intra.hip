@@ -33,6 +33,7 @@
 // Persistent workgroups (4 waves) loop over (chunk, head) items; in each item
 // every wave owns one 16-token sub-chunk, in a role that rotates per item.
 
+#include "kda_chain.h"
 #include "kda_common.h"
 
 namespace kda {
@@ -60,8 +61,8 @@ constexpr int NFAC = 15;
 constexpr int OFF_FAC = OFF_TOT + 4 * KD * 4;          // f32 [NFAC][128] decay factors
 constexpr int OFF_NB = OFF_FAC + NFAC * KD * 4;        // f32 [128] gate offsets
 constexpr int OFF_B = OFF_NB + KD * 4;                 // f32 [64] beta
-constexpr int OFF_FLAG = OFF_B + CH * 4;               // int [4] row-block ready tags, [4] claim
-constexpr int LDS_BYTES = OFF_FLAG + 8 * 4;
+constexpr int OFF_FLAG = OFF_B + CH * 4;               // int [8] ready tags, [1] claim, [1] record place
+constexpr int LDS_BYTES = OFF_FLAG + 12 * 4;
 static_assert(LDS_BYTES <= 80 * 1024, "two workgroups per CU");
 
 // decay-factor rows (per channel, log2 units, P_w = prefix before sub-chunk w):
@@ -108,17 +109,27 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8]) {
   return __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
 }
 
+}  // namespace
+
 // The chunk table, A_log and the record base are also passed as separate
 // __restrict__ arguments: with no possible aliasing by the record stores, the
 // wave-uniform loads from them can go through the scalar unit and never wait
 // behind the vector memory queue.  GATE_GIVEN is a template switch: a runtime
 // choice inside the per-element gate loop would split it into 32 branches and
 // keep the scan from interleaving.
-template <bool GATE_GIVEN>
-__global__ void __launch_bounds__(NTHREADS, 2)
-    kda_intra_kernel(IntraArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ choff,
-                     const float* __restrict__ A_log, char* __restrict__ recs) {
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+//
+// One workgroup's share of the (chunk, head) items.  Standalone (FUSED =
+// false): items are (last chunk - chunk) * H + head over every sequence, the
+// workgroup's first two are `first` and first + stride, later ones are claimed
+// from `claim`, and each record goes to recs[chunk][head].  FUSED: the items
+// of one XCD's heads of a single sequence in chunk order (chunk * hx + l for
+// head xcd + 8 l), each record goes to its head's ring slot or to
+// recs[chunk][head] (IntraFused), and its ready flag then says which.
+template <bool GATE_GIVEN, bool FUSED>
+__device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restrict__ cu,
+                                            const int32_t* __restrict__ choff, const float* __restrict__ A_log,
+                                            char* __restrict__ recs, char* smem, int first, int stride, int* claim,
+                                            const IntraFused& fz) {
   __bf16* sKRFh = reinterpret_cast<__bf16*>(smem + OFF_KRF_HI);
   __bf16* sKRFl = reinterpret_cast<__bf16*>(smem + OFF_KRF_LO);
   _Float16* sTbh = reinterpret_cast<_Float16*>(smem + OFF_TB_HI);
@@ -131,7 +142,8 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   float* sNB = reinterpret_cast<float*>(smem + OFF_NB);
   float* sB = reinterpret_cast<float*>(smem + OFF_B);
   int* sFlag = reinterpret_cast<int*>(smem + OFF_FLAG);
-  int* sClaim = sFlag + 4;
+  int* sClaim = sFlag + 8;
+  int* sDest = sFlag + 9;
 
   const int H = a.H;
 
@@ -142,16 +154,16 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   ChunkMap map = a.map;
   map.cu = cu;
   map.choff = choff;
-  const int64_t nchunk = total_chunks(map);
-  const int items = (int)(nchunk * H);
+  const int64_t nchunk = FUSED ? (int64_t)fz.nchunk : total_chunks(map);
+  const int items = FUSED ? (int)nchunk * fz.hx : (int)(nchunk * H);
   // The first two items of a workgroup are blockIdx.x and blockIdx.x + grid;
   // after that it claims items from a counter (one claim per processed item,
   // made an item ahead so that its latency stays hidden), so workgroups that
   // run faster take more items and all finish together.  Claims only grow:
   // once a workgroup's next item is past the end, so is every later claim.
-  int item = blockIdx.x;
+  int item = first;
   if (item >= items) return;
-  int next = item + (int)gridDim.x;
+  int next = item + stride;
   // ready tags hold the item whose data they publish; no item is -1.  Tags
   // 0-3: row-block b (its A blocks, and T_bb for b < 3); 5: A_33; 6: T_33.
   if (threadIdx.x < 8) sFlag[threadIdx.x] = -1;
@@ -165,6 +177,17 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   float dtb, alog;
   auto locate = [&](int it, int& hh, int64_t& gg, int64_t& cc0, int& LL) {
     it = __builtin_amdgcn_readfirstlane(it);  // wave-uniform: scalar math and loads
+    if constexpr (FUSED) {
+      // one sequence: chunk it / hx of head xcd + 8 (it % hx), first to last
+      const int ch = it / fz.hx;
+      hh = fz.xcd + 8 * (it - ch * fz.hx);
+      gg = ch;
+      int64_t bos, eos;
+      seq_bounds(map, 0, bos, eos);
+      cc0 = bos + (int64_t)ch * CH;
+      LL = (int)((eos - cc0) < CH ? (eos - cc0) : CH);
+      return;
+    }
     // chunks are produced last to first: the consumer starts at chunk 0, whose
     // records are then the most recently written (likeliest still in cache)
     hh = it % H;
@@ -243,19 +266,25 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   const int gq = lane >> 4;
   const int ti = 16 * w + tl;  // this lane's token within the chunk
   KDA_TIMER_MARK(0);
+  // Fused: a ring slot when the chain has moved past the slot's previous
+  // chunk (consumed >= g - R + 1), else the record's own place in recs.  One
+  // thread decides (before the sNB barrier below, shared through LDS), so that
+  // every wave writes the record to the same place.
+  if constexpr (FUSED) {
+    if (threadIdx.x == 0) {
+      const int done = __builtin_amdgcn_raw_buffer_load_b32(buf(fz.consumed, (uint32_t)(fz.H * FUSED_LINE)), 0,
+                                                             h * FUSED_LINE, SC1);
+      sDest[0] = (g < (int64_t)done + fz.ring) ? 1 : 2;
+    }
+  }
   char* rec = recs + ((size_t)g * H + h) * REC_BYTES;
-  _Float16* gNW = reinterpret_cast<_Float16*>(rec + REC_NW);
-  _Float16* gQG = reinterpret_cast<_Float16*>(rec + REC_QG);
-  _Float16* gKTH = reinterpret_cast<_Float16*>(rec + REC_KTH);
-  _Float16* gKTL = reinterpret_cast<_Float16*>(rec + REC_KTL);
-  _Float16* gAQK = reinterpret_cast<_Float16*>(rec + REC_AQK);
-  __bf16* gTBH = reinterpret_cast<__bf16*>(rec + REC_TBH);
-  __bf16* gTBL = reinterpret_cast<__bf16*>(rec + REC_TBL);
-  float* gGL = reinterpret_cast<float*>(rec + REC_GL);
+  _Float16 *gNW, *gQG, *gKTH, *gKTL, *gAQK;
+  __bf16 *gTBH, *gTBL;
+  float* gGL;
   const bool valid = ti < L;
   // claim the item after next (the value is shared before the operands barrier)
   int claimed = 0;
-  if (threadIdx.x == 0) claimed = atomicAdd(a.claim, 1);
+  if (threadIdx.x == 0) claimed = atomicAdd(claim, 1);
   // the next item's place (scalar table lookups, overlapped with this item)
   const bool more = next < items;
   int h2, L2;
@@ -271,6 +300,19 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   if (tid < KD) sNB[tid] = na * dtb;
   __syncthreads();  // sNB
   KDA_TIMER_MARK(1);
+  int dest = 2;
+  if constexpr (FUSED) {
+    dest = __builtin_amdgcn_readfirstlane(sDest[0]);
+    if (dest == 1) rec = fz.ringbuf + ((size_t)h * fz.ring + (size_t)(g % fz.ring)) * REC_BYTES;
+  }
+  gNW = reinterpret_cast<_Float16*>(rec + REC_NW);
+  gQG = reinterpret_cast<_Float16*>(rec + REC_QG);
+  gKTH = reinterpret_cast<_Float16*>(rec + REC_KTH);
+  gKTL = reinterpret_cast<_Float16*>(rec + REC_KTL);
+  gAQK = reinterpret_cast<_Float16*>(rec + REC_AQK);
+  gTBH = reinterpret_cast<__bf16*>(rec + REC_TBH);
+  gTBL = reinterpret_cast<__bf16*>(rec + REC_TBL);
+  gGL = reinterpret_cast<float*>(rec + REC_GL);
 
   // ============================ prep ======================================
   float gl[4][8];
@@ -400,7 +442,7 @@ __global__ void __launch_bounds__(NTHREADS, 2)
       const float kt = yv[e] * EL[e];               // k^ exp(G_L - G_t)
       const _Float16 kth = (_Float16)kt;
       kth8[e] = kth;
-      ktl8[e] = (_Float16)(kt - (float)kth);
+      ktl8[e] = (_Float16)((kt - (float)kth) * KT_LO_SCALE);
       qg[e] = (_Float16)(qv[e] * EP[e]);            // q^ exp(G_t)
     }
     split_bf16x8(xv, kLFh[kb], kLFl[kb]);
@@ -432,7 +474,7 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   if (threadIdx.x == 0) *sClaim = claimed;
   __syncthreads();
   KDA_TIMER_MARK(4);
-  const int next2 = __builtin_amdgcn_readfirstlane(*sClaim) + 2 * (int)gridDim.x;
+  const int next2 = __builtin_amdgcn_readfirstlane(*sClaim) + 2 * stride;
 
   // Wait until tag `t` holds this item (release/acquire on the LDS tag word).
   // Tags 0-3 and 5 are published with no wait before them, and tag 6 only
@@ -699,17 +741,125 @@ __global__ void __launch_bounds__(NTHREADS, 2)
     }
   }
   KDA_TIMER_MARK(8);
-  if (!more) break;
+  if constexpr (FUSED) {
+    // publish: every wave's record stores have completed (reached L2) before
+    // the ready flag is written (it holds where the record went)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __builtin_amdgcn_raw_buffer_store_b32(dest, buf(fz.flags, (uint32_t)fz.nchunk * fz.H * 4), 0,
+                                            (int)(g * H + h) * 4, SC1);
+    if (!more) break;
+  } else {
+    if (!more) break;
+    __syncthreads();  // LDS of this item is read above until the W phase
+  }
   item = next;
   next = next2;
   h = h2; g = g2; c0 = c02; L = L2;
-  __syncthreads();  // LDS of this item is read above until the W phase
   KDA_TIMER_MARK(9);
   }
   KDA_TIMER_STORE(a.timers);
 }
 
+namespace {
+
+template <bool GATE_GIVEN>
+__global__ void __launch_bounds__(NTHREADS, 2)
+    kda_intra_kernel(IntraArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ choff,
+                     const float* __restrict__ A_log, char* __restrict__ recs) {
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  const IntraFused none{};
+  intra_items<GATE_GIVEN, false>(a, cu, choff, A_log, recs, smem, (int)blockIdx.x, (int)gridDim.x, a.claim, none);
+}
+
 }  // namespace
+
+namespace {
+
+constexpr int FUSED_LDS = LDS_BYTES > chain::LDS_BYTES ? LDS_BYTES : chain::LDS_BYTES;
+constexpr int HW_REG_XCC_ID = (3 << 11) | 20;  // s_getreg operand: XCC_ID, bits 0-3
+
+// Clears the fused pipeline's ready flags, consumed and claim counters and
+// the call's fault word (a kernel rather than a memset, so that a captured
+// graph replays it as a kernel node).
+__global__ void kda_fused_reset_kernel(int* __restrict__ flags, int nflags, int* __restrict__ consumed, int H,
+                                       int* __restrict__ claims, unsigned* __restrict__ faults) {
+  const int stride = (int)(gridDim.x * blockDim.x);
+  const int i0 = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  for (int i = i0; i < nflags; i += stride) flags[i] = 0;
+  for (int i = i0; i < H; i += stride) consumed[i * (FUSED_LINE / 4)] = 0;
+  if (i0 < 8) claims[i0 * (FUSED_LINE / 4)] = 0;
+  if (i0 == 0) *faults = 0u;
+}
+
+// The fused pipeline over one sequence.  Workgroup b runs on XCD x = b mod 8
+// (the dispatcher's round robin, checked against the XCC_ID register) as
+// local workgroup j = b / 8 of the XCD's nw.  The XCD owns heads x, x + 8, ...
+// (hx of them): its last hx workgroups are their chains (highest ids, so
+// dispatched last), the others intra-chunk producers of those heads' items in
+// chunk order.  Producers never wait on a chain (a record whose ring slot is
+// still in use goes to the record area instead), so all items get produced
+// whatever the residency, and every chain's waits end.
+template <bool GATE_GIVEN>
+__global__ void __launch_bounds__(NTHREADS, 2)
+    kda_fused_kernel(IntraArgs ia, ChainArgs ca, FusedArgs fa, const float* __restrict__ A_log,
+                     char* __restrict__ recs) {
+  __shared__ __attribute__((aligned(16))) char smem[FUSED_LDS];
+  const int x = (int)(blockIdx.x & 7);
+  const int j = (int)(blockIdx.x >> 3);
+  const int nw = (int)(gridDim.x >> 3);
+  if (threadIdx.x == 0 && (int)(__builtin_amdgcn_s_getreg(HW_REG_XCC_ID) & 7) != x)
+    atomicOr(fa.faults, FAULT_PLACEMENT);
+  const int H = ia.H;
+  const int hx = x < H ? (H - 1 - x) / 8 + 1 : 0;
+  if (j >= nw - hx) {
+    ChainFused cf;
+    cf.ringbuf = fa.ringbuf;
+    cf.ring = FUSED_RING;
+    cf.flags = fa.flags;
+    cf.consumed = fa.consumed;
+    cf.faults = fa.faults;
+    cf.nchunk = fa.nchunk;
+    chain::chain_run<true>(ca, cf, 0, x + 8 * (nw - 1 - j), smem);
+  } else {
+    IntraFused f;
+    f.xcd = x;
+    f.hx = hx;
+    f.ring = FUSED_RING;
+    f.ringbuf = fa.ringbuf;
+    f.consumed = fa.consumed;
+    f.flags = fa.flags;
+    f.H = H;
+    f.nchunk = fa.nchunk;
+    intra_items<GATE_GIVEN, true>(ia, nullptr, nullptr, A_log, recs, smem, j, nw - hx,
+                                  fa.claims + x * (FUSED_LINE / 4), f);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fused(const IntraArgs& iargs, const ChainArgs& cargs, const FusedArgs& fargs, hipStream_t st) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  IntraArgs ia = iargs;
+  ChainArgs ca = cargs;
+  FusedArgs fa = fargs;
+  int nflags = fa.nchunk * ia.H, H = ia.H;
+  void* rargs[] = {(void*)&fa.flags, (void*)&nflags, (void*)&fa.consumed, (void*)&H, (void*)&fa.claims,
+                   (void*)&fa.faults};
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_fused_reset_kernel), dim3(64), dim3(256), rargs, 0, st);
+  if (e != hipSuccess) return e;
+  const float* alog = ia.A_log;
+  char* recs = ia.rec;
+  void* kargs[] = {(void*)&ia, (void*)&ca, (void*)&fa, (void*)&alog, (void*)&recs};
+  const void* fn = (ia.flags & FLAG_GATE_GIVEN) ? reinterpret_cast<const void*>(&kda_fused_kernel<true>)
+                                                : reinterpret_cast<const void*>(&kda_fused_kernel<false>);
+  // two workgroups per CU: all of them resident at once on an idle GPU
+  return hipLaunchKernel(fn, dim3((unsigned)(2 * cus)), dim3(NTHREADS), kargs, 0, st);
+}
 
 hipError_t launch_intra(const IntraArgs& args, int64_t max_chunks, hipStream_t st) {
   // persistent grid: two resident workgroups per CU (LDS and register budget)

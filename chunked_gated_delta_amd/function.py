@@ -10,7 +10,8 @@ from __future__ import annotations
 
 import torch
 
-from . import FLAG_REUSE_RECORDS, kda_bwd_ex, kda_bwd_workspace_size, kda_fwd, kda_workspace_size
+from . import (FLAG_KEEP_RECORDS, FLAG_REUSE_RECORDS, kda_bwd_ex, kda_bwd_workspace_size, kda_fwd_ex,
+               kda_workspace_size)
 
 __all__ = ["kda_chunk"]
 
@@ -31,8 +32,8 @@ class _KdaChunk(torch.autograd.Function):
         final_state = torch.empty(N, H, K, V, dtype=torch.float32, device=q.device)
         size = kda_bwd_workspace_size(B * T, H, N) if reuse_records else kda_workspace_size(B * T, H, N)
         ws = torch.empty(max(size, 1), dtype=torch.uint8, device=q.device)
-        kda_fwd(q, k, v, raw_gate, raw_beta, scale, out, ws, A_log, dt_bias, lower_bound, initial_state,
-                final_state, cu_seqlens)
+        kda_fwd_ex(q, k, v, raw_gate, raw_beta, scale, out, ws, A_log, dt_bias, lower_bound, initial_state,
+                   final_state, cu_seqlens, flags=FLAG_KEEP_RECORDS if reuse_records else 0)
         ctx.save_for_backward(q, k, v, raw_gate, raw_beta, A_log, dt_bias, initial_state, cu_seqlens)
         ctx.scale, ctx.lower_bound = scale, lower_bound
         # the backward workspace starts with the forward's layout: keep it, records included

@@ -94,6 +94,10 @@ int kda_is_supported(int64_t K, int64_t V, float lower_bound);
  *   B, T, H, K, V, N sizes as above (T >= 0; B, H, N >= 1)
  *   stream      hipStream_t as void*
  *
+ * The call builds the chunk records of all chunks first (one launch) and runs
+ * the recurrence over them afterwards (a second launch); kda_fwd_ex with
+ * KDA_FLAG_SINGLE_LAUNCH offers a one-launch pipeline for one sequence.
+ *
  * With few (sequence, head) pairs and long sequences (states not in place, not
  * KDA_FLAG_STATE_VK), the call runs its recurrence on shards of each sequence
  * and folds their affine maps (the kda_shard_affine / kda_shard_scan algebra)
@@ -214,18 +218,41 @@ kda_status_t kda_decode(const void* q, const void* k, const void* v, const void*
  * the per-(chunk, head) records that the previous call on this workspace left
  * there, for the second pass of the split-sequence flow (the KCP item of the
  * torchtitan PR page, "Summary"): kda_shard_affine, kda_shard_scan, then
- * kda_fwd_ex over the same shard batch from the scanned entering states.  The
- * records depend on q, k, raw_gate, raw_beta, A_log, dt_bias, lower_bound,
- * cu_seqlens, B, T, H, N and the GATE_GIVEN, BETA_GIVEN and NO_QK_NORM bits,
- * not on v or the states.  The caller guarantees that all of these equal those
- * of the call that wrote the records and that the workspace is unchanged since;
- * nothing checks it, and other records give wrong results.
+ * kda_fwd_ex over the same shard batch from the scanned entering states; or for
+ * a backward after its forward (kda_bwd_ex after kda_fwd_ex with
+ * KDA_FLAG_KEEP_RECORDS on the backward-sized workspace).  Records are left in
+ * the workspace by kda_shard_affine and by kda_fwd_ex with KDA_FLAG_KEEP_RECORDS;
+ * a forward without it may keep only a bounded ring of them.  The records
+ * depend on q, k, raw_gate, raw_beta, A_log, dt_bias, lower_bound, cu_seqlens,
+ * B, T, H, N and the GATE_GIVEN, BETA_GIVEN and NO_QK_NORM bits, not on v or
+ * the states.  The caller guarantees that all of these equal those of the call
+ * that wrote the records and that the workspace is unchanged since; nothing
+ * checks it, and other records give wrong results.
  */
 #define KDA_FLAG_REUSE_RECORDS 16u
 
 /*
- * kda_fwd with variant flags (any OR of the KDA_FLAG_* bits; other bits give
- * KDA_ERR_INVALID).  Every other argument is as for kda_fwd, and
+ * KDA_FLAG_KEEP_RECORDS (kda_fwd_ex only): build every chunk record into the
+ * workspace and leave it there for a later call with KDA_FLAG_REUSE_RECORDS
+ * (this rules out KDA_FLAG_SINGLE_LAUNCH).
+ */
+#define KDA_FLAG_KEEP_RECORDS 32u
+
+/*
+ * KDA_FLAG_SINGLE_LAUNCH (kda_fwd_ex only): with one sequence (N == 1), at
+ * least 16 heads, no shard split and a GPU of 8 equal XCDs (MI355X), run the
+ * forward as one persistent launch: per XCD, workgroups that build the chunk
+ * records of that XCD's heads hand them, through a small ring in the XCD's
+ * L2, to one workgroup per head that runs the recurrence, so records need not
+ * travel to HBM and back.  It gives the same bits as the two-launch schedule.
+ * Where the call does not meet these conditions the bit is ignored; it is
+ * also ignored with KDA_FLAG_KEEP_RECORDS or KDA_FLAG_REUSE_RECORDS.
+ */
+#define KDA_FLAG_SINGLE_LAUNCH 64u
+
+/*
+ * kda_fwd with variant flags (any OR of the KDA_FLAG_* bits above,
+ * KDA_FLAG_KEEP_RECORDS and KDA_FLAG_SINGLE_LAUNCH; other bits give KDA_ERR_INVALID).  Every other argument is as for kda_fwd, and
  * kda_fwd(...) == kda_fwd_ex(..., 0, stream).
  */
 kda_status_t kda_fwd_ex(const void* q, const void* k, const void* v, const void* raw_gate,
@@ -284,8 +311,9 @@ kda_status_t kda_bwd(const void* q, const void* k, const void* v, const void* ra
                      int64_t H, int64_t K, int64_t V, int64_t N, void* stream);
 
 /*
- * kda_bwd for the variants of kda_fwd_ex (any OR of the KDA_FLAG_* bits; other
- * bits give KDA_ERR_INVALID): the gradients of the kda_fwd_ex call with the
+ * kda_bwd for the variants of kda_fwd_ex (any OR of KDA_FLAG_GATE_GIVEN,
+ * KDA_FLAG_BETA_GIVEN, KDA_FLAG_NO_QK_NORM, KDA_FLAG_STATE_VK and
+ * KDA_FLAG_REUSE_RECORDS; other bits give KDA_ERR_INVALID): the gradients of the kda_fwd_ex call with the
  * same inputs and flags.  With KDA_FLAG_GATE_GIVEN, d_raw_gate is the gradient
  * with respect to the given decay (which must lie in [lower_bound, 0], as for
  * kda_fwd_ex); A_log and dt_bias are
@@ -317,10 +345,15 @@ kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void*
  *   KDA_FAULT_GATE_RANGE    KDA_FLAG_GATE_GIVEN with a decay outside
  *                           [lower_bound, 0]
  *   KDA_FAULT_QK_NORM       KDA_FLAG_NO_QK_NORM with |q|^2 or |k|^2 > 1 + 1/16
+ *   KDA_FAULT_PLACEMENT     a workgroup of the single-launch schedule ran on
+ *                           another XCD than the one planned (workgroup b on
+ *                           XCD b mod 8): records may then have been read from
+ *                           another XCD's cache, and the results are invalid
  */
 #define KDA_FAULT_WAIT_TIMEOUT 1u
 #define KDA_FAULT_GATE_RANGE 2u
 #define KDA_FAULT_QK_NORM 4u
+#define KDA_FAULT_PLACEMENT 8u
 
 /*
  * Read the fault word of the last call on `workspace` (a device buffer passed

@@ -211,8 +211,12 @@ def fwd_ex_call(flags, **over):
 
 
 def test_fwd_ex_flag_checks():
-    assert fwd_ex_call(32) == INVALID                     # unknown bit
+    assert fwd_ex_call(128) == INVALID                    # unknown bit
     assert fwd_ex_call(1 << 31) == INVALID
+    # the single-launch schedule is a known bit (ignored where the call does not qualify)
+    assert fwd_ex_call(kda.FLAG_SINGLE_LAUNCH, ws_bytes=8) == WORKSPACE
+    # keeping the records is a known bit
+    assert fwd_ex_call(kda.FLAG_KEEP_RECORDS, ws_bytes=8) == WORKSPACE
     # reusing the workspace's records is a known bit: the call proceeds to the workspace check
     assert fwd_ex_call(kda.FLAG_REUSE_RECORDS, ws_bytes=8) == WORKSPACE
     assert fwd_ex_call(0, A_log=None) == INVALID          # gate parameters needed without GATE_GIVEN
@@ -270,7 +274,8 @@ def bwd_ex_call(flags, **over):
 
 
 def test_bwd_ex_flag_checks():
-    assert bwd_ex_call(32) == INVALID                       # unknown bit
+    assert bwd_ex_call(32) == INVALID                       # unknown bit (KEEP_RECORDS is forward-only)
+    assert bwd_ex_call(64) == INVALID                       # so is SINGLE_LAUNCH
     assert bwd_ex_call(kda.FLAG_REUSE_RECORDS) == WORKSPACE  # a known bit: on to the workspace check
     assert bwd_ex_call(0, A_log=None) == INVALID            # gate parameters needed without GATE_GIVEN
     assert bwd_ex_call(0, dA=None) == INVALID
@@ -286,7 +291,7 @@ def test_fault_word_query_rejects_null_arguments():
     assert lib.kda_workspace_faults(None, ctypes.byref(word), None) == 1
     assert lib.kda_workspace_faults(FAKE, None, None) == 1
     assert word.value == 7  # untouched on rejection
-    assert (kda.FAULT_WAIT_TIMEOUT, kda.FAULT_GATE_RANGE, kda.FAULT_QK_NORM) == (1, 2, 4)
+    assert (kda.FAULT_WAIT_TIMEOUT, kda.FAULT_GATE_RANGE, kda.FAULT_QK_NORM, kda.FAULT_PLACEMENT) == (1, 2, 4, 8)
 
 
 def test_workspace_sizes_grow_with_the_batch():

@@ -68,8 +68,8 @@ def test_q_and_k_as_one_tensor_sum_their_gradients():
 
 
 def test_backward_on_the_forward_records_is_exact():
-    """kda_bwd_ex with FLAG_REUSE_RECORDS after kda_fwd on the same (backward-sized)
-    workspace gives the same bits as kda_bwd rebuilding the records."""
+    """kda_bwd_ex with FLAG_REUSE_RECORDS after kda_fwd_ex with FLAG_KEEP_RECORDS on the
+    same (backward-sized) workspace gives the same bits as kda_bwd rebuilding the records."""
     x = W.random_inputs("fn_reuse", 65, 1, 300, 3, lengths=[100, 200])
     t = {n: getattr(x, n).to(DEV) for n in ("q", "k", "v", "raw_gate", "raw_beta", "A_log", "dt_bias",
                                              "initial_state", "cu_seqlens")}
@@ -90,8 +90,9 @@ def test_backward_on_the_forward_records_is_exact():
     out = torch.empty_like(t["v"])
     fin = torch.empty(N, H, K, V, device=DEV)
     print("kda_fwd then kda_bwd_ex(REUSE_RECORDS) on one workspace", flush=True)
-    kda.kda_fwd(t["q"], t["k"], t["v"], t["raw_gate"], t["raw_beta"], x.scale, out, ws, t["A_log"], t["dt_bias"],
-                x.lower_bound, t["initial_state"], fin, t["cu_seqlens"])
+    kda.kda_fwd_ex(t["q"], t["k"], t["v"], t["raw_gate"], t["raw_beta"], x.scale, out, ws, t["A_log"],
+                   t["dt_bias"], x.lower_bound, t["initial_state"], fin, t["cu_seqlens"],
+                   flags=kda.FLAG_KEEP_RECORDS)
     reused = grads(ws, kda.FLAG_REUSE_RECORDS)
     fresh = grads(torch.empty(size, dtype=torch.uint8, device=DEV), 0)
     torch.cuda.synchronize()
