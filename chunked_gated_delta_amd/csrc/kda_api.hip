@@ -255,7 +255,9 @@ static bool use_fused(const Prepared& pr, unsigned flags, int64_t T_total, bool 
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return false;
-  return cus >= 192 && cus % 8 == 0;
+  // per XCD 2 cus / 8 workgroups, at most half of them chains
+  const int64_t hx = (pr.ia.H + 7) / 8;
+  return cus >= 192 && cus % 8 == 0 && FUSED_CHAINS * hx <= cus / 8;
 }
 
 InterArgs inter_args(const Prepared& pr, int64_t H) {
@@ -400,6 +402,8 @@ kda_status_t kda_fwd_ex(const void* q, const void* k, const void* v, const void*
     fa.claims = reinterpret_cast<int*>(pr.ws + pr.lay.fclaims);
     fa.faults = reinterpret_cast<unsigned*>(pr.ws + pr.lay.faults);
     fa.nchunk = (int)((B * T + CH - 1) / CH);
+    fa.ring = FUSED_RING;
+    fa.slot_wait = FUSED_SLOT_WAIT;
     return launch_status(launch_fused(ia, ca, fa, st), "fused");
   }
   if (!(flags & FLAG_REUSE_RECORDS) &&

@@ -1,5 +1,7 @@
 // Chain kernel of the gfx950 KDA forward: the sequential recurrence over the
-// chunks of one (sequence, head), all 128 state columns in one workgroup.
+// chunks of one (sequence, head), on NQ column quarters of 32 state columns
+// (NQ = 4: all 128 columns in one workgroup; NQ = 2: one 64-column half, two
+// workgroups per (sequence, head)).
 //
 // It computes what the inter-chunk kernel computes, from the same per-chunk
 // records of the intra-chunk kernel (kda_common.h), for each chunk:
@@ -8,24 +10,24 @@
 //     O = scale [ (Q exp(G)) S + A_qk D ]   -> bf16 output
 //     S = Diag(exp(G_L)) S + (K exp(G_L - G))^T D   (fp16 hi/lo x fp16 hi/lo)
 // with every product, operand split and accumulation order of that kernel,
-// so the two give the same bits.  Where the inter kernel spends two
-// workgroups (two 64-column halves) and 337 registers per lane on a chain,
-// this one spends one workgroup of 4 waves and at most 256 registers, with
-// 72.7 KB of LDS: two of them, or one of them and one intra-chunk workgroup,
-// fit on a CU.  The cost is that record operands are not prefetched a whole
-// chunk ahead (no room for a second register set): each group is loaded when
-// its previous use ends.
+// so the two give the same bits.  Where the inter kernel holds 337 registers
+// per lane (its record operands prefetched a whole chunk ahead), this one
+// holds at most 256, so that two of its workgroups, or one of them and one
+// intra-chunk workgroup, fit on a CU.  The cost is that record operands are
+// not prefetched a whole chunk ahead (no room for a second register set):
+// each group is loaded when its previous use ends.
 //
-// Wave w owns the state rows (channels) 32w..32w+31 of all 128 columns, 64
-// registers of fp32 accumulators, and the token rows 16w..16w+15 of U, D and
-// O.  A chunk step runs four column quarters q (32 columns, tiles 2q, 2q+1):
+// Wave w owns the state rows (channels) 32w..32w+31 of the workgroup's
+// columns (16 NQ registers of fp32 accumulators per row tile) and the token
+// rows 16w..16w+15 of U, D and O.  A chunk step runs the column quarters q
+// (32 columns, tiles 2q, 2q+1):
 //     A_q: U and D of quarter q, and the state part of O      -> D hi/lo to LDS
 //     barrier
 //     B_q: O += A_qk D; the state update of quarter q; the new fp16 state
 //          copy of quarter q; quarter q of the next chunk's V tile
-// in the order A0 | B0 A1 | B1 A2 | B2 A3 | B3.  D alternates between two
-// LDS buffers, so B_q and A_{q+1} need no barrier between them; every LDS
-// region a phase writes was last read before the barrier that precedes it.
+// in the order A0 | B0 A1 | B1 ... | B(NQ-1).  D alternates between two LDS
+// buffers, so B_q and A_{q+1} need no barrier between them; every LDS region
+// a phase writes was last read before the barrier that precedes it.
 
 #pragma once
 
@@ -37,12 +39,16 @@ namespace chain {
 constexpr int NTHREADS = 256;
 constexpr int VTP = CH + 8;      // token pitch of the V^T tile (halves)
 constexpr int OQP = 32 + 8;      // column pitch of the output staging rows (halves)
-constexpr int OFF_VT = 0;                          // bf16 [128 columns][VTP]       V^T
-constexpr int OFF_ST = OFF_VT + VD * VTP * 2;      // f16 32 fragments (4 nn + kb)  state copy
-constexpr int OFF_D = OFF_ST + 32 * FRAG;          // 2 buffers x 8 fragments      D hi (0-3), lo (4-7)
-constexpr int OFF_O = OFF_D + 2 * 8 * FRAG;        // bf16 [64 tokens][OQP]        output staging
-constexpr int LDS_BYTES = OFF_O + CH * OQP * 2;    // 72,704
-static_assert(LDS_BYTES <= 80 * 1024, "two workgroups per CU");
+template <int NQ>
+struct Lay {
+  static constexpr int NCOL = 32 * NQ;                      // state columns of the workgroup
+  static constexpr int OFF_VT = 0;                          // bf16 [NCOL columns][VTP]   V^T
+  static constexpr int OFF_ST = OFF_VT + NCOL * VTP * 2;    // f16 8 NQ fragments (4 nn + kb)  state copy
+  static constexpr int OFF_D = OFF_ST + 8 * NQ * FRAG;      // 2 buffers x 8 fragments   D hi (0-3), lo (4-7)
+  static constexpr int OFF_O = OFF_D + 2 * 8 * FRAG;        // bf16 [64 tokens][OQP]      output staging
+  static constexpr int LDS_BYTES = OFF_O + CH * OQP * 2;    // NQ = 4: 72,704; NQ = 2: 47,104
+  static_assert(LDS_BYTES <= 80 * 1024, "two workgroups per CU");
+};
 
 // Record operands of the A phases (U, D, the state part of O) and of the B
 // phases (the A_qk D part of O, the state update), per wave.
@@ -99,19 +105,22 @@ __device__ __forceinline__ void load_b(BOps& o, __amdgpu_buffer_rsrc_t r, int w,
 }
 
 // The V tile of a chunk, per thread: token t = tid / 4 and, for each quarter
-// q, the 8 columns 32q + 8p..+7 (p = tid % 4), as 4 packed dwords.  Rows past
-// the chunk end are loaded from the clamped last row and zeroed when written.
-// `r` covers the chunk's rows from its first token.
+// q, the 8 columns 32q + 8p..+7 (p = tid % 4) of the workgroup's columns, as
+// 4 packed dwords.  Rows past the chunk end are loaded from the clamped last
+// row and zeroed when written.  `r` covers the chunk's rows from its first
+// token and the workgroup's first column.
+template <int NQ>
 struct VTile {
-  uint32_t d[4][4];
+  uint32_t d[NQ][4];
 };
-__device__ __forceinline__ void load_vtile(VTile& vv, __amdgpu_buffer_rsrc_t r, int L, int H, int tid) {
+template <int NQ>
+__device__ __forceinline__ void load_vtile(VTile<NQ>& vv, __amdgpu_buffer_rsrc_t r, int L, int H, int tid) {
   const int t = tid >> 2;
   const int p = tid & 3;
   const int tc = t < L ? t : L - 1;  // L >= 1: the clamped row is inside the sequence
   const int voff = (tc * H * VD + 8 * p) * 2;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < NQ; ++q) {
     const u32x4 x = bload<u32x4>(r, voff, 64 * q);
     vv.d[q][0] = x[0]; vv.d[q][1] = x[1]; vv.d[q][2] = x[2]; vv.d[q][3] = x[3];
   }
@@ -123,7 +132,8 @@ __device__ __forceinline__ void load_vtile(VTile& vv, __amdgpu_buffer_rsrc_t r, 
 // Write quarter q of the V tile transposed, 2 tokens per dword: the threads of
 // tokens t and t ^ 1 (4 lanes apart) trade half of their 8 columns, so each
 // writes 4 columns x 2 tokens.
-__device__ __forceinline__ void store_vt_quarter(__bf16* sVt, const VTile& vv, int q, int tid, int L) {
+template <int NQ>
+__device__ __forceinline__ void store_vt_quarter(__bf16* sVt, const VTile<NQ>& vv, int q, int tid, int L) {
   const int t = tid >> 2;
   const int p = tid & 3;
   const bool keep = t < L;
@@ -146,19 +156,20 @@ __device__ __forceinline__ void store_vt_quarter(__bf16* sVt, const VTile& vv, i
   }
 }
 
-// Load (STORE = false) or store a (sequence, head)'s state held as S[mt][nn]
-// (channels 32w + 16mt + 4gq + ii, columns 16nn + tl) through buffer
-// operations: one lane offset, every element's place a compile-time or
-// wave-uniform offset.  The lane offsets are re-derived from an opaque thread
-// id, so none of them stays live across the chunk loop.  A null pointer
-// leaves zeros (load) or writes nothing (store).
-template <bool STORE>
-__device__ __forceinline__ void state_io(f32x4 (&S)[2][8], const float* p, int vk, int seq, int h, int H) {
+// Load (STORE = false) or store the workgroup's columns vs.. of a (sequence,
+// head)'s state held as S[mt][nn] (channels 32w + 16mt + 4gq + ii, columns
+// vs + 16nn + tl) through buffer operations: one lane offset, every element's
+// place a compile-time or wave-uniform offset.  The lane offsets are
+// re-derived from an opaque thread id, so none of them stays live across the
+// chunk loop.  A null pointer leaves zeros (load) or writes nothing (store).
+template <bool STORE, int NQ>
+__device__ __forceinline__ void state_io(f32x4 (&S)[2][2 * NQ], const float* p, int vk, int seq, int h, int H,
+                                         int vs) {
   if (!STORE) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn) S[mt][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nn = 0; nn < 2 * NQ; ++nn) S[mt][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   if (!p) return;
   int tid = threadIdx.x;
@@ -173,8 +184,8 @@ __device__ __forceinline__ void state_io(f32x4 (&S)[2][8], const float* p, int v
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn) {
-        const int soff = (16 * nn * KD + 32 * w + 16 * mt) * 4;
+      for (int nn = 0; nn < 2 * NQ; ++nn) {
+        const int soff = ((vs + 16 * nn) * KD + 32 * w + 16 * mt) * 4;
         if (STORE)
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, S[mt][nn]), r, voff, soff, 0);
         else
@@ -186,13 +197,13 @@ __device__ __forceinline__ void state_io(f32x4 (&S)[2][8], const float* p, int v
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn) {
+      for (int nn = 0; nn < 2 * NQ; ++nn) {
         // whole-vector bit casts: a cast of one element of S[mt][nn] straight
         // into the store builtin has stored element 0 for every element
         u32x4 bits = __builtin_bit_cast(u32x4, S[mt][nn]);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          const int soff = ((32 * w + 16 * mt + ii) * VD + 16 * nn) * 4;
+          const int soff = ((32 * w + 16 * mt + ii) * VD + vs + 16 * nn) * 4;
           if (STORE)
             __builtin_amdgcn_raw_buffer_store_b32(bits[ii], r, voff, soff, 0);
           else
@@ -203,16 +214,19 @@ __device__ __forceinline__ void state_io(f32x4 (&S)[2][8], const float* p, int v
   }
 }
 
-// One (sequence, head) chain: all its chunks, from its initial state to its
-// final state.  `smem` is this workgroup's LDS_BYTES.  FUSED: the single
-// sequence of a fused pipeline; each chunk's record is read once its ready
-// flag says where it is (ring slot or record area), and after every chunk the
-// chain publishes how many records it has finished reading (ChainFused).
-template <bool FUSED>
-__device__ __forceinline__ void chain_run(const ChainArgs& a, const ChainFused& fz, int seq, int h, char* smem) {
-  __bf16* sVt = reinterpret_cast<__bf16*>(smem + OFF_VT);
-  char* sSt = smem + OFF_ST;
-  __bf16* sO = reinterpret_cast<__bf16*>(smem + OFF_O);
+// One (sequence, head) chain on the state columns vs .. vs + 32 NQ - 1: all
+// its chunks, from its initial state to its final state.  `smem` is this
+// workgroup's Lay<NQ>::LDS_BYTES.  FUSED: the single sequence of a fused
+// pipeline; each chunk's record is read once its ready flag says where it is
+// (ring slot or record area), and after every chunk the chain publishes how
+// many records it has finished reading (ChainFused::consumed, its own line).
+template <bool FUSED, int NQ>
+__device__ __forceinline__ void chain_run(const ChainArgs& a, const ChainFused& fz, int seq, int h, int vs,
+                                          char* smem) {
+  using LY = Lay<NQ>;
+  __bf16* sVt = reinterpret_cast<__bf16*>(smem + LY::OFF_VT);
+  char* sSt = smem + LY::OFF_ST;
+  __bf16* sO = reinterpret_cast<__bf16*>(smem + LY::OFF_O);
   const int H = a.H;
   int64_t bos, eos;
   seq_bounds(a.map, seq, bos, eos);
@@ -223,11 +237,12 @@ __device__ __forceinline__ void chain_run(const ChainArgs& a, const ChainFused& 
   const int lane = tid & 63;
   const int tl = lane & 15;
   const int gq = lane >> 4;
-  const int ksmax = (w >= 2) ? 2 : 1;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform: scalar offsets
+  const int ksmax = (wu >= 2) ? 2 : 1;
 
-  // state rows (channels) 32w + 16mt + 4gq + ii, columns 16nn + tl
-  f32x4 S[2][8];
-  state_io<false>(S, a.init, a.state_vk, seq, h, H);
+  // state rows (channels) 32w + 16mt + 4gq + ii, columns vs + 16nn + tl
+  f32x4 S[2][2 * NQ];
+  state_io<false, NQ>(S, a.init, a.state_vk, seq, h, H, vs);
   // fp16 copy of the state's column tile nn (both row tiles of this wave):
   // fragment (nn, kb = w) holds channels 32w.. of columns 16nn..
   auto store_st_tile = [&](int nn) {
@@ -239,7 +254,7 @@ __device__ __forceinline__ void chain_run(const ChainArgs& a, const ChainFused& 
     }
   };
 #pragma unroll
-  for (int nn = 0; nn < 8; ++nn) store_st_tile(nn);
+  for (int nn = 0; nn < 2 * NQ; ++nn) store_st_tile(nn);
 
   auto chunk_len = [&](int64_t c) { return (int)((eos - c) < CH ? (eos - c) : CH); };
   // buffer descriptors of a chunk's record and of its V rows (64 token rows
@@ -273,23 +288,23 @@ __device__ __forceinline__ void chain_run(const ChainArgs& a, const ChainFused& 
     return buf(base, (uint32_t)REC_BYTES);
   };
   constexpr int LP = FUSED ? SC1 : 0;
+  // (the last row's columns vs.. end inside the row, which ends the range)
   auto v_buf = [&](int64_t c) {
-    return buf(a.v + (c * H + h) * VD, (uint32_t)(((CH - 1) * H + 1) * VD * 2));
+    return buf(a.v + (c * H + h) * VD + vs, (uint32_t)(((CH - 1) * H + 1) * VD * 2 - vs * 2));
   };
-  const int wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform: scalar offsets
   const int lo16 = lane * 16;
   const int gq16 = gq * 16;
   AOps ao;
   BOps bo;
-  VTile vn;
+  VTile<NQ> vn;
   if (bos < eos) {
-    VTile v0;
+    VTile<NQ> v0;
     load_vtile(v0, v_buf(bos), chunk_len(bos), H, tid);
     const __amdgpu_buffer_rsrc_t r0 = rec_buf(gfirst);
     load_a<LP>(ao, r0, wu, lo16, ksmax);
     load_b<LP>(bo, r0, wu, lo16, gq16, ksmax);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) store_vt_quarter(sVt, v0, q, tid, chunk_len(bos));
+    for (int q = 0; q < NQ; ++q) store_vt_quarter(sVt, v0, q, tid, chunk_len(bos));
   }
   __syncthreads();
 
@@ -301,12 +316,12 @@ __device__ __forceinline__ void chain_run(const ChainArgs& a, const ChainFused& 
     // the next chunk's V tile (past the end: this chunk's again, never read)
     load_vtile(vn, v_buf(in1 ? c1 : c0), in1 ? chunk_len(c1) : L, H, tid);
     // the next chunk's record (past the end: this one's again), found when its
-    // A operands are first loaded, at the end of A3
+    // A operands are first loaded, at the end of the last A phase
     __amdgpu_buffer_rsrc_t nrec;
 
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      char* sDh = smem + OFF_D + (q & 1) * 8 * FRAG;
+    for (int q = 0; q < NQ; ++q) {
+      char* sDh = smem + LY::OFF_D + (q & 1) * 8 * FRAG;
       char* sDl = sDh + 4 * FRAG;
       // ---- A_q: U = T diag(b) V, D = U - W S, O = (Q exp(G)) S on the two
       // column tiles 2q, 2q + 1 of this wave's token rows.  The B operands
@@ -367,7 +382,7 @@ __device__ __forceinline__ void chain_run(const ChainArgs& a, const ChainFused& 
         frag_write4(sDh, 2 * j + (w >> 1), 4 * (w & 1) + gq, tl, dh);
         frag_write4(sDl, 2 * j + (w >> 1), 4 * (w & 1) + gq, tl, dl);
       }
-      if (q == 3) {
+      if (q == NQ - 1) {
         // the A operands are dead: the next chunk's (past the end, this one's again)
         nrec = rec_buf(in1 ? gch + 1 : gch);
         __builtin_amdgcn_sched_barrier(0);
@@ -377,9 +392,9 @@ __device__ __forceinline__ void chain_run(const ChainArgs& a, const ChainFused& 
       __syncthreads();
       if constexpr (FUSED) {
         // every wave has used (so finished loading) all of this chunk's record
-        if (q == 3 && threadIdx.x == 0)
-          __builtin_amdgcn_raw_buffer_store_b32((int)(gch + 1), buf(fz.consumed, (uint32_t)H * FUSED_LINE), 0,
-                                                h * FUSED_LINE, SC1);
+        if (q == NQ - 1 && threadIdx.x == 0)
+          __builtin_amdgcn_raw_buffer_store_b32((int)(gch + 1), buf(fz.consumed, (uint32_t)FUSED_LINE), 0, 0,
+                                                SC1);
       }
 
       // ---- B_q: O += A_qk D; S = Diag(exp(G_L)) S + Kt^T D on tiles 2q, 2q + 1
@@ -427,13 +442,13 @@ __device__ __forceinline__ void chain_run(const ChainArgs& a, const ChainFused& 
         const int ocol = 8 * (lane & 3);
         if (orow < L) {
           const uint4 val = *reinterpret_cast<const uint4*>(sO + orow * OQP + ocol);
-          *reinterpret_cast<uint4*>(a.out + ((c0 + orow) * H + h) * VD + 32 * q + ocol) = val;
+          *reinterpret_cast<uint4*>(a.out + ((c0 + orow) * H + h) * VD + vs + 32 * q + ocol) = val;
         }
       }
       // quarter q of the next chunk's V tile (every wave read this chunk's
       // quarter q before the barrier above)
       store_vt_quarter(sVt, vn, q, tid, in1 ? chunk_len(c1) : L);
-      if (q == 3) {
+      if (q == NQ - 1) {
         // the B operands are dead: the next chunk's
         __builtin_amdgcn_sched_barrier(0);
         load_b<LP>(bo, nrec, wu, lo16, gq16, ksmax);
@@ -442,7 +457,7 @@ __device__ __forceinline__ void chain_run(const ChainArgs& a, const ChainFused& 
     }
   }
 
-  state_io<true>(S, a.fin, a.state_vk, seq, h, H);
+  state_io<true, NQ>(S, a.fin, a.state_vk, seq, h, H, vs);
 }
 
 }  // namespace chain

@@ -214,27 +214,34 @@ constexpr unsigned FAULT_QK_NORM = 4u;       // FLAG_NO_QK_NORM: a q or k row wi
 constexpr unsigned FAULT_PLACEMENT = 8u;     // a fused-pipeline workgroup ran on another XCD than planned
 
 // The fused forward pipeline (one sequence): per XCD, intra-chunk producer
-// workgroups hand the chunk records of that XCD's heads (h = xcd + 8 l) to one
-// chain workgroup per head through a ring of FUSED_RING records per head, in
-// that XCD's L2.  The per-head and per-XCD words sit FUSED_LINE bytes apart
-// (one L2 line each).
+// workgroups hand the chunk records of that XCD's heads (h = xcd + 8 l) to the
+// FUSED_CHAINS chain workgroups of each head (one per 64-column half of the
+// state) through a ring of FUSED_RING records per head, in that XCD's L2.  The
+// per-chain and per-XCD words sit FUSED_LINE bytes apart (one L2 line each).
 constexpr int FUSED_LINE = 128;
-constexpr int FUSED_RING = 8;
+constexpr int FUSED_RING = 8;     // ring slots per head (workspace capacity)
+constexpr int FUSED_CHAINS = 2;
+// Polls (each an L2 round trip plus a 512-cycle sleep) a producer spends
+// waiting for its ring slot to be freed before it writes the record to the
+// record area instead: producers pace themselves to the chains while every
+// chain is running, and still finish on their own if a chain is not.
+constexpr int FUSED_SLOT_WAIT = 4096;
 struct IntraFused {
   int xcd = 0;               // the producer's XCD
   int hx = 0;                // heads of that XCD
-  int ring = 1;              // ring slots per head
-  char* ringbuf = nullptr;   // [H][ring] records
-  const int* consumed = nullptr;  // per head: chunks its chain has finished reading
+  int ring = 1;              // ring slots per head in use
+  int slot_wait = 0;         // polls for a free slot before the record area is used
+  char* ringbuf = nullptr;   // [H][FUSED_RING] records
+  const int* consumed = nullptr;  // [H][FUSED_CHAINS]: chunks each chain has finished reading
   int* flags = nullptr;      // [chunks][H]: 0 not ready, 1 in the ring, 2 in the record area
   int H = 0;
   int nchunk = 0;
 };
 struct ChainFused {
-  const char* ringbuf = nullptr;  // [H][ring] records
-  int ring = 1;
+  const char* ringbuf = nullptr;  // [H][FUSED_RING] records
+  int ring = 1;                   // ring slots per head in use
   const int* flags = nullptr;     // [chunks][H] ready flags
-  int* consumed = nullptr;        // per head (FUSED_LINE apart)
+  int* consumed = nullptr;        // this chain's own consumed word
   unsigned* faults = nullptr;
   int nchunk = 0;
 };
@@ -277,8 +284,8 @@ struct InterArgs {
   float* states;         // [chunks][H][K][V] state entering every chunk (fp32)
   float* dtile;          // [chunks][H][64][V] the chunk's D = U - W S (rows past the chunk end zero)
 };
-// The chain kernel: the inter-chunk recurrence with one workgroup per
-// (sequence, head), all 128 columns (same results as the inter kernel).
+// The chain kernel: the inter-chunk recurrence with two workgroups per
+// (sequence, head), one per 64-column half (same results as the inter kernel).
 struct ChainArgs {
   const uint16_t* v;
   uint16_t* out;
@@ -293,17 +300,20 @@ struct ChainArgs {
 };
 hipError_t launch_intra(const IntraArgs& a, int64_t max_chunks, hipStream_t st);
 hipError_t launch_chain(const ChainArgs& a, hipStream_t st);
-// The fused pipeline over one sequence: intra-chunk producers and one chain
-// workgroup per head in a single persistent launch (`fz` carries the ring,
-// flags, consumed counters, per-XCD claim counters and the fault word, all
-// cleared by the launcher first).  Needs 8 XCDs of equal size and N == 1.
+// The fused pipeline over one sequence: intra-chunk producers and
+// FUSED_CHAINS chain workgroups per head in a single persistent launch (`fa`
+// carries the ring, flags, consumed counters, per-XCD claim counters and the
+// fault word, all cleared by the launcher first).  Needs 8 XCDs of equal size
+// and N == 1.
 struct FusedArgs {
   char* ringbuf;
   int* flags;      // [chunks][H]
-  int* consumed;   // [H] FUSED_LINE apart
+  int* consumed;   // [H][FUSED_CHAINS] FUSED_LINE apart
   int* claims;     // [8] FUSED_LINE apart
   unsigned* faults;
   int nchunk;
+  int ring;        // ring slots per head in use, 1..FUSED_RING
+  int slot_wait;   // a producer's polls for a free ring slot
 };
 hipError_t launch_fused(const IntraArgs& ia, const ChainArgs& ca, const FusedArgs& fa, hipStream_t st);
 hipError_t launch_inter(const InterArgs& a, hipStream_t st);

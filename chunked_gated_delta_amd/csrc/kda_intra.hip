@@ -266,15 +266,31 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
   const int gq = lane >> 4;
   const int ti = 16 * w + tl;  // this lane's token within the chunk
   KDA_TIMER_MARK(0);
-  // Fused: a ring slot when the chain has moved past the slot's previous
-  // chunk (consumed >= g - R + 1), else the record's own place in recs.  One
-  // thread decides (before the sNB barrier below, shared through LDS), so that
-  // every wave writes the record to the same place.
+  // Fused: a ring slot once every chain of the head has moved past the slot's
+  // previous chunk (consumed >= g - R + 1), waited for at most slot_wait
+  // polls; else the record's own place in recs.  One thread decides (before
+  // the sNB barrier below, shared through LDS), so that every wave writes the
+  // record to the same place.
   if constexpr (FUSED) {
     if (threadIdx.x == 0) {
-      const int done = __builtin_amdgcn_raw_buffer_load_b32(buf(fz.consumed, (uint32_t)(fz.H * FUSED_LINE)), 0,
-                                                             h * FUSED_LINE, SC1);
-      sDest[0] = (g < (int64_t)done + fz.ring) ? 1 : 2;
+      const __amdgpu_buffer_rsrc_t cr = buf(fz.consumed, (uint32_t)(fz.H * FUSED_CHAINS * FUSED_LINE));
+      int dest = 2;
+      for (int spin = 0;; ++spin) {
+        int done = 0x7fffffff;
+#pragma unroll
+        for (int c = 0; c < FUSED_CHAINS; ++c) {
+          const int d = __builtin_amdgcn_raw_buffer_load_b32(cr, 0, (h * FUSED_CHAINS + c) * FUSED_LINE, SC1);
+          done = d < done ? d : done;
+        }
+        if (g < (int64_t)done + fz.ring) {
+          dest = 1;
+          break;
+        }
+        if (spin >= fz.slot_wait) break;
+        __builtin_amdgcn_s_sleep(8);
+        asm volatile("" ::: "memory");
+      }
+      sDest[0] = dest;
     }
   }
   char* rec = recs + ((size_t)g * H + h) * REC_BYTES;
@@ -777,7 +793,10 @@ __global__ void __launch_bounds__(NTHREADS, 2)
 
 namespace {
 
-constexpr int FUSED_LDS = LDS_BYTES > chain::LDS_BYTES ? LDS_BYTES : chain::LDS_BYTES;
+constexpr int FUSED_NQ = 2;  // chain workgroups own 64-column halves
+constexpr int FUSED_LDS =
+    LDS_BYTES > chain::Lay<FUSED_NQ>::LDS_BYTES ? LDS_BYTES : chain::Lay<FUSED_NQ>::LDS_BYTES;
+static_assert(FUSED_CHAINS * 32 * FUSED_NQ == VD, "chains cover the state columns");
 constexpr int HW_REG_XCC_ID = (3 << 11) | 20;  // s_getreg operand: XCC_ID, bits 0-3
 
 // Clears the fused pipeline's ready flags, consumed and claim counters and
@@ -788,7 +807,7 @@ __global__ void kda_fused_reset_kernel(int* __restrict__ flags, int nflags, int*
   const int stride = (int)(gridDim.x * blockDim.x);
   const int i0 = (int)(blockIdx.x * blockDim.x + threadIdx.x);
   for (int i = i0; i < nflags; i += stride) flags[i] = 0;
-  for (int i = i0; i < H; i += stride) consumed[i * (FUSED_LINE / 4)] = 0;
+  for (int i = i0; i < H * FUSED_CHAINS; i += stride) consumed[i * (FUSED_LINE / 4)] = 0;
   if (i0 < 8) claims[i0 * (FUSED_LINE / 4)] = 0;
   if (i0 == 0) *faults = 0u;
 }
@@ -796,11 +815,13 @@ __global__ void kda_fused_reset_kernel(int* __restrict__ flags, int nflags, int*
 // The fused pipeline over one sequence.  Workgroup b runs on XCD x = b mod 8
 // (the dispatcher's round robin, checked against the XCC_ID register) as
 // local workgroup j = b / 8 of the XCD's nw.  The XCD owns heads x, x + 8, ...
-// (hx of them): its last hx workgroups are their chains (highest ids, so
-// dispatched last), the others intra-chunk producers of those heads' items in
-// chunk order.  Producers never wait on a chain (a record whose ring slot is
-// still in use goes to the record area instead), so all items get produced
-// whatever the residency, and every chain's waits end.
+// (hx of them): its last FUSED_CHAINS hx workgroups are their chains (highest
+// ids, so dispatched last; the two column halves of a head are neighbours),
+// the others intra-chunk producers of those heads' items in chunk order.
+// A producer waits for a chain only a bounded time (a record whose ring slot
+// is still in use after FusedArgs::slot_wait polls goes to the record area
+// instead), so all items get produced whatever the residency, and every
+// chain's waits end.
 template <bool GATE_GIVEN>
 __global__ void __launch_bounds__(NTHREADS, 2)
     kda_fused_kernel(IntraArgs ia, ChainArgs ca, FusedArgs fa, const float* __restrict__ A_log,
@@ -813,26 +834,32 @@ __global__ void __launch_bounds__(NTHREADS, 2)
     atomicOr(fa.faults, FAULT_PLACEMENT);
   const int H = ia.H;
   const int hx = x < H ? (H - 1 - x) / 8 + 1 : 0;
-  if (j >= nw - hx) {
+  const int nchains = FUSED_CHAINS * hx;
+  if (j >= nw - nchains) {
+    const int c = nw - 1 - j;  // FUSED_CHAINS l + half
+    const int l = c / FUSED_CHAINS;
+    const int half = c - FUSED_CHAINS * l;
+    const int h = x + 8 * l;
     ChainFused cf;
     cf.ringbuf = fa.ringbuf;
-    cf.ring = FUSED_RING;
+    cf.ring = fa.ring;
     cf.flags = fa.flags;
-    cf.consumed = fa.consumed;
+    cf.consumed = fa.consumed + (h * FUSED_CHAINS + half) * (FUSED_LINE / 4);
     cf.faults = fa.faults;
     cf.nchunk = fa.nchunk;
-    chain::chain_run<true>(ca, cf, 0, x + 8 * (nw - 1 - j), smem);
+    chain::chain_run<true, FUSED_NQ>(ca, cf, 0, h, 32 * FUSED_NQ * half, smem);
   } else {
     IntraFused f;
     f.xcd = x;
     f.hx = hx;
-    f.ring = FUSED_RING;
+    f.ring = fa.ring;
+    f.slot_wait = fa.slot_wait;
     f.ringbuf = fa.ringbuf;
     f.consumed = fa.consumed;
     f.flags = fa.flags;
     f.H = H;
     f.nchunk = fa.nchunk;
-    intra_items<GATE_GIVEN, true>(ia, nullptr, nullptr, A_log, recs, smem, j, nw - hx,
+    intra_items<GATE_GIVEN, true>(ia, nullptr, nullptr, A_log, recs, smem, j, nw - nchains,
                                   fa.claims + x * (FUSED_LINE / 4), f);
   }
 }
