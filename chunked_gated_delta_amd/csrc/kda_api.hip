@@ -128,7 +128,7 @@ size_t kda_workspace_size(int64_t T_total, int64_t H, int64_t N) {
 }
 
 int kda_is_supported(int64_t K, int64_t V, float lower_bound) {
-  return K == KD && V == VD && lower_bound >= -5.0f && lower_bound <= 0.0f;
+  return (K == 64 || K == KD) && (V == 64 || V == VD) && lower_bound >= -5.0f && lower_bound <= 0.0f;
 }
 
 kda_status_t kda_workspace_faults(const void* workspace, uint32_t* faults, void* stream) {
@@ -226,6 +226,9 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
   ia.A_log = A_log ? A_log : reinterpret_cast<const float*>(pr.rec);
   ia.dt_bias = dt_bias ? dt_bias : reinterpret_cast<const float*>(pr.rec);
   ia.flags = (int)(flags & (FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM));
+  ia.kd = (int)K;
+  pr.kd = (int)K;
+  pr.vd = (int)V;
   ia.claim = claim;
   ia.faults = reinterpret_cast<unsigned*>(pr.ws + pr.lay.faults);
   ia.rec = pr.rec;
@@ -248,7 +251,7 @@ kda_status_t prepare(const void* q, const void* k, const void* raw_gate, const v
 // least one token, enough heads, its records not wanted afterwards (KEEP) and
 // not given (REUSE), not split into shards, on a GPU of 8 equal XCDs.
 static bool use_fused(const Prepared& pr, unsigned flags, int64_t T_total, bool split) {
-  if (!(flags & FLAG_SINGLE_LAUNCH) || !pr.lay.fused || split || T_total < 1 ||
+  if (!(flags & FLAG_SINGLE_LAUNCH) || !pr.lay.fused || split || T_total < 1 || pr.kd != KD || pr.vd != VD ||
       (flags & (FLAG_REUSE_RECORDS | FLAG_KEEP_RECORDS)))
     return false;
   int dev = 0, cus = 0;
@@ -272,6 +275,8 @@ InterArgs inter_args(const Prepared& pr, int64_t H) {
   xa.order = pr.order;
   xa.map = pr.map;
   xa.H = (int)H;
+  xa.kd = pr.kd;
+  xa.vd = pr.vd;
   xa.scale = 1.0f;
   xa.states = nullptr;
   xa.dtile = nullptr;
@@ -436,6 +441,7 @@ kda_status_t kda_shard_affine(const void* q, const void* k, const void* v, const
                               float* R, const int32_t* cu_seqlens, int64_t B, int64_t T, int64_t H,
                               int64_t K, int64_t V, int64_t N, void* stream) {
   if ((B * T > 0 && !v) || !P || !R) return KDA_ERR_INVALID;
+  if (K != KD || V != VD) return KDA_ERR_UNSUPPORTED;  // P starts from the identity: K == V == 128
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   Prepared pr;
   const kda_status_t s = prepare(q, k, raw_gate, raw_beta, workspace, workspace_bytes, A_log, dt_bias,

@@ -1451,6 +1451,7 @@ kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void*
   if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID;
   if (B * T * H > ((int64_t)1 << 40) || N * H > ((int64_t)1 << 28) || N > ((int64_t)1 << 30))
     return KDA_ERR_INVALID;
+  if (K != KD || V != VD) return KDA_ERR_UNSUPPORTED;  // the backward is built for K = V = 128
   const BwdLayout bl = bwd_layout(B * T, H, N);
   if (!workspace || workspace_bytes < bl.total) return KDA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

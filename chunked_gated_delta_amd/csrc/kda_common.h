@@ -263,6 +263,7 @@ struct IntraArgs {
   float lb2;        // lower_bound * log2(e)
   float lb;         // lower_bound
   int flags;        // FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM
+  int kd;           // head dim K of the inputs: 64 or 128 (records always use the 128-channel layout)
   int* claim;       // work-item counter, zero when the kernel starts
   unsigned* faults; // the call's fault word (FAULT_* bits)
   unsigned long long* timers;  // phase timers (KDA_PHASE_TIMERS builds only), else nullptr
@@ -278,6 +279,7 @@ struct InterArgs {
   const int32_t* order;  // nullptr: identity order of sequences
   ChunkMap map;
   int H;
+  int kd, vd;            // head dims of the states, v and out: 64 or 128 each (state rows c >= kd are zero)
   float scale;
   unsigned long long* timers;  // phase timers (KDA_PHASE_TIMERS builds only), else nullptr
   // checkpoints for the backward pass (both nullptr in the forward):

@@ -153,7 +153,8 @@ extern "C" kda_status_t kda_decode(const void* q, const void* k, const void* v, 
   // token arrays may be NULL only when there are no tokens (empty tensors)
   if (T > 0 && (!q || !k || !v || !raw_gate || !raw_beta || !out)) return KDA_ERR_INVALID;
   if (!A_log || !dt_bias) return KDA_ERR_INVALID;
-  if (!kda_is_supported(K, V, lower_bound)) return KDA_ERR_UNSUPPORTED;
+  // the decode step is built for K = V = 128
+  if (K != KD || V != VD || !kda_is_supported(K, V, lower_bound)) return KDA_ERR_UNSUPPORTED;
   if (B * H * NDSL > ((int64_t)1 << 31) - 1 || B * T * H > ((int64_t)1 << 40)) return KDA_ERR_INVALID;
   DecodeArgs a;
   a.q = static_cast<const uint16_t*>(q);

@@ -113,6 +113,7 @@ struct Prepared {
   char* ws;
   Layout lay;
   int64_t max_chunks;
+  int kd = KD, vd = VD;  // the call's head dims (64 or 128 each)
   IntraArgs ia;  // the intra-chunk pass's arguments
 };
 
@@ -131,7 +132,9 @@ InterArgs inter_args(const Prepared& pr, int64_t H);
 // mean sequence length): only with the [K][V] state layout and a token count
 // that fits the int32 shard offsets.
 inline bool use_split(const Prepared& pr, unsigned flags, int64_t B, int64_t T) {
-  return pr.lay.S > 1 && !(flags & FLAG_STATE_VK) && T > 0 && B * T < ((int64_t)1 << 31);
+  // the shard maps P are K x K products started from the identity: K == V == 128
+  return pr.lay.S > 1 && !(flags & FLAG_STATE_VK) && T > 0 && B * T < ((int64_t)1 << 31) && pr.kd == KD &&
+         pr.vd == VD;
 }
 
 // Inter-chunk arguments over the shard map m2 (no v, outputs or states set).

@@ -31,7 +31,7 @@ constexpr int TP = CH + 8;       // token pitch of [v][token] arrays (halves)
 template <int NN>
 struct Cfg {
   static constexpr int VT = 16 * NN;                     // state columns per workgroup
-  static constexpr int NV = VD / VT;                     // V slices per (sequence, head)
+  static constexpr int NV = VD / VT;                     // V slices per (sequence, head) at V = 128
   static constexpr int OFF_VT = 0;                       // bf16 [VT][TP]   V^T
   static constexpr int OFF_ST = OFF_VT + VT * TP * 2;    // f16  4 NN fragments (nn, kb)   state copy
   static constexpr int OFF_DTH = OFF_ST + 4 * NN * FRAG; // f16  2 NN fragments (nn, ks)   D hi
@@ -119,11 +119,11 @@ struct VRow {
 };
 template <int NN>
 __device__ __forceinline__ void load_v(VRow<NN>& vv, const uint16_t* v, int64_t c0, int L, int H, int h,
-                                       int vs, int tid) {
+                                       int vs, int tid, int vd) {
   const int t = tid >> 2;
   const int cg = tid & 3;
   const int tc = t < L ? t : L - 1;  // L >= 1: the clamped row is inside the sequence
-  const uint16_t* row = v + ((c0 + tc) * H + h) * VD + vs + 4 * NN * cg;
+  const uint16_t* row = v + ((c0 + tc) * H + h) * vd + vs + 4 * NN * cg;
   if constexpr (NN == 1) {
     const uint2 x = *reinterpret_cast<const uint2*>(row);
     vv.d[0] = x.x; vv.d[1] = x.y;
@@ -179,7 +179,13 @@ __device__ __forceinline__ void store_vt(__bf16* sVt, const VRow<NN>& vv, int ti
 template <bool HAS_V, bool WRITE_OUT, bool CKPT = false, int NN = 4>
 __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
   using C = Cfg<NN>;
-  constexpr int NV = C::NV, VT = C::VT, OP = C::OP;
+  constexpr int VT = C::VT, OP = C::OP;
+  // V slices per (sequence, head): V / VT.  Head dims 64 (K or V) use the
+  // 128-channel, 128-column layout in registers and LDS: state rows c >= K
+  // start at zero and stay there (their Kt rows are zero), and V = 64 has
+  // half the slices.
+  const int kd = a.kd, vd = a.vd;
+  const int NV = vd / VT;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   __bf16* sVt = reinterpret_cast<__bf16*>(smem + C::OFF_VT);
   char* sSt = smem + C::OFF_ST;
@@ -214,7 +220,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
   // state rows (channels) 32w + 16mt + 4gq + ii, columns vs + 16n + tl
   f32x4 S[2][NN];
   {
-    const float* src = a.init ? a.init + ((int64_t)seq * H + h) * KD * VD : nullptr;
+    const float* src = a.init ? a.init + ((int64_t)seq * H + h) * kd * vd : nullptr;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -223,7 +229,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
         for (int ii = 0; ii < 4; ++ii) {
           const int c = 32 * w + 16 * mt + 4 * gq + ii;
           const int col = vs + 16 * nn + tl;
-          S[mt][nn][ii] = src ? src[a.state_vk ? col * KD + c : c * VD + col]
+          S[mt][nn][ii] = src ? (c < kd ? src[a.state_vk ? col * kd + c : c * vd + col] : 0.0f)
                               : ((a.init_identity && c == col) ? 1.0f : 0.0f);
         }
   }
@@ -251,7 +257,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
   const bool odd = ((eos - bos + CH - 1) / CH) & 1;
   if (bos < eos) {
     VRow<NN> v0;
-    if constexpr (HAS_V) load_v(v0, a.v, bos, chunk_len(bos), H, h, vs, tid);
+    if constexpr (HAS_V) load_v(v0, a.v, bos, chunk_len(bos), H, h, vs, tid, vd);
     const char* r0 = a.rec + ((size_t)gfirst * H + h) * REC_BYTES;
     if (odd)
       load_ops_all<HAS_V, WRITE_OUT>(opsA, r0, w, lane, gq, ksmax);
@@ -291,7 +297,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
           for (int ii = 0; ii < 4; ++ii)
             dst[(32 * w + 16 * mt + 4 * gq + ii) * VD + vs + 16 * nn + tl] = S[mt][nn][ii];
     }
-    if constexpr (HAS_V) KDA_ISSUE(load_v(vn, a.v, in1 ? c1 : c0, in1 ? chunk_len(c1) : L, H, h, vs, tid));
+    if constexpr (HAS_V) KDA_ISSUE(load_v(vn, a.v, in1 ? c1 : c0, in1 ? chunk_len(c1) : L, H, h, vs, tid, vd));
     KDA_ISSUE((load_ops<0, HAS_V, WRITE_OUT>(pre, prec, w, lane, gq, ksmax)));
     KDA_TIMER_MARK(1);
 
@@ -443,7 +449,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
       const int ocol = 16 * (lane % NN);
       if (lane < 16 * NN && orow < L) {
         const uint4* srcp = reinterpret_cast<const uint4*>(sO + orow * OP + ocol);
-        uint4* dstp = reinterpret_cast<uint4*>(a.out + ((c0 + orow) * H + h) * VD + vs + ocol);
+        uint4* dstp = reinterpret_cast<uint4*>(a.out + ((c0 + orow) * H + h) * vd + vs + ocol);
         dstp[0] = srcp[0];
         dstp[1] = srcp[1];
       }
@@ -468,7 +474,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
   KDA_TIMER_STORE(a.timers);
 
   if (a.fin) {
-    float* dst = a.fin + ((int64_t)seq * H + h) * KD * VD;
+    float* dst = a.fin + ((int64_t)seq * H + h) * kd * vd;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -477,7 +483,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_inter_kernel(InterArgs a) {
         for (int ii = 0; ii < 4; ++ii) {
           const int c = 32 * w + 16 * mt + 4 * gq + ii;
           const int col = vs + 16 * nn + tl;
-          dst[a.state_vk ? col * KD + c : c * VD + col] = S[mt][nn][ii];
+          if (c < kd) dst[a.state_vk ? col * kd + c : c * vd + col] = S[mt][nn][ii];
         }
   }
 }
@@ -519,8 +525,8 @@ hipError_t launch_inter(const InterArgs& args, hipStream_t st) {
   else
     fn = a.out ? reinterpret_cast<const void*>(&kda_inter_kernel<false, true>)
                : reinterpret_cast<const void*>(&kda_inter_kernel<false, false>);
-  // ids 8m + x (x = XCD) cover the VD / (16 nn) slices of items 8(m / slices) + x
-  const int64_t grid = (items + 7) / 8 * 8 * (VD / (16 * nn));
+  // ids 8m + x (x = XCD) cover the V / (16 nn) slices of items 8(m / slices) + x
+  const int64_t grid = (items + 7) / 8 * 8 * (a.vd / (16 * nn));
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(NTHREADS), kargs, 0, st);
 }
 

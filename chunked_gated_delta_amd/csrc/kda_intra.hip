@@ -125,7 +125,12 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8]) {
 // of one XCD's heads of a single sequence in chunk order (chunk * hx + l for
 // head xcd + 8 l), each record goes to its head's ring slot or to
 // recs[chunk][head] (IntraFused), and its ready flag then says which.
-template <bool GATE_GIVEN, bool FUSED>
+// KIN: the head dim K of q, k, raw_gate and dt_bias in memory (64 or 128).
+// With K = 64 the item is computed in the 128-channel layout with channels
+// 64..127 of q and k zero (so they add nothing to any norm, dot product or
+// record entry) and their gate inputs zero (a finite decay that multiplies
+// only those zero channels); the record layout is that of K = 128.
+template <bool GATE_GIVEN, bool FUSED, int KIN = KD>
 __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restrict__ cu,
                                             const int32_t* __restrict__ choff, const float* __restrict__ A_log,
                                             char* __restrict__ recs, char* smem, int first, int stride, int* claim,
@@ -222,18 +227,28 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
     if (part == 0) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const int64_t off = trow * KD + 32 * kb + 8 * grp;
-        pq[kb] = *reinterpret_cast<const uint4*>(a.q + off);
-        pk[kb] = *reinterpret_cast<const uint4*>(a.k + off);
+        const int64_t off = trow * KIN + 32 * kb + 8 * grp;
+        if (32 * kb < KIN) {
+          pq[kb] = *reinterpret_cast<const uint4*>(a.q + off);
+          pk[kb] = *reinterpret_cast<const uint4*>(a.k + off);
+        } else {
+          pq[kb] = make_uint4(0u, 0u, 0u, 0u);
+          pk[kb] = make_uint4(0u, 0u, 0u, 0u);
+        }
       }
     } else {
       braw16 = a.beta[trow];
       alog = A_log[hh + (t >> 31)];
-      dtb = a.dt_bias[hh * KD + (t & (KD - 1))];
+      const int ch = t & (KD - 1);
+      dtb = a.dt_bias[hh * KIN + (ch & (KIN - 1))];
+      if (KIN < KD && ch >= KIN) dtb = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const int64_t off = trow * KD + 32 * kb + 8 * grp;
-        pg[kb] = *reinterpret_cast<const uint4*>(a.g + off);
+        const int64_t off = trow * KIN + 32 * kb + 8 * grp;
+        if (32 * kb < KIN)
+          pg[kb] = *reinterpret_cast<const uint4*>(a.g + off);
+        else
+          pg[kb] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
   };
@@ -780,13 +795,14 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
 
 namespace {
 
-template <bool GATE_GIVEN>
+template <bool GATE_GIVEN, int KIN>
 __global__ void __launch_bounds__(NTHREADS, 2)
     kda_intra_kernel(IntraArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ choff,
                      const float* __restrict__ A_log, char* __restrict__ recs) {
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   const IntraFused none{};
-  intra_items<GATE_GIVEN, false>(a, cu, choff, A_log, recs, smem, (int)blockIdx.x, (int)gridDim.x, a.claim, none);
+  intra_items<GATE_GIVEN, false, KIN>(a, cu, choff, A_log, recs, smem, (int)blockIdx.x, (int)gridDim.x, a.claim,
+                                      none);
 }
 
 }  // namespace
@@ -903,8 +919,11 @@ hipError_t launch_intra(const IntraArgs& args, int64_t max_chunks, hipStream_t s
   const float* alog = a.A_log;
   char* recs = a.rec;
   void* kargs[] = {(void*)&a, (void*)&cu, (void*)&choff, (void*)&alog, (void*)&recs};
-  const void* fn = (a.flags & FLAG_GATE_GIVEN) ? reinterpret_cast<const void*>(&kda_intra_kernel<true>)
-                                               : reinterpret_cast<const void*>(&kda_intra_kernel<false>);
+  const bool given = a.flags & FLAG_GATE_GIVEN;
+  const void* fn = a.kd == KD ? (given ? reinterpret_cast<const void*>(&kda_intra_kernel<true, KD>)
+                                       : reinterpret_cast<const void*>(&kda_intra_kernel<false, KD>))
+                              : (given ? reinterpret_cast<const void*>(&kda_intra_kernel<true, 64>)
+                                       : reinterpret_cast<const void*>(&kda_intra_kernel<false, 64>));
   return hipLaunchKernel(fn, dim3((unsigned)grid),
                          dim3(NTHREADS), kargs, 0, st);
 }

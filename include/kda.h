@@ -44,7 +44,7 @@ extern "C" {
 typedef enum {
   KDA_SUCCESS = 0,
   KDA_ERR_INVALID = 1,     /* NULL required pointer, bad sizes, inconsistent B/N */
-  KDA_ERR_UNSUPPORTED = 2, /* K != 128, V != 128, or lower_bound outside [-5, 0] */
+  KDA_ERR_UNSUPPORTED = 2, /* head dims or lower_bound outside what the entry point supports */
   KDA_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than kda_workspace_size() */
   KDA_ERR_LAUNCH = 4       /* a kernel launch failed (hipGetLastError after launch) */
 } kda_status_t;
@@ -62,9 +62,14 @@ size_t kda_workspace_size(int64_t T_total, int64_t H, int64_t N);
 
 /*
  * 1 if kda_fwd supports head dims K, V with this lower_bound, else 0 (the
- * page's is_flashkda_supported(128, bf16, lower_bound) probe).  Supported:
- * K == V == 128 and -5 <= lower_bound <= 0.  The -5 limit keeps every
- * 16-token decay ratio inside fp32/bf16 range (exp(16 * 5) < FLT_MAX).
+ * page's is_flashkda_supported(128, bf16, lower_bound) probe, whose first
+ * argument is the head size).  Supported: K and V each 64 or 128, and
+ * -5 <= lower_bound <= 0.  The -5 limit keeps every 16-token decay ratio
+ * inside fp32/bf16 range (exp(16 * 5) < FLT_MAX).  kda_fwd and kda_fwd_ex
+ * take every supported pair; kda_shard_affine, kda_shard_scan, kda_decode
+ * and the backward take K == V == 128 only (KDA_ERR_UNSUPPORTED otherwise).
+ * Head dim 64 runs in the 128-channel layout of the kernels with the missing
+ * channels held at zero, so it costs about what 128 costs.
  */
 int kda_is_supported(int64_t K, int64_t V, float lower_bound);
 
@@ -130,8 +135,8 @@ kda_status_t kda_fwd(const void* q, const void* k, const void* v, const void* ra
  *   P   fp32 [N, H, K, K] written: P[n][h][i][j] multiplies S[j][:] into row i
  *   R   fp32 [N, H, K, V] written
  *
- * Needs K == V (P is computed as the final state of the V = 0 recurrence from
- * S = I).  Shards then combine with kda_shard_scan, and kda_fwd with the
+ * Needs K == V == 128 (P is computed as the final state of the V = 0
+ * recurrence from S = I).  Shards then combine with kda_shard_scan, and kda_fwd with the
  * scanned entering states as initial_state produces the shards' outputs.
  * Same errors as kda_fwd; P and R must not overlap the inputs.
  */

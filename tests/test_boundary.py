@@ -80,8 +80,10 @@ def test_is_supported():
     assert kda.kda_is_supported(128, 128, -5.0)
     assert kda.kda_is_supported(128, 128, 0.0)
     assert kda.kda_is_supported(128, 128, -2.5)
-    assert not kda.kda_is_supported(64, 128, -5.0)
-    assert not kda.kda_is_supported(128, 256, -5.0)
+    for K, V in ((64, 64), (64, 128), (128, 64)):
+        assert kda.kda_is_supported(K, V, -5.0)
+    for K, V in ((128, 256), (256, 256), (32, 32), (96, 128), (128, 0), (0, 128)):
+        assert not kda.kda_is_supported(K, V, -5.0)
     assert not kda.kda_is_supported(128, 128, -5.5)
     assert not kda.kda_is_supported(128, 128, 0.5)
 
@@ -111,7 +113,7 @@ def test_bad_sizes_are_invalid(over):
     assert call(**over) == INVALID
 
 
-@pytest.mark.parametrize("over", [dict(K=64), dict(V=64), dict(K=256, V=256), dict(lb=-6.0),
+@pytest.mark.parametrize("over", [dict(K=32), dict(V=96), dict(K=256, V=256), dict(lb=-6.0),
                                   dict(lb=1.0)])
 def test_unsupported_shapes(over):
     assert call(**over) == UNSUPPORTED
@@ -162,7 +164,8 @@ def test_shard_affine_null_pointer_is_invalid(field):
 
 
 def test_shard_affine_checks():
-    assert shard_affine_call(K=64, V=64) == UNSUPPORTED
+    assert shard_affine_call(K=64, V=64) == UNSUPPORTED     # the forward's other head dims: not here
+    assert shard_affine_call(K=128, V=64) == UNSUPPORTED
     assert shard_affine_call(lb=-6.0) == UNSUPPORTED
     assert shard_affine_call(B=2, N=1) == INVALID
     assert shard_affine_call(ws_bytes=16) == WORKSPACE
@@ -221,7 +224,7 @@ def test_fwd_ex_flag_checks():
     assert fwd_ex_call(kda.FLAG_REUSE_RECORDS, ws_bytes=8) == WORKSPACE
     assert fwd_ex_call(0, A_log=None) == INVALID          # gate parameters needed without GATE_GIVEN
     assert fwd_ex_call(kda.FLAG_BETA_GIVEN, dt=None) == INVALID
-    assert fwd_ex_call(kda.FLAG_GATE_GIVEN, K=64, V=64, A_log=None, dt=None) == UNSUPPORTED
+    assert fwd_ex_call(kda.FLAG_GATE_GIVEN, K=256, V=256, A_log=None, dt=None) == UNSUPPORTED
     assert fwd_ex_call(kda.FLAG_STATE_VK, ws_bytes=8) == WORKSPACE
 
 
@@ -247,7 +250,8 @@ def test_bwd_checks():
     assert bwd_call(T=-1) == INVALID
     assert bwd_call(scale=float("nan")) == INVALID
     assert bwd_call(B=2, N=1) == INVALID                    # N must equal B without cu_seqlens
-    assert bwd_call(K=64, V=64) == UNSUPPORTED
+    assert bwd_call(K=64, V=64) == UNSUPPORTED              # the backward is built for 128 only
+    assert bwd_call(K=64) == UNSUPPORTED
     assert bwd_call(lb=-6.0) == UNSUPPORTED
     assert bwd_call(ws=None) == WORKSPACE
     need = kda.kda_bwd_workspace_size(64, 2, 1)

@@ -58,6 +58,19 @@ def test_brute_force_small(seed, T, K, V, with_state):
         assert np.abs(fin[0, h] - fb).max() <= 1e-13
 
 
+def test_brute_force_head_dim_64():
+    """The head dim the forward also takes besides 128 (K = V = 64), against the decimal
+    product form, with a carried initial state."""
+    x = W.random_inputs("brute64", 21, 1, 4, 1, K=64, V=64, init_std=0.5)
+    out, fin = run(x)
+    ob, fb = brute_fwd(x.q, x.k, x.v, x.raw_gate, x.raw_beta, x.scale, x.A_log, x.dt_bias,
+                       x.lower_bound, x.initial_state, head=0)
+    ob = np.array([[float(a) for a in r] for r in ob])
+    fb = np.array([[float(a) for a in r] for r in fb])
+    assert np.abs(out[:, 0] - ob).max() <= 1e-13
+    assert np.abs(fin[0, 0] - fb).max() <= 1e-13
+
+
 def test_brute_force_golden_k128():
     with open(os.path.join(HERE, "golden", "brute_k128_T5.json")) as f:
         doc = json.load(f)
@@ -82,6 +95,18 @@ def test_chunked_form_matches(chunk):
     out, fin = run(x)
     o2, f2 = chunked_fwd(x.q, x.k, x.v, x.raw_gate, x.raw_beta, x.scale, x.A_log, x.dt_bias,
                          x.lower_bound, x.initial_state, x.cu_seqlens, chunk=chunk)
+    assert np.abs(out - o2).max() <= 1e-12
+    assert np.abs(fin - f2).max() <= 1e-12
+
+
+@pytest.mark.parametrize("K,V", [(64, 64), (64, 128), (128, 64)])
+def test_chunked_form_matches_at_other_head_dims(K, V):
+    lengths = [1, 63, 64, 65, 137]
+    x = W.random_inputs(f"chunked_{K}x{V}", 22, 1, sum(lengths), 2, K=K, V=V, lengths=lengths)
+    out, fin = run(x)
+    o2, f2 = chunked_fwd(x.q, x.k, x.v, x.raw_gate, x.raw_beta, x.scale, x.A_log, x.dt_bias,
+                         x.lower_bound, x.initial_state, x.cu_seqlens, chunk=64)
+    assert out.shape == (sum(lengths), 2, V) and fin.shape == (len(lengths), 2, K, V)
     assert np.abs(out - o2).max() <= 1e-12
     assert np.abs(fin - f2).max() <= 1e-12
 
