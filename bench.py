@@ -55,6 +55,8 @@ KERNEL_SRCS = [os.path.join(ROOT, "chunked_gated_delta_amd", "csrc", f)
                          "kda_chain.hip", "kda_api.hip")] + [
     os.path.join(ROOT, "chunked_gated_delta_amd", "build.py")]  # compile flags shape the kernels too
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_fwd_c3_traffic.json")
+# the same counters taken over the single-launch schedule (--single-launch)
+TRAFFIC_FILE_SINGLE = os.path.join(ROOT, "profiles", "kda_fwd_c3_single_launch_traffic.json")
 
 
 def kernel_source_hash() -> str:
@@ -65,10 +67,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(single=False):
     """HBM bytes per launch from the committed counter summary, if still current."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE_SINGLE if single else TRAFFIC_FILE) as f:
             doc = json.load(f)
     except (OSError, ValueError):
         return None
@@ -139,7 +141,7 @@ def copy_calibration(gib: float = 2.0):
     print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 3}))
 
 
-def write_traffic(fwd_fetch, fwd_write, copy_fetch, copy_write, copy_bytes=2 << 30):
+def write_traffic(fwd_fetch, fwd_write, copy_fetch, copy_write, copy_bytes=2 << 30, single=False):
     """Turn four rocprofv3 --pmc counter CSVs (FETCH_SIZE / WRITE_SIZE, KiB per
     dispatch) of this benchmark and of --copy-calibration into the traffic file.
 
@@ -174,13 +176,14 @@ def write_traffic(fwd_fetch, fwd_write, copy_fetch, copy_write, copy_bytes=2 << 
             short = m.group(1)
             kernels.setdefault(short, {})[key] = sum(ks) / len(ks) * 1024.0 * fac
     total = sum(v.get("read_bytes", 0.0) + v.get("write_bytes", 0.0) for v in kernels.values())
-    doc = {"workload": "kda_fwd B=1 T=32768 H=96 K=V=128 (bench.py defaults)",
+    doc = {"workload": "kda_fwd B=1 T=32768 H=96 K=V=128 (bench.py defaults" +
+                       (", --single-launch)" if single else ")"),
            "kernel_source_sha256": kernel_source_hash(),
            "hbm_bytes_per_launch": total,
            "kernels": kernels,
            "calibration": {"copy_bytes": copy_bytes, "fetch_size_factor": ff,
                            "write_size_factor": wf}}
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(TRAFFIC_FILE_SINGLE if single else TRAFFIC_FILE, "w") as f:
         json.dump(doc, f, indent=1)
         f.write("\n")
     print(json.dumps(doc))
@@ -464,7 +467,11 @@ def bench_forward(args):
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if cold else None
 
     def step():
-        kda.kda_fwd(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, init, fin, cu, stream=sh)
+        if args.single_launch:
+            kda.kda_fwd_ex(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, init, fin, cu,
+                           flags=kda.FLAG_SINGLE_LAUNCH, stream=sh)
+        else:
+            kda.kda_fwd(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, init, fin, cu, stream=sh)
 
     for _ in range(args.warmup):
         step()
@@ -504,11 +511,12 @@ def bench_forward(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": CONFIGS[args.config].format(T=x.B * x.T, H=x.H),
+        "config": {"workload": CONFIGS[args.config].format(T=x.B * x.T, H=x.H) +
+                   ("; single-launch schedule (KDA_FLAG_SINGLE_LAUNCH)" if args.single_launch else ""),
                    "B": x.B, "T": x.T, "H": x.H, "K": 128, "V": 128, "N": x.N},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic() if headline else None,
+                     "traffic": measured_traffic(args.single_launch) if headline else None,
                      "kernel": "kda_fwd (every kernel of one forward)",
                      "median_kernel_ms": med_s * 1e3,
                      "mean_kernel_ms": sum(kern_ms) / len(kern_ms),
@@ -545,10 +553,13 @@ def main():
     ap.add_argument("--kcp-shards", type=int, default=0,
                     help="time the split-sequence path with this many shards instead")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FWD_FETCH", "FWD_WRITE", "COPY_FETCH", "COPY_WRITE"),
-                    help="rocprofv3 counter_collection.csv files -> profiles/kda_fwd_c3_traffic.json")
+                    help="rocprofv3 counter_collection.csv files -> profiles/kda_fwd_c3_traffic.json "
+                         "(with --single-launch: profiles/kda_fwd_c3_single_launch_traffic.json)")
+    ap.add_argument("--single-launch", action="store_true",
+                    help="time kda_fwd_ex with KDA_FLAG_SINGLE_LAUNCH (the one-launch producer/chain pipeline)")
     args = ap.parse_args()
     if args.write_traffic:
-        write_traffic(*args.write_traffic)
+        write_traffic(*args.write_traffic, single=args.single_launch)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
