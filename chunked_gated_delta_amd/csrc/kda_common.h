@@ -211,7 +211,7 @@ constexpr int FLAG_SINGLE_LAUNCH = 64;  // one-sequence calls: the one-launch pr
 constexpr unsigned FAULT_WAIT_TIMEOUT = 1u;  // a bounded wait gave up; results are invalid
 constexpr unsigned FAULT_GATE_RANGE = 2u;    // FLAG_GATE_GIVEN: a decay outside [lower_bound, 0]
 constexpr unsigned FAULT_QK_NORM = 4u;       // FLAG_NO_QK_NORM: a q or k row with |x|^2 > 1 + 1/16
-constexpr unsigned FAULT_PLACEMENT = 8u;     // a fused-pipeline workgroup ran on another XCD than planned
+constexpr unsigned FAULT_PLACEMENT = 8u;     // single launch: the workgroups of one id residue ran on two XCDs
 
 // The fused forward pipeline (one sequence): per XCD, intra-chunk producer
 // workgroups hand the chunk records of that XCD's heads (h = xcd + 8 l) to the
@@ -311,7 +311,7 @@ struct FusedArgs {
   char* ringbuf;
   int* flags;      // [chunks][H]
   int* consumed;   // [H][FUSED_CHAINS] FUSED_LINE apart
-  int* claims;     // [8] FUSED_LINE apart
+  int* claims;     // [8] claim counters, then [8] XCDs of the id residues, FUSED_LINE apart
   unsigned* faults;
   int nchunk;
   int ring;        // ring slots per head in use, 1..FUSED_RING

@@ -45,7 +45,8 @@ struct Layout {
   size_t scu, schoff, sP, sR, sstart, sfin;
   // fused-pipeline areas (N == 1, H >= kFusedMinHeads): the ring of
   // FUSED_RING records per head, ready flags [chunks][H], consumed counters
-  // [H][FUSED_CHAINS] and per-XCD claim counters [8] (FUSED_LINE apart)
+  // [H][FUSED_CHAINS], per-XCD claim counters [8] and the XCD of each id residue [8]
+  // (FUSED_LINE apart)
   bool fused;
   size_t fring, fflags, fcons, fclaims;
 };
@@ -81,7 +82,7 @@ inline Layout workspace_layout(int64_t T_total, int64_t H, int64_t N) {
     l.fflags = l.fring + (size_t)H * FUSED_RING * REC_BYTES;
     l.fcons = l.fflags + align256(max_chunks * (size_t)H * 4);
     l.fclaims = l.fcons + align256((size_t)H * FUSED_CHAINS * FUSED_LINE);
-    l.total = l.fclaims + 8 * FUSED_LINE;
+    l.total = l.fclaims + 16 * FUSED_LINE;
   }
   return l;
 }

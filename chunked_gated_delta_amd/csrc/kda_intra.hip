@@ -815,8 +815,8 @@ constexpr int FUSED_LDS =
 static_assert(FUSED_CHAINS * 32 * FUSED_NQ == VD, "chains cover the state columns");
 constexpr int HW_REG_XCC_ID = (3 << 11) | 20;  // s_getreg operand: XCC_ID, bits 0-3
 
-// Clears the fused pipeline's ready flags, consumed and claim counters and
-// the call's fault word (a kernel rather than a memset, so that a captured
+// Clears the fused pipeline's ready flags, consumed and claim counters, the
+// XCD-of-residue words and the call's fault word (a kernel rather than a memset, so that a captured
 // graph replays it as a kernel node).
 __global__ void kda_fused_reset_kernel(int* __restrict__ flags, int nflags, int* __restrict__ consumed, int H,
                                        int* __restrict__ claims, unsigned* __restrict__ faults) {
@@ -824,16 +824,22 @@ __global__ void kda_fused_reset_kernel(int* __restrict__ flags, int nflags, int*
   const int i0 = (int)(blockIdx.x * blockDim.x + threadIdx.x);
   for (int i = i0; i < nflags; i += stride) flags[i] = 0;
   for (int i = i0; i < H * FUSED_CHAINS; i += stride) consumed[i * (FUSED_LINE / 4)] = 0;
-  if (i0 < 8) claims[i0 * (FUSED_LINE / 4)] = 0;
+  if (i0 < 8) claims[i0 * (FUSED_LINE / 4)] = 0;                  // claim counters
+  if (i0 < 8) claims[(8 + i0) * (FUSED_LINE / 4)] = -1;           // XCD of each id residue: none yet
   if (i0 == 0) *faults = 0u;
 }
 
-// The fused pipeline over one sequence.  Workgroup b runs on XCD x = b mod 8
-// (the dispatcher's round robin, checked against the XCC_ID register) as
-// local workgroup j = b / 8 of the XCD's nw.  The XCD owns heads x, x + 8, ...
-// (hx of them): its last FUSED_CHAINS hx workgroups are their chains (highest
-// ids, so dispatched last; the two column halves of a head are neighbours),
-// the others intra-chunk producers of those heads' items in chunk order.
+// The fused pipeline over one sequence.  The dispatcher hands workgroups to
+// the 8 XCDs round robin, so the workgroups b = 8 j + x of one residue x all
+// run on one XCD, though not necessarily XCD x (under graph replay the round
+// robin starts elsewhere): residue x, local workgroup j of nw = grid / 8, owns
+// heads x, x + 8, ... (hx of them).  Its last FUSED_CHAINS hx workgroups are
+// their chains (highest ids, so dispatched last; the two column halves of a
+// head are neighbours), the others intra-chunk producers of those heads'
+// items in chunk order; all of them meet in the one XCD's L2.  Each workgroup
+// records the XCD (XCC_ID register) of its residue; one that finds its residue
+// on another XCD reports KDA_FAULT_PLACEMENT (records may then have crossed
+// XCDs).
 // A producer waits for a chain only a bounded time (a record whose ring slot
 // is still in use after FusedArgs::slot_wait polls goes to the record area
 // instead), so all items get produced whatever the residency, and every
@@ -846,8 +852,11 @@ __global__ void __launch_bounds__(NTHREADS, 2)
   const int x = (int)(blockIdx.x & 7);
   const int j = (int)(blockIdx.x >> 3);
   const int nw = (int)(gridDim.x >> 3);
-  if (threadIdx.x == 0 && (int)(__builtin_amdgcn_s_getreg(HW_REG_XCC_ID) & 7) != x)
-    atomicOr(fa.faults, FAULT_PLACEMENT);
+  if (threadIdx.x == 0) {
+    const int xr = (int)(__builtin_amdgcn_s_getreg(HW_REG_XCC_ID) & 7);
+    const int seen = atomicCAS(fa.claims + (8 + x) * (FUSED_LINE / 4), -1, xr);
+    if (seen != -1 && seen != xr) atomicOr(fa.faults, FAULT_PLACEMENT);
+  }
   const int H = ia.H;
   const int hx = x < H ? (H - 1 - x) / 8 + 1 : 0;
   const int nchains = FUSED_CHAINS * hx;

@@ -345,15 +345,15 @@ kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void*
  * kda_bwd_ex call detect on the device, where no status can be returned.
  * Each such call clears the fault word of its workspace when it starts and
  * ORs these bits into it:
- *   KDA_FAULT_WAIT_TIMEOUT  a bounded wait between waves gave up: the call's
- *                           results are invalid
+ *   KDA_FAULT_WAIT_TIMEOUT  a bounded wait between waves or workgroups gave
+ *                           up: the call's results are invalid
  *   KDA_FAULT_GATE_RANGE    KDA_FLAG_GATE_GIVEN with a decay outside
  *                           [lower_bound, 0]
  *   KDA_FAULT_QK_NORM       KDA_FLAG_NO_QK_NORM with |q|^2 or |k|^2 > 1 + 1/16
- *   KDA_FAULT_PLACEMENT     a workgroup of the single-launch schedule ran on
- *                           another XCD than the one planned (workgroup b on
- *                           XCD b mod 8): records may then have been read from
- *                           another XCD's cache, and the results are invalid
+ *   KDA_FAULT_PLACEMENT     KDA_FLAG_SINGLE_LAUNCH: workgroups whose ids agree
+ *                           mod 8 (planned as one XCD's share, handing records
+ *                           over through its L2) ran on two different XCDs:
+ *                           the results are invalid
  */
 #define KDA_FAULT_WAIT_TIMEOUT 1u
 #define KDA_FAULT_GATE_RANGE 2u

@@ -6,7 +6,7 @@ It computes every product, operand split and accumulation in the order of the
 two-launch schedule (records built first, recurrence after), which the same
 call takes without the flag; so the two must agree bit for bit, and
 both must meet the oracle's bar.  Every call must also leave the workspace's
-fault word clear (no timed-out wait, no workgroup on an unplanned XCD).
+fault word clear (no timed-out wait, no id residue split over two XCDs).
 """
 
 import numpy as np
