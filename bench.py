@@ -50,31 +50,50 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 BF16_DENSE_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
 BYTES_PER_HEAD_TOKEN = 4 * 128 * 2 + 2 + 128 * 2
 STATE_BYTES = 128 * 128 * 4
-KERNEL_SRCS = [os.path.join(ROOT, "chunked_gated_delta_amd", "csrc", f)
-               for f in ("kda_common.h", "kda_host.h", "kda_intra.hip", "kda_inter.hip", "kda_chain.h",
-                         "kda_chain.hip", "kda_api.hip")] + [
-    os.path.join(ROOT, "chunked_gated_delta_amd", "build.py")]  # compile flags shape the kernels too
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_fwd_c3_traffic.json")
-# the same counters taken over the single-launch schedule (--single-launch)
-TRAFFIC_FILE_SINGLE = os.path.join(ROOT, "profiles", "kda_fwd_c3_single_launch_traffic.json")
+_CSRC = os.path.join(ROOT, "chunked_gated_delta_amd", "csrc")
+_FWD_SRCS = ("kda_common.h", "kda_host.h", "kda_intra.hip", "kda_inter.hip", "kda_chain.h", "kda_chain.hip",
+             "kda_api.hip")
+# the sources whose kernels each mode's counters measure (the build script too:
+# compile flags shape the kernels)
+KERNEL_SRCS = {
+    "fwd": _FWD_SRCS,
+    "single": _FWD_SRCS,
+    "bwd": _FWD_SRCS + ("kda_bwd.h", "kda_bwd.hip"),
+    "decode": ("kda_common.h", "kda_decode.hip"),
+}
+# rocprofv3 FETCH_SIZE / WRITE_SIZE summaries per mode (--write-traffic writes them)
+TRAFFIC_FILES = {
+    "fwd": os.path.join(ROOT, "profiles", "kda_fwd_c3_traffic.json"),
+    "single": os.path.join(ROOT, "profiles", "kda_fwd_c3_single_launch_traffic.json"),
+    "bwd": os.path.join(ROOT, "profiles", "kda_bwd_c3_traffic.json"),
+    "decode": os.path.join(ROOT, "profiles", "kda_decode_B64_H96_traffic.json"),
+}
+WORKLOADS = {
+    "fwd": "kda_fwd B=1 T=32768 H=96 K=V=128 (bench.py defaults)",
+    "single": "kda_fwd B=1 T=32768 H=96 K=V=128 (bench.py defaults, --single-launch)",
+    "bwd": "kda_bwd B=1 T=32768 H=96 K=V=128 (bench.py --bwd)",
+    "decode": "kda_decode B=64 T=1 H=96 K=V=128 (bench.py --decode 64)",
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(mode="fwd") -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
+    for path in [os.path.join(_CSRC, f) for f in KERNEL_SRCS[mode]] + [
+            os.path.join(ROOT, "chunked_gated_delta_amd", "build.py")]:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(single=False):
-    """HBM bytes per launch from the committed counter summary, if still current."""
+def measured_traffic(mode="fwd"):
+    """HBM bytes per launch (call) from the committed counter summary of `mode`, if
+    its kernel sources still hash to the value stored with it."""
     try:
-        with open(TRAFFIC_FILE_SINGLE if single else TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILES[mode]) as f:
             doc = json.load(f)
     except (OSError, ValueError):
         return None
-    if doc.get("kernel_source_sha256") != kernel_source_hash():
+    if doc.get("kernel_source_sha256") != kernel_source_hash(mode):
         return None
     return doc.get("hbm_bytes_per_launch")
 
@@ -141,12 +160,15 @@ def copy_calibration(gib: float = 2.0):
     print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 3}))
 
 
-def write_traffic(fwd_fetch, fwd_write, copy_fetch, copy_write, copy_bytes=2 << 30, single=False):
+def write_traffic(fetch_csv, write_csv, copy_fetch, copy_write, calls, mode="fwd", copy_bytes=2 << 30):
     """Turn four rocprofv3 --pmc counter CSVs (FETCH_SIZE / WRITE_SIZE, KiB per
-    dispatch) of this benchmark and of --copy-calibration into the traffic file.
+    dispatch) of `calls` identical calls of a bench mode and of --copy-calibration
+    into that mode's traffic file.
 
-    Each counter is scaled by what it reads for the plain copy of known size;
-    the forward's figure is the average over its dispatches of each kernel."""
+    Each counter is scaled by what it reads for the plain copy of known size.  A
+    kernel's bytes per call are the sum over its dispatches divided by `calls`
+    (so a kernel launched twice per call counts twice); the call's total sums the
+    library's kernels."""
     import collections
     import csv
 
@@ -167,23 +189,22 @@ def write_traffic(fwd_fetch, fwd_write, copy_fetch, copy_write, copy_bytes=2 << 
 
     ff, wf = factor(copy_fetch, "FETCH_SIZE"), factor(copy_write, "WRITE_SIZE")
     kernels = {}
-    for path, counter, fac, key in ((fwd_fetch, "FETCH_SIZE", ff, "read_bytes"),
-                                    (fwd_write, "WRITE_SIZE", wf, "write_bytes")):
+    for path, counter, fac, key in ((fetch_csv, "FETCH_SIZE", ff, "read_bytes"),
+                                    (write_csv, "WRITE_SIZE", wf, "write_bytes")):
         for name, ks in per_kernel(path, counter).items():
-            m = re.search(r"(kda_\w+_kernel)", name)
+            m = re.search(r"(kda_\w+_kernel(?:<[^>]*>)?)", name)
             if not m:
                 continue
-            short = m.group(1)
-            kernels.setdefault(short, {})[key] = sum(ks) / len(ks) * 1024.0 * fac
+            kernels.setdefault(m.group(1), {})[key] = sum(ks) / calls * 1024.0 * fac
     total = sum(v.get("read_bytes", 0.0) + v.get("write_bytes", 0.0) for v in kernels.values())
-    doc = {"workload": "kda_fwd B=1 T=32768 H=96 K=V=128 (bench.py defaults" +
-                       (", --single-launch)" if single else ")"),
-           "kernel_source_sha256": kernel_source_hash(),
+    doc = {"workload": WORKLOADS[mode],
+           "kernel_source_sha256": kernel_source_hash(mode),
+           "calls_profiled": calls,
            "hbm_bytes_per_launch": total,
            "kernels": kernels,
            "calibration": {"copy_bytes": copy_bytes, "fetch_size_factor": ff,
                            "write_size_factor": wf}}
-    with open(TRAFFIC_FILE_SINGLE if single else TRAFFIC_FILE, "w") as f:
+    with open(TRAFFIC_FILES[mode], "w") as f:
         json.dump(doc, f, indent=1)
         f.write("\n")
     print(json.dumps(doc))
@@ -305,7 +326,8 @@ def bench_decode(args):
         "ms_per_step": ms, "higher_is_better": True, "dtype": "fp32 state, bf16 io", "data": "synthetic",
         "config": {"workload": f"kda_decode B={x.B} T=1 H={x.H} K=V=128, in-place fp32 state"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg},
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg,
+                     "traffic": measured_traffic("decode") if (x.B, x.H) == (64, 96) else None},
         "cpu_baseline": None if args.no_cpu_baseline else dict(
             cpu_baseline(x, list(range(x.H))), unit="sequence-heads/s"),
     }), flush=True)
@@ -342,14 +364,16 @@ def bench_bwd(args):
     ms = timed(lambda: kda.kda_bwd(q, k, v, g, b, x.scale, d_out, dq, dk, dv, dg, db, dA, ddt, ws, al, dt,
                                    x.lower_bound, initial_state=init, d_final=d_fin, d_initial_state=dinit,
                                    stream=sh), args.steps, args.warmup, stream)
-    # the same gradients on the records a forward call left in this workspace
-    out, fin = torch.empty_like(v), torch.empty_like(init)
-    kda.kda_fwd_ex(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, init, fin, flags=kda.FLAG_KEEP_RECORDS,
-                   stream=sh)
-    ms_reuse = timed(lambda: kda.kda_bwd_ex(q, k, v, g, b, x.scale, d_out, dq, dk, dv, dg, db, dA, ddt, ws, al,
-                                            dt, x.lower_bound, initial_state=init, d_final=d_fin,
-                                            d_initial_state=dinit, flags=kda.FLAG_REUSE_RECORDS, stream=sh),
-                     args.steps, args.warmup, stream)
+    ms_reuse = None
+    if not args.no_reuse:
+        # the same gradients on the records a forward call left in this workspace
+        out, fin = torch.empty_like(v), torch.empty_like(init)
+        kda.kda_fwd_ex(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, init, fin,
+                       flags=kda.FLAG_KEEP_RECORDS, stream=sh)
+        ms_reuse = timed(lambda: kda.kda_bwd_ex(q, k, v, g, b, x.scale, d_out, dq, dk, dv, dg, db, dA, ddt, ws,
+                                                al, dt, x.lower_bound, initial_state=init, d_final=d_fin,
+                                                d_initial_state=dinit, flags=kda.FLAG_REUSE_RECORDS, stream=sh),
+                         args.steps, args.warmup, stream)
     ht = x.T * x.H
     alg = ht * (9 * 128 * 2 + 2 * 2) + 3 * x.H * STATE_BYTES
     gbs = alg / (ms / 1e3) / 1e9
@@ -361,7 +385,8 @@ def bench_bwd(args):
         "config": {"workload": f"kda_bwd B=1 T={x.T} H={x.H} K=V=128 chunk=64 lower_bound=-5, "
                                "output and final-state gradients given"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg},
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg,
+                     "traffic": measured_traffic("bwd") if (x.T, x.H) == (32768, 96) else None},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_bwd(x, 256, [0, 1]),
     }), flush=True)
 
@@ -516,7 +541,7 @@ def bench_forward(args):
                    "B": x.B, "T": x.T, "H": x.H, "K": 128, "V": 128, "N": x.N},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(args.single_launch) if headline else None,
+                     "traffic": measured_traffic("single" if args.single_launch else "fwd") if headline else None,
                      "kernel": "kda_fwd (every kernel of one forward)",
                      "median_kernel_ms": med_s * 1e3,
                      "mean_kernel_ms": sum(kern_ms) / len(kern_ms),
@@ -552,14 +577,17 @@ def main():
     ap.add_argument("--bwd", action="store_true", help="time the backward pass (kda_bwd) instead")
     ap.add_argument("--kcp-shards", type=int, default=0,
                     help="time the split-sequence path with this many shards instead")
-    ap.add_argument("--write-traffic", nargs=4, metavar=("FWD_FETCH", "FWD_WRITE", "COPY_FETCH", "COPY_WRITE"),
-                    help="rocprofv3 counter_collection.csv files -> profiles/kda_fwd_c3_traffic.json "
-                         "(with --single-launch: profiles/kda_fwd_c3_single_launch_traffic.json)")
+    ap.add_argument("--write-traffic", nargs=6, metavar=("MODE", "CALLS", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 counter_collection.csv files of CALLS identical calls of MODE (fwd, single, "
+                         "bwd, decode) and of --copy-calibration -> that mode's traffic file under profiles/")
+    ap.add_argument("--no-reuse", action="store_true",
+                    help="with --bwd: skip the second timing on a preceding forward's records")
     ap.add_argument("--single-launch", action="store_true",
                     help="time kda_fwd_ex with KDA_FLAG_SINGLE_LAUNCH (the one-launch producer/chain pipeline)")
     args = ap.parse_args()
     if args.write_traffic:
-        write_traffic(*args.write_traffic, single=args.single_launch)
+        mode, calls, *files = args.write_traffic
+        write_traffic(*files, calls=int(calls), mode=mode)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
