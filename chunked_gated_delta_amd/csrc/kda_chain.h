@@ -10,16 +10,16 @@
 //     O = scale [ (Q exp(G)) S + A_qk D ]   -> bf16 output
 //     S = Diag(exp(G_L)) S + (K exp(G_L - G))^T D   (fp16 hi/lo x fp16 hi/lo)
 // with every product, operand split and accumulation order of that kernel,
-// so the two give the same bits.  Where the inter kernel holds about 350
-// registers per lane (its record operands prefetched a whole chunk ahead), this one
+// so the two give the same bits.  Where the inter kernel holds 337 registers
+// per lane (its record operands prefetched a whole chunk ahead), this one
 // holds at most 256, so that two of its workgroups, or one of them and one
 // intra-chunk workgroup, fit on a CU.  The cost is that record operands are
 // not prefetched a whole chunk ahead (no room for a second register set):
 // each group is loaded when its previous use ends.
 //
 // Wave w owns the state rows (channels) 32w..32w+31 of the workgroup's
-// columns (2 row tiles x 2 NQ column tiles of fp32 accumulators, 16 NQ
-// registers) and the token rows 16w..16w+15 of U, D and O.  A chunk step runs the column quarters q
+// columns (16 NQ registers of fp32 accumulators per row tile) and the token
+// rows 16w..16w+15 of U, D and O.  A chunk step runs the column quarters q
 // (32 columns, tiles 2q, 2q+1):
 //     A_q: U and D of quarter q, and the state part of O      -> D hi/lo to LDS
 //     barrier
