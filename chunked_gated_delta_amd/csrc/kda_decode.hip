@@ -8,13 +8,14 @@
 // instagit FlashKDA page, "Usage Examples"), for the serving path that the
 // vLLM report's risk section mentions.  All arithmetic is fp32.
 //
-// The work is bound by the state's HBM traffic (64 KB read and 64 KB written
+// The work is bound by the state's HBM traffic (4 K V bytes read and written
 // per sequence and head), so it runs on the vector ALUs: one workgroup of 256
 // threads per (sequence, head, 32-column slice).  Thread t owns column
-// j = t % 32 of the slice and rows 16 (t / 32) .. + 15, so a state row of the
-// slice is one contiguous 128-byte access per 32 lanes.  Per token, threads
-// 0..127 compute the per-channel factors (normalised k and q, exp(g)) into LDS;
-// the two column reductions S^T k^ and S^T q^ go through LDS.
+// j = t % 32 of the slice and rows (K / 8) (t / 32) .. + K / 8 - 1, so a state
+// row of the slice is one contiguous 128-byte access per 32 lanes.  Per token,
+// threads 0..K-1 compute the per-channel factors (normalised k and q, exp(g))
+// into LDS; the two column reductions S^T k^ and S^T q^ go through LDS.  The
+// head dims K, V (64 or 128 each) are template parameters.
 
 #include "../../include/kda.h"
 #include "kda_common.h"
@@ -24,8 +25,7 @@ namespace {
 
 constexpr int DT = 256;       // threads
 constexpr int DSL = 32;       // state columns per workgroup
-constexpr int NDSL = VD / DSL;
-constexpr int DRG = 16;       // rows per thread
+constexpr int NRG = DT / DSL; // row groups
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -45,10 +45,14 @@ struct DecodeArgs {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
+template <int KK, int VV>
 __global__ void __launch_bounds__(DT) kda_decode_kernel(DecodeArgs a) {
-  __shared__ float sK[KD], sQ[KD], sE[KD];  // k^, q^, exp(g) of the current token
-  __shared__ float sRed[2][DT / DSL][DSL];  // column partial sums (S^T k^, S^T q^)
-  __shared__ float sNorm[2][2];             // per-wave partial |k|^2, |q|^2 (threads 0..127)
+  constexpr int NDSL = VV / DSL;  // slices per (sequence, head)
+  constexpr int DRG = KK / NRG;   // rows per thread
+  constexpr int NKW = KK / 64;    // waves holding the per-channel factors
+  __shared__ float sK[KK], sQ[KK], sE[KK];  // k^, q^, exp(g) of the current token
+  __shared__ float sRed[2][NRG][DSL];       // column partial sums (S^T k^, S^T q^)
+  __shared__ float sNorm[NKW][2];           // per-wave partial |k|^2, |q|^2 (threads 0..K-1)
   __shared__ float sBeta;
 
   const int H = a.H;
@@ -60,23 +64,23 @@ __global__ void __launch_bounds__(DT) kda_decode_kernel(DecodeArgs a) {
   const int j = t % DSL;
   const int rg = t / DSL;
   const int col = sl * DSL + j;
-  const size_t st0 = (size_t)bh * KD * VD;
+  const size_t st0 = (size_t)bh * KK * VV;
 
   float S[DRG];
 #pragma unroll
-  for (int r = 0; r < DRG; ++r) S[r] = a.init ? a.init[st0 + (size_t)(DRG * rg + r) * VD + col] : 0.0f;
+  for (int r = 0; r < DRG; ++r) S[r] = a.init ? a.init[st0 + (size_t)(DRG * rg + r) * VV + col] : 0.0f;
 
-  // per-channel constants of this head (threads 0..127 own channel t)
+  // per-channel constants of this head (threads 0..K-1 own channel t)
   const float na = -__expf(a.A_log[h]) * LOG2E;
-  const float nb = t < KD ? na * a.dt_bias[h * KD + t] : 0.0f;
+  const float nb = t < KK ? na * a.dt_bias[h * KK + t] : 0.0f;
 
   for (int tok = 0; tok < a.T; ++tok) {
     const size_t row = ((size_t)b * a.T + tok) * H + h;  // token row of [B, T, H, *]
     // ---- per-channel factors of this token
-    if (t < KD) {
-      const float kv = bf16_to_f32(a.k[row * KD + t]);
-      const float qv = bf16_to_f32(a.q[row * KD + t]);
-      const float gv = bf16_to_f32(a.g[row * KD + t]);
+    if (t < KK) {
+      const float kv = bf16_to_f32(a.k[row * KK + t]);
+      const float qv = bf16_to_f32(a.q[row * KK + t]);
+      const float gv = bf16_to_f32(a.g[row * KK + t]);
       float ssk = kv * kv, ssq = qv * qv;
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) {
@@ -94,10 +98,16 @@ __global__ void __launch_bounds__(DT) kda_decode_kernel(DecodeArgs a) {
       if (t == 0) sBeta = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-bf16_to_f32(a.beta[row]) * LOG2E));
     }
     __syncthreads();
-    const float rk = __builtin_amdgcn_rsqf(sNorm[0][0] + sNorm[1][0] + L2_EPS);
-    const float rq = __builtin_amdgcn_rsqf(sNorm[0][1] + sNorm[1][1] + L2_EPS);
+    float nk = 0.0f, nq = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NKW; ++u) {
+      nk += sNorm[u][0];
+      nq += sNorm[u][1];
+    }
+    const float rk = __builtin_amdgcn_rsqf(nk + L2_EPS);
+    const float rq = __builtin_amdgcn_rsqf(nq + L2_EPS);
     const float beta = sBeta;
-    const float vj = bf16_to_f32(a.v[row * VD + col]);
+    const float vj = bf16_to_f32(a.v[row * VV + col]);
 
     // ---- decay, then this thread's part of S^T k^
     float pk = 0.0f;
@@ -111,7 +121,7 @@ __global__ void __launch_bounds__(DT) kda_decode_kernel(DecodeArgs a) {
     __syncthreads();
     float dk = 0.0f;
 #pragma unroll
-    for (int u = 0; u < DT / DSL; ++u) dk += sRed[0][u][j];
+    for (int u = 0; u < NRG; ++u) dk += sRed[0][u][j];
     const float delta = beta * (vj - dk * rk);
 
     // ---- write, then this thread's part of S^T q^
@@ -127,15 +137,15 @@ __global__ void __launch_bounds__(DT) kda_decode_kernel(DecodeArgs a) {
     if (rg == 0) {
       float o = 0.0f;
 #pragma unroll
-      for (int u = 0; u < DT / DSL; ++u) o += sRed[1][u][j];
-      a.out[row * VD + col] = __builtin_bit_cast(uint16_t, (__bf16)(o * rq * a.scale));
+      for (int u = 0; u < NRG; ++u) o += sRed[1][u][j];
+      a.out[row * VV + col] = __builtin_bit_cast(uint16_t, (__bf16)(o * rq * a.scale));
     }
     // the next token overwrites sK/sQ/sE/sNorm/sRed only after everyone has read them
     __syncthreads();
   }
   if (a.fin) {
 #pragma unroll
-    for (int r = 0; r < DRG; ++r) a.fin[st0 + (size_t)(DRG * rg + r) * VD + col] = S[r];
+    for (int r = 0; r < DRG; ++r) a.fin[st0 + (size_t)(DRG * rg + r) * VV + col] = S[r];
   }
 }
 
@@ -153,9 +163,9 @@ extern "C" kda_status_t kda_decode(const void* q, const void* k, const void* v, 
   // token arrays may be NULL only when there are no tokens (empty tensors)
   if (T > 0 && (!q || !k || !v || !raw_gate || !raw_beta || !out)) return KDA_ERR_INVALID;
   if (!A_log || !dt_bias) return KDA_ERR_INVALID;
-  // the decode step is built for K = V = 128
-  if (K != KD || V != VD || !kda_is_supported(K, V, lower_bound)) return KDA_ERR_UNSUPPORTED;
-  if (B * H * NDSL > ((int64_t)1 << 31) - 1 || B * T * H > ((int64_t)1 << 40)) return KDA_ERR_INVALID;
+  if (!kda_is_supported(K, V, lower_bound)) return KDA_ERR_UNSUPPORTED;  // K, V each 64 or 128
+  const int64_t ndsl = V / DSL;
+  if (B * H * ndsl > ((int64_t)1 << 31) - 1 || B * T * H > ((int64_t)1 << 40)) return KDA_ERR_INVALID;
   DecodeArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -173,8 +183,11 @@ extern "C" kda_status_t kda_decode(const void* q, const void* k, const void* v, 
   a.T = (int)T;
   a.H = (int)H;
   void* args[] = {(void*)&a};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_decode_kernel),
-                                       dim3((unsigned)(B * H * NDSL)), dim3(DT), args, 0,
+  const void* fn = K == KD ? (V == VD ? reinterpret_cast<const void*>(&kda_decode_kernel<KD, VD>)
+                                      : reinterpret_cast<const void*>(&kda_decode_kernel<KD, 64>))
+                           : (V == VD ? reinterpret_cast<const void*>(&kda_decode_kernel<64, VD>)
+                                      : reinterpret_cast<const void*>(&kda_decode_kernel<64, 64>));
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(B * H * ndsl)), dim3(DT), args, 0,
                                        reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_SUCCESS : KDA_ERR_LAUNCH;
 }

@@ -65,9 +65,9 @@ size_t kda_workspace_size(int64_t T_total, int64_t H, int64_t N);
  * page's is_flashkda_supported(128, bf16, lower_bound) probe, whose first
  * argument is the head size).  Supported: K and V each 64 or 128, and
  * -5 <= lower_bound <= 0.  The -5 limit keeps every 16-token decay ratio
- * inside fp32/bf16 range (exp(16 * 5) < FLT_MAX).  kda_fwd and kda_fwd_ex
- * take every supported pair; kda_shard_affine, kda_shard_scan, kda_decode
- * and the backward take K == V == 128 only (KDA_ERR_UNSUPPORTED otherwise).
+ * inside fp32/bf16 range (exp(16 * 5) < FLT_MAX).  kda_fwd, kda_fwd_ex and
+ * kda_decode take every supported pair; kda_shard_affine, kda_shard_scan and
+ * the backward take K == V == 128 only (KDA_ERR_UNSUPPORTED otherwise).
  * Head dim 64 runs in the 128-channel layout of the kernels with the missing
  * channels held at zero, so it costs about what 128 costs.
  */
@@ -179,7 +179,7 @@ kda_status_t kda_shard_scan(const float* P, const float* R, const float* initial
  *   initial_state fp32 [B, H, K, V] or NULL for zeros
  *   final_state   fp32 [B, H, K, V] written, or NULL; may equal initial_state
  *                 (the usual in-place decode update)
- *   B, H >= 1, T >= 0; K == V == 128, lower_bound in [-5, 0]
+ *   B, H >= 1, T >= 0; K and V each 64 or 128, lower_bound in [-5, 0]
  *
  * Returns KDA_SUCCESS after enqueueing, KDA_ERR_INVALID / KDA_ERR_UNSUPPORTED
  * from the host checks, or KDA_ERR_LAUNCH.  For long prompts use kda_fwd,

@@ -200,7 +200,8 @@ def test_decode_checks():
     assert decode_call(H=0) == INVALID
     assert decode_call(T=-1) == INVALID
     assert decode_call(scale=float("nan")) == INVALID
-    assert decode_call(K=64, V=64) == UNSUPPORTED
+    assert decode_call(K=32, V=32) == UNSUPPORTED
+    assert decode_call(K=128, V=256) == UNSUPPORTED
     assert decode_call(lb=0.5) == UNSUPPORTED
 
 

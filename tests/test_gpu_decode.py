@@ -125,3 +125,36 @@ def test_decode_serving_shape_sampled_heads():
     heads = [0, 47, 95]
     ro, rf = oracle(x, heads=heads)
     check(o[:, heads], f[:, heads], ro, rf, "B=64 T=1 H=96, heads 0/47/95")
+
+
+@pytest.mark.parametrize("K,V", [(64, 64), (64, 128), (128, 64)])
+def test_decode_other_head_dims(K, V):
+    """Head dims 64 (instantiations of their own: K / 8 state rows per thread, V / 32
+    column slices), in place, from a chunked prefill of the same head dims."""
+    x = W.random_inputs(f"decode_{K}x{V}", 66 + K + V, 5, 3, 3, K=K, V=V, init_std=0.3)
+    o, f = gpu_decode(x)
+    check(o, f, *oracle(x), f"K={K} V={V}")
+    o2, f2 = gpu_decode(x, in_place=True)
+    assert np.array_equal(o, o2) and np.array_equal(f, f2)
+
+
+def test_decode_continues_a_chunked_prefill_at_head_dim_64():
+    T0, T1 = 130, 2
+    x = W.random_inputs("decode64", 67, 1, T0 + T1, 3, K=64, V=64, init_std=0.1)
+    pre = [t[:, :T0].contiguous() for t in (x.q, x.k, x.v, x.raw_gate, x.raw_beta)]
+    dec = [t[:, T0:].contiguous() for t in (x.q, x.k, x.v, x.raw_gate, x.raw_beta)]
+    state = d(x.initial_state.clone())
+    out_p = torch.empty_like(d(pre[2]))
+    ws = torch.empty(kda.kda_workspace_size(T0, x.H, 1), dtype=torch.uint8, device=DEV)
+    kda.kda_fwd(*(d(t) for t in pre[:5]), x.scale, out_p, ws, d(x.A_log), d(x.dt_bias), x.lower_bound,
+                state, state)
+    out_d = torch.empty_like(d(dec[2]))
+    kda.kda_decode(*(d(t) for t in dec[:5]), x.scale, out_d, d(x.A_log), d(x.dt_bias), x.lower_bound,
+                   state, state)
+    torch.cuda.synchronize()
+    ro, rf = oracle(x)
+    o = torch.cat([out_p, out_d], dim=1).double().cpu().numpy().reshape(T0 + T1, x.H, x.V)
+    mo, mf = metrics(o, ro), metrics(state.double().cpu().numpy(), rf)
+    print(f"prefill+decode K=V=64: out rel_l2={mo['rel_l2']:.3e} final rel_l2={mf['rel_l2']:.3e}", flush=True)
+    assert mo["rel_l2"] <= OUT_REL and mo["max_abs"] <= OUT_ABS, mo
+    assert mf["rel_l2"] <= 1e-3, mf
