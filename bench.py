@@ -58,7 +58,7 @@ _FWD_SRCS = ("kda_common.h", "kda_host.h", "kda_intra.hip", "kda_inter.hip", "kd
 KERNEL_SRCS = {
     "fwd": _FWD_SRCS,
     "single": _FWD_SRCS,
-    "bwd": _FWD_SRCS + ("kda_bwd.h", "kda_bwd.hip"),
+    "bwd": _FWD_SRCS + ("kda_bwd.h", "kda_bwd_dev.h", "kda_bwd.hip", "kda_bwd_grad.hip"),
     "decode": ("kda_common.h", "kda_decode.hip"),
 }
 # rocprofv3 FETCH_SIZE / WRITE_SIZE summaries per mode (--write-traffic writes them)

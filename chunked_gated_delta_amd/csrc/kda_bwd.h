@@ -56,5 +56,7 @@ struct BwdShards {
 };
 // `sh` == nullptr: one reverse pass over whole sequences
 hipError_t launch_bwd(const BwdArgs& a, int64_t max_chunks, const BwdShards* sh, hipStream_t st);
+// the token-gradient kernel over `items` (chunk, head) workgroups (kda_bwd_grad.hip)
+hipError_t launch_grad(const BwdArgs& a, int64_t items, hipStream_t st);
 
 }  // namespace kda

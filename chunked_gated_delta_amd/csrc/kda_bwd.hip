@@ -33,81 +33,13 @@
 // operand of a product that contracts over its rows.
 
 #include "kda_bwd.h"
+#include "kda_bwd_dev.h"
 #include "kda_host.h"
 
 namespace kda {
 namespace {
 
 constexpr int NT = 256;  // recurrence kernel: 4 waves
-constexpr int QP = KD + 4;  // pitch (floats) of [64][128] LDS tiles
-constexpr int MP = CH + 4;  // pitch of [64][64] LDS tiles
-constexpr int VH = VD / 2;  // state columns per recurrence workgroup
-
-// Chunk record of the backward (offsets in floats).  T and KK are fp32,
-// row-major.  The four operands of the reverse recurrence are bf16 hi/lo
-// pairs in the forward record's MFMA fragment order (frag_tc / frag_tt /
-// frag_ct): the hi array of a region, then its lo array.  The output scale is
-// folded into A_qk^T and QG^T, and W^T is stored negated.
-constexpr int BR_T = 0;                   // T = (I + diag(beta) KK)^-1, unit lower, [64][64] row-major
-constexpr int BR_KK = BR_T + CH * CH;     // KK = K^ K^T . decay, strictly lower,     [64][64] row-major
-constexpr int BR_AQKT = BR_KK + CH * CH;  // scale A_qk^T (rows i, contraction j),  frag_tt, hi + lo
-constexpr int BR_WT = BR_AQKT + CH * CH;  // -W^T (rows k, contraction i),          frag_ct, hi + lo
-constexpr int BR_KT = BR_WT + CH * KD;    // Kt = K^ exp(G_L - G) (rows i, contraction k), frag_tc, hi + lo
-constexpr int BR_QGT = BR_KT + CH * KD;   // scale QG^T (rows k, contraction i),     frag_ct, hi + lo
-constexpr int BR_GL = BR_QGT + CH * KD;   // exp(G_L)                                 [128]
-constexpr int BR_BETA = BR_GL + KD;       // beta                                     [64]
-static_assert(BR_BETA + CH == BWD_REC_FLOATS, "record size");
-
-// Store x0..x3 (4 consecutive fragment elements starting at idx) of an n-element
-// bf16 hi/lo region: hi at idx, lo = x - hi at n + idx.
-__device__ __forceinline__ void store_hl4(float* region, int n, int idx, float x0, float x1, float x2, float x3) {
-  __bf16* hi = reinterpret_cast<__bf16*>(region);
-  const float x[4] = {x0, x1, x2, x3};
-  bf16x4 h, l;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    h[e] = (__bf16)x[e];
-    l[e] = (__bf16)(x[e] - (float)h[e]);
-  }
-  *reinterpret_cast<bf16x4*>(hi + idx) = h;
-  *reinterpret_cast<bf16x4*>(hi + n + idx) = l;
-}
-
-__device__ __forceinline__ void split_hl8(const float (&x)[8], bf16x8& h, bf16x8& l) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = (__bf16)x[e];
-    l[e] = (__bf16)(x[e] - (float)h[e]);
-  }
-}
-// 8 consecutive floats from global memory as a bf16 hi/lo pair
-__device__ __forceinline__ void ld_hl8(const float* p, bf16x8& h, bf16x8& l) {
-  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  split_hl8(x, h, l);
-}
-
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ __forceinline__ float el(const float4& v, int s) {
-  return s == 0 ? v.x : (s == 1 ? v.y : (s == 2 ? v.z : v.w));
-}
-__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-__device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even (finite inputs)
-  const uint32_t u = __float_as_uint(f);
-  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
-__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + expf(-x)); }
-
-// (sequence, first token, length) of global chunk gch
-__device__ __forceinline__ void chunk_of(const ChunkMap& m, int64_t gch, int64_t& c0, int& L) {
-  const int seq = chunk_owner(m, gch);
-  int64_t bos, eos;
-  seq_bounds(m, seq, bos, eos);
-  c0 = bos + (gch - first_chunk(m, seq)) * CH;
-  L = (int)((eos - c0) < CH ? (eos - c0) : CH);
-}
-
 // Per-token preparation of one chunk into LDS: q^, k^ (rows past the end are
 // zero), G = cumulative log2-decay (constant past the end), beta, the row
 // norms of q and k.  NTH threads: NTH / 64 per token, KD / (NTH / 64) channels
@@ -496,13 +428,6 @@ __device__ __forceinline__ void store_dot(__bf16* sO, const uint4 (&vv)[2], int 
   }
 }
 
-__device__ __forceinline__ void split_hl4(const f32x4& x, bf16x4& h, bf16x4& l) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    h[e] = (__bf16)x[e];
-    l[e] = (__bf16)(x[e] - (float)h[e]);
-  }
-}
 
 __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DHU_BYTES];
@@ -712,598 +637,6 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// kda_bwd_grad_kernel: per (chunk, head), 8 waves.  Wave (w, p) = (wave % 4,
-// wave / 4) owns token block 16w..16w+15 and half p of the work: channels
-// 64p..64p+63 of every token-by-channel product, V half p of Z, alternate
-// column blocks of the 64 x 64 products.  Two waves per SIMD hide each
-// other's memory latency.
-//
-// V index permutation: a float4 load gives a lane 4 consecutive v, so in a
-// 64-wide V half hv the A-operand row tl of "virtual tile" e is
-// v = 64 hv + 4 tl + e, and C row 4 gq + ii of that tile is
-// v = 64 hv + 16 gq + 4 ii + e.  Contractions over v use the same order, so
-// every v-operand is a float4 (or 16-bf16) load.
-// ---------------------------------------------------------------------------
-constexpr int NT8 = 512;
-constexpr int GRAD_FLOATS = 3 * CH * QP + 3 * CH * MP + 4 * CH + NT8 + 4 * KD + KD + 4 * KD + 4 * CH;
-static_assert(GRAD_FLOATS * 4 <= 163840, "LDS");
-
-__global__ void __launch_bounds__(NT8, 1) kda_bwd_grad_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) float smem[GRAD_FLOATS];
-  float* sQn = smem;
-  float* sKn = sQn + CH * QP;
-  float* sG = sKn + CH * QP;
-  float* sT = sG + CH * QP;
-  float* sM1 = sT + CH * MP;   // dA_qk
-  float* sM2 = sM1 + CH * MP;  // dTb -> dT, then X = dT T^T, then dKK
-  float* sBeta = sM2 + CH * MP;
-  float* sRq = sBeta + CH;
-  float* sRk = sRq + CH;
-  float* sdB = sRk + CH;       // gradient of beta (atomically accumulated)
-  float* sTmp = sdB + CH;      // [512]
-  float* sGLw = sTmp + NT8;    // [4][128] per-block sums of dKt . Kt, later of d dt_bias
-  float* sGL2 = sGLw + 4 * KD; // [128] exp(G_L) sum_v dS' . S0
-  float* sCS = sGL2 + KD;      // [4][128] per-block column totals of dG
-  float* sDot = sCS + 4 * KD;  // [2][64][2] half-row dots q^.dq^, k^.dk^
-  // bf16 output staging, over sT / sM1 / sM2 once the pairwise products are done
-  uint16_t* sOut = reinterpret_cast<uint16_t*>(sT);  // [3][64][128]: dq, dk, d raw_gate
-
-  const int H = a.H;
-  const int64_t gch = blockIdx.x / H;
-  const int h = blockIdx.x - (int)gch * H;
-  if (gch >= total_chunks(a.map)) return;
-  int64_t c0;
-  int L;
-  chunk_of(a.map, gch, c0, L);
-  const size_t it = blockIdx.x;
-  const float* br = a.br + it * BWD_REC_FLOATS;
-  const float* S0 = a.states + it * KD * VD;
-  const float* dSn = a.dstates + it * KD * VD;
-  const float* Dt = a.dtile + it * CH * VD;
-  const float* dDt = a.ddtile + it * CH * VD;
-
-  KDA_TIMER_DECL
-  KDA_TIMER_MARK(0);
-  const int tid = threadIdx.x;
-  // loads that do not depend on the preparation, issued first
-  float4 tcp[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) tcp[u] = ld4(br + BR_T + 4 * (tid + NT8 * u));
-  float gl2 = 0.f;
-  {
-    const int c = tid >> 2;
-    const int v0 = 32 * (tid & 3);
-    float4 x[8], y[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      x[u] = ld4(dSn + c * VD + v0 + 4 * u);
-      y[u] = ld4(S0 + c * VD + v0 + 4 * u);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) gl2 += x[u].x * y[u].x + x[u].y * y[u].y + x[u].z * y[u].z + x[u].w * y[u].w;
-    gl2 += __shfl_xor(gl2, 1);
-    gl2 += __shfl_xor(gl2, 2);
-  }
-  prep_chunk<NT8>(a, c0, L, h, sQn, sKn, sG, sBeta, sRq, sRk, sTmp);
-  KDA_TIMER_MARK(1);
-
-  const int wv = tid >> 6;
-  const int w = wv & 3;
-  const int p = wv >> 2;
-  const int lane = tid & 63;
-  const int tl = lane & 15;
-  const int gq = lane >> 4;
-  const int jw = 16 * w + tl;  // this lane's token as an A row / B column
-
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = 4 * (tid + NT8 * u);
-    *reinterpret_cast<float4*>(sT + (e >> 6) * MP + (e & 63)) = tcp[u];
-  }
-  if ((tid & 3) == 0) sGL2[tid >> 2] = gl2 * fexp2(sG[(CH - 1) * QP + (tid >> 2)]);
-  for (int e = tid; e < CH * MP; e += NT8) {
-    sM1[e] = 0.f;
-    sM2[e] = 0.f;
-  }
-  if (tid < CH) sdB[tid] = 0.f;
-  __syncthreads();
-  KDA_TIMER_MARK(2);
-
-  const bool jok = jw < L;
-  const size_t jrow = ((size_t)(c0 + (jok ? jw : 0)) * H + h);
-  const float bj = sBeta[jw];
-
-  // ---- Z^T, V half p: Z^T[v][jw] = V[jw][v] - sum_k S0[k][v] KG[jw][k]
-  f32x4 Zt[4];
-  {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Zt[e] = zero4();
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float4 kn = ld4(sKn + jw * QP + 16 * t + 4 * gq), gg = ld4(sG + jw * QP + 16 * t + 4 * gq);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const float kg = el(kn, s) * fexp2(el(gg, s));
-        const float4 a4 = ld4(S0 + (16 * t + 4 * gq + s) * VD + 64 * p + 4 * tl);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Zt[e] = mfma_f32(el(a4, e), kg, Zt[e]);
-      }
-    }
-    float vv[16];
-    if (jok) {
-      const uint4* src = reinterpret_cast<const uint4*>(a.v + jrow * VD + 64 * p + 16 * gq);
-      unpack_bf16x8(src[0], *reinterpret_cast<float(*)[8]>(vv));
-      unpack_bf16x8(src[1], *reinterpret_cast<float(*)[8]>(vv + 8));
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) vv[r] = 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) Zt[e][ii] = vv[4 * ii + e] - Zt[e][ii];
-  }
-  // ---- dTb[i][jw] for i >= 16w, V half p (atomically summed over p): dD Z^T on
-  // bf16 MFMA, hi/lo on both sides.  k-step `half` takes v = 64p + 16gq + 8half + 0..7,
-  // which Zt holds as Zt[e8 % 4][2 half + e8 / 4].
-  {
-    bf16x8 zh[2], zl[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float zx[8];
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) zx[e8] = Zt[e8 & 3][2 * half + (e8 >> 2)];
-      split_hl8(zx, zh[half], zl[half]);
-    }
-#pragma unroll
-    for (int ab = 0; ab < 4; ++ab) {
-      if (ab < w) continue;
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 ah, al;
-        ld_hl8(dDt + (16 * ab + tl) * VD + 64 * p + 16 * gq + 8 * half, ah, al);
-        acc = mfma_bf16(ah, zh[half], acc);
-        acc = mfma_bf16(ah, zl[half], acc);
-        acc = mfma_bf16(al, zh[half], acc);
-      }
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) atomicAdd(sM2 + (16 * ab + 4 * gq + ii) * MP + jw, acc[ii]);
-    }
-  }
-  KDA_TIMER_MARK(3);
-
-  // ---- dv^T, both V halves: dv[jw][v] = sum_{i >= jw} Tb[i][jw] dD[i][v]
-  f32x4 dvT[2][4];
-  {
-#pragma unroll
-    for (int hv = 0; hv < 2; ++hv)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dvT[hv][e] = zero4();
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
-      if (ib < w) continue;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int kap = 16 * ib + 4 * gq + s;
-        const float tb = sT[kap * MP + jw] * bj;
-#pragma unroll
-        for (int hv = 0; hv < 2; ++hv) {
-          const float4 a4 = ld4(dDt + kap * VD + 64 * hv + 4 * tl);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dvT[hv][e] = mfma_f32(el(a4, e), tb, dvT[hv][e]);
-        }
-      }
-    }
-    if (jok) {  // wave p writes V half p: 16 consecutive v per lane
-      uint32_t pk[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int r0 = 2 * r, r1 = 2 * r + 1;  // r = 4 ii + e
-        const float x0 = p ? dvT[1][r0 & 3][r0 >> 2] : dvT[0][r0 & 3][r0 >> 2];
-        const float x1 = p ? dvT[1][r1 & 3][r1 >> 2] : dvT[0][r1 & 3][r1 >> 2];
-        pk[r] = (uint32_t)f2bf(x0) | ((uint32_t)f2bf(x1) << 16);
-      }
-      uint4* dst = reinterpret_cast<uint4*>(a.dv + jrow * VD + 64 * p + 16 * gq);
-      dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-    }
-  }
-  KDA_TIMER_MARK(4);
-
-  // ---- bf16 MFMA operands over v for the products below.  k-step (hv, half)
-  // takes v = 64hv + 16gq + 8half + 0..7 in lane group gq:
-  //   dO[jw][v] (exact bf16, the scale is applied to the results),
-  //   -dv[jw][v] hi/lo (dvT holds it as dvT[hv][e8 % 4][2 half + e8 / 4]),
-  //   D[jw][v] hi/lo (loaded where it is used).
-  bf16x8 doA[2][2], dvh[2][2], dvl[2][2];
-#pragma unroll
-  for (int hv = 0; hv < 2; ++hv)
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (jok)
-        doA[hv][half] = *reinterpret_cast<const bf16x8*>(a.dout + jrow * VD + 64 * hv + 16 * gq + 8 * half);
-      else
-        doA[hv][half] = bf16x8{};
-      float x[8];
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) x[e8] = -dvT[hv][e8 & 3][2 * half + (e8 >> 2)];
-      split_hl8(x, dvh[hv][half], dvl[hv][half]);
-    }
-  // ---- dA_qk[block w][block b] = scale dO D^T (j <= i), column blocks b <= w of parity p
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    if (b > w || (b & 1) != p) continue;
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int hv = 0; hv < 2; ++hv)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 bh, bl;
-        ld_hl8(Dt + (16 * b + tl) * VD + 64 * hv + 16 * gq + 8 * half, bh, bl);
-        acc = mfma_bf16(doA[hv][half], bh, acc);
-        acc = mfma_bf16(doA[hv][half], bl, acc);
-      }
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int i = 16 * w + 4 * gq + ii, j = 16 * b + tl;
-      sM1[i * MP + j] = (j <= i) ? acc[ii] * a.scale : 0.f;
-    }
-  }
-
-  // ---- dQG = scale dO S0^T, dKG = -dv S0^T, dKt = D dS'^T for channels 64p..64p+63,
-  // and their elementwise contributions to dq^, dk^, dG
-  f32x4 dqh[4], dkh[4], dGa[4];
-#pragma unroll
-  for (int nn = 0; nn < 4; ++nn) {
-    const int kc = 64 * p + 16 * nn + tl;
-    f32x4 aQ = zero4(), aK = zero4(), aT = zero4();
-#pragma unroll
-    for (int hv = 0; hv < 2; ++hv)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 sh, sl, th, tl8, dah, dal;
-        ld_hl8(S0 + kc * VD + 64 * hv + 16 * gq + 8 * half, sh, sl);
-        ld_hl8(dSn + kc * VD + 64 * hv + 16 * gq + 8 * half, th, tl8);
-        ld_hl8(Dt + jw * VD + 64 * hv + 16 * gq + 8 * half, dah, dal);
-        aQ = mfma_bf16(doA[hv][half], sh, aQ);
-        aQ = mfma_bf16(doA[hv][half], sl, aQ);
-        aK = mfma_bf16(dvh[hv][half], sh, aK);
-        aK = mfma_bf16(dvh[hv][half], sl, aK);
-        aK = mfma_bf16(dvl[hv][half], sh, aK);
-        aT = mfma_bf16(dah, th, aT);
-        aT = mfma_bf16(dah, tl8, aT);
-        aT = mfma_bf16(dal, th, aT);
-      }
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) aQ[ii] *= a.scale;
-    const int c = 64 * p + 16 * nn + tl;
-    float glsum = 0.f;
-    const float gl2c = sG[(CH - 1) * QP + c];
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int j = 16 * w + 4 * gq + ii;
-      const float qn = sQn[j * QP + c], kn = sKn[j * QP + c], g2 = sG[j * QP + c];
-      const float gam = fexp2(g2), el2 = fexp2(gl2c - g2);
-      const float kt = kn * el2;
-      dqh[nn][ii] = aQ[ii] * gam;
-      dkh[nn][ii] = aK[ii] * gam + aT[ii] * el2;
-      dGa[nn][ii] = aQ[ii] * qn * gam + aK[ii] * kn * gam - aT[ii] * kt;
-      glsum += aT[ii] * kt;
-    }
-    glsum += __shfl_xor(glsum, 16);
-    glsum += __shfl_xor(glsum, 32);
-    if (gq == 0) sGLw[w * KD + c] = glsum;
-  }
-  KDA_TIMER_MARK(5);
-
-  __syncthreads();
-  KDA_TIMER_MARK(6);
-
-  // ---- dT = dTb diag(beta) in place; column sums of dTb . T -> dbeta (rows split by p)
-  {
-    float colsum = 0.f;
-#pragma unroll
-    for (int ab = 0; ab < 4; ++ab) {
-      if (ab < w || ((ab - w) & 1) != p) continue;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int i = 16 * ab + 4 * gq + ii;
-        const float v = sM2[i * MP + jw];
-        colsum += v * sT[i * MP + jw];
-        sM2[i * MP + jw] = v * bj;
-      }
-    }
-    colsum += __shfl_xor(colsum, 16);
-    colsum += __shfl_xor(colsum, 32);
-    if (gq == 0) atomicAdd(sdB + jw, colsum);
-  }
-  __syncthreads();
-  // ---- X = dT T^T, row block w, column blocks q <= w of parity p
-  {
-    f32x4 X[2];
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      const int q = 2 * qq + p;
-      X[qq] = zero4();
-      if (q > w) continue;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (b > q) continue;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int kap = 16 * b + 4 * gq + s;
-          X[qq] = mfma_f32(sM2[jw * MP + kap], sT[(16 * q + tl) * MP + kap], X[qq]);
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      const int q = 2 * qq + p;
-      if (q > w) continue;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) sM2[(16 * w + 4 * gq + ii) * MP + 16 * q + tl] = X[qq][ii];
-    }
-  }
-  __syncthreads();
-  // ---- dA_kk[block w][m < a] = -T^T X; row sums of dA_kk . KK -> dbeta; dKK = dA_kk beta_a
-  {
-    f32x4 dkk[2];
-    float rows[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      const int q = 2 * qq + p;
-      f32x4 acc = zero4();
-      if (q <= w) {
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-          if (pb < w) continue;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const int kap = 16 * pb + 4 * gq + s;
-            acc = mfma_f32(-sT[kap * MP + jw], sM2[kap * MP + 16 * q + tl], acc);
-          }
-        }
-      }
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int ar = 16 * w + 4 * gq + ii, mc = 16 * q + tl;
-        const float v = (q <= w && mc < ar) ? acc[ii] : 0.f;
-        rows[ii] += v * br[BR_KK + ar * CH + (mc & 63)];
-        acc[ii] = v * sBeta[ar];
-      }
-      dkk[qq] = acc;
-    }
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      float r = rows[ii];
-      r += __shfl_xor(r, 1);
-      r += __shfl_xor(r, 2);
-      r += __shfl_xor(r, 4);
-      r += __shfl_xor(r, 8);
-      if (tl == 0) atomicAdd(sdB + 16 * w + 4 * gq + ii, r);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      const int q = 2 * qq + p;
-      if (q > w) continue;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) sM2[(16 * w + 4 * gq + ii) * MP + 16 * q + tl] = dkk[qq][ii];
-    }
-  }
-  __syncthreads();
-  KDA_TIMER_MARK(7);
-
-  // ---- pairwise products, row role: i in block w, j in blocks b <= w
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    if (b > w) continue;
-    const int r = (b < w) ? 16 * b + 15 : 16 * w;
-    float m1[4], m2[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      m1[s] = sM1[jw * MP + 16 * b + 4 * gq + s];
-      m2[s] = sM2[jw * MP + 16 * b + 4 * gq + s];
-    }
-#pragma unroll
-    for (int nn = 0; nn < 4; ++nn) {
-      const int c = 64 * p + 16 * nn + tl;
-      const float gr = sG[r * QP + c];
-      f32x4 a1 = zero4(), a2 = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int kap = 16 * b + 4 * gq + s;
-        const float y = sKn[kap * QP + c] * fexp2(gr - sG[kap * QP + c]);
-        a1 = mfma_f32(m1[s], y, a1);
-        a2 = mfma_f32(m2[s], y, a2);
-      }
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int i = 16 * w + 4 * gq + ii;
-        const float f = fexp2(sG[i * QP + c] - gr);
-        const float v1 = a1[ii] * f, v2 = a2[ii] * f;
-        dqh[nn][ii] += v1;
-        dkh[nn][ii] += v2;
-        dGa[nn][ii] += sQn[i * QP + c] * v1 + sKn[i * QP + c] * v2;
-      }
-    }
-  }
-  KDA_TIMER_MARK(8);
-  // ---- pairwise products, column role: j in block w, i in blocks a >= w
-#pragma unroll
-  for (int ab = 0; ab < 4; ++ab) {
-    if (ab < w) continue;
-    const int r = (ab > w) ? 16 * w + 15 : 16 * w;
-    float m1[4], m2[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      m1[s] = sM1[(16 * ab + 4 * gq + s) * MP + jw];
-      m2[s] = sM2[(16 * ab + 4 * gq + s) * MP + jw];
-    }
-#pragma unroll
-    for (int nn = 0; nn < 4; ++nn) {
-      const int c = 64 * p + 16 * nn + tl;
-      const float gr = sG[r * QP + c];
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int kap = 16 * ab + 4 * gq + s;
-        const float f = fexp2(sG[kap * QP + c] - gr);
-        acc = mfma_f32(m1[s], sQn[kap * QP + c] * f, acc);
-        acc = mfma_f32(m2[s], sKn[kap * QP + c] * f, acc);
-      }
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int j = 16 * w + 4 * gq + ii;
-        const float v = acc[ii] * fexp2(gr - sG[j * QP + c]);
-        dkh[nn][ii] += v;
-        dGa[nn][ii] -= sKn[j * QP + c] * v;
-      }
-    }
-  }
-  KDA_TIMER_MARK(9);
-
-  // ---- dG_L on the last token, then the reverse cumulative sum -> dg
-  const int lastw = (L - 1) >> 4;
-#pragma unroll
-  for (int nn = 0; nn < 4; ++nn) {
-    const int c = 64 * p + 16 * nn + tl;
-    if (w == lastw) {
-      const float dgl = sGL2[c] + sGLw[c] + sGLw[KD + c] + sGLw[2 * KD + c] + sGLw[3 * KD + c];
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        if (16 * w + 4 * gq + ii == L - 1) dGa[nn][ii] += dgl;
-    }
-    f32x4 x = dGa[nn];
-    x[2] += x[3];
-    x[1] += x[2];
-    x[0] += x[1];
-    const float tot = x[0];
-    const float t1 = __shfl(tot, tl + 16), t2 = __shfl(tot, tl + 32), t3 = __shfl(tot, tl + 48);
-    const float off = (gq < 1 ? t1 : 0.f) + (gq < 2 ? t2 : 0.f) + (gq < 3 ? t3 : 0.f);
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) x[ii] += off;
-    dGa[nn] = x;
-    if (gq == 0) sCS[w * KD + c] = x[0];
-  }
-  // half-row dots q^.dq^ and k^.dk^ over this wave's 64 channels
-#pragma unroll
-  for (int ii = 0; ii < 4; ++ii) {
-    const int j = 16 * w + 4 * gq + ii;
-    float dq_dot = 0.f, dk_dot = 0.f;
-#pragma unroll
-    for (int nn = 0; nn < 4; ++nn) {
-      const int c = 64 * p + 16 * nn + tl;
-      dq_dot += sQn[j * QP + c] * dqh[nn][ii];
-      dk_dot += sKn[j * QP + c] * dkh[nn][ii];
-    }
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
-      dq_dot += __shfl_xor(dq_dot, d);
-      dk_dot += __shfl_xor(dk_dot, d);
-    }
-    if (tl == 0) {
-      sDot[(p * CH + j) * 2] = dq_dot;
-      sDot[(p * CH + j) * 2 + 1] = dk_dot;
-    }
-  }
-  __syncthreads();
-  KDA_TIMER_MARK(10);
-
-  // ---- outputs, staged in LDS: d raw_gate, dq, dk; partial sums of d dt_bias, dA_log
-  const bool gate_given = a.flags & FLAG_GATE_GIVEN;
-  const float al = gate_given ? 0.f : expf(a.A_log[h]);
-  float pA = 0.f;
-  uint16_t* oq = sOut;
-  uint16_t* ok_ = sOut + CH * KD;
-  uint16_t* og = sOut + 2 * CH * KD;
-#pragma unroll
-  for (int nn = 0; nn < 4; ++nn) {
-    const int c = 64 * p + 16 * nn + tl;
-    float later = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (u > w) later += sCS[u * KD + c];
-    const float dtb = gate_given ? 0.f : a.dt_bias[(size_t)h * KD + c];
-    float pdt = 0.f;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int j = 16 * w + 4 * gq + ii;
-      const float dgv = dGa[nn][ii] + later;  // gradient of the natural-log decay g_j
-      float dgo = 0.f;
-      if (j < L) {
-        const size_t o = ((size_t)(c0 + j) * H + h) * KD + c;
-        const float rg = bf2f(a.g[o]);
-        if (gate_given) {
-          // g = clamp(raw_gate, lower_bound, 0): the gradient passes inside the closed interval
-          dgo = (rg >= a.lb && rg <= 0.f) ? dgv : 0.f;
-        } else {
-          const float x = al * (rg + dtb);
-          const float sg = sigmoidf(x);
-          const float dx = dgv * a.lb * sg * (1.f - sg);
-          dgo = dx * al;
-          pdt += dgo;
-          pA += dx * x;
-        }
-      }
-      og[j * KD + c] = f2bf(dgo);
-    }
-    pdt += __shfl_xor(pdt, 16);
-    pdt += __shfl_xor(pdt, 32);
-    if (gq == 0) sGLw[w * KD + c] = pdt;  // sGLw is free again: dG_L was added before the barrier
-  }
-  // dq = (dq^ - q^ (q^ . dq^)) / |q|, same for k
-#pragma unroll
-  for (int ii = 0; ii < 4; ++ii) {
-    const int j = 16 * w + 4 * gq + ii;
-    // dq = dq^ when q is used without the L2 norm (the projection term and the row norm drop)
-    const bool norm = !(a.flags & FLAG_NO_QK_NORM);
-    const float dq_dot = norm ? sDot[j * 2] + sDot[(CH + j) * 2] : 0.f;
-    const float dk_dot = norm ? sDot[j * 2 + 1] + sDot[(CH + j) * 2 + 1] : 0.f;
-    const float irq = 1.f / sRq[j], irk = 1.f / sRk[j];
-#pragma unroll
-    for (int nn = 0; nn < 4; ++nn) {
-      const int c = 64 * p + 16 * nn + tl;
-      oq[j * KD + c] = f2bf((dqh[nn][ii] - sQn[j * QP + c] * dq_dot) * irq);
-      ok_[j * KD + c] = f2bf((dkh[nn][ii] - sKn[j * QP + c] * dk_dot) * irk);
-    }
-  }
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) pA += __shfl_xor(pA, d);
-  if (lane == 0) sTmp[wv] = pA;
-  if (p == 0 && lane < 16 && jw < L) {
-    const float b = sBeta[jw];
-    a.dbeta[(size_t)(c0 + jw) * H + h] = f2bf((a.flags & FLAG_BETA_GIVEN) ? sdB[jw] : sdB[jw] * b * (1.f - b));
-  }
-  __syncthreads();
-  // 16-byte stores of the staged rows: thread -> (row, 16-byte column block)
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = tid + NT8 * u;  // 0 .. 1023
-    const int row = e >> 4;
-    const int cb = 8 * (e & 15);
-    if (row < L) {
-      const size_t o = ((size_t)(c0 + row) * H + h) * KD + cb;
-      *reinterpret_cast<uint4*>(a.dq + o) = *reinterpret_cast<const uint4*>(oq + row * KD + cb);
-      *reinterpret_cast<uint4*>(a.dk + o) = *reinterpret_cast<const uint4*>(ok_ + row * KD + cb);
-      *reinterpret_cast<uint4*>(a.dg + o) = *reinterpret_cast<const uint4*>(og + row * KD + cb);
-    }
-  }
-  float* part = a.part + it * (KD + 1);
-  if (tid < KD) part[tid] = sGLw[tid] + sGLw[KD + tid] + sGLw[2 * KD + tid] + sGLw[3 * KD + tid];
-  if (tid == KD) {
-    float sA = 0.f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) sA += sTmp[u];
-    part[KD] = sA;
-  }
-  KDA_TIMER_MARK(11);
-  KDA_TIMER_STORE(a.timers ? a.timers + (size_t)gridDim.x * 16 : nullptr);
-}
-
-// ---------------------------------------------------------------------------
 // kda_bwd_reduce_kernel: per head, sum the per-chunk partials.  Thread t sums
 // column t % 129 over the chunks of residue t / 129 mod 4, then the four
 // partial sums meet in LDS.
@@ -1379,8 +712,7 @@ hipError_t launch_bwd(const BwdArgs& args, int64_t max_chunks, const BwdShards* 
   }
   if (e != hipSuccess) return e;
   if (items > 0) {
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_bwd_grad_kernel), dim3((unsigned)items), dim3(NT8),
-                        kargs, 0, st);
+    e = launch_grad(a, items, st);
     if (e != hipSuccess) return e;
   }
   return hipLaunchKernel(reinterpret_cast<const void*>(&kda_bwd_reduce_kernel), dim3((unsigned)a.H), dim3(NTR),

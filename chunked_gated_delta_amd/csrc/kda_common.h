@@ -182,12 +182,13 @@ __device__ __forceinline__ void frag_write4(char* base, int frag, int q, int tl,
 }
 
 // Optional per-phase cycle counters, compiled out unless KDA_PHASE_TIMERS is
-// defined: thread 0 of each workgroup accumulates cycle-counter deltas between
-// phase marks and stores them to timers[blockIdx.x * 16 + i].
+// defined: every wave accumulates cycle-counter deltas between phase marks
+// (wave-uniform values, so they stay in scalar registers) and thread 0 stores
+// its wave's to timers[blockIdx.x * 16 + i].
 #ifdef KDA_PHASE_TIMERS
 #define KDA_TIMER_DECL unsigned long long tacc_[15] = {0}; unsigned long long tlast_ = 0;
-#define KDA_TIMER_MARK(i) do { if (threadIdx.x == 0) { const unsigned long long t_ = __builtin_readcyclecounter(); \
-    if ((i) > 0) tacc_[(i) - 1] += t_ - tlast_; tlast_ = t_; } } while (0)
+#define KDA_TIMER_MARK(i) do { const unsigned long long t_ = __builtin_readcyclecounter(); \
+    if ((i) > 0) tacc_[(i) - 1] += t_ - tlast_; tlast_ = t_; } while (0)
 #define KDA_TIMER_STORE(ptr) do { if (threadIdx.x == 0 && (ptr)) for (int i_ = 0; i_ < 15; ++i_) \
     (ptr)[(size_t)blockIdx.x * 16 + i_] = tacc_[i_]; } while (0)
 #else
