@@ -59,7 +59,7 @@ constexpr int GR_S = GR_X + GR_X_BYTES;     // beta, 1/|q|, 1/|k| [64] each, dbe
 constexpr int GR_S_FLOATS = 7 * CH + 8;
 constexpr int GRAD_LDS = GR_S + GR_S_FLOATS * 4;
 static_assert(FRAG == 1024, "1 KB fragments");
-static_assert(CH * SP * 2 <= GR_X_BYTES && 8 * CH * XP * 4 <= GR_X_BYTES &&
+static_assert(CH * SP * 2 <= GR_X_BYTES && 8 * CH * XP * 4 <= GR_X_BYTES && 4 * 10 * FRAG <= GR_X_BYTES &&
               GX_DOT + (8 * CH * 2 + CH * 2) * 4 <= GR_X_BYTES, "region X");
 static_assert(GRAD_LDS <= 163840, "LDS");
 
@@ -91,6 +91,22 @@ __device__ __forceinline__ f32x4 mfma_hl(const HL4& a, const HL4& b, f32x4 c) {
   c = mfma16(a.l, b.h, c);
   return c;
 }
+
+// Sums over the lanes of a 16-lane DPP row without the LDS crossbar: xor 1
+// and xor 2 by quad permutes, then the half-row and row mirrors (after each
+// step the lanes being paired hold equal partial sums, so a mirror is an
+// exchange).  sum8 stops after 8 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  return x;
+}
+__device__ __forceinline__ float sum16(float x) { return sum8(x) + dpp<0x140>(sum8(x)); }  // + row_mirror
 
 // Staging of half a chunk (token blocks 2 half, 2 half + 1) of D and dD (fp32,
 // split into bf16 hi/lo) and dO (bf16) as A-operand fragments.  Thread tid
@@ -224,11 +240,8 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
         sk += y[e] * y[e];
       }
     }
-#pragma unroll
-    for (int d = 1; d < 8; d <<= 1) {
-      sq += __shfl_xor(sq, d);
-      sk += __shfl_xor(sk, d);
-    }
+    sq = sum8(sq);
+    sk = sum8(sk);
     if ((tid & 7) == 0) {
       sIq[sr] = norm ? 1.0f / sqrtf(sq + L2_EPS) : 1.0f;
       sIk[sr] = norm ? 1.0f / sqrtf(sk + L2_EPS) : 1.0f;
@@ -485,17 +498,30 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
     for (int ab = 0; ab < 4; ++ab)
 #pragma unroll
       for (int bb = 0; bb <= ab; ++bb) P[ab * (ab + 1) / 2 + bb] = mfma_hl(yh[ab], kg[bb], zero4());
+    // a fixed-order tree over the waves (4..7 into 0..3, 2..3 into 0..1, 1
+    // into 0) through LDS slots of 10 x 1 KB per sending wave, over the KG
+    // rows (every wave has read its own before the first barrier below)
+    f32x4* slot = reinterpret_cast<f32x4*>(sX) + lane;  // + ((sender - lv) * 10 + k) * 64
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int lv = 4; lv >= 1; lv >>= 1) {
       __syncthreads();
-      if (wv == r) {
+      if (wv >= lv && wv < 2 * lv) {
 #pragma unroll
-        for (int ab = 0; ab < 4; ++ab)
-#pragma unroll
-          for (int bb = 0; bb <= ab; ++bb)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) sM2q[(16 * ab + ii) * MP + 16 * bb] -= P[ab * (ab + 1) / 2 + bb][ii];
+        for (int k = 0; k < 10; ++k) slot[((wv - lv) * 10 + k) * 64] = P[k];
       }
+      __syncthreads();
+      if (wv < lv) {
+#pragma unroll
+        for (int k = 0; k < 10; ++k) P[k] += slot[(wv * 10 + k) * 64];
+      }
+    }
+    if (wv == 0) {
+#pragma unroll
+      for (int ab = 0; ab < 4; ++ab)
+#pragma unroll
+        for (int bb = 0; bb <= ab; ++bb)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) sM2q[(16 * ab + ii) * MP + 16 * bb] -= P[ab * (ab + 1) / 2 + bb][ii];
     }
   }
   __syncthreads();
@@ -589,10 +615,7 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       float r = rows[ii];
-      r += __shfl_xor(r, 1);
-      r += __shfl_xor(r, 2);
-      r += __shfl_xor(r, 4);
-      r += __shfl_xor(r, 8);
+      r = sum16(r);
       if (tl == 0) (sdBp + (2 + p) * CH + 4 * gq)[16 * w + ii] = r;
     }
     __syncthreads();
@@ -701,11 +724,8 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       float dq_dot = qn(16 * b + ii) * xq[ii], dk_dot = Kn[b][ii] * xk[ii];
-#pragma unroll
-      for (int d = 1; d < 16; d <<= 1) {
-        dq_dot += __shfl_xor(dq_dot, d);
-        dk_dot += __shfl_xor(dk_dot, d);
-      }
+      dq_dot = sum16(dq_dot);
+      dk_dot = sum16(dk_dot);
       if (tl == 0) {
         float* d = sDot + (wv * CH + 4 * gq) * 2;
         d[(16 * b + ii) * 2] = dq_dot;
@@ -723,50 +743,56 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
   __syncthreads();
   KDA_TIMER_MARK(10);
 
-  // ---- outputs: d raw_gate, dq, dk straight from the lanes (16 lanes write
-  // 32 contiguous bytes of a row); partial sums of d dt_bias (per channel)
-  // and dA_log
+  // ---- outputs, staged as bf16 rows over T, dA_qk and dKK (no longer read):
+  // d raw_gate, dq, dk; partial sums of d dt_bias (per channel) and dA_log
   float pA = 0.f, pdt = 0.f;
   float* part = a.part + it * (KD + 1);
+  uint16_t* og = reinterpret_cast<uint16_t*>(sT);  // [64][128] each (16 KB of the 17 KB)
+  uint16_t* oq = reinterpret_cast<uint16_t*>(sM1);
+  uint16_t* ok_ = reinterpret_cast<uint16_t*>(sM2);
   {
     const uint16_t* gb = sGr + 4 * gq * SP + c;
     const float* dtq = sDotT + 8 * gq;
     const float* ikb = sIk + 4 * gq;
+    uint16_t* ogb = og + 4 * gq * KD + c;
+    uint16_t* oqb = oq + 4 * gq * KD + c;
+    uint16_t* okb = ok_ + 4 * gq * KD + c;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const f32x4 xq = pdq[b * 64], xk = pdk[b * 64];
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int jj = 16 * b + ii;  // token 4gq + jj
-        if (4 * gq + jj >= L) continue;
         const float dgv = dGa[b][ii];  // gradient of the natural-log decay g_j
-        float dgo;
-        const float rg = bf2f(gb[jj * SP]);
-        if (gate_given) {
-          // g = clamp(raw_gate, lower_bound, 0): the gradient passes inside the closed interval
-          dgo = (rg >= a.lb && rg <= 0.f) ? dgv : 0.f;
-        } else {
-          const float x = al * (rg + dtb);
-          const float sg = fsigmoid(x);
-          const float dx = dgv * a.lb * sg * (1.f - sg);
-          dgo = dx * al;
-          pdt += dgo;
-          pA += dx * x;
+        float dgo = 0.f;
+        if (4 * gq + jj < L) {
+          const float rg = bf2f(gb[jj * SP]);
+          if (gate_given) {
+            // g = clamp(raw_gate, lower_bound, 0): the gradient passes inside the closed interval
+            dgo = (rg >= a.lb && rg <= 0.f) ? dgv : 0.f;
+          } else {
+            const float x = al * (rg + dtb);
+            const float sg = fsigmoid(x);
+            const float dx = dgv * a.lb * sg * (1.f - sg);
+            dgo = dx * al;
+            pdt += dgo;
+            pA += dx * x;
+          }
         }
         // dq = (dq^ - q^ (q^ . dq^)) / |q|, same for k; without the L2 norm dq = dq^
         const float dqd = norm ? dtq[2 * jj] : 0.f, dkd = norm ? dtq[2 * jj + 1] : 0.f;
-        const size_t o = ((size_t)(c0 + 4 * gq + jj) * H + h) * KD + c;
-        a.dg[o] = f2bf(dgo);
-        a.dq[o] = f2bf((xq[ii] - qn(jj) * dqd) * iqlb[jj]);
-        a.dk[o] = f2bf((xk[ii] - Kn[b][ii] * dkd) * ikb[jj]);
+        ogb[jj * KD] = f2bf(dgo);
+        oqb[jj * KD] = f2bf((xq[ii] - qn(jj) * dqd) * iqlb[jj]);
+        okb[jj * KD] = f2bf((xk[ii] - Kn[b][ii] * dkd) * ikb[jj]);
       }
     }
   }
   pdt += __shfl_xor(pdt, 16);
   pdt += __shfl_xor(pdt, 32);
   if (gq == 0) part[c] = pdt;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) pA += __shfl_xor(pA, d);
+  pA = sum16(pA);
+  pA += __shfl_xor(pA, 16);
+  pA += __shfl_xor(pA, 32);
   if (lane == 0) sRed[wv] = pA;
   if (tid < CH && tid < L) {
     const float bt = sBeta[tid];
@@ -774,6 +800,19 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
     a.dbeta[(size_t)(c0 + tid) * H + h] = f2bf((a.flags & FLAG_BETA_GIVEN) ? db : db * bt * (1.f - bt));
   }
   __syncthreads();
+  // 16-byte stores of the staged rows: thread -> (row, 16-byte column block)
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + NTG * u;  // 0 .. 1023
+    const int row = e >> 4;
+    const int cb = 8 * (e & 15);
+    if (row < L) {
+      const size_t o = ((size_t)(c0 + row) * H + h) * KD + cb;
+      *reinterpret_cast<uint4*>(a.dq + o) = *reinterpret_cast<const uint4*>(oq + row * KD + cb);
+      *reinterpret_cast<uint4*>(a.dk + o) = *reinterpret_cast<const uint4*>(ok_ + row * KD + cb);
+      *reinterpret_cast<uint4*>(a.dg + o) = *reinterpret_cast<const uint4*>(og + row * KD + cb);
+    }
+  }
   if (tid == 0) {
     float sA = 0.f;
 #pragma unroll
