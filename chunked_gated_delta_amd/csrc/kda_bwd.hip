@@ -75,11 +75,9 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
     sq += qv[c] * qv[c];
     sk += kv[c] * kv[c];
   }
-#pragma unroll
-  for (int d = 1; d < TPR; d <<= 1) {
-    sq += __shfl_xor(sq, d);
-    sk += __shfl_xor(sk, d);
-  }
+  static_assert(TPR == 8, "one token per 8 lanes");
+  sq = sum8(sq);
+  sk = sum8(sk);
   const bool norm = !(a.flags & FLAG_NO_QK_NORM);
   const bool gate_given = a.flags & FLAG_GATE_GIVEN;
   const float rq = norm ? sqrtf(sq + L2_EPS) : 1.0f, rk = norm ? sqrtf(sk + L2_EPS) : 1.0f;
@@ -95,7 +93,7 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
       if (gate_given)
         gn = fminf(fmaxf(gv[c + e], a.lb), 0.f);
       else
-        gn = a.lb * sigmoidf(al * (gv[c + e] + a.dt_bias[(size_t)h * KD + CPT * part + c + e]));
+        gn = a.lb * fsigmoid(al * (gv[c + e] + a.dt_bias[(size_t)h * KD + CPT * part + c + e]));
       gg[e] = ok ? gn * LOG2E : 0.f;
     }
     *reinterpret_cast<float4*>(sQn + i * QP + CPT * part + c) =
@@ -196,6 +194,7 @@ __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
     }
     const int r = (b < w) ? 16 * b + 15 : 16 * w;
     f32x4 ak = zero4(), aq = zero4();
+    // 16x16x16 hi/lo MFMAs, contraction over channels 16t + 4gq + 0..3
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int c = 16 * t + 4 * gq;
@@ -203,13 +202,15 @@ __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
       const float4 gx = ld4(sG + (16 * w + tl) * QP + c);
       const float4 ky = ld4(sKn + (16 * b + tl) * QP + c), gy = ld4(sG + (16 * b + tl) * QP + c);
       const float4 gr = ld4(sG + r * QP + c);
+      float fx[4], yb[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const float fx = fexp2(el(gx, s) - el(gr, s));
-        const float yb = el(ky, s) * fexp2(el(gr, s) - el(gy, s));
-        ak = mfma_f32(el(kx, s) * fx, yb, ak);
-        aq = mfma_f32(el(qx, s) * fx, yb, aq);
+        fx[s] = fexp2(el(gx, s) - el(gr, s));
+        yb[s] = el(ky, s) * fexp2(el(gr, s) - el(gy, s));
       }
+      const HL4 y = hl4(yb[0], yb[1], yb[2], yb[3]);
+      ak = mfma_hl(hl4(kx.x * fx[0], kx.y * fx[1], kx.z * fx[2], kx.w * fx[3]), y, ak);
+      aq = mfma_hl(hl4(qx.x * fx[0], qx.y * fx[1], qx.z * fx[2], qx.w * fx[3]), y, aq);
     }
     float qk4[4];
 #pragma unroll
@@ -301,12 +302,13 @@ __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
         if (jb > w) continue;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int kap = 16 * jb + 4 * gq + s;
-          const int c = 16 * n + tl;
-          acc = mfma_f32(tb[jb][s], sKn[kap * QP + c] * fexp2(sG[kap * QP + c]), acc);
-        }
+        const int c = 16 * n + tl;
+        const float* kp = sKn + (16 * jb + 4 * gq) * QP + c;
+        const float* gp = sG + (16 * jb + 4 * gq) * QP + c;
+        acc = mfma_hl(hl4(tb[jb][0], tb[jb][1], tb[jb][2], tb[jb][3]),
+                      hl4(kp[0] * fexp2(gp[0]), kp[QP] * fexp2(gp[QP]), kp[2 * QP] * fexp2(gp[2 * QP]),
+                          kp[3 * QP] * fexp2(gp[3 * QP])),
+                      acc);
       }
       // -W^T[k][i]: rows k = 16n + tl, contraction i = 16w + 4gq + ii
       store_hl4(br + BR_WT, CH * KD, frag_ct(16 * n + tl, 16 * w + 4 * gq), -acc[0], -acc[1], -acc[2], -acc[3]);

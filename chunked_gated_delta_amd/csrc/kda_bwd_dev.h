@@ -85,4 +85,43 @@ __device__ __forceinline__ void split_hl4(const f32x4& x, bf16x4& h, bf16x4& l) 
   }
 }
 
+// 16x16x16 bf16 MFMA: lane (gq, tl) supplies A[tl][4gq + 0..3] and
+// B[4gq + 0..3][tl], the layout of four steps of the fp32 16x16x4 MFMA.
+// Operands are fp32 values split into bf16 hi/lo pairs (three passes).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+struct HL4 {
+  bf16x4 h, l;
+};
+__device__ __forceinline__ HL4 hl4(float x0, float x1, float x2, float x3) {
+  HL4 r;
+  split_hl4(f32x4{x0, x1, x2, x3}, r.h, r.l);
+  return r;
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                   0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_hl(const HL4& a, const HL4& b, f32x4 c) {
+  c = mfma16(a.h, b.h, c);
+  c = mfma16(a.h, b.l, c);
+  c = mfma16(a.l, b.h, c);
+  return c;
+}
+
+// Sums over the lanes of a 16-lane DPP row without the LDS crossbar: xor 1
+// and xor 2 by quad permutes, then the half-row and row mirrors (after each
+// step the lanes being paired hold equal partial sums, so a mirror is an
+// exchange).  sum8 stops after 8 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  return x;
+}
+__device__ __forceinline__ float sum16(float x) { return sum8(x) + dpp<0x140>(sum8(x)); }  // + row_mirror
+
 }  // namespace kda
