@@ -34,6 +34,7 @@ struct BwdArgs {
   const int32_t* order;   // nullptr: identity order of sequences
   ChunkMap map;
   int H;
+  int kd, vd;             // head dims of the caller's tensors (64 or 128); the internal layouts keep 128
   float scale;
   float lb;               // lower_bound
   int flags;              // FLAG_GATE_GIVEN | FLAG_BETA_GIVEN | FLAG_NO_QK_NORM | FLAG_STATE_VK

@@ -54,14 +54,16 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
   const int part = t % TPR;
   const bool ok = i < L;
   const int64_t row = c0 + (ok ? i : L - 1);  // L >= 1: the clamped row is in range
-  const size_t base = ((size_t)row * a.H + h) * KD + CPT * part;
+  const bool cok = CPT * part < a.kd;  // channels past the head dim read as zero
+  const size_t base = ((size_t)row * a.H + h) * a.kd + CPT * part;
   float qv[CPT], kv[CPT], gv[CPT];
 #pragma unroll
   for (int u = 0; u < CPT / 8; ++u) {
     float tq[8], tk[8], tg[8];
-    unpack_bf16x8(reinterpret_cast<const uint4*>(a.q + base)[u], tq);
-    unpack_bf16x8(reinterpret_cast<const uint4*>(a.k + base)[u], tk);
-    unpack_bf16x8(reinterpret_cast<const uint4*>(a.g + base)[u], tg);
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    unpack_bf16x8(cok ? reinterpret_cast<const uint4*>(a.q + base)[u] : z, tq);
+    unpack_bf16x8(cok ? reinterpret_cast<const uint4*>(a.k + base)[u] : z, tk);
+    unpack_bf16x8(cok ? reinterpret_cast<const uint4*>(a.g + base)[u] : z, tg);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       qv[8 * u + e] = tq[e];
@@ -93,7 +95,7 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
       if (gate_given)
         gn = fminf(fmaxf(gv[c + e], a.lb), 0.f);
       else
-        gn = a.lb * fsigmoid(al * (gv[c + e] + a.dt_bias[(size_t)h * KD + CPT * part + c + e]));
+        gn = a.lb * fsigmoid(al * (gv[c + e] + (cok ? a.dt_bias[(size_t)h * a.kd + CPT * part + c + e] : 0.f)));
       gg[e] = ok ? gn * LOG2E : 0.f;
     }
     *reinterpret_cast<float4*>(sQn + i * QP + CPT * part + c) =
@@ -466,21 +468,22 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
   f32x4 dS[2][4];
   const bool svk = a.flags & FLAG_STATE_VK;  // d_final / d_initial_state stored [V][K]
   {
-    const float* src = a.dfin ? a.dfin + ((size_t)seq * H + h) * KD * VD : nullptr;
+    const int kd = a.kd, vd = a.vd;
+    const float* src = a.dfin ? a.dfin + ((size_t)seq * H + h) * kd * vd : nullptr;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nn = 0; nn < 4; ++nn)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          dS[mt][nn][ii] = src ? src[svk ? (vs + 16 * nn + tl) * KD + 32 * w + 16 * mt + 4 * gq + ii
-                                         : (32 * w + 16 * mt + 4 * gq + ii) * VD + vs + 16 * nn + tl]
-                               : 0.f;
+        for (int ii = 0; ii < 4; ++ii) {
+          const int k = 32 * w + 16 * mt + 4 * gq + ii, v = vs + 16 * nn + tl;
+          dS[mt][nn][ii] = src && k < kd && v < vd ? src[svk ? v * kd + k : k * vd + v] : 0.f;
+        }
   }
   auto dorow_of = [&](int ci, bool& ok) {
     const int64_t c0 = bos + (int64_t)ci * CH;
-    ok = c0 + orow < eos;
-    return a.dout + ((size_t)(c0 + (ok ? orow : 0)) * H + h) * VD + vs + ocol;
+    ok = c0 + orow < eos && vs + ocol < a.vd;  // columns past the head dim read as zero
+    return a.dout + ((size_t)(c0 + (ok ? orow : 0)) * H + h) * a.vd + (ok ? vs + ocol : 0);
   };
 
   DhuOps cur, nxt;
@@ -626,15 +629,17 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
   }
 
   if (a.dinit) {
-    float* dst = a.dinit + ((size_t)seq * H + h) * KD * VD;
+    const int kd = a.kd, vd = a.vd;
+    float* dst = a.dinit + ((size_t)seq * H + h) * kd * vd;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nn = 0; nn < 4; ++nn)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          dst[svk ? (vs + 16 * nn + tl) * KD + 32 * w + 16 * mt + 4 * gq + ii
-                  : (32 * w + 16 * mt + 4 * gq + ii) * VD + vs + 16 * nn + tl] = dS[mt][nn][ii];
+        for (int ii = 0; ii < 4; ++ii) {
+          const int k = 32 * w + 16 * mt + 4 * gq + ii, v = vs + 16 * nn + tl;
+          if (k < kd && v < vd) dst[svk ? v * kd + k : k * vd + v] = dS[mt][nn][ii];
+        }
   }
 }
 
@@ -660,7 +665,7 @@ __global__ void __launch_bounds__(NTR) kda_bwd_reduce_kernel(BwdArgs a) {
   if (rr == 0) {
     const float v = red[col] + red[(KD + 1) + col] + red[2 * (KD + 1) + col] + red[3 * (KD + 1) + col];
     if (col < KD) {
-      if (a.ddt) a.ddt[(size_t)h * KD + col] = v;
+      if (a.ddt && col < a.kd) a.ddt[(size_t)h * a.kd + col] = v;
     } else if (a.dA_log) {
       a.dA_log[h] = v;
     }
@@ -785,7 +790,7 @@ kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void*
   if (B < 1 || T < 0 || H < 1 || N < 1) return KDA_ERR_INVALID;
   if (B * T * H > ((int64_t)1 << 40) || N * H > ((int64_t)1 << 28) || N > ((int64_t)1 << 30))
     return KDA_ERR_INVALID;
-  if (K != KD || V != VD) return KDA_ERR_UNSUPPORTED;  // the backward is built for K = V = 128
+  if ((K != 64 && K != KD) || (V != 64 && V != VD)) return KDA_ERR_UNSUPPORTED;  // head dims 64 or 128
   const BwdLayout bl = bwd_layout(B * T, H, N);
   if (!workspace || workspace_bytes < bl.total) return KDA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -841,6 +846,8 @@ kda_status_t kda_bwd_ex(const void* q, const void* k, const void* v, const void*
   ba.order = pr.order;
   ba.map = pr.map;
   ba.H = (int)H;
+  ba.kd = (int)K;
+  ba.vd = (int)V;
   ba.scale = scale;
   ba.lb = lower_bound;
   ba.flags = (int)flags;

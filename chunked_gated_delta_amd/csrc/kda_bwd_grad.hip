@@ -81,12 +81,14 @@ __device__ __forceinline__ void tok_load(TokStage& s, const BwdArgs& a, const fl
                                          int64_t c0, int L, int h, int half, int tid) {
   const int f = tid >> 6, l = tid & 63;
   const int r = 32 * half + 16 * (f >> 2) + (l & 15), col = 32 * (f & 3) + 8 * (l >> 4);
-  s.d[0] = ld4(Dt + r * VD + col);
-  s.d[1] = ld4(Dt + r * VD + col + 4);
-  s.e[0] = ld4(dDt + r * VD + col);
-  s.e[1] = ld4(dDt + r * VD + col + 4);
-  s.o = r < L ? *reinterpret_cast<const uint4*>(a.dout + ((size_t)(c0 + r) * a.H + h) * VD + col)
-              : make_uint4(0u, 0u, 0u, 0u);
+  const bool cok = col < a.vd;  // columns past the head dim: zero (the checkpoints leave them unwritten)
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  s.d[0] = cok ? ld4(Dt + r * VD + col) : z;
+  s.d[1] = cok ? ld4(Dt + r * VD + col + 4) : z;
+  s.e[0] = cok ? ld4(dDt + r * VD + col) : z;
+  s.e[1] = cok ? ld4(dDt + r * VD + col + 4) : z;
+  s.o = r < L && cok ? *reinterpret_cast<const uint4*>(a.dout + ((size_t)(c0 + r) * a.H + h) * a.vd + col)
+                     : make_uint4(0u, 0u, 0u, 0u);
 }
 __device__ __forceinline__ void tok_store(const TokStage& s, char* sX, int tid) {
   const int f = tid >> 6, l = tid & 63;
@@ -162,22 +164,23 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      s0r[ks][hf] = ld4(S0 + c * VD + 8 * gq + 32 * ks + 4 * hf);
-      dsr[ks][hf] = ld4(dSn + c * VD + 8 * gq + 32 * ks + 4 * hf);
+      const bool vok = 8 * gq + 32 * ks < a.vd;  // columns past the head dim: zero
+      s0r[ks][hf] = vok ? ld4(S0 + c * VD + 8 * gq + 32 * ks + 4 * hf) : make_float4(0.f, 0.f, 0.f, 0.f);
+      dsr[ks][hf] = vok ? ld4(dSn + c * VD + 8 * gq + 32 * ks + 4 * hf) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   float ddv[4][4];  // dD[16ib + 4gq + s][c]
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) ddv[ib][s] = (dDt + 4 * gq * VD + c)[(16 * ib + s) * VD];
+    for (int s = 0; s < 4; ++s) ddv[ib][s] = c < a.vd ? (dDt + 4 * gq * VD + c)[(16 * ib + s) * VD] : 0.f;
   float4 tcp[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) tcp[u] = ld4(br + BR_T + 4 * (tid + NTG * u));
   const int sr = tid >> 3, sc = 16 * (tid & 7);
   const bool sok = sr < L;
   uint4 rq[2], rk[2], rg[2];
-  if (sok) {
-    const size_t o = ((size_t)(c0 + sr) * H + h) * KD + sc;
+  if (sok && sc < a.kd) {  // channels past the head dim: zero
+    const size_t o = ((size_t)(c0 + sr) * H + h) * a.kd + sc;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       rq[u] = reinterpret_cast<const uint4*>(a.q + o)[u];
@@ -233,7 +236,7 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
   // the tile, a scan over ii in the lane, over gq across lanes, over b; q^
   // is read from the raw rows where it is used
   const float al = gate_given ? 0.f : expf(a.A_log[h]);
-  const float dtb = gate_given ? 0.f : a.dt_bias[(size_t)h * KD + c];
+  const float dtb = gate_given || c >= a.kd ? 0.f : a.dt_bias[(size_t)h * a.kd + c];
   f32x4 Kn[4], G[4];
   auto prep = [&](auto given) {
     // lane bases: token 4gq (+ 16b + ii as immediate offsets), channel c
@@ -330,9 +333,9 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
     for (int u = 0; u < 2; ++u) {
       const int e = tid + NTG * u;  // 0 .. 1023
       const int f = e >> 6, ln = e & 63;
-      const int j = 16 * (f >> 2) + (ln & 15);
-      if (j < L)
-        *reinterpret_cast<uint4*>(a.dv + ((size_t)(c0 + j) * H + h) * VD + 32 * (f & 3) + 8 * (ln >> 4)) =
+      const int j = 16 * (f >> 2) + (ln & 15), col = 32 * (f & 3) + 8 * (ln >> 4);
+      if (j < L && col < a.vd)
+        *reinterpret_cast<uint4*>(a.dv + ((size_t)(c0 + j) * H + h) * a.vd + col) =
             *reinterpret_cast<const uint4*>(dvh + 16 * e);
     }
   }
@@ -403,7 +406,7 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
       }
       const int jr = 16 * bb + tl;
       const bool jok = jr < L;
-      const size_t jo = ((size_t)(c0 + (jok ? jr : 0)) * H + h) * VD;
+      const size_t jo = ((size_t)(c0 + (jok ? jr : 0)) * H + h) * a.vd;
       const bool bstaged = (bb >> 1) == half;
       f32x4 accQ = zero4(), accV = zero4();
 #pragma unroll
@@ -411,13 +414,16 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
         const int fa = 4 * (ab & 1) + ks;
         const bf16x8 doa = lds_frag(xl + GX_O, fa);
         const bf16x8 eh = lds_frag(xl + GX_E, fa), el8 = lds_frag(xl + GX_E, 8 + fa);
-        const bf16x8 vb = jok ? *reinterpret_cast<const bf16x8*>(a.v + jo + 32 * ks + 8 * gq) : bf16x8{};
+        const bool vok = 32 * ks + 8 * gq < a.vd;
+        const bf16x8 vb = jok && vok ? *reinterpret_cast<const bf16x8*>(a.v + jo + 32 * ks + 8 * gq) : bf16x8{};
         bf16x8 dh, dl;
         if (bstaged) {
           dh = lds_frag(xl + GX_D, 4 * (bb & 1) + ks);
           dl = lds_frag(xl + GX_D, 8 + 4 * (bb & 1) + ks);
-        } else {
+        } else if (vok) {
           ld_hl8(Dt + jr * VD + 32 * ks + 8 * gq, dh, dl);
+        } else {
+          dh = dl = bf16x8{};
         }
         accQ = mfma_bf16(doa, dh, accQ);
         accQ = mfma_bf16(doa, dl, accQ);
@@ -767,8 +773,8 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
     const int e = tid + NTG * u;  // 0 .. 1023
     const int row = e >> 4;
     const int cb = 8 * (e & 15);
-    if (row < L) {
-      const size_t o = ((size_t)(c0 + row) * H + h) * KD + cb;
+    if (row < L && cb < a.kd) {
+      const size_t o = ((size_t)(c0 + row) * H + h) * a.kd + cb;
       *reinterpret_cast<uint4*>(a.dq + o) = *reinterpret_cast<const uint4*>(oq + row * KD + cb);
       *reinterpret_cast<uint4*>(a.dk + o) = *reinterpret_cast<const uint4*>(ok_ + row * KD + cb);
       *reinterpret_cast<uint4*>(a.dg + o) = *reinterpret_cast<const uint4*>(og + row * KD + cb);

@@ -65,9 +65,10 @@ size_t kda_workspace_size(int64_t T_total, int64_t H, int64_t N);
  * page's is_flashkda_supported(128, bf16, lower_bound) probe, whose first
  * argument is the head size).  Supported: K and V each 64 or 128, and
  * -5 <= lower_bound <= 0.  The -5 limit keeps every 16-token decay ratio
- * inside fp32/bf16 range (exp(16 * 5) < FLT_MAX).  kda_fwd, kda_fwd_ex and
- * kda_decode take every supported pair; kda_shard_affine, kda_shard_scan and
- * the backward take K == V == 128 only (KDA_ERR_UNSUPPORTED otherwise).
+ * inside fp32/bf16 range (exp(16 * 5) < FLT_MAX).  kda_fwd, kda_fwd_ex,
+ * kda_decode, kda_bwd and kda_bwd_ex take every supported pair;
+ * kda_shard_affine and kda_shard_scan take K == V == 128 only
+ * (KDA_ERR_UNSUPPORTED otherwise).
  * Head dim 64 runs in the 128-channel layout of the kernels with the missing
  * channels held at zero, so it costs about what 128 costs.
  */

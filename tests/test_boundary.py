@@ -251,8 +251,10 @@ def test_bwd_checks():
     assert bwd_call(T=-1) == INVALID
     assert bwd_call(scale=float("nan")) == INVALID
     assert bwd_call(B=2, N=1) == INVALID                    # N must equal B without cu_seqlens
-    assert bwd_call(K=64, V=64) == UNSUPPORTED              # the backward is built for 128 only
-    assert bwd_call(K=64) == UNSUPPORTED
+    assert bwd_call(K=32, V=32) == UNSUPPORTED              # head dims 64 and 128 only
+    assert bwd_call(K=128, V=256) == UNSUPPORTED
+    assert bwd_call(K=64, V=64, ws_bytes=8) == WORKSPACE     # 64: on to the workspace check
+    assert bwd_call(K=64, V=128, ws_bytes=8) == WORKSPACE
     assert bwd_call(lb=-6.0) == UNSUPPORTED
     assert bwd_call(ws=None) == WORKSPACE
     need = kda.kda_bwd_workspace_size(64, 2, 1)

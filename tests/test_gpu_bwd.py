@@ -121,14 +121,13 @@ def test_bwd_strong_decay_and_gate_parameters():
     compare(gpu_bwd(x, d_out, d_fin), oracle(x, d_out, d_fin))
 
 
-def test_bwd_tp_share_c2_sampled_heads():
-    """B=2, T=4096, H=12 on the GPU; heads 0 and 7 checked against the chunked fp64 backward."""
-    x = W.c2_tp_share()
-    d_out, d_fin = cotangents(x, 6)
+def check_sampled_heads(x, d_out, d_fin, heads):
+    """GPU gradients of every head; the sampled heads against the chunked fp64 backward."""
     got = gpu_bwd(x, d_out, d_fin)
-    for h in (0, 7):
-        xs = W.KdaInputs(name=f"c2_head{h}", q=x.q[:, :, h:h + 1].contiguous(), k=x.k[:, :, h:h + 1].contiguous(),
-                         v=x.v[:, :, h:h + 1].contiguous(), raw_gate=x.raw_gate[:, :, h:h + 1].contiguous(),
+    for h in heads:
+        xs = W.KdaInputs(name=f"{x.name}_head{h}", q=x.q[:, :, h:h + 1].contiguous(),
+                         k=x.k[:, :, h:h + 1].contiguous(), v=x.v[:, :, h:h + 1].contiguous(),
+                         raw_gate=x.raw_gate[:, :, h:h + 1].contiguous(),
                          raw_beta=x.raw_beta[:, :, h:h + 1].contiguous(), A_log=x.A_log[h:h + 1].contiguous(),
                          dt_bias=x.dt_bias[h:h + 1].contiguous(),
                          initial_state=x.initial_state[:, h:h + 1].contiguous(), cu_seqlens=None,
@@ -138,6 +137,20 @@ def test_bwd_tp_share_c2_sampled_heads():
                                                                              "d_raw_beta", "d_initial_state")
                    else got[n][h:h + 1]) for n in NAMES}
         compare(sub, ref)
+
+
+def test_bwd_tp_share_c2_sampled_heads():
+    """B=2, T=4096, H=12 on the GPU; heads 0 and 7 checked against the chunked fp64 backward."""
+    x = W.c2_tp_share()
+    d_out, d_fin = cotangents(x, 6)
+    check_sampled_heads(x, d_out, d_fin, (0, 7))
+
+
+def test_bwd_c2_shape_head_dim_64():
+    """The C2 shape (B=2, T=4096, H=12, initial states) with K = V = 64: heads 3 and 11."""
+    x = W.random_inputs("c2_B2_T4096_H12_K64", 11, 2, 4096, 12, K=64, V=64)
+    d_out, d_fin = cotangents(x, 16)
+    check_sampled_heads(x, d_out, d_fin, (3, 11))
 
 
 def test_bwd_packed_equals_separate_documents():
