@@ -210,15 +210,20 @@ def write_traffic(fetch_csv, write_csv, copy_fetch, copy_write, calls, mode="fwd
     print(json.dumps(doc))
 
 
-def timed(fn, steps, warmup, stream):
-    """Median device time (ms) of fn() over `steps` launches, HIP events on `stream`."""
+def timed(fn, steps, warmup, stream, setup=None):
+    """Median device time (ms) of fn() over `steps` launches, HIP events on `stream`
+    (setup(), if given, runs before each launch, outside its events)."""
     import torch
 
     for _ in range(warmup):
+        if setup:
+            setup()
         fn()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in evs:
+        if setup:
+            setup()
         a.record(stream)
         fn()
         b.record(stream)
@@ -368,12 +373,14 @@ def bench_bwd(args):
     if not args.no_reuse:
         # the same gradients on the records a forward call left in this workspace
         out, fin = torch.empty_like(v), torch.empty_like(init)
-        kda.kda_fwd_ex(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, init, fin,
-                       flags=kda.FLAG_KEEP_RECORDS, stream=sh)
+        # (the backward's factor record is written over the forward's records, so
+        # every timed call gets a fresh forward first, outside its events)
         ms_reuse = timed(lambda: kda.kda_bwd_ex(q, k, v, g, b, x.scale, d_out, dq, dk, dv, dg, db, dA, ddt, ws,
                                                 al, dt, x.lower_bound, initial_state=init, d_final=d_fin,
                                                 d_initial_state=dinit, flags=kda.FLAG_REUSE_RECORDS, stream=sh),
-                         args.steps, args.warmup, stream)
+                         args.steps, args.warmup, stream,
+                         setup=lambda: kda.kda_fwd_ex(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, init,
+                                                      fin, flags=kda.FLAG_KEEP_RECORDS, stream=sh))
     ht = x.T * x.H
     alg = ht * (9 * 128 * 2 + 2 * 2) + 3 * x.H * STATE_BYTES
     gbs = alg / (ms / 1e3) / 1e9

@@ -43,8 +43,8 @@ constexpr int NT = 256;  // recurrence kernel: 4 waves
 // Per-token preparation of one chunk into LDS: q^, k^ (rows past the end are
 // zero), G = cumulative log2-decay (constant past the end), beta, the row
 // norms of q and k.  NTH threads: NTH / 64 per token, KD / (NTH / 64) channels
-// each.  sTmp needs NTH floats.
-template <int NTH>
+// each.  sTmp needs NTH floats.  FULL: K == 128, where no channel is masked.
+template <int NTH, bool FULL>
 __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQn, float* sKn, float* sG,
                            float* sBeta, float* sRq, float* sRk, float* sTmp) {
   constexpr int TPR = NTH / CH;  // threads per token
@@ -54,16 +54,23 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
   const int part = t % TPR;
   const bool ok = i < L;
   const int64_t row = c0 + (ok ? i : L - 1);  // L >= 1: the clamped row is in range
-  const bool cok = CPT * part < a.kd;  // channels past the head dim read as zero
-  const size_t base = ((size_t)row * a.H + h) * a.kd + CPT * part;
+  const int kd = FULL ? KD : a.kd;
+  // channels past the head dim read as zero: their loads go to channel 0 (kept
+  // unconditional, so they stay 16-byte loads) and are dropped after
+  const bool cok = FULL || CPT * part < kd;
+  const int c0l = cok ? CPT * part : 0;
+  const size_t base = ((size_t)row * a.H + h) * kd + c0l;
   float qv[CPT], kv[CPT], gv[CPT];
 #pragma unroll
   for (int u = 0; u < CPT / 8; ++u) {
     float tq[8], tk[8], tg[8];
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    unpack_bf16x8(cok ? reinterpret_cast<const uint4*>(a.q + base)[u] : z, tq);
-    unpack_bf16x8(cok ? reinterpret_cast<const uint4*>(a.k + base)[u] : z, tk);
-    unpack_bf16x8(cok ? reinterpret_cast<const uint4*>(a.g + base)[u] : z, tg);
+    const uint4 lq = reinterpret_cast<const uint4*>(a.q + base)[u];
+    const uint4 lk = reinterpret_cast<const uint4*>(a.k + base)[u];
+    const uint4 lg = reinterpret_cast<const uint4*>(a.g + base)[u];
+    unpack_bf16x8(cok ? lq : z, tq);
+    unpack_bf16x8(cok ? lk : z, tk);
+    unpack_bf16x8(cok ? lg : z, tg);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       qv[8 * u + e] = tq[e];
@@ -94,8 +101,10 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
       float gn;
       if (gate_given)
         gn = fminf(fmaxf(gv[c + e], a.lb), 0.f);
-      else
-        gn = a.lb * fsigmoid(al * (gv[c + e] + (cok ? a.dt_bias[(size_t)h * a.kd + CPT * part + c + e] : 0.f)));
+      else {
+        const float db = a.dt_bias[(size_t)h * kd + c0l + c + e];
+        gn = a.lb * fsigmoid(al * (gv[c + e] + (cok ? db : 0.f)));
+      }
       gg[e] = ok ? gn * LOG2E : 0.f;
     }
     *reinterpret_cast<float4*>(sQn + i * QP + CPT * part + c) =
@@ -146,6 +155,7 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
 constexpr int NTP = 512;
 constexpr int PREP_FLOATS = 3 * CH * QP + 2 * CH * MP + 3 * CH + NTP;
 
+template <bool FULL>
 __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float smem[PREP_FLOATS];
   float* sQn = smem;
@@ -167,7 +177,7 @@ __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
   chunk_of(a.map, gch, c0, L);
   float* br = a.br + (size_t)blockIdx.x * BWD_REC_FLOATS;
 
-  prep_chunk<NTP>(a, c0, L, h, sQn, sKn, sG, sBeta, sRq, sRk, sTmp);
+  prep_chunk<NTP, FULL>(a, c0, L, h, sQn, sKn, sG, sBeta, sRq, sRk, sTmp);
 
   const int tid = threadIdx.x;
   const int wv = tid >> 6;
@@ -688,7 +698,9 @@ hipError_t launch_bwd(const BwdArgs& args, int64_t max_chunks, const BwdShards* 
   const int64_t items = max_chunks * a.H;
   hipError_t e;
   if (items > 0) {
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&kda_bwd_prep_kernel), dim3((unsigned)items), dim3(NTP),
+    e = hipLaunchKernel(a.kd == KD ? reinterpret_cast<const void*>(&kda_bwd_prep_kernel<true>)
+                                    : reinterpret_cast<const void*>(&kda_bwd_prep_kernel<false>),
+                        dim3((unsigned)items), dim3(NTP),
                         kargs, 0, st);
     if (e != hipSuccess) return e;
   }
@@ -731,9 +743,12 @@ hipError_t launch_bwd(const BwdArgs& args, int64_t max_chunks, const BwdShards* 
 namespace kda {
 namespace {
 
-// The backward pass keeps, after the forward's areas: the state entering and
-// the state gradient leaving every chunk, every chunk's D and dD, its fp32
-// factor record and its partial parameter-gradient sums.
+// The backward pass keeps, besides the forward's areas: the state entering
+// and the state gradient leaving every chunk, every chunk's D and dD, its fp32
+// factor record and its partial parameter-gradient sums.  The factor record is
+// written after the checkpointing pass has read the forward's chunk records
+// for the last time, so it starts where they start, unless the call splits
+// its sequences (the shard maps after the records are read after it).
 struct BwdLayout {
   Layout fwd;
   size_t states, dtile, dstates, ddtile, br, part, total;
@@ -743,12 +758,14 @@ BwdLayout bwd_layout(int64_t T_total, int64_t H, int64_t N) {
   BwdLayout l;
   l.fwd = workspace_layout(T_total, H, N);
   const size_t items = ((size_t)(T_total / CH) + (size_t)N) * (size_t)H;
-  l.states = align256(l.fwd.total);
+  const size_t brb = align256(items * BWD_REC_FLOATS * 4);
+  l.br = l.fwd.S > 1 ? align256(l.fwd.total) : l.fwd.rec;
+  const size_t after = l.br + brb > l.fwd.total ? l.br + brb : l.fwd.total;
+  l.states = align256(after);
   l.dtile = l.states + align256(items * KD * VD * 4);
   l.dstates = l.dtile + align256(items * CH * VD * 4);
   l.ddtile = l.dstates + align256(items * KD * VD * 4);
-  l.br = l.ddtile + align256(items * CH * VD * 4);
-  l.part = l.br + align256(items * BWD_REC_FLOATS * 4);
+  l.part = l.ddtile + align256(items * CH * VD * 4);
   l.total = l.part + align256(items * (KD + 1) * 4);
   return l;
 }

@@ -78,16 +78,16 @@ struct TokStage {
   uint4 o;
 };
 __device__ __forceinline__ void tok_load(TokStage& s, const BwdArgs& a, const float* Dt, const float* dDt,
-                                         int64_t c0, int L, int h, int half, int tid) {
+                                         int64_t c0, int L, int h, int half, int tid, int vd) {
   const int f = tid >> 6, l = tid & 63;
   const int r = 32 * half + 16 * (f >> 2) + (l & 15), col = 32 * (f & 3) + 8 * (l >> 4);
-  const bool cok = col < a.vd;  // columns past the head dim: zero (the checkpoints leave them unwritten)
+  const bool cok = col < vd;  // columns past the head dim: zero (the checkpoints leave them unwritten)
   const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
   s.d[0] = cok ? ld4(Dt + r * VD + col) : z;
   s.d[1] = cok ? ld4(Dt + r * VD + col + 4) : z;
   s.e[0] = cok ? ld4(dDt + r * VD + col) : z;
   s.e[1] = cok ? ld4(dDt + r * VD + col + 4) : z;
-  s.o = r < L && cok ? *reinterpret_cast<const uint4*>(a.dout + ((size_t)(c0 + r) * a.H + h) * a.vd + col)
+  s.o = r < L && cok ? *reinterpret_cast<const uint4*>(a.dout + ((size_t)(c0 + r) * a.H + h) * vd + col)
                      : make_uint4(0u, 0u, 0u, 0u);
 }
 __device__ __forceinline__ void tok_store(const TokStage& s, char* sX, int tid) {
@@ -104,7 +104,10 @@ __device__ __forceinline__ void tok_store(const TokStage& s, char* sX, int tid) 
   *reinterpret_cast<uint4*>(sX + GX_O + f * FRAG + l * 16) = s.o;
 }
 
+// FULL: K == V == 128, where none of the head-dim masks below can be false
+template <bool FULL>
 __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
+  const int kd = FULL ? KD : a.kd, vd = FULL ? VD : a.vd;  // the caller's head dims
   __shared__ __attribute__((aligned(16))) char smem[GRAD_LDS];
   float* sT = reinterpret_cast<float*>(smem + GR_T);
   float* sM1 = reinterpret_cast<float*>(smem + GR_M1);  // dA_qk
@@ -164,7 +167,7 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const bool vok = 8 * gq + 32 * ks < a.vd;  // columns past the head dim: zero
+      const bool vok = 8 * gq + 32 * ks < vd;  // columns past the head dim: zero
       s0r[ks][hf] = vok ? ld4(S0 + c * VD + 8 * gq + 32 * ks + 4 * hf) : make_float4(0.f, 0.f, 0.f, 0.f);
       dsr[ks][hf] = vok ? ld4(dSn + c * VD + 8 * gq + 32 * ks + 4 * hf) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -172,15 +175,15 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) ddv[ib][s] = c < a.vd ? (dDt + 4 * gq * VD + c)[(16 * ib + s) * VD] : 0.f;
+    for (int s = 0; s < 4; ++s) ddv[ib][s] = c < vd ? (dDt + 4 * gq * VD + c)[(16 * ib + s) * VD] : 0.f;
   float4 tcp[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) tcp[u] = ld4(br + BR_T + 4 * (tid + NTG * u));
   const int sr = tid >> 3, sc = 16 * (tid & 7);
   const bool sok = sr < L;
   uint4 rq[2], rk[2], rg[2];
-  if (sok && sc < a.kd) {  // channels past the head dim: zero
-    const size_t o = ((size_t)(c0 + sr) * H + h) * a.kd + sc;
+  if (sok && sc < kd) {  // channels past the head dim: zero
+    const size_t o = ((size_t)(c0 + sr) * H + h) * kd + sc;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       rq[u] = reinterpret_cast<const uint4*>(a.q + o)[u];
@@ -236,7 +239,7 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
   // the tile, a scan over ii in the lane, over gq across lanes, over b; q^
   // is read from the raw rows where it is used
   const float al = gate_given ? 0.f : expf(a.A_log[h]);
-  const float dtb = gate_given || c >= a.kd ? 0.f : a.dt_bias[(size_t)h * a.kd + c];
+  const float dtb = gate_given || c >= kd ? 0.f : a.dt_bias[(size_t)h * kd + c];
   f32x4 Kn[4], G[4];
   auto prep = [&](auto given) {
     // lane bases: token 4gq (+ 16b + ii as immediate offsets), channel c
@@ -292,7 +295,7 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
   gl2 += __shfl_xor(gl2, 16);
   gl2 += __shfl_xor(gl2, 32);
   TokStage stg;
-  tok_load(stg, a, Dt, dDt, c0, L, h, 0, tid);
+  tok_load(stg, a, Dt, dDt, c0, L, h, 0, tid, vd);
   __syncthreads();  // the raw k rows are read: region X takes dv and the staged halves
   KDA_TIMER_MARK(2);
 
@@ -334,8 +337,8 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
       const int e = tid + NTG * u;  // 0 .. 1023
       const int f = e >> 6, ln = e & 63;
       const int j = 16 * (f >> 2) + (ln & 15), col = 32 * (f & 3) + 8 * (ln >> 4);
-      if (j < L && col < a.vd)
-        *reinterpret_cast<uint4*>(a.dv + ((size_t)(c0 + j) * H + h) * a.vd + col) =
+      if (j < L && col < vd)
+        *reinterpret_cast<uint4*>(a.dv + ((size_t)(c0 + j) * H + h) * vd + col) =
             *reinterpret_cast<const uint4*>(dvh + 16 * e);
     }
   }
@@ -351,7 +354,7 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     if (half == 1) {
-      tok_load(stg, a, Dt, dDt, c0, L, h, 1, tid);
+      tok_load(stg, a, Dt, dDt, c0, L, h, 1, tid, vd);
       __syncthreads();  // the first half's fragments are read
       tok_store(stg, sX, tid);
       __syncthreads();
@@ -406,7 +409,7 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
       }
       const int jr = 16 * bb + tl;
       const bool jok = jr < L;
-      const size_t jo = ((size_t)(c0 + (jok ? jr : 0)) * H + h) * a.vd;
+      const size_t jo = ((size_t)(c0 + (jok ? jr : 0)) * H + h) * vd;
       const bool bstaged = (bb >> 1) == half;
       f32x4 accQ = zero4(), accV = zero4();
 #pragma unroll
@@ -414,7 +417,7 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
         const int fa = 4 * (ab & 1) + ks;
         const bf16x8 doa = lds_frag(xl + GX_O, fa);
         const bf16x8 eh = lds_frag(xl + GX_E, fa), el8 = lds_frag(xl + GX_E, 8 + fa);
-        const bool vok = 32 * ks + 8 * gq < a.vd;
+        const bool vok = 32 * ks + 8 * gq < vd;
         const bf16x8 vb = jok && vok ? *reinterpret_cast<const bf16x8*>(a.v + jo + 32 * ks + 8 * gq) : bf16x8{};
         bf16x8 dh, dl;
         if (bstaged) {
@@ -773,8 +776,8 @@ __global__ void __launch_bounds__(NTG, 1) kda_bwd_grad_kernel(BwdArgs a) {
     const int e = tid + NTG * u;  // 0 .. 1023
     const int row = e >> 4;
     const int cb = 8 * (e & 15);
-    if (row < L && cb < a.kd) {
-      const size_t o = ((size_t)(c0 + row) * H + h) * a.kd + cb;
+    if (row < L && cb < kd) {
+      const size_t o = ((size_t)(c0 + row) * H + h) * kd + cb;
       *reinterpret_cast<uint4*>(a.dq + o) = *reinterpret_cast<const uint4*>(oq + row * KD + cb);
       *reinterpret_cast<uint4*>(a.dk + o) = *reinterpret_cast<const uint4*>(ok_ + row * KD + cb);
       *reinterpret_cast<uint4*>(a.dg + o) = *reinterpret_cast<const uint4*>(og + row * KD + cb);
@@ -796,8 +799,9 @@ hipError_t launch_grad(const BwdArgs& args, int64_t items, hipStream_t st) {
   if (items <= 0) return hipSuccess;
   BwdArgs a = args;
   void* kargs[] = {(void*)&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_bwd_grad_kernel), dim3((unsigned)items), dim3(NTG),
-                         kargs, 0, st);
+  const void* fn = a.kd == KD && a.vd == VD ? reinterpret_cast<const void*>(&kda_bwd_grad_kernel<true>)
+                                             : reinterpret_cast<const void*>(&kda_bwd_grad_kernel<false>);
+  return hipLaunchKernel(fn, dim3((unsigned)items), dim3(NTG), kargs, 0, st);
 }
 
 }  // namespace kda

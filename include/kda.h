@@ -233,7 +233,10 @@ kda_status_t kda_decode(const void* q, const void* k, const void* v, const void*
  * B, T, H, N and the GATE_GIVEN, BETA_GIVEN and NO_QK_NORM bits, not on v or
  * the states.  The caller guarantees that all of these equal those of the call
  * that wrote the records and that the workspace is unchanged since; nothing
- * checks it, and other records give wrong results.
+ * checks it, and other records give wrong results.  A backward uses up the
+ * records: it writes its own factor record over them once its checkpointing
+ * pass has read them (unless the call splits its sequences into shards), so a
+ * second backward on the same records needs the forward again.
  */
 #define KDA_FLAG_REUSE_RECORDS 16u
 
