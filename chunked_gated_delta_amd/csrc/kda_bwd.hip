@@ -40,12 +40,53 @@ namespace kda {
 namespace {
 
 constexpr int NT = 256;  // recurrence kernel: 4 waves
-// Per-token preparation of one chunk into LDS: q^, k^ (rows past the end are
-// zero), G = cumulative log2-decay (constant past the end), beta, the row
-// norms of q and k.  NTH threads: NTH / 64 per token, KD / (NTH / 64) channels
-// each.  sTmp needs NTH floats.  FULL: K == 128, where no channel is masked.
+// One chunk's raw per-token inputs for the NTH threads of prep_chunk (NTH / 64
+// per token, KD / (NTH / 64) channels each), loaded into registers ahead of
+// their use: a persistent workgroup loads the next item's while it works on
+// the current one.
+template <int NTH>
+struct PrepIn {
+  static constexpr int CPT = KD / (NTH / CH);  // channels per thread
+  uint4 q[CPT / 8], k[CPT / 8], g[CPT / 8];
+  float db[CPT];       // dt_bias of the thread's channels (zero with the gate given)
+  float A_log;         // the head's A_log (zero with the gate given)
+  uint16_t beta;       // raw beta of the thread's token, bf16 bits (converted at use,
+                       // so that nothing waits for the load)
+};
+
 template <int NTH, bool FULL>
-__device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQn, float* sKn, float* sG,
+__device__ __forceinline__ void prep_load(const BwdArgs& a, int64_t c0, int L, int h, PrepIn<NTH>& in) {
+  constexpr int TPR = NTH / CH;
+  constexpr int CPT = PrepIn<NTH>::CPT;
+  const int t = threadIdx.x;
+  const int i = t / TPR;
+  const int part = t % TPR;
+  const int64_t row = c0 + (i < L ? i : L - 1);  // L >= 1: the clamped row is in range
+  const int kd = FULL ? KD : a.kd;
+  // channels past the head dim: the loads go to channel 0 (kept unconditional,
+  // so they stay 16-byte loads) and prep_chunk drops them
+  const int c0l = FULL || CPT * part < kd ? CPT * part : 0;
+  const size_t base = ((size_t)row * a.H + h) * kd + c0l;
+#pragma unroll
+  for (int u = 0; u < CPT / 8; ++u) {
+    in.q[u] = reinterpret_cast<const uint4*>(a.q + base)[u];
+    in.k[u] = reinterpret_cast<const uint4*>(a.k + base)[u];
+    in.g[u] = reinterpret_cast<const uint4*>(a.g + base)[u];
+  }
+  // with the gate given, A_log and dt_bias may be absent and are not read
+  const bool gate_given = a.flags & FLAG_GATE_GIVEN;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) in.db[c] = gate_given ? 0.f : a.dt_bias[(size_t)h * kd + c0l + c];
+  in.A_log = gate_given ? 0.f : a.A_log[h];
+  in.beta = a.beta[(size_t)row * a.H + h];
+}
+
+// Per-token preparation of one chunk into LDS from its loaded inputs: q^, k^
+// (rows past the end are zero), G = cumulative log2-decay (constant past the
+// end), beta, the row norms of q and k.  sTmp needs NTH floats.  FULL: K ==
+// 128, where no channel is masked.
+template <int NTH, bool FULL>
+__device__ void prep_chunk(const BwdArgs& a, const PrepIn<NTH>& in, int L, float* sQn, float* sKn, float* sG,
                            float* sBeta, float* sRq, float* sRk, float* sTmp) {
   constexpr int TPR = NTH / CH;  // threads per token
   constexpr int CPT = KD / TPR;  // channels per thread
@@ -53,24 +94,16 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
   const int i = t / TPR;
   const int part = t % TPR;
   const bool ok = i < L;
-  const int64_t row = c0 + (ok ? i : L - 1);  // L >= 1: the clamped row is in range
   const int kd = FULL ? KD : a.kd;
-  // channels past the head dim read as zero: their loads go to channel 0 (kept
-  // unconditional, so they stay 16-byte loads) and are dropped after
-  const bool cok = FULL || CPT * part < kd;
-  const int c0l = cok ? CPT * part : 0;
-  const size_t base = ((size_t)row * a.H + h) * kd + c0l;
+  const bool cok = FULL || CPT * part < kd;  // channels past the head dim read as zero
   float qv[CPT], kv[CPT], gv[CPT];
 #pragma unroll
   for (int u = 0; u < CPT / 8; ++u) {
     float tq[8], tk[8], tg[8];
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    const uint4 lq = reinterpret_cast<const uint4*>(a.q + base)[u];
-    const uint4 lk = reinterpret_cast<const uint4*>(a.k + base)[u];
-    const uint4 lg = reinterpret_cast<const uint4*>(a.g + base)[u];
-    unpack_bf16x8(cok ? lq : z, tq);
-    unpack_bf16x8(cok ? lk : z, tk);
-    unpack_bf16x8(cok ? lg : z, tg);
+    unpack_bf16x8(cok ? in.q[u] : z, tq);
+    unpack_bf16x8(cok ? in.k[u] : z, tk);
+    unpack_bf16x8(cok ? in.g[u] : z, tg);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       qv[8 * u + e] = tq[e];
@@ -91,8 +124,7 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
   const bool gate_given = a.flags & FLAG_GATE_GIVEN;
   const float rq = norm ? sqrtf(sq + L2_EPS) : 1.0f, rk = norm ? sqrtf(sk + L2_EPS) : 1.0f;
   const float iq = ok ? 1.0f / rq : 0.f, ik = ok ? 1.0f / rk : 0.f;
-  // with the gate given, A_log and dt_bias may be absent and are not read
-  const float al = gate_given ? 0.f : expf(a.A_log[h]);
+  const float al = gate_given ? 0.f : expf(in.A_log);
 #pragma unroll
   for (int c = 0; c < CPT; c += 4) {
     float gg[4];
@@ -101,10 +133,8 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
       float gn;
       if (gate_given)
         gn = fminf(fmaxf(gv[c + e], a.lb), 0.f);
-      else {
-        const float db = a.dt_bias[(size_t)h * kd + c0l + c + e];
-        gn = a.lb * fsigmoid(al * (gv[c + e] + (cok ? db : 0.f)));
-      }
+      else
+        gn = a.lb * fsigmoid(al * (gv[c + e] + (cok ? in.db[c + e] : 0.f)));
       gg[e] = ok ? gn * LOG2E : 0.f;
     }
     *reinterpret_cast<float4*>(sQn + i * QP + CPT * part + c) =
@@ -114,7 +144,7 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
     *reinterpret_cast<float4*>(sG + i * QP + CPT * part + c) = make_float4(gg[0], gg[1], gg[2], gg[3]);
   }
   if (part == 0) {
-    const float rb = bf2f(a.beta[(size_t)row * a.H + h]);
+    const float rb = bf2f(in.beta);
     sBeta[i] = ok ? ((a.flags & FLAG_BETA_GIVEN) ? rb : sigmoidf(rb)) : 0.f;
     sRq[i] = rq;
     sRk[i] = rk;
@@ -150,10 +180,13 @@ __device__ void prep_chunk(const BwdArgs& a, int64_t c0, int L, int h, float* sQ
 // ---------------------------------------------------------------------------
 // kda_bwd_prep_kernel: per (chunk, head), the chunk factors in fp32.  8 waves:
 // wave (w, p) = (wave % 4, wave / 4) owns row block w and the column blocks
-// (or channel tiles) of parity p.
+// (or channel tiles) of parity p.  Persistent: workgroup b takes items b,
+// b + grid, ... and loads each next item's inputs while it works on the
+// current one (its LDS allows one workgroup per CU).
 // ---------------------------------------------------------------------------
 constexpr int NTP = 512;
 constexpr int PREP_FLOATS = 3 * CH * QP + 2 * CH * MP + 3 * CH + NTP;
+constexpr int PREP_WGS = 256;  // one per CU
 
 template <bool FULL>
 __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
@@ -169,190 +202,224 @@ __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
   float* sTmp = sRk + CH;
 
   const int H = a.H;
-  const int64_t gch = blockIdx.x / H;
-  const int h = blockIdx.x - (int)gch * H;
-  if (gch >= total_chunks(a.map)) return;
-  int64_t c0;
-  int L;
-  chunk_of(a.map, gch, c0, L);
-  float* br = a.br + (size_t)blockIdx.x * BWD_REC_FLOATS;
+  const int64_t n_items = total_chunks(a.map) * H;
+  auto geometry = [&](int64_t item, int64_t& c0, int& L, int& h) {
+    const int64_t gch = item / H;
+    h = (int)(item - gch * H);
+    chunk_of(a.map, gch, c0, L);
+  };
+  KDA_TIMER_DECL
+  KDA_TIMER_MARK(0);
+  PrepIn<NTP> in;
+  int64_t item = blockIdx.x;
+  int L = 0;  // the current item's token count
+  if (item < n_items) {
+    int64_t c0;
+    int h;
+    geometry(item, c0, L, h);
+    prep_load<NTP, FULL>(a, c0, L, h, in);
+  }
+  // Wait for the first item's loads here.  The loop's own wait for its
+  // inputs then only has to cover the loads issued in the previous iteration,
+  // not the record stores issued after them (a vmcnt wait is in order).
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  for (; item < n_items; item += gridDim.x) {
+    float* br = a.br + (size_t)item * BWD_REC_FLOATS;
 
-  prep_chunk<NTP, FULL>(a, c0, L, h, sQn, sKn, sG, sBeta, sRq, sRk, sTmp);
+    prep_chunk<NTP, FULL>(a, in, L, sQn, sKn, sG, sBeta, sRq, sRk, sTmp);
+    KDA_TIMER_MARK(1);
+    // the next item's inputs, while this one is worked on
+    int Ln = 0;
+    if (item + gridDim.x < n_items) {
+      int64_t c0n;
+      int hn;
+      geometry(item + gridDim.x, c0n, Ln, hn);
+      prep_load<NTP, FULL>(a, c0n, Ln, hn, in);
+    }
+    KDA_TIMER_MARK(2);
 
-  const int tid = threadIdx.x;
-  const int wv = tid >> 6;
-  const int w = wv & 3;
-  const int p = wv >> 2;
-  const int lane = tid & 63;
-  const int tl = lane & 15;
-  const int gq = lane >> 4;
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6;
+    const int w = wv & 3;
+    const int p = wv >> 2;
+    const int lane = tid & 63;
+    const int tl = lane & 15;
+    const int gq = lane >> 4;
 
-  // ---- KK and A_qk, row block w, column blocks b of parity p.  Reference
-  // token r between i and j: the last token of block b (b < w), else the
-  // first of w.  Blocks above the diagonal are zero.
-#pragma unroll
-  for (int bb = 0; bb < 2; ++bb) {
-    const int b = 2 * bb + p;
-    if (b > w) {
-#pragma unroll
+    // ---- KK and A_qk, row block w, column blocks b of parity p.  Reference
+    // token r between i and j: the last token of block b (b < w), else the
+    // first of w.  Blocks above the diagonal are zero.
+  #pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int b = 2 * bb + p;
+      if (b > w) {
+  #pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int i = 16 * w + 4 * gq + ii, j = 16 * b + tl;
+          sKK[i * MP + j] = 0.f;
+          br[BR_KK + i * CH + j] = 0.f;
+        }
+        // A_qk^T tile (rows block b, contraction block w) is above the diagonal: zero
+        store_hl4(br + BR_AQKT, CH * CH, frag_tt(16 * b + tl, 16 * w + 4 * gq), 0.f, 0.f, 0.f, 0.f);
+        continue;
+      }
+      const int r = (b < w) ? 16 * b + 15 : 16 * w;
+      f32x4 ak = zero4(), aq = zero4();
+      // 16x16x16 hi/lo MFMAs, contraction over channels 16t + 4gq + 0..3
+  #pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int c = 16 * t + 4 * gq;
+        const float4 kx = ld4(sKn + (16 * w + tl) * QP + c), qx = ld4(sQn + (16 * w + tl) * QP + c);
+        const float4 gx = ld4(sG + (16 * w + tl) * QP + c);
+        const float4 ky = ld4(sKn + (16 * b + tl) * QP + c), gy = ld4(sG + (16 * b + tl) * QP + c);
+        const float4 gr = ld4(sG + r * QP + c);
+        float fx[4], yb[4];
+  #pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          fx[s] = fexp2(el(gx, s) - el(gr, s));
+          yb[s] = el(ky, s) * fexp2(el(gr, s) - el(gy, s));
+        }
+        const HL4 y = hl4(yb[0], yb[1], yb[2], yb[3]);
+        ak = mfma_hl(hl4(kx.x * fx[0], kx.y * fx[1], kx.z * fx[2], kx.w * fx[3]), y, ak);
+        aq = mfma_hl(hl4(qx.x * fx[0], qx.y * fx[1], qx.z * fx[2], qx.w * fx[3]), y, aq);
+      }
+      float qk4[4];
+  #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int i = 16 * w + 4 * gq + ii, j = 16 * b + tl;
-        sKK[i * MP + j] = 0.f;
-        br[BR_KK + i * CH + j] = 0.f;
+        const float kk = (b < w || j < i) ? ak[ii] : 0.f;
+        qk4[ii] = (b < w || j <= i) ? aq[ii] : 0.f;
+        sKK[i * MP + j] = kk;
+        br[BR_KK + i * CH + j] = kk;
       }
-      // A_qk^T tile (rows block b, contraction block w) is above the diagonal: zero
-      store_hl4(br + BR_AQKT, CH * CH, frag_tt(16 * b + tl, 16 * w + 4 * gq), 0.f, 0.f, 0.f, 0.f);
-      continue;
-    }
-    const int r = (b < w) ? 16 * b + 15 : 16 * w;
-    f32x4 ak = zero4(), aq = zero4();
-    // 16x16x16 hi/lo MFMAs, contraction over channels 16t + 4gq + 0..3
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int c = 16 * t + 4 * gq;
-      const float4 kx = ld4(sKn + (16 * w + tl) * QP + c), qx = ld4(sQn + (16 * w + tl) * QP + c);
-      const float4 gx = ld4(sG + (16 * w + tl) * QP + c);
-      const float4 ky = ld4(sKn + (16 * b + tl) * QP + c), gy = ld4(sG + (16 * b + tl) * QP + c);
-      const float4 gr = ld4(sG + r * QP + c);
-      float fx[4], yb[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        fx[s] = fexp2(el(gx, s) - el(gr, s));
-        yb[s] = el(ky, s) * fexp2(el(gr, s) - el(gy, s));
-      }
-      const HL4 y = hl4(yb[0], yb[1], yb[2], yb[3]);
-      ak = mfma_hl(hl4(kx.x * fx[0], kx.y * fx[1], kx.z * fx[2], kx.w * fx[3]), y, ak);
-      aq = mfma_hl(hl4(qx.x * fx[0], qx.y * fx[1], qx.z * fx[2], qx.w * fx[3]), y, aq);
-    }
-    float qk4[4];
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int i = 16 * w + 4 * gq + ii, j = 16 * b + tl;
-      const float kk = (b < w || j < i) ? ak[ii] : 0.f;
-      qk4[ii] = (b < w || j <= i) ? aq[ii] : 0.f;
-      sKK[i * MP + j] = kk;
-      br[BR_KK + i * CH + j] = kk;
-    }
-    // scale A_qk^T[j][i]: rows j = 16b + tl, contraction i = 16w + 4gq + ii
-    store_hl4(br + BR_AQKT, CH * CH, frag_tt(16 * b + tl, 16 * w + 4 * gq), a.scale * qk4[0], a.scale * qk4[1],
-              a.scale * qk4[2], a.scale * qk4[3]);
-  }
-  __syncthreads();
-
-  // ---- T = (I + diag(beta) KK)^-1.  Diagonal 16x16 blocks by forward
-  // substitution (waves with p = 0; lane tl owns column tl); waves with p = 1
-  // zero the upper blocks.
-  if (p == 0) {
-    const int j = tl;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float acc = (i == j) ? 1.f : 0.f;
-      const float bi = sBeta[16 * w + i];
-#pragma unroll
-      for (int m = 0; m < i; ++m) acc -= bi * sKK[(16 * w + i) * MP + 16 * w + m] * x[m];
-      x[i] = acc;
-    }
-    if (gq == 0) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sT[(16 * w + i) * MP + 16 * w + j] = x[i];
-    }
-  } else {
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (b > w) {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) sT[(16 * w + 4 * gq + ii) * MP + 16 * b + tl] = 0.f;
-      }
-  }
-  __syncthreads();
-  // off-diagonal blocks by diagonals: T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb,
-  // one 16 x 16 block per block row and level (waves with p = 0)
-#pragma unroll
-  for (int d = 1; d < 4; ++d) {
-    if (p == 0 && w >= d) {
-      const int aa = w, bb = w - d;
-      f32x4 X = zero4();
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (c < bb || c >= aa) continue;
-        const float ba = sBeta[16 * aa + tl];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int kap = 16 * c + 4 * gq + s;
-          X = mfma_f32(ba * sKK[(16 * aa + tl) * MP + kap], sT[kap * MP + 16 * bb + tl], X);
-        }
-      }
-      f32x4 res = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s) res = mfma_f32(-sT[(16 * aa + tl) * MP + 16 * aa + 4 * gq + s], X[s], res);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) sT[(16 * aa + 4 * gq + ii) * MP + 16 * bb + tl] = res[ii];
+      // scale A_qk^T[j][i]: rows j = 16b + tl, contraction i = 16w + 4gq + ii
+      store_hl4(br + BR_AQKT, CH * CH, frag_tt(16 * b + tl, 16 * w + 4 * gq), a.scale * qk4[0], a.scale * qk4[1],
+                a.scale * qk4[2], a.scale * qk4[3]);
     }
     __syncthreads();
-  }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = 4 * (tid + NTP * u);
-    *reinterpret_cast<float4*>(br + BR_T + e) = ld4(sT + (e >> 6) * MP + (e & 63));
-  }
+    KDA_TIMER_MARK(3);
 
-  // ---- W = Tb KG, row block w, channel tiles n of parity p; contraction over tokens j < 16w + 16
-  {
-    float tb[4][4];  // Tb[16w + tl][16 jb + 4 gq + s]
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int kap = 16 * jb + 4 * gq + s;
-        tb[jb][s] = sT[(16 * w + tl) * MP + kap] * sBeta[kap];
+    // ---- T = (I + diag(beta) KK)^-1.  Diagonal 16x16 blocks by forward
+    // substitution (waves with p = 0; lane tl owns column tl); waves with p = 1
+    // zero the upper blocks.
+    if (p == 0) {
+      const int j = tl;
+      float x[16];
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float acc = (i == j) ? 1.f : 0.f;
+        const float bi = sBeta[16 * w + i];
+  #pragma unroll
+        for (int m = 0; m < i; ++m) acc -= bi * sKK[(16 * w + i) * MP + 16 * w + m] * x[m];
+        x[i] = acc;
       }
-#pragma unroll
-    for (int n4 = 0; n4 < 4; ++n4) {
-      const int n = 2 * n4 + p;
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        if (jb > w) continue;
-        const int c = 16 * n + tl;
-        const float* kp = sKn + (16 * jb + 4 * gq) * QP + c;
-        const float* gp = sG + (16 * jb + 4 * gq) * QP + c;
-        acc = mfma_hl(hl4(tb[jb][0], tb[jb][1], tb[jb][2], tb[jb][3]),
-                      hl4(kp[0] * fexp2(gp[0]), kp[QP] * fexp2(gp[QP]), kp[2 * QP] * fexp2(gp[2 * QP]),
-                          kp[3 * QP] * fexp2(gp[3 * QP])),
-                      acc);
+      if (gq == 0) {
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) sT[(16 * w + i) * MP + 16 * w + j] = x[i];
       }
-      // -W^T[k][i]: rows k = 16n + tl, contraction i = 16w + 4gq + ii
-      store_hl4(br + BR_WT, CH * KD, frag_ct(16 * n + tl, 16 * w + 4 * gq), -acc[0], -acc[1], -acc[2], -acc[3]);
+    } else {
+  #pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (b > w) {
+  #pragma unroll
+          for (int ii = 0; ii < 4; ++ii) sT[(16 * w + 4 * gq + ii) * MP + 16 * b + tl] = 0.f;
+        }
     }
-  }
+    __syncthreads();
+    // off-diagonal blocks by diagonals: T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb,
+    // one 16 x 16 block per block row and level (waves with p = 0)
+  #pragma unroll
+    for (int d = 1; d < 4; ++d) {
+      if (p == 0 && w >= d) {
+        const int aa = w, bb = w - d;
+        f32x4 X = zero4();
+  #pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (c < bb || c >= aa) continue;
+          const float ba = sBeta[16 * aa + tl];
+  #pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int kap = 16 * c + 4 * gq + s;
+            X = mfma_f32(ba * sKK[(16 * aa + tl) * MP + kap], sT[kap * MP + 16 * bb + tl], X);
+          }
+        }
+        f32x4 res = zero4();
+  #pragma unroll
+        for (int s = 0; s < 4; ++s) res = mfma_f32(-sT[(16 * aa + tl) * MP + 16 * aa + 4 * gq + s], X[s], res);
+  #pragma unroll
+        for (int ii = 0; ii < 4; ++ii) sT[(16 * aa + 4 * gq + ii) * MP + 16 * bb + tl] = res[ii];
+      }
+      __syncthreads();
+    }
+  #pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = 4 * (tid + NTP * u);
+      *reinterpret_cast<float4*>(br + BR_T + e) = ld4(sT + (e >> 6) * MP + (e & 63));
+    }
+    KDA_TIMER_MARK(4);
 
-  // ---- Kt (thread: token tid / 8, 16 channels), QG^T (thread: channel tid / 4,
-  // 16 tokens), exp(G_L), beta
-  {
-    const int i = tid >> 3;
-    const int c8 = 16 * (tid & 7);
-#pragma unroll
-    for (int c = c8; c < c8 + 16; c += 4) {
-      const float4 kn = ld4(sKn + i * QP + c), gg = ld4(sG + i * QP + c);
-      const float4 gl = ld4(sG + (CH - 1) * QP + c);
-      float4 kt;
-      kt.x = kn.x * fexp2(gl.x - gg.x); kt.y = kn.y * fexp2(gl.y - gg.y);
-      kt.z = kn.z * fexp2(gl.z - gg.z); kt.w = kn.w * fexp2(gl.w - gg.w);
-      store_hl4(br + BR_KT, CH * KD, frag_tc(i, c), kt.x, kt.y, kt.z, kt.w);
+    // ---- W = Tb KG, row block w, channel tiles n of parity p; contraction over tokens j < 16w + 16
+    {
+      float tb[4][4];  // Tb[16w + tl][16 jb + 4 gq + s]
+  #pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+  #pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int kap = 16 * jb + 4 * gq + s;
+          tb[jb][s] = sT[(16 * w + tl) * MP + kap] * sBeta[kap];
+        }
+  #pragma unroll
+      for (int n4 = 0; n4 < 4; ++n4) {
+        const int n = 2 * n4 + p;
+        f32x4 acc = zero4();
+  #pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          if (jb > w) continue;
+          const int c = 16 * n + tl;
+          const float* kp = sKn + (16 * jb + 4 * gq) * QP + c;
+          const float* gp = sG + (16 * jb + 4 * gq) * QP + c;
+          acc = mfma_hl(hl4(tb[jb][0], tb[jb][1], tb[jb][2], tb[jb][3]),
+                        hl4(kp[0] * fexp2(gp[0]), kp[QP] * fexp2(gp[QP]), kp[2 * QP] * fexp2(gp[2 * QP]),
+                            kp[3 * QP] * fexp2(gp[3 * QP])),
+                        acc);
+        }
+        // -W^T[k][i]: rows k = 16n + tl, contraction i = 16w + 4gq + ii
+        store_hl4(br + BR_WT, CH * KD, frag_ct(16 * n + tl, 16 * w + 4 * gq), -acc[0], -acc[1], -acc[2], -acc[3]);
+      }
     }
-    const int k = tid >> 2;
-    const int i0 = 16 * (tid & 3);
-#pragma unroll
-    for (int ib = i0; ib < i0 + 16; ib += 4) {
-      float q4[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) q4[u] = a.scale * sQn[(ib + u) * QP + k] * fexp2(sG[(ib + u) * QP + k]);
-      store_hl4(br + BR_QGT, CH * KD, frag_ct(k, ib), q4[0], q4[1], q4[2], q4[3]);
+    KDA_TIMER_MARK(5);
+
+    // ---- Kt (thread: token tid / 8, 16 channels), QG^T (thread: channel tid / 4,
+    // 16 tokens), exp(G_L), beta
+    {
+      const int i = tid >> 3;
+      const int c8 = 16 * (tid & 7);
+  #pragma unroll
+      for (int c = c8; c < c8 + 16; c += 4) {
+        const float4 kn = ld4(sKn + i * QP + c), gg = ld4(sG + i * QP + c);
+        const float4 gl = ld4(sG + (CH - 1) * QP + c);
+        float4 kt;
+        kt.x = kn.x * fexp2(gl.x - gg.x); kt.y = kn.y * fexp2(gl.y - gg.y);
+        kt.z = kn.z * fexp2(gl.z - gg.z); kt.w = kn.w * fexp2(gl.w - gg.w);
+        store_hl4(br + BR_KT, CH * KD, frag_tc(i, c), kt.x, kt.y, kt.z, kt.w);
+      }
+      const int k = tid >> 2;
+      const int i0 = 16 * (tid & 3);
+  #pragma unroll
+      for (int ib = i0; ib < i0 + 16; ib += 4) {
+        float q4[4];
+  #pragma unroll
+        for (int u = 0; u < 4; ++u) q4[u] = a.scale * sQn[(ib + u) * QP + k] * fexp2(sG[(ib + u) * QP + k]);
+        store_hl4(br + BR_QGT, CH * KD, frag_ct(k, ib), q4[0], q4[1], q4[2], q4[3]);
+      }
+      if (tid < KD) br[BR_GL + tid] = fexp2(sG[(CH - 1) * QP + tid]);
+      if (tid < CH) br[BR_BETA + tid] = sBeta[tid];
     }
-    if (tid < KD) br[BR_GL + tid] = fexp2(sG[(CH - 1) * QP + tid]);
-    if (tid < CH) br[BR_BETA + tid] = sBeta[tid];
+    KDA_TIMER_MARK(6);
+    __syncthreads();  // the next item's preparation rewrites the LDS tiles
+    L = Ln;
   }
+  KDA_TIMER_STORE(a.timers);
 }
 
 // ---------------------------------------------------------------------------
@@ -496,6 +563,8 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
     return a.dout + ((size_t)(c0 + (ok ? orow : 0)) * H + h) * a.vd + (ok ? vs + ocol : 0);
   };
 
+  KDA_TIMER_DECL
+  KDA_TIMER_MARK(0);
   DhuOps cur, nxt;
   if (nch > 0) {
     bool ok;
@@ -512,6 +581,7 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
       const uint16_t* dr = dorow_of(cn, ok);
       dhu_load(nxt, a.br + ((size_t)(gfirst + cn) * H + h) * BWD_REC_FLOATS, dr, ok, w, lane, gq);
     }
+    KDA_TIMER_MARK(1);
 
     // dS' of this chunk: fp32 to the checkpoint buffer (unless only the
     // entering gradient is wanted), bf16 hi/lo to LDS
@@ -532,7 +602,9 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
         frag_write4(sSl, 4 * nn + w, 4 * mt + gq, tl, lv);
       }
     store_dot(sO, cur.dob, tid);
+    KDA_TIMER_MARK(2);
     __syncthreads();
+    KDA_TIMER_MARK(3);
 
     // dD rows 16w.. = Kt dS' + (scale A_qk^T) dO.  The B operands come in six
     // groups of four (one per column tile): four k-blocks of dS' hi/lo, then
@@ -589,7 +661,9 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
         frag_write4(sDl, 2 * nn + (w >> 1), 4 * (w & 1) + gq, tl, lv);
       }
     }
+    KDA_TIMER_MARK(4);
     __syncthreads();
+    KDA_TIMER_MARK(5);
 
     // dS = Diag(exp(G_L)) dS' + (scale QG^T) dO + (-W^T) dD; a column tile's six
     // B operands are read one tile ahead
@@ -634,9 +708,13 @@ __global__ void __launch_bounds__(NT, 1) kda_bwd_dhu_kernel(BwdArgs a) {
         }
       }
     }
+    KDA_TIMER_MARK(6);
     __syncthreads();
+    KDA_TIMER_MARK(7);
     cur = nxt;
+    KDA_TIMER_MARK(8);
   }
+  KDA_TIMER_STORE(a.timers);
 
   if (a.dinit) {
     const int kd = a.kd, vd = a.vd;
@@ -700,12 +778,13 @@ hipError_t launch_bwd(const BwdArgs& args, int64_t max_chunks, const BwdShards* 
   if (items > 0) {
     e = hipLaunchKernel(a.kd == KD ? reinterpret_cast<const void*>(&kda_bwd_prep_kernel<true>)
                                     : reinterpret_cast<const void*>(&kda_bwd_prep_kernel<false>),
-                        dim3((unsigned)items), dim3(NTP),
-                        kargs, 0, st);
+                        dim3((unsigned)(items < PREP_WGS ? items : PREP_WGS)), dim3(NTP), kargs, 0, st);
     if (e != hipSuccess) return e;
   }
   if (!sh) {
-    e = launch_dhu(a, st);
+    BwdArgs ad = a;
+    if (ad.timers) ad.timers += (size_t)2 * 16 * items;  // timer builds: after the prep and grad counters
+    e = launch_dhu(ad, st);
   } else {
     BwdArgs a1 = a;  // each shard's own entering gradient, no per-chunk stores
     a1.map = sh->m2;
