@@ -134,11 +134,11 @@ def cpu_baseline_bwd(x, T_sample, heads):
 
     from oracle.grad import oracle_bwd
 
-    sl = lambda t: t[:, :T_sample][:, :, heads].contiguous()  # noqa: E731
+    sl = lambda t: t[:1, :T_sample][:, :, heads].contiguous()  # noqa: E731  (the first batch row)
     gen = torch.Generator().manual_seed(9)
     d_out = torch.randn(1, T_sample, len(heads), x.V, generator=gen).to(torch.bfloat16)
     t0 = time.perf_counter()
-    oracle_bwd(sl(x.q), sl(x.k), sl(x.v), sl(x.raw_gate), x.raw_beta[:, :T_sample][:, :, heads].contiguous(),
+    oracle_bwd(sl(x.q), sl(x.k), sl(x.v), sl(x.raw_gate), x.raw_beta[:1, :T_sample][:, :, heads].contiguous(),
                x.scale, x.A_log[heads], x.dt_bias[heads], x.lower_bound, d_out)
     dt = time.perf_counter() - t0
     ht = T_sample * len(heads)
@@ -339,61 +339,82 @@ def bench_decode(args):
 
 
 def bench_bwd(args):
-    """Backward pass (kda_bwd: the gradients of every input) on the headline
+    """Backward pass (kda_bwd: the gradients of every input) on the --config
     workload, for a bf16 N(0,1) output gradient and an fp32 N(0,1) final-state
     gradient.  Roofline view: the algorithmic HBM bytes of the call are the
     inputs q, k, v, raw_gate, d_out (5 x 128 x 2 B per head-token) and raw_beta
     (2 B), the outputs dq, dk, dv, d_raw_gate (4 x 128 x 2 B) and d_raw_beta
     (2 B), plus the initial state, final-state gradient and initial-state
-    gradient (3 x 64 KiB fp32 per (sequence, head))."""
+    gradient (3 x 64 KiB fp32 per (sequence, head)).  Workloads under 256 MB
+    of those bytes (C2) run cold, as in the forward mode."""
     import torch
 
     import chunked_gated_delta_amd as kda
     import workloads
 
-    x = workloads.c3_headline(T=args.T, H=args.H)
-    x.initial_state = torch.zeros(1, x.H, x.K, x.V, dtype=torch.float32)
+    if args.config == "c3":
+        x = workloads.c3_headline(T=args.T, H=args.H)
+        x.initial_state = torch.zeros(1, x.H, x.K, x.V, dtype=torch.float32)
+    elif args.config == "c2":
+        x = workloads.c2_tp_share()
+    else:
+        x = workloads.c4_varlen()
     dev = torch.device("cuda:0")
-    d = lambda t: t.to(dev)  # noqa: E731
-    q, k, v, g, b, al, dt, init = (d(t) for t in (x.q, x.k, x.v, x.raw_gate, x.raw_beta, x.A_log, x.dt_bias,
-                                                  x.initial_state))
+    d = lambda t: None if t is None else t.to(dev)  # noqa: E731
+    q, k, v, g, b, al, dt, init, cu = (d(t) for t in (x.q, x.k, x.v, x.raw_gate, x.raw_beta, x.A_log,
+                                                      x.dt_bias, x.initial_state, x.cu_seqlens))
     gen = torch.Generator().manual_seed(9)
-    d_out = d(torch.randn(1, x.T, x.H, x.V, generator=gen).to(torch.bfloat16))
-    d_fin = d(torch.randn(1, x.H, x.K, x.V, generator=gen))
+    d_out = d(torch.randn(x.B, x.T, x.H, x.V, generator=gen).to(torch.bfloat16))
+    d_fin = d(torch.randn(x.N, x.H, x.K, x.V, generator=gen))
     dq, dk, dg = torch.empty_like(q), torch.empty_like(k), torch.empty_like(g)
     dv, db = torch.empty_like(v), torch.empty_like(b)
     dA, ddt, dinit = torch.empty_like(al), torch.empty_like(dt), torch.empty_like(init)
-    ws = torch.empty(kda.kda_bwd_workspace_size(x.T, x.H, 1), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kda.kda_bwd_workspace_size(x.B * x.T, x.H, x.N), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
+    ht = x.B * x.T * x.H
+    alg = ht * (9 * 128 * 2 + 2 * 2) + 3 * x.N * x.H * STATE_BYTES
+    cold = alg < (256 << 20)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if cold else None
+    evict = (lambda: flush.zero_()) if cold else (lambda: None)  # noqa: E731
     ms = timed(lambda: kda.kda_bwd(q, k, v, g, b, x.scale, d_out, dq, dk, dv, dg, db, dA, ddt, ws, al, dt,
                                    x.lower_bound, initial_state=init, d_final=d_fin, d_initial_state=dinit,
-                                   stream=sh), args.steps, args.warmup, stream)
+                                   cu_seqlens=cu, stream=sh), args.steps, args.warmup, stream, setup=evict)
     ms_reuse = None
     if not args.no_reuse:
         # the same gradients on the records a forward call left in this workspace
         out, fin = torch.empty_like(v), torch.empty_like(init)
-        # (the backward's factor record is written over the forward's records, so
-        # every timed call gets a fresh forward first, outside its events)
+
+        def forward_first():
+            # the backward's factor record is written over the forward's records,
+            # so every timed call gets a fresh forward first, outside its events
+            kda.kda_fwd_ex(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, init, fin, cu,
+                           flags=kda.FLAG_KEEP_RECORDS, stream=sh)
+            evict()
+
         ms_reuse = timed(lambda: kda.kda_bwd_ex(q, k, v, g, b, x.scale, d_out, dq, dk, dv, dg, db, dA, ddt, ws,
                                                 al, dt, x.lower_bound, initial_state=init, d_final=d_fin,
-                                                d_initial_state=dinit, flags=kda.FLAG_REUSE_RECORDS, stream=sh),
-                         args.steps, args.warmup, stream,
-                         setup=lambda: kda.kda_fwd_ex(q, k, v, g, b, x.scale, out, ws, al, dt, x.lower_bound, init,
-                                                      fin, flags=kda.FLAG_KEEP_RECORDS, stream=sh))
-    ht = x.T * x.H
-    alg = ht * (9 * 128 * 2 + 2 * 2) + 3 * x.H * STATE_BYTES
+                                                d_initial_state=dinit, cu_seqlens=cu,
+                                                flags=kda.FLAG_REUSE_RECORDS, stream=sh),
+                         args.steps, args.warmup, stream, setup=forward_first)
     gbs = alg / (ms / 1e3) / 1e9
+    headline = args.config == "c3" and (x.T, x.H) == (32768, 96)
+    workload = {"c3": f"kda_bwd B=1 T={x.T} H={x.H} K=V=128 chunk=64 lower_bound=-5",
+                "c2": "kda_bwd B=2 T=4096 H=12 K=V=128 (one TP8 rank's share of H=96) lower_bound=-5, "
+                      "initial state, run cold (MALL flushed between launches)",
+                "c4": f"kda_bwd varlen: 16 packed sequences of U[1, 8192] tokens ({x.B * x.T} in all), H=32, "
+                      "K=V=128, lower_bound=-5, per-sequence initial states"}[args.config]
     print(json.dumps({
         "metric": "KDA backward (all input gradients) head-tokens/s", "value": ht / (ms / 1e3),
         "ms_reusing_forward_records": ms_reuse,
         "unit": "head-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "dtype": "fp32 compute, bf16 io", "data": "synthetic",
-        "config": {"workload": f"kda_bwd B=1 T={x.T} H={x.H} K=V=128 chunk=64 lower_bound=-5, "
-                               "output and final-state gradients given"},
+        "config": {"workload": workload + ", output and final-state gradients given",
+                   "B": x.B, "T": x.T, "H": x.H, "N": x.N},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg,
-                     "traffic": measured_traffic("bwd") if (x.T, x.H) == (32768, 96) else None},
+                     "traffic": measured_traffic("bwd") if headline else None},
+        "cold": cold,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_bwd(x, 256, [0, 1]),
     }), flush=True)
 

@@ -746,8 +746,20 @@ __global__ void __launch_bounds__(NTR) kda_bwd_reduce_kernel(BwdArgs a) {
   const int t = threadIdx.x;
   const int col = t % (KD + 1);
   const int rr = t / (KD + 1);
+  const float* src = a.part + (size_t)h * (KD + 1) + col;
+  const size_t stride = (size_t)4 * H * (KD + 1);  // four chunks on
   float acc = 0.f;
-  for (int64_t g = rr; g < nch; g += 4) acc += a.part[((size_t)g * H + h) * (KD + 1) + col];
+  int64_t g = rr;
+  // eight loads in flight, then added in chunk order (the sum's order is fixed)
+  constexpr int U = 8;
+  for (; g + 4 * (U - 1) < nch; g += 4 * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[(size_t)g * H * (KD + 1) + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc += v[u];
+  }
+  for (; g < nch; g += 4) acc += src[(size_t)g * H * (KD + 1)];
   red[t] = acc;
   __syncthreads();
   if (rr == 0) {
