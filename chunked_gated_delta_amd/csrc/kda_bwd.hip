@@ -254,11 +254,7 @@ __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
       const int b = 2 * bb + p;
       if (b > w) {
   #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int i = 16 * w + 4 * gq + ii, j = 16 * b + tl;
-          sKK[i * MP + j] = 0.f;
-          br[BR_KK + i * CH + j] = 0.f;
-        }
+        for (int ii = 0; ii < 4; ++ii) sKK[(16 * w + 4 * gq + ii) * MP + 16 * b + tl] = 0.f;
         // A_qk^T tile (rows block b, contraction block w) is above the diagonal: zero
         store_hl4(br + BR_AQKT, CH * CH, frag_tt(16 * b + tl, 16 * w + 4 * gq), 0.f, 0.f, 0.f, 0.f);
         continue;
@@ -290,7 +286,6 @@ __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
         const float kk = (b < w || j < i) ? ak[ii] : 0.f;
         qk4[ii] = (b < w || j <= i) ? aq[ii] : 0.f;
         sKK[i * MP + j] = kk;
-        br[BR_KK + i * CH + j] = kk;
       }
       // scale A_qk^T[j][i]: rows j = 16b + tl, contraction i = 16w + 4gq + ii
       store_hl4(br + BR_AQKT, CH * CH, frag_tt(16 * b + tl, 16 * w + 4 * gq), a.scale * qk4[0], a.scale * qk4[1],
@@ -352,9 +347,10 @@ __global__ void __launch_bounds__(NTP, 1) kda_bwd_prep_kernel(BwdArgs a) {
       __syncthreads();
     }
   #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 2; ++u) {  // T and KK (zero on and above the diagonal) to the record, 16 bytes a lane
       const int e = 4 * (tid + NTP * u);
       *reinterpret_cast<float4*>(br + BR_T + e) = ld4(sT + (e >> 6) * MP + (e & 63));
+      *reinterpret_cast<float4*>(br + BR_KK + e) = ld4(sKK + (e >> 6) * MP + (e & 63));
     }
     KDA_TIMER_MARK(4);
 
