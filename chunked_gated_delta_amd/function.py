@@ -75,8 +75,9 @@ def kda_chunk(q, k, v, raw_gate, raw_beta, A_log, dt_bias, *, scale=None, lower_
 
     ``reuse_records`` runs the forward in a backward-sized workspace and keeps it until
     the backward, which then skips rebuilding the chunk records (KDA_FLAG_REUSE_RECORDS).
-    It trades memory for time: the workspace (about 0.43 MB per chunk and head, 21 GB at
-    T = 32768, H = 96) stays allocated from the forward to the backward.
+    It trades memory for time: the workspace (about 0.35 MB per chunk and head, 17 GB at
+    T = 32768, H = 96) stays allocated from the forward to the backward, which uses the
+    records up (a second backward would need the forward again).
     """
     if scale is None:
         scale = q.shape[-1] ** -0.5
