@@ -595,7 +595,8 @@ def main():
     ap.add_argument("--T", type=int, default=32768)
     ap.add_argument("--H", type=int, default=96)
     ap.add_argument("--config", choices=["c3", "c2", "c4"], default="c3",
-                    help="forward workload: c3 headline (default), c2 one TP8 rank's share, c4 packed varlen")
+                    help="workload of the forward (and of --bwd): c3 headline (default), c2 one TP8 rank's "
+                         "share, c4 packed varlen")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true", help="skip the loaded-clock probe")
     ap.add_argument("--cpu-heads", type=int, default=96)
