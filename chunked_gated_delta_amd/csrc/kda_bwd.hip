@@ -15,12 +15,12 @@
 //
 // Kernels, after the forward's intra-chunk kernel and the checkpointing
 // inter-chunk kernel (entering states S0 and D of every chunk):
-//   kda_bwd_prep_kernel    per (chunk, head): fp32 T, A_kk / beta, A_qk, W, Kt, QG, exp(G_L)
+//   kda_bwd_prep_kernel    per (chunk, head), persistent: fp32 T, A_kk / beta, A_qk, W, Kt, QG, exp(G_L)
 //   kda_bwd_dhu_kernel     per (sequence, head, V half): the reverse recurrence -> dS', dD
 //   kda_bwd_grad_kernel    per (chunk, head): dq, dk, dv, d raw_gate, d raw_beta, partials
 //   kda_bwd_reduce_kernel  per head: dA_log and d dt_bias from the per-chunk partials
-// Arithmetic is fp32 throughout: fp32 MFMA 16x16x4, or bf16 MFMA 16x16x32 with
-// every fp32 operand split into a bf16 hi/lo pair (3 passes; 2 where the other
+// Arithmetic is fp32 throughout: fp32 MFMA 16x16x4, or bf16 MFMA (16x16x32 and
+// 16x16x16) with every fp32 operand split into a bf16 hi/lo pair (3 passes; 2 where the other
 // side is an exact bf16 input), which keeps about 16 significant bits per
 // operand.  Exponents are kept in log2 units and every exp(G_i - G_j) factor
 // is split at a reference token between i and j (16-token sub-chunks), so no
