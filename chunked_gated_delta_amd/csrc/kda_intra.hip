@@ -109,6 +109,20 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8]) {
   return __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// A store to the chunk record.  Non-temporal in the two-launch schedule, where
+// the next kernel reads every record back from HBM anyway (C3 forward 2.666 ->
+// 2.624 ms); plain in the single-launch schedule, whose chains read the
+// records through the producer's L2.
+template <bool FUSED, typename T>
+__device__ __forceinline__ void rec_store(T* p, T v) {
+  if constexpr (FUSED)
+    *p = v;
+  else
+    __builtin_nontemporal_store(v, p);
+}
+
 }  // namespace
 
 // The chunk table, A_log and the record base are also passed as separate
@@ -432,7 +446,7 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
     sFac[FAC_F20 * KD + tid] = fexp2(P[2] - P[1]);
     sFac[FAC_F30 * KD + tid] = fexp2(P[3] - P[1]);
     sFac[FAC_F31 * KD + tid] = fexp2(P[3] - P[2]);
-    gGL[tid] = fexp2(P[4]);
+    rec_store<FUSED>(&gGL[tid], fexp2(P[4]));
   }
   __syncthreads();
   KDA_TIMER_MARK(3);
@@ -480,7 +494,7 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
     split_bf16x8(yv, kEh[kb], kEl[kb]);
     qLF[kb] = to_bf16x8(qv);
     split_bf16x8(rv, krh, krl);
-    *reinterpret_cast<f16x8*>(gQG + frag_tc(ti, 32 * kb + 8 * gq)) = qg;
+    rec_store<FUSED>(reinterpret_cast<f16x8*>(gQG + frag_tc(ti, 32 * kb + 8 * gq)), qg);
     // (K^ exp(G_L - G))^T hi/lo and (K^ exp(G))^T: f16 x 1 products summed in
     // fp32 are exact, so these transposes are exact
 #pragma unroll
@@ -493,8 +507,8 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
       const f16x4 h4 = {(_Float16)th[0], (_Float16)th[1], (_Float16)th[2], (_Float16)th[3]};
       const f16x4 l4 = {(_Float16)tlo[0], (_Float16)tlo[1], (_Float16)tlo[2], (_Float16)tlo[3]};
       const f16x4 g4 = {(_Float16)tg[0], (_Float16)tg[1], (_Float16)tg[2], (_Float16)tg[3]};
-      *reinterpret_cast<f16x4*>(gKTH + frag_ct(cc, 16 * w + 4 * gq)) = h4;
-      *reinterpret_cast<f16x4*>(gKTL + frag_ct(cc, 16 * w + 4 * gq)) = l4;
+      rec_store<FUSED>(reinterpret_cast<f16x4*>(gKTH + frag_ct(cc, 16 * w + 4 * gq)), h4);
+      rec_store<FUSED>(reinterpret_cast<f16x4*>(gKTL + frag_ct(cc, 16 * w + 4 * gq)), l4);
       *reinterpret_cast<f16x4*>(sKG + cc * TP + 16 * w + 4 * gq) = g4;
     }
     if (w < 3) {
@@ -612,14 +626,14 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
       f16x4 q4;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) q4[ii] = (_Float16)((16 * b + 4 * gq + ii <= ti) ? aqk[ii] : 0.0f);
-      *reinterpret_cast<f16x4*>(gAQK + frag_tt(ti, 16 * b + 4 * gq)) = q4;
+      rec_store<FUSED>(reinterpret_cast<f16x4*>(gAQK + frag_tt(ti, 16 * b + 4 * gq)), q4);
       if (w == 3 && it == 0) publish(5);  // A_33
     }
     // zero blocks above the diagonal; rows 0..31 skip tokens 32..63, a whole
     // record fragment that the reader never loads
     for (int b = w + 1; b < (w < 2 ? 2 : 4); ++b) {
       const f16x4 z4 = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
-      *reinterpret_cast<f16x4*>(gAQK + frag_tt(ti, 16 * b + 4 * gq)) = z4;
+      rec_store<FUSED>(reinterpret_cast<f16x4*>(gAQK + frag_tt(ti, 16 * b + 4 * gq)), z4);
     }
     // T_ww for w < 3 (T_33 is the role-0 wave's, below).  This wave wrote A_ww
     // above and LDS operations of one wave complete in order.
@@ -679,8 +693,8 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
         const f32x2 r = {t[2 * p] - __uint_as_float(hb[p] << 16), t[2 * p + 1] - __uint_as_float(hb[p] & 0xffff0000u)};
         lb[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
       }
-      *reinterpret_cast<uint2*>(gTBH + frag_tt(i, 16 * w + 4 * gq)) = make_uint2(hb[0], hb[1]);
-      *reinterpret_cast<uint2*>(gTBL + frag_tt(i, 16 * w + 4 * gq)) = make_uint2(lb[0], lb[1]);
+      rec_store<FUSED>(reinterpret_cast<u32x2*>(gTBH + frag_tt(i, 16 * w + 4 * gq)), u32x2{hb[0], hb[1]});
+      rec_store<FUSED>(reinterpret_cast<u32x2*>(gTBL + frag_tt(i, 16 * w + 4 * gq)), u32x2{lb[0], lb[1]});
     };
     if (w == 3) wait_tag(6);
     f32x4 Tc[4];
@@ -768,7 +782,7 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
     for (int nn = 0; nn < 2; ++nn) {
       const f16x4 w4 = {(_Float16)(-acc[nn][0]), (_Float16)(-acc[nn][1]), (_Float16)(-acc[nn][2]),
                         (_Float16)(-acc[nn][3])};
-      *reinterpret_cast<f16x4*>(gNW + frag_tc(16 * m + tl, 32 * w + 16 * nn + 4 * gq)) = w4;
+      rec_store<FUSED>(reinterpret_cast<f16x4*>(gNW + frag_tc(16 * m + tl, 32 * w + 16 * nn + 4 * gq)), w4);
     }
   }
   KDA_TIMER_MARK(8);
