@@ -75,7 +75,7 @@ def oracle_fwd(q, k, v, raw_gate, raw_beta, scale, A_log, dt_bias, lower_bound,
     A_log fp32 [H]; dt_bias fp32 [H, K]; initial_state fp32 [N, H, K, V] or None;
     cu_seqlens int32 [N+1] or None (then N = B sequences of length T).
     heads: optional list of head indices to evaluate (default: all).
-    Returns (out fp64 [B*T, nh, V], final fp64 [N, nh, K, V] or None).
+    Returns (out fp64 [B*T, nh, V], final fp64 [N, nh, K, V] ([N, nh, V, K] with STATE_VK) or None).
     """
     B, T, H, K = q.shape
     V = v.shape[-1]
@@ -95,7 +95,9 @@ def oracle_fwd(q, k, v, raw_gate, raw_beta, scale, A_log, dt_bias, lower_bound,
     al, dt = _f32(A_log), _f32(dt_bias)
     init = None if initial_state is None else _f32(initial_state)
     out = np.empty((B * T, nh, V), dtype=np.float64)
-    fin = np.empty((N, nh, K, V), dtype=np.float64) if want_final else None
+    # the C routine writes each final state in the layout the flags name: [V][K] with STATE_VK
+    fin_shape = (N, nh, V, K) if flags & STATE_VK else (N, nh, K, V)
+    fin = np.empty(fin_shape, dtype=np.float64) if want_final else None
     ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
     rc = _lib().kda_oracle_fwd(ptr(qb), ptr(kb), ptr(vb), ptr(gb), ptr(bb), float(scale),
                                ptr(al), ptr(dt), float(lower_bound), ptr(init), ptr(cu),
