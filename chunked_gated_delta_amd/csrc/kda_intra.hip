@@ -111,16 +111,19 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8]) {
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// A store to the chunk record.  Non-temporal in the two-launch schedule, where
-// the next kernel reads every record back from HBM anyway (C3 forward 2.666 ->
-// 2.624 ms); plain in the single-launch schedule, whose chains read the
-// records through the producer's L2.
-template <bool FUSED, typename T>
+// A store to the chunk record.  Non-temporal (NT) when the call's record area
+// is too large to stay in the Infinity Cache, so that the next kernel reads
+// every record back from HBM anyway (B=1, T=32768, H=96 forward 2.652 ->
+// 2.610 ms); plain when it fits (B=2, T=4096, H=12: 139 MB of records, 0.228
+// -> 0.190 ms cold, the inter kernel then reading them from the cache) and in
+// the single-launch schedule, whose chains read the records through the
+// producer's L2.
+template <bool NT, typename T>
 __device__ __forceinline__ void rec_store(T* p, T v) {
-  if constexpr (FUSED)
-    *p = v;
-  else
+  if constexpr (NT)
     __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
 }
 
 }  // namespace
@@ -144,7 +147,7 @@ __device__ __forceinline__ void rec_store(T* p, T v) {
 // 64..127 of q and k zero (so they add nothing to any norm, dot product or
 // record entry) and their gate inputs zero (a finite decay that multiplies
 // only those zero channels); the record layout is that of K = 128.
-template <bool GATE_GIVEN, bool FUSED, int KIN = KD>
+template <bool GATE_GIVEN, bool FUSED, int KIN = KD, bool NT = false>
 __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restrict__ cu,
                                             const int32_t* __restrict__ choff, const float* __restrict__ A_log,
                                             char* __restrict__ recs, char* smem, int first, int stride, int* claim,
@@ -446,7 +449,7 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
     sFac[FAC_F20 * KD + tid] = fexp2(P[2] - P[1]);
     sFac[FAC_F30 * KD + tid] = fexp2(P[3] - P[1]);
     sFac[FAC_F31 * KD + tid] = fexp2(P[3] - P[2]);
-    rec_store<FUSED>(&gGL[tid], fexp2(P[4]));
+    rec_store<NT>(&gGL[tid], fexp2(P[4]));
   }
   __syncthreads();
   KDA_TIMER_MARK(3);
@@ -494,7 +497,7 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
     split_bf16x8(yv, kEh[kb], kEl[kb]);
     qLF[kb] = to_bf16x8(qv);
     split_bf16x8(rv, krh, krl);
-    rec_store<FUSED>(reinterpret_cast<f16x8*>(gQG + frag_tc(ti, 32 * kb + 8 * gq)), qg);
+    rec_store<NT>(reinterpret_cast<f16x8*>(gQG + frag_tc(ti, 32 * kb + 8 * gq)), qg);
     // (K^ exp(G_L - G))^T hi/lo and (K^ exp(G))^T: f16 x 1 products summed in
     // fp32 are exact, so these transposes are exact
 #pragma unroll
@@ -507,8 +510,8 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
       const f16x4 h4 = {(_Float16)th[0], (_Float16)th[1], (_Float16)th[2], (_Float16)th[3]};
       const f16x4 l4 = {(_Float16)tlo[0], (_Float16)tlo[1], (_Float16)tlo[2], (_Float16)tlo[3]};
       const f16x4 g4 = {(_Float16)tg[0], (_Float16)tg[1], (_Float16)tg[2], (_Float16)tg[3]};
-      rec_store<FUSED>(reinterpret_cast<f16x4*>(gKTH + frag_ct(cc, 16 * w + 4 * gq)), h4);
-      rec_store<FUSED>(reinterpret_cast<f16x4*>(gKTL + frag_ct(cc, 16 * w + 4 * gq)), l4);
+      rec_store<NT>(reinterpret_cast<f16x4*>(gKTH + frag_ct(cc, 16 * w + 4 * gq)), h4);
+      rec_store<NT>(reinterpret_cast<f16x4*>(gKTL + frag_ct(cc, 16 * w + 4 * gq)), l4);
       *reinterpret_cast<f16x4*>(sKG + cc * TP + 16 * w + 4 * gq) = g4;
     }
     if (w < 3) {
@@ -626,14 +629,14 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
       f16x4 q4;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) q4[ii] = (_Float16)((16 * b + 4 * gq + ii <= ti) ? aqk[ii] : 0.0f);
-      rec_store<FUSED>(reinterpret_cast<f16x4*>(gAQK + frag_tt(ti, 16 * b + 4 * gq)), q4);
+      rec_store<NT>(reinterpret_cast<f16x4*>(gAQK + frag_tt(ti, 16 * b + 4 * gq)), q4);
       if (w == 3 && it == 0) publish(5);  // A_33
     }
     // zero blocks above the diagonal; rows 0..31 skip tokens 32..63, a whole
     // record fragment that the reader never loads
     for (int b = w + 1; b < (w < 2 ? 2 : 4); ++b) {
       const f16x4 z4 = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
-      rec_store<FUSED>(reinterpret_cast<f16x4*>(gAQK + frag_tt(ti, 16 * b + 4 * gq)), z4);
+      rec_store<NT>(reinterpret_cast<f16x4*>(gAQK + frag_tt(ti, 16 * b + 4 * gq)), z4);
     }
     // T_ww for w < 3 (T_33 is the role-0 wave's, below).  This wave wrote A_ww
     // above and LDS operations of one wave complete in order.
@@ -693,8 +696,8 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
         const f32x2 r = {t[2 * p] - __uint_as_float(hb[p] << 16), t[2 * p + 1] - __uint_as_float(hb[p] & 0xffff0000u)};
         lb[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
       }
-      rec_store<FUSED>(reinterpret_cast<u32x2*>(gTBH + frag_tt(i, 16 * w + 4 * gq)), u32x2{hb[0], hb[1]});
-      rec_store<FUSED>(reinterpret_cast<u32x2*>(gTBL + frag_tt(i, 16 * w + 4 * gq)), u32x2{lb[0], lb[1]});
+      rec_store<NT>(reinterpret_cast<u32x2*>(gTBH + frag_tt(i, 16 * w + 4 * gq)), u32x2{hb[0], hb[1]});
+      rec_store<NT>(reinterpret_cast<u32x2*>(gTBL + frag_tt(i, 16 * w + 4 * gq)), u32x2{lb[0], lb[1]});
     };
     if (w == 3) wait_tag(6);
     f32x4 Tc[4];
@@ -782,7 +785,7 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
     for (int nn = 0; nn < 2; ++nn) {
       const f16x4 w4 = {(_Float16)(-acc[nn][0]), (_Float16)(-acc[nn][1]), (_Float16)(-acc[nn][2]),
                         (_Float16)(-acc[nn][3])};
-      rec_store<FUSED>(reinterpret_cast<f16x4*>(gNW + frag_tc(16 * m + tl, 32 * w + 16 * nn + 4 * gq)), w4);
+      rec_store<NT>(reinterpret_cast<f16x4*>(gNW + frag_tc(16 * m + tl, 32 * w + 16 * nn + 4 * gq)), w4);
     }
   }
   KDA_TIMER_MARK(8);
@@ -809,14 +812,14 @@ __device__ __forceinline__ void intra_items(IntraArgs a, const int32_t* __restri
 
 namespace {
 
-template <bool GATE_GIVEN, int KIN>
+template <bool GATE_GIVEN, int KIN, bool NT>
 __global__ void __launch_bounds__(NTHREADS, 2)
     kda_intra_kernel(IntraArgs a, const int32_t* __restrict__ cu, const int32_t* __restrict__ choff,
                      const float* __restrict__ A_log, char* __restrict__ recs) {
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   const IntraFused none{};
-  intra_items<GATE_GIVEN, false, KIN>(a, cu, choff, A_log, recs, smem, (int)blockIdx.x, (int)gridDim.x, a.claim,
-                                      none);
+  intra_items<GATE_GIVEN, false, KIN, NT>(a, cu, choff, A_log, recs, smem, (int)blockIdx.x, (int)gridDim.x,
+                                          a.claim, none);
 }
 
 }  // namespace
@@ -927,6 +930,11 @@ hipError_t launch_fused(const IntraArgs& iargs, const ChainArgs& cargs, const Fu
   return hipLaunchKernel(fn, dim3((unsigned)(2 * cus)), dim3(NTHREADS), kargs, 0, st);
 }
 
+// Record areas up to this size are written with plain stores and stay in the
+// 256 MB Infinity Cache until the inter kernel reads them; larger ones would
+// only evict each other and go out non-temporally.
+constexpr size_t kRecordsCachedBytes = (size_t)160 << 20;
+
 hipError_t launch_intra(const IntraArgs& args, int64_t max_chunks, hipStream_t st) {
   // persistent grid: two resident workgroups per CU (LDS and register budget)
   int dev = 0, cus = 0;
@@ -943,10 +951,19 @@ hipError_t launch_intra(const IntraArgs& args, int64_t max_chunks, hipStream_t s
   char* recs = a.rec;
   void* kargs[] = {(void*)&a, (void*)&cu, (void*)&choff, (void*)&alog, (void*)&recs};
   const bool given = a.flags & FLAG_GATE_GIVEN;
-  const void* fn = a.kd == KD ? (given ? reinterpret_cast<const void*>(&kda_intra_kernel<true, KD>)
-                                       : reinterpret_cast<const void*>(&kda_intra_kernel<false, KD>))
-                              : (given ? reinterpret_cast<const void*>(&kda_intra_kernel<true, 64>)
-                                       : reinterpret_cast<const void*>(&kda_intra_kernel<false, 64>));
+  // records that fit the Infinity Cache are stored plainly, larger areas non-temporally
+  const bool nt = (size_t)items * REC_BYTES > kRecordsCachedBytes;
+  const void* fn;
+  if (a.kd == KD)
+    fn = given ? (nt ? reinterpret_cast<const void*>(&kda_intra_kernel<true, KD, true>)
+                     : reinterpret_cast<const void*>(&kda_intra_kernel<true, KD, false>))
+               : (nt ? reinterpret_cast<const void*>(&kda_intra_kernel<false, KD, true>)
+                     : reinterpret_cast<const void*>(&kda_intra_kernel<false, KD, false>));
+  else
+    fn = given ? (nt ? reinterpret_cast<const void*>(&kda_intra_kernel<true, 64, true>)
+                     : reinterpret_cast<const void*>(&kda_intra_kernel<true, 64, false>))
+               : (nt ? reinterpret_cast<const void*>(&kda_intra_kernel<false, 64, true>)
+                     : reinterpret_cast<const void*>(&kda_intra_kernel<false, 64, false>));
   return hipLaunchKernel(fn, dim3((unsigned)grid),
                          dim3(NTHREADS), kargs, 0, st);
 }
